@@ -1,0 +1,233 @@
+#!/usr/bin/env python3
+"""Benchmark of the position-independent KV-reuse hot path on one MI355X.
+
+One step = one batch through the whole path: plan + gather/re-rotate the
+prefix (pic_assemble), then the query prefill of every layer
+(pic_query_prefill: rotate and append the new tokens, attention over prefix +
+new rows).  Inputs (pool, span tables, every layer's q/k/v) are resident in
+HBM before the timed region.  Steps cycle through pre-generated batch layouts
+over the same pool.
+
+Prints one JSON line.  `value` is the whole step's attention throughput
+(algorithmic attention FLOPs of a step / step time, so assembly and prologue
+time count against it); per-kernel rates, latency percentiles, the roofline of
+the dominant kernel and the CPU-oracle baseline ride along.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--variant M|F]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "assembly GB/s + query-prefill attn TFLOP/s (% roofline), p99 µs/request"
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
+FP32_PEAK_TFLOPS = 157.3        # MI355X fp32 vector
+KERNEL_GATHER, KERNEL_PROLOGUE, KERNEL_ATTN, KERNEL_PLAN = 0, 1, 2, 3
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=40)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="turborag_b16")
+    ap.add_argument("--variant", default="M", choices=["M", "F"])
+    ap.add_argument("--layouts", type=int, default=8, help="pre-generated batch layouts to cycle through")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="time budget of the oracle sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def percentile(xs, q):
+    """Nearest-rank percentile."""
+    s = sorted(xs)
+    k = max(0, min(len(s) - 1, int(-(-q * len(s) // 100)) - 1))
+    return s[k]
+
+
+def cpu_baseline(wl, pool, dw, budget_s: float):
+    """Time the fp64 oracle on a bounded sample of the same workload: request
+    0, one layer after another until the time budget is spent."""
+    import numpy as np
+    import threadpoolctl
+    from oracle import pic_oracle as orc
+    import workloads as W
+    r = wl.requests[0]
+    m = wl.model
+    planned = orc.plan_spans([tuple(int(x) for x in s) for s in r.spans], wl.pool.chunk_orig)
+    pos_new = orc.new_token_positions(planned, r.n_new, r.new_pos)
+    nb = int(wl.new_ptr()[0])
+    flops = 0
+    spent = 0.0
+    layers = 0
+    n_visible = 0
+    for l in range(m.layers):
+        ck, cv = {}, {}
+        for c in sorted(set(int(c) for c in r.spans[:, 0])):
+            k, v = W.chunk_kv(wl, pool, c, [l])
+            ck[c], cv[c] = k.numpy(), v.numpy()
+        q, kn, vn = dw.layer_inputs(l)
+        sl = slice(nb, nb + r.n_new)
+        qn, kk, vv = (t[sl].float().cpu().double().numpy() for t in (q, kn, vn))
+        t0 = time.perf_counter()
+        kp, vp, pp = orc.assemble(ck, cv, [tuple(int(x) for x in s) for s in r.spans], m.theta, m.dtype,
+                                  chunk_orig=wl.pool.chunk_orig)
+        orc.query_prefill_layer(kp[0], vp[0], pp, qn, kk, vv, pos_new, m.theta, m.dtype, m.kv_heads)
+        spent += time.perf_counter() - t0
+        layers += 1
+        if l == 0:
+            rows = np.concatenate([pp, pos_new])
+            n_visible = int(sum(int((rows <= p).sum()) for p in pos_new))
+        flops += 4 * m.head_dim * m.q_heads * n_visible
+        if spent >= budget_s:
+            break
+    threads = max((d.get("num_threads", 1) for d in threadpoolctl.threadpool_info()), default=1)
+    return {"value": flops / spent / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"request 0 of {wl.name}, {layers} of {m.layers} layers (gather, re-rotation and "
+                      f"attention in fp64 numpy), {spent:.1f} s; host has {os.cpu_count()} logical CPUs"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the path would shard "
+              f"requests or kv heads across GPUs with no exchange, see the design notes)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import workloads as W
+    from workloads.device import open_workload
+    from position_independent_kv_pic_amd import VARIANT_FUSED, VARIANT_MATERIALIZED
+
+    assert torch.cuda.is_available(), "bench.py needs a ROCm GPU"
+    variant = VARIANT_FUSED if args.variant == "F" else VARIANT_MATERIALIZED
+    wls = [W.get(args.workload, layout=i) for i in range(args.layouts)]
+    wl = wls[0]
+    m = wl.model
+    log(f"[bench] workload {wl.name}: batch {wl.batch}, layers {m.layers}, rows {wl.rows_total}")
+    dw = open_workload(wl)
+    sess = dw.session
+    cap = max(w.rows_total for w in wls)
+    sess.ensure_capacity(cap)
+    n_new = max(w.n_new_total for w in wls)
+    assert all(w.n_new_total == n_new for w in wls), "layouts must share the new-token count"
+    inputs = [dw.layer_inputs(l) for l in range(m.layers)]
+    outs = [torch.empty_like(inputs[l][0]) for l in range(m.layers)]
+    tables = [(w.span_ptr(), w.spans_flat(), w.new_ptr(), w.new_pos_flat()) for w in wls]
+    stream = torch.cuda.current_stream()
+    plan = sess.plan
+    plan_flag = 1 if variant == VARIANT_FUSED else 0
+
+    def step(i):
+        sp, spans, npt, npos = tables[i % len(tables)]
+        plan.assemble(sp, spans, npt, npos, sess.asm_k, sess.asm_v, sess.capacity, plan_flag, stream)
+        for l in range(m.layers):
+            q, k, v = inputs[l]
+            plan.query_prefill(l, q, k, v, outs[l], variant, stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    log(f"[bench] warmup done ({args.warmup} steps)")
+
+    # timed region: K steps, per-step events on the launch stream
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev[0].record(stream)
+    for i in range(args.steps):
+        step(i)
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    step_ms = [ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps)]
+    total_ms = ev[0].elapsed_time(ev[-1])
+    log(f"[bench] timed {args.steps} steps: {total_ms:.2f} ms (host wall {wall * 1e3:.2f} ms)")
+
+    # per-kernel durations: a second pass with the library's event brackets on
+    plan.timing(True)
+    plan.timing_reset()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    kt = {k: plan.timing_read(k) for k in (KERNEL_GATHER, KERNEL_PROLOGUE, KERNEL_ATTN, KERNEL_PLAN)}
+    plan.timing(False)
+
+    asm_bytes = sum(W.assembly_bytes(w) for w in (wls * args.steps)[:args.steps]) / args.steps
+    attn_flops = sum(W.attention_flops(w) for w in (wls * args.steps)[:args.steps]) / args.steps
+    ms_step = total_ms / args.steps
+    n_g, t_g = kt[KERNEL_GATHER]
+    n_a, t_a = kt[KERNEL_ATTN]
+    n_p, t_p = kt[KERNEL_PROLOGUE]
+    gather_ms = t_g / max(n_g, 1)
+    attn_ms = t_a / max(n_a, 1)
+    asm_gbps = asm_bytes / (gather_ms * 1e-3) / 1e9 if n_g else None
+    attn_launch_flops = attn_flops / m.layers
+    attn_tflops = attn_launch_flops / (attn_ms * 1e-3) / 1e12 if n_a else None
+    value = attn_flops / (ms_step * 1e-3) / 1e12
+    peak = BF16_PEAK_TFLOPS if m.dtype == "bf16" else FP32_PEAK_TFLOPS
+
+    res = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": m.dtype,
+        "data": "synthetic",
+        "config": {"workload": wl.name, "model_shape": f"L{m.layers} Hq{m.q_heads} Hkv{m.kv_heads} d{m.head_dim}",
+                   "batch": wl.batch, "prefix_rows_per_step": wl.prefix_rows_total,
+                   "new_tokens_per_step": wl.n_new_total, "variant": args.variant,
+                   "layouts": args.layouts, "parallelism": "none (1 GPU)"},
+        "assembly_GBps": None if asm_gbps is None else round(asm_gbps, 1),
+        "assembly_frac_hbm": None if asm_gbps is None else round(asm_gbps / HBM_PEAK_GBPS, 4),
+        "attention_TFLOPs": None if attn_tflops is None else round(attn_tflops, 2),
+        "attention_frac_peak": None if attn_tflops is None else round(attn_tflops / peak, 4),
+        "p50_us_per_request": round(percentile(step_ms, 50) * 1e3, 1),
+        "p99_us_per_request": round(percentile(step_ms, 99) * 1e3, 1),
+        "amortized_us_per_request": round(ms_step * 1e3 / wl.batch, 2),
+        "kernel_ms": {"gather": round(gather_ms, 4), "attention_per_layer": round(attn_ms, 4),
+                      "prologue_per_layer": round(t_p / max(n_p, 1), 4),
+                      "plan": round(kt[KERNEL_PLAN][1] / max(kt[KERNEL_PLAN][0], 1), 4)},
+        "roofline": {"bound": "mfma", "achieved": None if attn_tflops is None else round(attn_tflops, 2),
+                     "peak": peak, "unit": "TFLOP/s",
+                     "frac": None if attn_tflops is None else round(attn_tflops / peak, 4),
+                     "traffic": None, "kernel": "attention_bf16_kernel (+ split merge)",
+                     "per_launch_flops": int(attn_launch_flops)},
+        "roofline_assembly": {"bound": "hbm", "achieved": None if asm_gbps is None else round(asm_gbps, 1),
+                              "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                              "frac": None if asm_gbps is None else round(asm_gbps / HBM_PEAK_GBPS, 4),
+                              "traffic": None, "kernel": "gather_kernel", "per_launch_bytes": int(asm_bytes)},
+        "not_ttft": "assembly + per-layer attention only; no projections, MLP or sampling",
+    }
+    if variant == VARIANT_FUSED:
+        res["roofline_assembly"]["achieved"] = None
+        res["assembly_GBps"] = None
+        res["roofline_assembly"]["note"] = "fused variant gathers inside attention; no gather kernel"
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle sample")
+        res["cpu_baseline"] = cpu_baseline(wl, dw.pool, dw, args.cpu_seconds)
+    else:
+        res["cpu_baseline"] = None
+    print(json.dumps(res), flush=True)
+    dw.close()
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,249 @@
+/*
+ * pic.h - position-independent KV-cache reuse on AMD Instinct MI355X (gfx950).
+ *
+ * C ABI of libpic.so.  Plain pointers and sizes only.  Every device buffer is
+ * owned by the caller; the library owns only its opaque handles and their
+ * device-side planning tables.  All GPU work is enqueued on the stream the
+ * caller passes (a hipStream_t given as void*, NULL = the default stream);
+ * the library never synchronises the device implicitly except where a call's
+ * comment says so.
+ *
+ * Terms (the pages' notation):
+ *   chunk c     a document or chunk whose per-layer K/V cache C_c was computed
+ *               offline, tokens 0 .. len_c-1 (CoinRAG page, section 2.1: one
+ *               forward pass of the whole chunk; TurboRAG review page,
+ *               pipeline of Figure 3-b; SemPIC page: compiled document caches).
+ *   span        (c, s, e, target): the tokens s..e (e INCLUSIVE) of chunk c,
+ *               placed so that token s lands at position `target` (CoinRAG
+ *               page, section 2.2: retrieval returns (b_i, s_i, e_i); section
+ *               2.3: Rot(C_b[s:e]; Delta_i) concatenated into C_ctx).
+ *   prefix      the spans of one request gathered in table order (C_ctx).
+ *   new tokens  the request's fresh tokens (query, inline segments) that are
+ *               prefilled against the prefix: KV_M(q; C_ctx).
+ *
+ * Conventions: positions are 0-based.  Cached keys are stored rotated by
+ * standard half-split RoPE (pairs (k, k + d/2), omega_k = theta^(-2k/d)) at
+ * their original position orig_c + t.  A span is moved by rotating each of its
+ * keys by delta = target - (orig_c + s); values are copied.  A new token at
+ * position P sees every row, cached or new, whose position is <= P: this is
+ * the TurboRAG review page's independent attention (Figure 4: the query sees
+ * all chunks and itself, chunks never see each other) and the SemPIC page's
+ * causal interleave of compiled and inline caches.
+ *
+ * Errors: every call validates its arguments on the host before it enqueues
+ * anything; on an error nothing is written and a message is available from
+ * pic_last_error() (thread-local, valid until the next call on that thread).
+ * A failure reported by the HIP runtime after a launch returns PIC_EDEVICE and
+ * leaves the plan unusable (PIC_ESTATE afterwards).
+ */
+#ifndef PIC_H
+#define PIC_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PIC_OK = 0,
+  PIC_EINVAL = -1,       /* malformed argument (null pointer, bad shape, bad table) */
+  PIC_ERANGE = -2,       /* index or size out of range (chunk id, span bounds, capacity) */
+  PIC_ENOMEM = -3,       /* host or device allocation for library-owned tables failed */
+  PIC_EDEVICE = -4,      /* the HIP runtime reported an error */
+  PIC_ESTATE = -5,       /* handle in the wrong state (released, not assembled, failed) */
+  PIC_EALIGN = -6,       /* a device pointer is not 16-byte aligned */
+  PIC_EUNSUPPORTED = -7  /* valid request this build does not implement */
+} pic_status;
+
+typedef enum { PIC_F32 = 0, PIC_BF16 = 1 } pic_dtype;
+
+/* Model shape.  head_dim even, a multiple of 16, at most 256; q_heads a
+ * multiple of kv_heads (query head h reads kv head h / (q_heads / kv_heads)). */
+typedef struct {
+  int32_t layers;
+  int32_t q_heads;
+  int32_t kv_heads;
+  int32_t head_dim;
+  double rope_theta;
+  int32_t dtype;          /* pic_dtype: storage and I/O type of every tensor */
+} pic_model;
+
+/* One span of a request's span table.  e is inclusive.  target is the new
+ * position of token s, or PIC_TARGET_AUTO: right after the previous span of
+ * the same request (0 for the first).  With the prompt cache as span 0 and
+ * every other span AUTO this is CoinRAG's Delta_i = |p| + sum_{j<i}(e_j-s_j+1)
+ * (section 2.3, Delta equation; TurboRAG's Reordered Positions). */
+typedef struct {
+  int32_t chunk;
+  int32_t s;
+  int32_t e;
+  int32_t target;
+} pic_span;
+
+#define PIC_TARGET_AUTO (-1)
+
+/* pic_assemble flags */
+#define PIC_ASSEMBLE_PLAN_ONLY 1  /* plan on host and device, gather nothing (variant F) */
+#define PIC_ASSEMBLE_DRY_RUN   2  /* validate and plan on the host only; touch no device */
+
+/* pic_query_prefill variants */
+#define PIC_VARIANT_MATERIALIZED 0  /* read keys/values from the assembled buffers */
+#define PIC_VARIANT_FUSED        1  /* read cached rows from the pool, rotating keys on load */
+
+typedef struct pic_pool pic_pool;
+typedef struct pic_plan pic_plan;
+
+/*
+ * Register a paged chunk-KV pool that already lives in device memory.
+ *
+ * Layout of `pool` (device, caller-owned, never copied or freed): n_pages
+ * pages of page_bytes = layers * 2 * kv_heads * page_tokens * head_dim * s
+ * bytes each (s = 2 for bf16, 4 for f32); inside a page
+ * [layer][0 = K, 1 = V][kv_head][token slot][head_dim], row-major.
+ * Token t of chunk c is in page page_ids[chunk_page_ptr[c] + t / page_tokens]
+ * at slot t % page_tokens.
+ *
+ *   model          shape and dtype (copied)
+ *   pool           device base pointer, 16-byte aligned
+ *   pool_bytes     size of the allocation, >= n_pages * page_bytes
+ *   page_tokens    tokens per page, a power of two in [1, 4096]
+ *   n_pages        number of pages in the allocation
+ *   n_chunks       number of chunk caches
+ *   chunk_len      host int32[n_chunks], each >= 0
+ *   chunk_orig     host int32[n_chunks] original base positions, or NULL (all 0)
+ *   chunk_page_ptr host int32[n_chunks + 1], CSR offsets into page_ids, starting
+ *                  at 0, non-decreasing, with room for ceil(len_c / page_tokens)
+ *                  pages per chunk
+ *   page_ids       host int32[chunk_page_ptr[n_chunks]], each in [0, n_pages)
+ *   out            receives the handle
+ * The host tables are copied; device copies are made on first use.
+ */
+pic_status pic_pool_register(const pic_model* model, void* pool, int64_t pool_bytes,
+                             int32_t page_tokens, int32_t n_pages, int32_t n_chunks,
+                             const int32_t* chunk_len, const int32_t* chunk_orig,
+                             const int32_t* chunk_page_ptr, const int32_t* page_ids,
+                             pic_pool** out);
+
+/* Release a pool handle (not the pool memory).  Plans made from it must be
+ * released first (PIC_ESTATE otherwise).  Synchronises the device if device
+ * tables were made. */
+pic_status pic_pool_release(pic_pool* pool);
+
+/* Create a plan object for batches over `pool`.  Its host and device tables
+ * grow on demand and are reused by later pic_assemble calls. */
+pic_status pic_plan_create(pic_pool* pool, pic_plan** out);
+
+/* Release a plan and its tables.  Synchronises the device. */
+pic_status pic_plan_release(pic_plan* plan);
+
+/*
+ * Plan a batch and gather its prefixes (CoinRAG section 2.3, the C_ctx
+ * equation; TurboRAG's Reordered Positions; SemPIC's hit path: assign final
+ * logical positions and re-rotate the cached keys).
+ *
+ *   batch          number of requests (>= 0)
+ *   span_ptr       host int32[batch + 1], CSR offsets into spans (from 0)
+ *   spans          host pic_span[span_ptr[batch]]; 0 <= s <= e < len_chunk;
+ *                  explicit targets >= 0; every position must fit int32
+ *   new_ptr        host int32[batch + 1], CSR offsets of the new tokens
+ *   new_pos        host int32[new_ptr[batch]] explicit positions, strictly
+ *                  increasing within a request, or NULL: the new tokens of a
+ *                  request then follow its last span (P_j = target_last +
+ *                  len_last + j; j if the request has no spans)
+ *   asm_k, asm_v   device buffers [layers][kv_heads][asm_rows_capacity][head_dim]
+ *                  of the model dtype, 16-byte aligned (may be NULL with DRY_RUN)
+ *   asm_rows_capacity  rows per (layer, kv head) plane
+ *   flags          0, PIC_ASSEMBLE_PLAN_ONLY or PIC_ASSEMBLE_DRY_RUN
+ *   stream         hipStream_t
+ *
+ * Row layout: request b owns rows [row_base_b, row_base_b + prefix_b + n_new_b)
+ * of every plane, row_base_b = sum over earlier requests of (prefix + n_new).
+ * Its prefix rows come first in span-table order (span i, token s_i + t at
+ * row row_base_b + sum_{j<i} n_j + t), followed by the new tokens' rows, which
+ * pic_query_prefill fills layer by layer.  Prefix keys are rotated by their
+ * span's delta in fp32 arithmetic with a phase computed in fp64 and rounded
+ * once to the storage type; a span with delta == 0 is copied bit for bit, as
+ * are all values.  Overlapping or repeated spans are legal and gathered as
+ * often as they appear.  The call replaces the plan's previous batch.
+ */
+pic_status pic_assemble(pic_plan* plan, int32_t batch, const int32_t* span_ptr,
+                        const pic_span* spans, const int32_t* new_ptr, const int32_t* new_pos,
+                        void* asm_k, void* asm_v, int64_t asm_rows_capacity, int32_t flags,
+                        void* stream);
+
+/*
+ * One layer of the query prefill, KV_M(q; C_ctx) (CoinRAG section 2.3, last
+ * equation; TurboRAG: only the query is prefilled online; SemPIC: inline
+ * tokens run through the decoder and interleave with compiled caches under a
+ * causal mask).
+ *
+ *   layer      in [0, layers)
+ *   q          device [n_new_total][q_heads][head_dim], un-rotated
+ *   k_new      device [n_new_total][kv_heads][head_dim], un-rotated
+ *   v_new      device [n_new_total][kv_heads][head_dim]
+ *   out        device [n_new_total][q_heads][head_dim]
+ *   variant    PIC_VARIANT_MATERIALIZED or PIC_VARIANT_FUSED
+ * New tokens are packed in request order (new_ptr of the assemble call).
+ * Steps: rotate q and k_new to the tokens' positions and round them to the
+ * storage type; write k' and v_new into the new-token rows of this layer's
+ * assembled planes (so the planes hold C_ctx (+) KV_M(q; C_ctx) for decoding);
+ * then for every new token j and query head h
+ *   out[j][h] = sum_r softmax_r(<q'_j,h, k_r> / sqrt(d)) v_r
+ * over the request's rows r with pos_r <= pos_j.  Variant FUSED reads the
+ * prefix rows straight from the pool (its plan may come from PLAN_ONLY) and
+ * is implemented for bf16 with head_dim 128; MATERIALIZED needs a full
+ * assemble.  bf16 attention uses bf16 MFMA products with fp32 accumulation
+ * and an fp32 online softmax; f32 attention computes in fp32.
+ */
+pic_status pic_query_prefill(pic_plan* plan, int32_t layer, const void* q, const void* k_new,
+                             const void* v_new, void* out, int32_t variant, void* stream);
+
+/* Host-side description of the plan's current batch. */
+typedef struct {
+  int32_t batch;
+  int32_t n_spans;
+  int64_t prefix_rows;     /* sum of span lengths */
+  int64_t new_rows;        /* new_ptr[batch] */
+  int64_t rows;            /* prefix_rows + new_rows: rows used in each plane */
+  int32_t max_position;    /* largest position of any row */
+  int32_t materialized;    /* 1 if the prefix rows were gathered */
+} pic_plan_summary;
+
+pic_status pic_plan_get_summary(const pic_plan* plan, pic_plan_summary* out);
+
+/* Per-request host arrays of the current batch (any pointer may be NULL):
+ * row_base int64[batch], prefix_rows int32[batch], first new-token position
+ * int32[batch]. */
+pic_status pic_plan_get_requests(const pic_plan* plan, int64_t* row_base, int32_t* prefix_rows,
+                                 int32_t* first_new_pos);
+
+/* Per-span host arrays (any pointer may be NULL): resolved target int32[n_spans],
+ * delta int32[n_spans], first assembled row int64[n_spans]. */
+pic_status pic_plan_get_spans(const pic_plan* plan, int32_t* target, int32_t* delta,
+                              int64_t* first_row);
+
+/* Per-new-token host arrays: position int32[new_rows], assembled row int64[new_rows]. */
+pic_status pic_plan_get_new_tokens(const pic_plan* plan, int32_t* position, int64_t* row);
+
+/* Kernel timing: when enabled, the library brackets its main kernels with HIP
+ * events on the caller's stream.  pic_timing_read synchronises on the last
+ * recorded event and returns the number of launches and their summed
+ * duration in milliseconds for one kernel class since the last reset.
+ * kernel: 0 = assembly gather, 1 = new-token prologue, 2 = attention
+ * (including its split merge), 3 = planning. */
+pic_status pic_timing_enable(pic_plan* plan, int32_t on);
+pic_status pic_timing_read(pic_plan* plan, int32_t kernel, int64_t* launches, double* total_ms);
+pic_status pic_timing_reset(pic_plan* plan);
+
+/* Message of the last failed call on this thread ("" if none). */
+const char* pic_last_error(void);
+
+/* Library version string. */
+const char* pic_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PIC_H */

@@ -1,0 +1,254 @@
+"""ctypes binding of libpic (argument marshalling only).
+
+Buffers are passed as raw device addresses (ints) or as objects with a
+`data_ptr()` method (torch tensors); streams as a raw hipStream_t value or an
+object with a `cuda_stream` attribute.  Nothing here computes any part of the
+method: a missing library raises, it never falls back.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+PIC_F32 = 0
+PIC_BF16 = 1
+TARGET_AUTO = -1
+PLAN_ONLY = 1
+DRY_RUN = 2
+VARIANT_MATERIALIZED = 0
+VARIANT_FUSED = 1
+
+_STATUS = {0: "PIC_OK", -1: "PIC_EINVAL", -2: "PIC_ERANGE", -3: "PIC_ENOMEM", -4: "PIC_EDEVICE",
+           -5: "PIC_ESTATE", -6: "PIC_EALIGN", -7: "PIC_EUNSUPPORTED"}
+
+EXPORTED = (
+    "pic_pool_register", "pic_pool_release", "pic_plan_create", "pic_plan_release",
+    "pic_assemble", "pic_query_prefill", "pic_plan_get_summary", "pic_plan_get_requests",
+    "pic_plan_get_spans", "pic_plan_get_new_tokens", "pic_timing_enable", "pic_timing_read",
+    "pic_timing_reset", "pic_last_error", "pic_version",
+)
+
+
+class PicError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{_STATUS.get(status, status)}: {message}")
+        self.status = status
+        self.name = _STATUS.get(status, str(status))
+
+
+class PicModel(ctypes.Structure):
+    _fields_ = [("layers", ctypes.c_int32), ("q_heads", ctypes.c_int32),
+                ("kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("rope_theta", ctypes.c_double), ("dtype", ctypes.c_int32)]
+
+
+class PicSpan(ctypes.Structure):
+    _fields_ = [("chunk", ctypes.c_int32), ("s", ctypes.c_int32), ("e", ctypes.c_int32),
+                ("target", ctypes.c_int32)]
+
+
+class PicPlanSummary(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("n_spans", ctypes.c_int32),
+                ("prefix_rows", ctypes.c_int64), ("new_rows", ctypes.c_int64),
+                ("rows", ctypes.c_int64), ("max_position", ctypes.c_int32),
+                ("materialized", ctypes.c_int32)]
+
+
+def library_path() -> str:
+    return os.path.join(HERE, "libpic.so")
+
+
+_LIB = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libpic.so (built in-tree by build.py); raise if it is missing."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    path = library_path()
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built; run `python -m position_independent_kv_pic_amd.build`")
+    L = ctypes.CDLL(path)
+    P = ctypes.c_void_p
+    I32 = ctypes.c_int32
+    I64 = ctypes.c_int64
+    pi32 = ctypes.POINTER(ctypes.c_int32)
+    pi64 = ctypes.POINTER(ctypes.c_int64)
+    sig = {
+        "pic_pool_register": [ctypes.POINTER(PicModel), P, I64, I32, I32, I32, pi32, pi32, pi32, pi32,
+                              ctypes.POINTER(P)],
+        "pic_pool_release": [P],
+        "pic_plan_create": [P, ctypes.POINTER(P)],
+        "pic_plan_release": [P],
+        "pic_assemble": [P, I32, pi32, ctypes.POINTER(PicSpan), pi32, pi32, P, P, I64, I32, P],
+        "pic_query_prefill": [P, I32, P, P, P, P, I32, P],
+        "pic_plan_get_summary": [P, ctypes.POINTER(PicPlanSummary)],
+        "pic_plan_get_requests": [P, pi64, pi32, pi32],
+        "pic_plan_get_spans": [P, pi32, pi32, pi64],
+        "pic_plan_get_new_tokens": [P, pi32, pi64],
+        "pic_timing_enable": [P, I32],
+        "pic_timing_read": [P, I32, pi64, ctypes.POINTER(ctypes.c_double)],
+        "pic_timing_reset": [P],
+    }
+    for name, args in sig.items():
+        fn = getattr(L, name)
+        fn.argtypes = args
+        fn.restype = ctypes.c_int
+    L.pic_last_error.argtypes = []
+    L.pic_last_error.restype = ctypes.c_char_p
+    L.pic_version.argtypes = []
+    L.pic_version.restype = ctypes.c_char_p
+    _LIB = L
+    return L
+
+
+def _check(status: int):
+    if status != 0:
+        raise PicError(status, lib().pic_last_error().decode())
+
+
+def _ptr(x) -> Optional[int]:
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return int(x.data_ptr())
+
+
+def _stream(s) -> Optional[int]:
+    if s is None:
+        return None
+    if isinstance(s, int):
+        return s
+    return int(s.cuda_stream)
+
+
+def _i32(a) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(a, dtype=np.int32))
+
+
+def _p32(a: Optional[np.ndarray]):
+    if a is None:
+        return None
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+
+
+def model_struct(layers, q_heads, kv_heads, head_dim, theta, dtype) -> PicModel:
+    dt = {"bf16": PIC_BF16, "f32": PIC_F32}.get(dtype, dtype)
+    return PicModel(int(layers), int(q_heads), int(kv_heads), int(head_dim), float(theta), int(dt))
+
+
+class Pool:
+    """A registered paged chunk-KV pool (the memory stays the caller's)."""
+
+    def __init__(self, model: PicModel, pool, pool_bytes: int, page_tokens: int, n_pages: int,
+                 chunk_len, chunk_page_ptr, page_ids, chunk_orig=None):
+        self.model = model
+        self._keep = (_i32(chunk_len), _i32(chunk_page_ptr), _i32(page_ids),
+                      None if chunk_orig is None else _i32(chunk_orig))
+        cl, cp, pg, co = self._keep
+        h = ctypes.c_void_p()
+        _check(lib().pic_pool_register(ctypes.byref(model), ctypes.c_void_p(_ptr(pool)), int(pool_bytes),
+                                       int(page_tokens), int(n_pages), int(cl.shape[0]), _p32(cl),
+                                       _p32(co), _p32(cp), _p32(pg), ctypes.byref(h)))
+        self.handle = h
+
+    def release(self):
+        if self.handle:
+            _check(lib().pic_pool_release(self.handle))
+            self.handle = None
+
+
+class Plan:
+    """Plan object: assemble batches, then run the per-layer query prefill."""
+
+    def __init__(self, pool: Pool):
+        self.pool = pool
+        h = ctypes.c_void_p()
+        _check(lib().pic_plan_create(pool.handle, ctypes.byref(h)))
+        self.handle = h
+        self.batch = 0
+        self.n_spans = 0
+
+    def release(self):
+        if self.handle:
+            _check(lib().pic_plan_release(self.handle))
+            self.handle = None
+
+    def assemble(self, span_ptr, spans, new_ptr, new_pos=None, asm_k=None, asm_v=None,
+                 capacity: int = 0, flags: int = 0, stream=None):
+        sp = _i32(span_ptr)
+        npt = _i32(new_ptr)
+        tbl = _i32(spans).reshape(-1, 4)
+        arr = (PicSpan * max(1, tbl.shape[0]))()
+        if tbl.shape[0]:
+            ctypes.memmove(arr, tbl.ctypes.data, tbl.nbytes)
+        npos = None if new_pos is None else _i32(new_pos)
+        batch = int(sp.shape[0]) - 1
+        # the C side trusts the CSR ends to match the array lengths
+        if batch < 0 or npt.shape[0] != sp.shape[0]:
+            raise ValueError("span_ptr and new_ptr need batch + 1 entries")
+        if int(sp[-1]) != tbl.shape[0]:
+            raise ValueError(f"span_ptr ends at {int(sp[-1])} but {tbl.shape[0]} spans were given")
+        if npos is not None and int(npt[-1]) != npos.shape[0]:
+            raise ValueError(f"new_ptr ends at {int(npt[-1])} but {npos.shape[0]} positions were given")
+        self._keep = (sp, npt, tbl, arr, npos)
+        _check(lib().pic_assemble(self.handle, batch, _p32(sp), arr, _p32(npt), _p32(npos),
+                                  ctypes.c_void_p(_ptr(asm_k)), ctypes.c_void_p(_ptr(asm_v)),
+                                  int(capacity), int(flags), ctypes.c_void_p(_stream(stream))))
+        self.batch = batch
+        self.n_spans = int(tbl.shape[0])
+
+    def query_prefill(self, layer: int, q, k_new, v_new, out, variant: int = VARIANT_MATERIALIZED,
+                      stream=None):
+        _check(lib().pic_query_prefill(self.handle, int(layer), ctypes.c_void_p(_ptr(q)),
+                                       ctypes.c_void_p(_ptr(k_new)), ctypes.c_void_p(_ptr(v_new)),
+                                       ctypes.c_void_p(_ptr(out)), int(variant),
+                                       ctypes.c_void_p(_stream(stream))))
+
+    def summary(self) -> dict:
+        s = PicPlanSummary()
+        _check(lib().pic_plan_get_summary(self.handle, ctypes.byref(s)))
+        return {f: getattr(s, f) for f, _ in PicPlanSummary._fields_}
+
+    def requests(self):
+        rb = np.zeros(self.batch, np.int64)
+        pr = np.zeros(self.batch, np.int32)
+        fp = np.zeros(self.batch, np.int32)
+        _check(lib().pic_plan_get_requests(self.handle, rb.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
+                                           _p32(pr), _p32(fp)))
+        return rb, pr, fp
+
+    def spans(self):
+        t = np.zeros(self.n_spans, np.int32)
+        d = np.zeros(self.n_spans, np.int32)
+        r = np.zeros(self.n_spans, np.int64)
+        _check(lib().pic_plan_get_spans(self.handle, _p32(t), _p32(d),
+                                        r.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))))
+        return t, d, r
+
+    def new_tokens(self):
+        n = self.summary()["new_rows"]
+        p = np.zeros(n, np.int32)
+        r = np.zeros(n, np.int64)
+        _check(lib().pic_plan_get_new_tokens(self.handle, _p32(p),
+                                             r.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))))
+        return p, r
+
+    def timing(self, enable: bool):
+        _check(lib().pic_timing_enable(self.handle, 1 if enable else 0))
+
+    def timing_read(self, kernel: int):
+        n = ctypes.c_int64()
+        ms = ctypes.c_double()
+        _check(lib().pic_timing_read(self.handle, int(kernel), ctypes.byref(n), ctypes.byref(ms)))
+        return int(n.value), float(ms.value)
+
+    def timing_reset(self):
+        _check(lib().pic_timing_reset(self.handle))

@@ -1,0 +1,593 @@
+// C ABI of libpic: handles, validation, planning upload, kernel launches.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <utility>
+#include <vector>
+
+#include "pic.h"
+#include "pic_kernels.h"
+#include "pic_plan.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+pic_status set_err(pic_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+pic_status set_err(pic_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+pic_status ok() {
+  g_err.clear();
+  return PIC_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+constexpr int kTimedKernels = 4;
+
+}  // namespace
+
+struct pic_pool {
+  pic::PoolInfo info;
+  int n_plans = 0;
+  int device = -1;
+  int32_t* d_page_ids = nullptr;
+};
+
+struct pic_plan {
+  pic_pool* pool = nullptr;
+  pic::HostPlan hp;
+  bool has_batch = false;
+  bool materialized = false;
+  bool failed = false;
+  char* asm_k = nullptr;
+  char* asm_v = nullptr;
+  int64_t cap = 0;
+  int device = -1;
+
+  // device workspace: uploaded tables followed by generated tables
+  char* ws = nullptr;
+  size_t ws_cap = 0;
+  size_t off_spans = 0, off_crow = 0, off_reqs = 0, off_new_pos = 0, off_new_row = 0,
+         off_new_req = 0, off_work = 0, off_omega = 0, blob_bytes = 0;
+  size_t off_pos = 0, off_rowsrc = 0, off_phase_span = 0, off_phase_new = 0, off_qrot = 0,
+         off_opart = 0, off_ml = 0, ws_bytes = 0;
+
+  // pinned staging for the upload, reused once its copy has completed
+  char* staging = nullptr;
+  size_t staging_cap = 0;
+  hipEvent_t staging_ev = nullptr;
+  bool staging_pending = false;
+
+  // optional kernel timing
+  bool timing = false;
+  std::vector<std::pair<hipEvent_t, hipEvent_t>> events[kTimedKernels];
+  size_t used[kTimedKernels] = {0, 0, 0, 0};
+};
+
+namespace {
+
+pic_status device_error(pic_plan* p, hipError_t e, const char* what) {
+  if (p) p->failed = true;
+  return set_err(PIC_EDEVICE, "%s: %s", what, hipGetErrorString(e));
+}
+
+// Bracket one launch with events when timing is on.
+struct Timed {
+  pic_plan* p;
+  int k;
+  hipStream_t s;
+  hipEvent_t stop = nullptr;
+  Timed(pic_plan* plan, int kernel, hipStream_t stream) : p(plan), k(kernel), s(stream) {
+    if (!p->timing) return;
+    auto& v = p->events[k];
+    if (p->used[k] == v.size()) {
+      hipEvent_t a = nullptr, b = nullptr;
+      if (hipEventCreate(&a) != hipSuccess || hipEventCreate(&b) != hipSuccess) {
+        if (a) (void)hipEventDestroy(a);
+        return;
+      }
+      v.emplace_back(a, b);
+    }
+    auto& pr = v[p->used[k]++];
+    (void)hipEventRecord(pr.first, s);
+    stop = pr.second;
+  }
+  ~Timed() {
+    if (stop) (void)hipEventRecord(stop, s);
+  }
+};
+
+pic_status ensure_pool_device(pic_pool* pool) {
+  if (pool->d_page_ids || pool->info.page_ids.empty()) return PIC_OK;
+  size_t bytes = pool->info.page_ids.size() * sizeof(int32_t);
+  hipError_t e = hipMalloc(reinterpret_cast<void**>(&pool->d_page_ids), bytes);
+  if (e != hipSuccess) {
+    pool->d_page_ids = nullptr;
+    return set_err(PIC_ENOMEM, "hipMalloc of the page table failed: %s", hipGetErrorString(e));
+  }
+  e = hipMemcpy(pool->d_page_ids, pool->info.page_ids.data(), bytes, hipMemcpyHostToDevice);
+  if (e != hipSuccess) return set_err(PIC_EDEVICE, "page table upload: %s", hipGetErrorString(e));
+  return PIC_OK;
+}
+
+void layout_workspace(pic_plan* p) {
+  const pic::ModelInfo& m = p->pool->info.m;
+  const pic::HostPlan& hp = p->hp;
+  const size_t half = size_t(m.head_dim) / 2;
+  size_t o = 0;
+  auto take = [&o](size_t bytes) {
+    size_t at = o;
+    o = align256(o + bytes);
+    return at;
+  };
+  p->off_spans = take(hp.spans.size() * sizeof(pic::SpanRec));
+  p->off_crow = take(hp.crow.size() * sizeof(int32_t));
+  p->off_reqs = take(hp.reqs.size() * sizeof(pic::ReqRec));
+  p->off_new_pos = take(hp.new_pos.size() * sizeof(int32_t));
+  p->off_new_row = take(hp.new_row.size() * sizeof(int32_t));
+  p->off_new_req = take(hp.new_req.size() * sizeof(int32_t));
+  p->off_work = take(hp.work.size() * sizeof(pic::AttnWork));
+  p->off_omega = take(half * sizeof(double));
+  p->blob_bytes = o;
+  p->off_pos = take(size_t(hp.rows) * sizeof(int32_t));
+  p->off_rowsrc = take(size_t(hp.rows) * sizeof(int2));
+  p->off_phase_span = take(size_t(hp.n_spans) * half * sizeof(pic::Phase));
+  p->off_phase_new = take(size_t(hp.new_rows) * half * sizeof(pic::Phase));
+  p->off_qrot = take(size_t(hp.new_rows) * m.q_heads * m.head_dim * m.elem_bytes);
+  const size_t nsplit = hp.n_split > 1 ? size_t(hp.n_split) : 0;
+  p->off_opart = take(nsplit * size_t(hp.new_rows) * m.q_heads * m.head_dim * sizeof(float));
+  p->off_ml = take(nsplit * size_t(hp.new_rows) * m.q_heads * sizeof(float2));
+  p->ws_bytes = o;
+}
+
+pic_status ensure_capacity(pic_plan* p) {
+  if (p->ws_bytes > p->ws_cap) {
+    if (p->ws) {
+      hipError_t e = hipDeviceSynchronize();
+      if (e != hipSuccess) return device_error(p, e, "synchronise before growing the workspace");
+      (void)hipFree(p->ws);
+      p->ws = nullptr;
+      p->ws_cap = 0;
+    }
+    size_t want = align256(p->ws_bytes + p->ws_bytes / 4);
+    hipError_t e = hipMalloc(reinterpret_cast<void**>(&p->ws), want);
+    if (e != hipSuccess) {
+      p->ws = nullptr;
+      return set_err(PIC_ENOMEM, "hipMalloc of %zu workspace bytes failed: %s", want,
+                     hipGetErrorString(e));
+    }
+    p->ws_cap = want;
+  }
+  if (p->blob_bytes > p->staging_cap) {
+    if (p->staging_pending) {
+      hipError_t e = hipEventSynchronize(p->staging_ev);
+      if (e != hipSuccess) return device_error(p, e, "wait for the previous plan upload");
+      p->staging_pending = false;
+    }
+    if (p->staging) (void)hipHostFree(p->staging);
+    p->staging = nullptr;
+    p->staging_cap = 0;
+    size_t want = align256(p->blob_bytes + p->blob_bytes / 4);
+    hipError_t e = hipHostMalloc(reinterpret_cast<void**>(&p->staging), want, hipHostMallocDefault);
+    if (e != hipSuccess) {
+      p->staging = nullptr;
+      return set_err(PIC_ENOMEM, "hipHostMalloc of %zu staging bytes failed: %s", want,
+                     hipGetErrorString(e));
+    }
+    p->staging_cap = want;
+  }
+  if (!p->staging_ev) {
+    hipError_t e = hipEventCreateWithFlags(&p->staging_ev, hipEventDisableTiming);
+    if (e != hipSuccess) return device_error(p, e, "create the staging event");
+  }
+  return PIC_OK;
+}
+
+template <typename T>
+void put(char* base, size_t off, const std::vector<T>& v) {
+  if (!v.empty()) std::memcpy(base + off, v.data(), v.size() * sizeof(T));
+}
+
+pic_status check_device(pic_plan* p) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return device_error(nullptr, e, "hipGetDevice");
+  if (p->device < 0) p->device = dev;
+  if (p->device != dev)
+    return set_err(PIC_ESTATE, "plan was created for device %d, current device is %d", p->device, dev);
+  if (p->pool->device < 0) p->pool->device = dev;
+  if (p->pool->device != dev)
+    return set_err(PIC_ESTATE, "pool tables live on device %d, current device is %d", p->pool->device,
+                   dev);
+  return PIC_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pic_last_error(void) { return g_err.c_str(); }
+
+const char* pic_version(void) { return "libpic 0.1 (gfx950)"; }
+
+pic_status pic_pool_register(const pic_model* model, void* pool, int64_t pool_bytes,
+                             int32_t page_tokens, int32_t n_pages, int32_t n_chunks,
+                             const int32_t* chunk_len, const int32_t* chunk_orig,
+                             const int32_t* chunk_page_ptr, const int32_t* page_ids,
+                             pic_pool** out) {
+  if (!out) return set_err(PIC_EINVAL, "out is NULL");
+  *out = nullptr;
+  pic::PoolInfo info;
+  std::string err;
+  pic_status st = pic::build_pool(model, pool, pool_bytes, page_tokens, n_pages, n_chunks, chunk_len,
+                                  chunk_orig, chunk_page_ptr, page_ids, &info, &err);
+  if (st != PIC_OK) return set_err(st, "%s", err.c_str());
+  pic_pool* p = new (std::nothrow) pic_pool;
+  if (!p) return set_err(PIC_ENOMEM, "out of host memory");
+  p->info = std::move(info);
+  *out = p;
+  return ok();
+}
+
+pic_status pic_pool_release(pic_pool* pool) {
+  if (!pool) return set_err(PIC_EINVAL, "pool is NULL");
+  if (pool->n_plans > 0) return set_err(PIC_ESTATE, "%d plans still use this pool", pool->n_plans);
+  if (pool->d_page_ids) {
+    (void)hipDeviceSynchronize();
+    (void)hipFree(pool->d_page_ids);
+  }
+  delete pool;
+  return ok();
+}
+
+pic_status pic_plan_create(pic_pool* pool, pic_plan** out) {
+  if (!out) return set_err(PIC_EINVAL, "out is NULL");
+  *out = nullptr;
+  if (!pool) return set_err(PIC_EINVAL, "pool is NULL");
+  pic_plan* p = new (std::nothrow) pic_plan;
+  if (!p) return set_err(PIC_ENOMEM, "out of host memory");
+  p->pool = pool;
+  pool->n_plans++;
+  *out = p;
+  return ok();
+}
+
+pic_status pic_plan_release(pic_plan* p) {
+  if (!p) return set_err(PIC_EINVAL, "plan is NULL");
+  if (p->ws || p->staging || p->staging_ev) (void)hipDeviceSynchronize();
+  if (p->ws) (void)hipFree(p->ws);
+  if (p->staging) (void)hipHostFree(p->staging);
+  if (p->staging_ev) (void)hipEventDestroy(p->staging_ev);
+  for (auto& v : p->events)
+    for (auto& pr : v) {
+      (void)hipEventDestroy(pr.first);
+      (void)hipEventDestroy(pr.second);
+    }
+  p->pool->n_plans--;
+  delete p;
+  return ok();
+}
+
+pic_status pic_assemble(pic_plan* p, int32_t batch, const int32_t* span_ptr, const pic_span* spans,
+                        const int32_t* new_ptr, const int32_t* new_pos, void* asm_k, void* asm_v,
+                        int64_t asm_rows_capacity, int32_t flags, void* stream) {
+  if (!p) return set_err(PIC_EINVAL, "plan is NULL");
+  if (p->failed) return set_err(PIC_ESTATE, "plan is unusable after a device error");
+  if (flags & ~(PIC_ASSEMBLE_PLAN_ONLY | PIC_ASSEMBLE_DRY_RUN))
+    return set_err(PIC_EINVAL, "unknown flags 0x%x", flags);
+  const bool dry = (flags & PIC_ASSEMBLE_DRY_RUN) != 0;
+  const bool plan_only = (flags & PIC_ASSEMBLE_PLAN_ONLY) != 0;
+  if (asm_rows_capacity < 0) return set_err(PIC_EINVAL, "asm_rows_capacity must be >= 0");
+  if (!dry) {
+    if (!asm_k || !asm_v) return set_err(PIC_EINVAL, "asm_k and asm_v are required");
+    if (!aligned16(asm_k) || !aligned16(asm_v))
+      return set_err(PIC_EALIGN, "assembled buffers must be 16-byte aligned");
+  }
+  const pic::PoolInfo& pi = p->pool->info;
+  pic::HostPlan hp;
+  std::string err;
+  pic_status st = pic::build_plan(pi, batch, span_ptr, spans, new_ptr, new_pos, asm_rows_capacity,
+                                  &hp, &err);
+  if (st != PIC_OK) return set_err(st, "%s", err.c_str());
+  if (pi.m.dtype == PIC_BF16 && pi.m.head_dim == 128)
+    pic::build_attention_work(&hp, pi.m.kv_heads, pi.m.group, pic::kAttnColsPerWG,
+                              pic::kAttnRowsPerTile, /*target_wgs=*/512, /*max_split=*/16,
+                              /*min_tiles_per_split=*/4);
+  if (dry) {
+    p->hp = std::move(hp);
+    p->has_batch = true;
+    p->materialized = false;
+    p->asm_k = p->asm_v = nullptr;
+    p->cap = asm_rows_capacity;
+    return ok();
+  }
+  if (!pic::gather_supported(pi.m.dtype, pi.m.head_dim))
+    return set_err(PIC_EUNSUPPORTED, "head_dim %d is not implemented (64 and 128 are)",
+                   pi.m.head_dim);
+  st = check_device(p);
+  if (st != PIC_OK) return st;
+  st = ensure_pool_device(p->pool);
+  if (st != PIC_OK) return st;
+
+  p->hp = std::move(hp);
+  p->has_batch = false;
+  p->asm_k = static_cast<char*>(asm_k);
+  p->asm_v = static_cast<char*>(asm_v);
+  p->cap = asm_rows_capacity;
+  const pic::HostPlan& h = p->hp;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (batch == 0 || h.rows == 0) {
+    p->has_batch = true;
+    p->materialized = !plan_only;
+    return ok();
+  }
+
+  layout_workspace(p);
+  st = ensure_capacity(p);
+  if (st != PIC_OK) return st;
+  if (p->staging_pending) {
+    hipError_t e = hipEventSynchronize(p->staging_ev);
+    if (e != hipSuccess) return device_error(p, e, "wait for the previous plan upload");
+    p->staging_pending = false;
+  }
+  std::vector<double> omega(size_t(pi.m.head_dim) / 2);
+  for (size_t k = 0; k < omega.size(); ++k)
+    omega[k] = std::pow(pi.m.theta, -2.0 * double(k) / double(pi.m.head_dim));
+  put(p->staging, p->off_spans, h.spans);
+  put(p->staging, p->off_crow, h.crow);
+  put(p->staging, p->off_reqs, h.reqs);
+  put(p->staging, p->off_new_pos, h.new_pos);
+  put(p->staging, p->off_new_row, h.new_row);
+  put(p->staging, p->off_new_req, h.new_req);
+  put(p->staging, p->off_work, h.work);
+  put(p->staging, p->off_omega, omega);
+  {
+    Timed tm(p, 3, s);
+    hipError_t e = hipMemcpyAsync(p->ws, p->staging, p->blob_bytes, hipMemcpyHostToDevice, s);
+    if (e != hipSuccess) return device_error(p, e, "plan upload");
+    e = hipEventRecord(p->staging_ev, s);
+    if (e != hipSuccess) return device_error(p, e, "record the upload event");
+    p->staging_pending = true;
+
+    pic::PlanArgs pa;
+    pa.spans = reinterpret_cast<const pic::SpanRec*>(p->ws + p->off_spans);
+    pa.crow = reinterpret_cast<const int32_t*>(p->ws + p->off_crow);
+    pa.new_pos = reinterpret_cast<const int32_t*>(p->ws + p->off_new_pos);
+    pa.new_row = reinterpret_cast<const int32_t*>(p->ws + p->off_new_row);
+    pa.page_ids = p->pool->d_page_ids;
+    pa.omega = reinterpret_cast<const double*>(p->ws + p->off_omega);
+    pa.n_spans = h.n_spans;
+    pa.n_new = int32_t(h.new_rows);
+    pa.page_shift = pi.page_shift;
+    pa.half_dim = pi.m.head_dim / 2;
+    pa.prefix_rows = h.prefix_rows;
+    pa.pos = reinterpret_cast<int32_t*>(p->ws + p->off_pos);
+    pa.rowsrc = reinterpret_cast<int2*>(p->ws + p->off_rowsrc);
+    pa.phase_span = reinterpret_cast<pic::Phase*>(p->ws + p->off_phase_span);
+    pa.phase_new = reinterpret_cast<pic::Phase*>(p->ws + p->off_phase_new);
+    e = pic::launch_plan(pa, s);
+    if (e != hipSuccess) return device_error(p, e, "plan kernels");
+  }
+  if (!plan_only && h.prefix_rows > 0) {
+    Timed tm(p, 0, s);
+    pic::GatherArgs ga;
+    ga.spans = reinterpret_cast<const pic::SpanRec*>(p->ws + p->off_spans);
+    ga.crow = reinterpret_cast<const int32_t*>(p->ws + p->off_crow);
+    ga.page_ids = p->pool->d_page_ids;
+    ga.phase_span = reinterpret_cast<const pic::Phase*>(p->ws + p->off_phase_span);
+    ga.pool = static_cast<const char*>(pi.base);
+    ga.asm_k = p->asm_k;
+    ga.asm_v = p->asm_v;
+    ga.prefix_rows = h.prefix_rows;
+    ga.cap = p->cap;
+    ga.page_bytes = pi.page_bytes;
+    ga.n_spans = h.n_spans;
+    ga.page_shift = pi.page_shift;
+    ga.page_tokens = pi.page_tokens;
+    ga.layers = pi.m.layers;
+    ga.kv_heads = pi.m.kv_heads;
+    ga.planes_per_block = 8;
+    hipError_t e = pic::launch_gather(pi.m.dtype, pi.m.head_dim, ga, s);
+    if (e != hipSuccess) return device_error(p, e, "gather kernel");
+  }
+  p->has_batch = true;
+  p->materialized = !plan_only;
+  return ok();
+}
+
+pic_status pic_query_prefill(pic_plan* p, int32_t layer, const void* q, const void* k_new,
+                             const void* v_new, void* out, int32_t variant, void* stream) {
+  if (!p) return set_err(PIC_EINVAL, "plan is NULL");
+  if (p->failed) return set_err(PIC_ESTATE, "plan is unusable after a device error");
+  if (!p->has_batch || !p->asm_k)
+    return set_err(PIC_ESTATE, "no assembled batch (call pic_assemble without DRY_RUN first)");
+  const pic::PoolInfo& pi = p->pool->info;
+  const pic::ModelInfo& m = pi.m;
+  if (layer < 0 || layer >= m.layers)
+    return set_err(PIC_ERANGE, "layer %d outside [0, %d)", layer, m.layers);
+  if (variant != PIC_VARIANT_MATERIALIZED && variant != PIC_VARIANT_FUSED)
+    return set_err(PIC_EINVAL, "unknown variant %d", variant);
+  const bool fused = variant == PIC_VARIANT_FUSED;
+  if (!fused && !p->materialized)
+    return set_err(PIC_ESTATE, "the materialised variant needs an assemble without PLAN_ONLY");
+  if (!pic::attention_supported(m.dtype, m.head_dim, fused))
+    return set_err(PIC_EUNSUPPORTED, "attention variant %d is not implemented for dtype %d, head_dim %d",
+                   variant, m.dtype, m.head_dim);
+  const pic::HostPlan& h = p->hp;
+  if (h.new_rows == 0) return ok();
+  if (!q || !k_new || !v_new || !out) return set_err(PIC_EINVAL, "q, k_new, v_new and out are required");
+  if (!aligned16(q) || !aligned16(k_new) || !aligned16(v_new) || !aligned16(out))
+    return set_err(PIC_EALIGN, "q, k_new, v_new and out must be 16-byte aligned");
+  pic_status st = check_device(p);
+  if (st != PIC_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t plane_bytes = p->cap * m.row_bytes;
+  char* kpl = p->asm_k + int64_t(layer) * m.kv_heads * plane_bytes;
+  char* vpl = p->asm_v + int64_t(layer) * m.kv_heads * plane_bytes;
+  {
+    Timed tm(p, 1, s);
+    pic::PrologueArgs pa;
+    pa.q = static_cast<const char*>(q);
+    pa.k_new = static_cast<const char*>(k_new);
+    pa.v_new = static_cast<const char*>(v_new);
+    pa.new_pos = reinterpret_cast<const int32_t*>(p->ws + p->off_new_pos);
+    pa.new_row = reinterpret_cast<const int32_t*>(p->ws + p->off_new_row);
+    pa.phase_new = reinterpret_cast<const pic::Phase*>(p->ws + p->off_phase_new);
+    pa.q_rot = p->ws + p->off_qrot;
+    pa.asm_k = kpl;
+    pa.asm_v = vpl;
+    pa.cap = p->cap;
+    pa.n_new = int32_t(h.new_rows);
+    pa.q_heads = m.q_heads;
+    pa.kv_heads = m.kv_heads;
+    hipError_t e = pic::launch_prologue(m.dtype, m.head_dim, pa, s);
+    if (e != hipSuccess) return device_error(p, e, "prologue kernel");
+  }
+  {
+    Timed tm(p, 2, s);
+    hipError_t e;
+    if (m.dtype == PIC_BF16) {
+      pic::AttnArgs aa;
+      aa.q_rot = reinterpret_cast<const uint16_t*>(p->ws + p->off_qrot);
+      aa.k_plane = reinterpret_cast<const uint16_t*>(kpl);
+      aa.v_plane = reinterpret_cast<const uint16_t*>(vpl);
+      aa.cap = p->cap;
+      aa.pos = reinterpret_cast<const int32_t*>(p->ws + p->off_pos);
+      aa.reqs = reinterpret_cast<const pic::ReqRec*>(p->ws + p->off_reqs);
+      aa.new_pos = reinterpret_cast<const int32_t*>(p->ws + p->off_new_pos);
+      aa.work = reinterpret_cast<const pic::AttnWork*>(p->ws + p->off_work);
+      aa.n_work = int32_t(h.work.size());
+      aa.q_heads = m.q_heads;
+      aa.group = m.group;
+      aa.n_new = int32_t(h.new_rows);
+      aa.n_split = h.n_split;
+      aa.scale_log2 = float(1.4426950408889634 / std::sqrt(double(m.head_dim)));
+      aa.out = static_cast<uint16_t*>(out);
+      aa.opart = reinterpret_cast<float*>(p->ws + p->off_opart);
+      aa.ml = reinterpret_cast<float2*>(p->ws + p->off_ml);
+      aa.pool = static_cast<const char*>(pi.base);
+      aa.rowsrc = reinterpret_cast<const int2*>(p->ws + p->off_rowsrc);
+      aa.phase_span = reinterpret_cast<const pic::Phase*>(p->ws + p->off_phase_span);
+      aa.page_bytes = pi.page_bytes;
+      aa.kv_plane_off = int64_t(layer) * 2 * m.kv_heads * pi.page_tokens * m.row_bytes;
+      aa.v_off = int64_t(m.kv_heads) * pi.page_tokens * m.row_bytes;
+      aa.page_shift = pi.page_shift;
+      aa.page_tokens = pi.page_tokens;
+      aa.kv_heads = m.kv_heads;
+      e = pic::launch_attention_bf16(aa, fused, s);
+    } else {
+      pic::AttnF32Args aa;
+      aa.q_rot = p->ws + p->off_qrot;
+      aa.k_plane = kpl;
+      aa.v_plane = vpl;
+      aa.cap = p->cap;
+      aa.pos = reinterpret_cast<const int32_t*>(p->ws + p->off_pos);
+      aa.reqs = reinterpret_cast<const pic::ReqRec*>(p->ws + p->off_reqs);
+      aa.new_pos = reinterpret_cast<const int32_t*>(p->ws + p->off_new_pos);
+      aa.new_req = reinterpret_cast<const int32_t*>(p->ws + p->off_new_req);
+      aa.n_new = int32_t(h.new_rows);
+      aa.q_heads = m.q_heads;
+      aa.group = m.group;
+      aa.out = static_cast<char*>(out);
+      e = pic::launch_attention_f32(m.head_dim, aa, s);
+    }
+    if (e != hipSuccess) return device_error(p, e, "attention kernel");
+  }
+  return ok();
+}
+
+pic_status pic_plan_get_summary(const pic_plan* p, pic_plan_summary* out) {
+  if (!p || !out) return set_err(PIC_EINVAL, "plan and out are required");
+  if (!p->has_batch) return set_err(PIC_ESTATE, "no batch planned");
+  out->batch = p->hp.batch;
+  out->n_spans = p->hp.n_spans;
+  out->prefix_rows = p->hp.prefix_rows;
+  out->new_rows = p->hp.new_rows;
+  out->rows = p->hp.rows;
+  out->max_position = p->hp.max_position;
+  out->materialized = p->materialized ? 1 : 0;
+  return ok();
+}
+
+pic_status pic_plan_get_requests(const pic_plan* p, int64_t* row_base, int32_t* prefix_rows,
+                                 int32_t* first_new_pos) {
+  if (!p) return set_err(PIC_EINVAL, "plan is NULL");
+  if (!p->has_batch) return set_err(PIC_ESTATE, "no batch planned");
+  for (size_t b = 0; b < p->hp.reqs.size(); ++b) {
+    const pic::ReqRec& r = p->hp.reqs[b];
+    if (row_base) row_base[b] = r.row_base;
+    if (prefix_rows) prefix_rows[b] = r.prefix_rows;
+    if (first_new_pos) first_new_pos[b] = r.first_new_pos;
+  }
+  return ok();
+}
+
+pic_status pic_plan_get_spans(const pic_plan* p, int32_t* target, int32_t* delta, int64_t* first_row) {
+  if (!p) return set_err(PIC_EINVAL, "plan is NULL");
+  if (!p->has_batch) return set_err(PIC_ESTATE, "no batch planned");
+  for (size_t i = 0; i < p->hp.spans.size(); ++i) {
+    const pic::SpanRec& s = p->hp.spans[i];
+    if (target) target[i] = s.target;
+    if (delta) delta[i] = s.delta;
+    if (first_row) first_row[i] = s.dst_row;
+  }
+  return ok();
+}
+
+pic_status pic_plan_get_new_tokens(const pic_plan* p, int32_t* position, int64_t* row) {
+  if (!p) return set_err(PIC_EINVAL, "plan is NULL");
+  if (!p->has_batch) return set_err(PIC_ESTATE, "no batch planned");
+  for (size_t u = 0; u < p->hp.new_pos.size(); ++u) {
+    if (position) position[u] = p->hp.new_pos[u];
+    if (row) row[u] = p->hp.new_row[u];
+  }
+  return ok();
+}
+
+pic_status pic_timing_enable(pic_plan* p, int32_t on) {
+  if (!p) return set_err(PIC_EINVAL, "plan is NULL");
+  p->timing = on != 0;
+  return ok();
+}
+
+pic_status pic_timing_read(pic_plan* p, int32_t kernel, int64_t* launches, double* total_ms) {
+  if (!p) return set_err(PIC_EINVAL, "plan is NULL");
+  if (kernel < 0 || kernel >= kTimedKernels) return set_err(PIC_ERANGE, "kernel %d outside [0, 4)", kernel);
+  double sum = 0.0;
+  for (size_t i = 0; i < p->used[kernel]; ++i) {
+    auto& pr = p->events[kernel][i];
+    hipError_t e = hipEventSynchronize(pr.second);
+    if (e != hipSuccess) return device_error(p, e, "timing event");
+    float ms = 0.0f;
+    e = hipEventElapsedTime(&ms, pr.first, pr.second);
+    if (e != hipSuccess) return device_error(p, e, "timing event");
+    sum += ms;
+  }
+  if (launches) *launches = int64_t(p->used[kernel]);
+  if (total_ms) *total_ms = sum;
+  return ok();
+}
+
+pic_status pic_timing_reset(pic_plan* p) {
+  if (!p) return set_err(PIC_EINVAL, "plan is NULL");
+  for (auto& u : p->used) u = 0;
+  return ok();
+}
+
+}  // extern "C"

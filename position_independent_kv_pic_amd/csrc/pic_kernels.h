@@ -1,0 +1,106 @@
+// Internal launch interface between the C ABI layer and the HIP kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "pic_plan.h"
+
+namespace pic {
+
+// Phase of one rotation: (cos, sin) of an fp64 angle, each split into an fp32
+// head and the fp32 remainder: {cos_hi, cos_lo, sin_hi, sin_lo}.
+using Phase = float4;
+
+struct PlanArgs {
+  const SpanRec* spans;
+  const int32_t* crow;
+  const int32_t* new_pos;
+  const int32_t* new_row;
+  const int32_t* page_ids;
+  const double* omega;      // [head_dim / 2]
+  int32_t n_spans, n_new, page_shift, half_dim;
+  int64_t prefix_rows;
+  int32_t* pos;             // [rows]
+  int2* rowsrc;             // [rows]: (pool token slot, span or -1)
+  Phase* phase_span;        // [n_spans][half_dim]
+  Phase* phase_new;         // [n_new][half_dim]
+};
+
+struct GatherArgs {
+  const SpanRec* spans;
+  const int32_t* crow;
+  const int32_t* page_ids;
+  const Phase* phase_span;
+  const char* pool;
+  char* asm_k;
+  char* asm_v;
+  int64_t prefix_rows, cap, page_bytes;
+  int32_t n_spans, page_shift, page_tokens, layers, kv_heads, planes_per_block;
+};
+
+struct PrologueArgs {
+  const char* q;
+  const char* k_new;
+  const char* v_new;
+  const int32_t* new_pos;
+  const int32_t* new_row;
+  const Phase* phase_new;
+  char* q_rot;
+  char* asm_k;              // plane base of this layer
+  char* asm_v;
+  int64_t cap;
+  int32_t n_new, q_heads, kv_heads;
+};
+
+struct AttnArgs {
+  const uint16_t* q_rot;    // [n_new][Hq][128]
+  const uint16_t* k_plane;  // this layer: [Hkv][cap][128]
+  const uint16_t* v_plane;
+  int64_t cap;
+  const int32_t* pos;
+  const ReqRec* reqs;
+  const int32_t* new_pos;
+  const AttnWork* work;
+  int32_t n_work, q_heads, group, n_new, n_split;
+  float scale_log2;         // log2(e) / sqrt(head_dim)
+  uint16_t* out;            // n_split == 1
+  float* opart;             // [n_split][n_new][Hq][128]
+  float2* ml;               // [n_split][n_new][Hq]: (max in log2 units, sum)
+  // fused variant: prefix rows come from the pool
+  const char* pool;
+  const int2* rowsrc;
+  const Phase* phase_span;
+  int64_t page_bytes;
+  int64_t kv_plane_off;     // byte offset of (layer, K, head 0) inside a page
+  int64_t v_off;            // byte offset from a K row to its V row inside a page
+  int32_t page_shift, page_tokens, kv_heads;
+};
+
+struct AttnF32Args {
+  const char* q_rot;
+  const char* k_plane;
+  const char* v_plane;
+  int64_t cap;
+  const int32_t* pos;
+  const ReqRec* reqs;
+  const int32_t* new_pos;
+  const int32_t* new_req;
+  int32_t n_new, q_heads, group;
+  char* out;
+};
+
+constexpr int kAttnColsPerWG = 128;   // 4 waves x 32 query columns
+constexpr int kAttnRowsPerTile = 64;
+
+hipError_t launch_plan(const PlanArgs& a, hipStream_t s);
+hipError_t launch_gather(int dtype, int head_dim, const GatherArgs& a, hipStream_t s);
+hipError_t launch_prologue(int dtype, int head_dim, const PrologueArgs& a, hipStream_t s);
+hipError_t launch_attention_bf16(const AttnArgs& a, bool fused, hipStream_t s);
+hipError_t launch_attention_f32(int head_dim, const AttnF32Args& a, hipStream_t s);
+// head_dim, dtype combinations the kernels implement
+bool gather_supported(int dtype, int head_dim);
+bool attention_supported(int dtype, int head_dim, bool fused);
+
+}  // namespace pic

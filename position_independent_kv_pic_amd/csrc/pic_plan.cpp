@@ -1,0 +1,271 @@
+// Host-side validation and planning for libpic (pure C++17, no HIP).
+#include "pic_plan.h"
+
+#include <algorithm>
+#include <climits>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+
+namespace pic {
+namespace {
+
+pic_status fail(std::string* err, pic_status code, const char* fmt, ...)
+    __attribute__((format(printf, 3, 4)));
+
+pic_status fail(std::string* err, pic_status code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  if (err) *err = buf;
+  return code;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Largest position a row may take.  INT32_MAX itself is reserved: the
+// attention kernel marks rows past the end of a request with it.
+constexpr int64_t kMaxPosition = INT32_MAX - 1;
+
+}  // namespace
+
+pic_status check_model(const pic_model* m, ModelInfo* out, std::string* err) {
+  if (!m) return fail(err, PIC_EINVAL, "model is NULL");
+  if (m->layers < 1 || m->q_heads < 1 || m->kv_heads < 1)
+    return fail(err, PIC_EINVAL, "layers, q_heads and kv_heads must be >= 1");
+  if (m->q_heads % m->kv_heads)
+    return fail(err, PIC_EINVAL, "q_heads (%d) must be a multiple of kv_heads (%d)", m->q_heads,
+                m->kv_heads);
+  if (m->head_dim < 16 || m->head_dim > 256 || m->head_dim % 16)
+    return fail(err, PIC_EINVAL, "head_dim must be a multiple of 16 in [16, 256], got %d",
+                m->head_dim);
+  if (!(m->rope_theta > 1.0) || !std::isfinite(m->rope_theta))
+    return fail(err, PIC_EINVAL, "rope_theta must be finite and > 1");
+  if (m->dtype != PIC_F32 && m->dtype != PIC_BF16)
+    return fail(err, PIC_EINVAL, "dtype must be PIC_F32 or PIC_BF16");
+  ModelInfo mi;
+  mi.layers = m->layers;
+  mi.q_heads = m->q_heads;
+  mi.kv_heads = m->kv_heads;
+  mi.head_dim = m->head_dim;
+  mi.dtype = m->dtype;
+  mi.theta = m->rope_theta;
+  mi.elem_bytes = m->dtype == PIC_BF16 ? 2 : 4;
+  mi.group = m->q_heads / m->kv_heads;
+  mi.row_bytes = int64_t(m->head_dim) * mi.elem_bytes;
+  *out = mi;
+  return PIC_OK;
+}
+
+pic_status build_pool(const pic_model* model, void* pool, int64_t pool_bytes, int32_t page_tokens,
+                      int32_t n_pages, int32_t n_chunks, const int32_t* chunk_len,
+                      const int32_t* chunk_orig, const int32_t* chunk_page_ptr,
+                      const int32_t* page_ids, PoolInfo* out, std::string* err) {
+  PoolInfo p;
+  pic_status st = check_model(model, &p.m, err);
+  if (st != PIC_OK) return st;
+  if (!pool) return fail(err, PIC_EINVAL, "pool pointer is NULL");
+  if (!aligned16(pool)) return fail(err, PIC_EALIGN, "pool pointer is not 16-byte aligned");
+  if (page_tokens < 1 || page_tokens > 4096 || (page_tokens & (page_tokens - 1)))
+    return fail(err, PIC_EINVAL, "page_tokens must be a power of two in [1, 4096], got %d",
+                page_tokens);
+  if (n_pages < 0 || n_chunks < 0) return fail(err, PIC_EINVAL, "negative page or chunk count");
+  if (n_chunks > 0 && (!chunk_len || !chunk_page_ptr))
+    return fail(err, PIC_EINVAL, "chunk_len and chunk_page_ptr are required");
+  p.base = pool;
+  p.bytes = pool_bytes;
+  p.page_tokens = page_tokens;
+  p.page_shift = 0;
+  while ((1 << p.page_shift) < page_tokens) ++p.page_shift;
+  p.n_pages = n_pages;
+  p.n_chunks = n_chunks;
+  p.page_bytes = int64_t(p.m.layers) * 2 * p.m.kv_heads * page_tokens * p.m.row_bytes;
+  if (int64_t(n_pages) > 0 && pool_bytes / int64_t(n_pages) < p.page_bytes)
+    return fail(err, PIC_ERANGE, "pool_bytes %lld too small for %d pages of %lld bytes",
+                (long long)pool_bytes, n_pages, (long long)p.page_bytes);
+  if (int64_t(n_pages) * page_tokens > INT32_MAX)
+    return fail(err, PIC_ERANGE, "pool holds more than 2^31 token slots");
+  if (n_chunks > 0 && chunk_page_ptr[0] != 0)
+    return fail(err, PIC_EINVAL, "chunk_page_ptr[0] must be 0");
+  p.chunk_len.assign(chunk_len, chunk_len + n_chunks);
+  p.chunk_page_ptr.assign(chunk_page_ptr, chunk_page_ptr + n_chunks + 1);
+  if (chunk_orig)
+    p.chunk_orig.assign(chunk_orig, chunk_orig + n_chunks);
+  else
+    p.chunk_orig.assign(n_chunks, 0);
+  for (int32_t c = 0; c < n_chunks; ++c) {
+    int32_t len = p.chunk_len[c];
+    if (len < 0) return fail(err, PIC_EINVAL, "chunk %d has negative length", c);
+    if (p.chunk_orig[c] < 0) return fail(err, PIC_EINVAL, "chunk %d has a negative origin", c);
+    if (int64_t(p.chunk_orig[c]) + len > INT32_MAX)
+      return fail(err, PIC_ERANGE, "chunk %d positions overflow int32", c);
+    int64_t have = int64_t(p.chunk_page_ptr[c + 1]) - p.chunk_page_ptr[c];
+    int64_t need = (int64_t(len) + page_tokens - 1) / page_tokens;
+    if (have < need)
+      return fail(err, PIC_EINVAL, "chunk %d needs %lld pages, page table gives %lld", c,
+                  (long long)need, (long long)have);
+  }
+  int32_t n_ids = n_chunks > 0 ? p.chunk_page_ptr[n_chunks] : 0;
+  if (n_ids > 0 && !page_ids) return fail(err, PIC_EINVAL, "page_ids is NULL");
+  p.page_ids.assign(page_ids ? page_ids : nullptr, page_ids ? page_ids + n_ids : nullptr);
+  for (int32_t i = 0; i < n_ids; ++i)
+    if (p.page_ids[i] < 0 || p.page_ids[i] >= n_pages)
+      return fail(err, PIC_ERANGE, "page_ids[%d] = %d outside [0, %d)", i, p.page_ids[i], n_pages);
+  *out = std::move(p);
+  return PIC_OK;
+}
+
+pic_status build_plan(const PoolInfo& pool, int32_t batch, const int32_t* span_ptr,
+                      const pic_span* spans, const int32_t* new_ptr, const int32_t* new_pos,
+                      int64_t capacity, HostPlan* out, std::string* err) {
+  if (batch < 0) return fail(err, PIC_EINVAL, "batch must be >= 0");
+  if (batch > 0 && (!span_ptr || !new_ptr))
+    return fail(err, PIC_EINVAL, "span_ptr and new_ptr are required");
+  HostPlan p;
+  p.batch = batch;
+  if (batch > 0) {
+    if (span_ptr[0] != 0 || new_ptr[0] != 0)
+      return fail(err, PIC_EINVAL, "span_ptr[0] and new_ptr[0] must be 0");
+    for (int32_t b = 0; b < batch; ++b) {
+      if (span_ptr[b + 1] < span_ptr[b]) return fail(err, PIC_EINVAL, "span_ptr decreases at %d", b);
+      if (new_ptr[b + 1] < new_ptr[b]) return fail(err, PIC_EINVAL, "new_ptr decreases at %d", b);
+    }
+    p.n_spans = span_ptr[batch];
+    p.new_rows = new_ptr[batch];
+    if (p.n_spans > 0 && !spans) return fail(err, PIC_EINVAL, "spans is NULL");
+  }
+  p.spans.resize(p.n_spans);
+  p.crow.resize(size_t(p.n_spans) + 1);
+  p.reqs.resize(batch);
+  p.new_pos.resize(size_t(p.new_rows));
+  p.new_row.resize(size_t(p.new_rows));
+  p.new_req.resize(size_t(p.new_rows));
+
+  int64_t row = 0, crow = 0;
+  int32_t max_pos = 0;
+  for (int32_t b = 0; b < batch; ++b) {
+    ReqRec& r = p.reqs[b];
+    r.row_base = int32_t(row);  // range-checked below before it can overflow
+    r.span_begin = span_ptr[b];
+    r.span_end = span_ptr[b + 1];
+    r.new_begin = new_ptr[b];
+    r.n_new = new_ptr[b + 1] - new_ptr[b];
+    int64_t next = 0;  // AUTO continuation position
+    int64_t prefix = 0;
+    for (int32_t i = span_ptr[b]; i < span_ptr[b + 1]; ++i) {
+      const pic_span& sp = spans[i];
+      if (sp.chunk < 0 || sp.chunk >= pool.n_chunks)
+        return fail(err, PIC_ERANGE, "span %d: chunk %d outside [0, %d)", i, sp.chunk, pool.n_chunks);
+      int32_t len = pool.chunk_len[sp.chunk];
+      if (sp.s < 0 || sp.s > sp.e || sp.e >= len)
+        return fail(err, PIC_ERANGE, "span %d: need 0 <= s <= e < len, got s=%d e=%d len=%d", i,
+                    sp.s, sp.e, len);
+      if (sp.target < 0 && sp.target != PIC_TARGET_AUTO)
+        return fail(err, PIC_EINVAL, "span %d: target %d is neither >= 0 nor PIC_TARGET_AUTO", i,
+                    sp.target);
+      int64_t n = int64_t(sp.e) - sp.s + 1;
+      int64_t target = sp.target == PIC_TARGET_AUTO ? next : int64_t(sp.target);
+      if (target + n - 1 > kMaxPosition)
+        return fail(err, PIC_ERANGE, "span %d: positions exceed %lld", i, (long long)kMaxPosition);
+      int64_t delta = target - (int64_t(pool.chunk_orig[sp.chunk]) + sp.s);
+      SpanRec& s = p.spans[i];
+      s.crow = int32_t(crow);
+      s.dst_row = int32_t(row + prefix);
+      s.page_off = pool.chunk_page_ptr[sp.chunk];
+      s.s = sp.s;
+      s.n = int32_t(n);
+      s.target = int32_t(target);
+      s.delta = int32_t(delta);
+      s.req = b;
+      p.crow[i] = int32_t(crow);
+      max_pos = std::max<int64_t>(max_pos, target + n - 1);
+      next = target + n;
+      prefix += n;
+      crow += n;
+      if (crow > INT32_MAX || row + prefix > INT32_MAX)
+        return fail(err, PIC_ERANGE, "batch has more than 2^31 rows");
+    }
+    r.prefix_rows = int32_t(prefix);
+    for (int32_t j = 0; j < r.n_new; ++j) {
+      int32_t u = r.new_begin + j;
+      int64_t pos;
+      if (new_pos) {
+        pos = new_pos[u];
+        if (pos < 0) return fail(err, PIC_EINVAL, "new token %d: negative position", u);
+        if (pos > kMaxPosition) return fail(err, PIC_ERANGE, "new token %d: position too large", u);
+        if (j > 0 && pos <= p.new_pos[u - 1])
+          return fail(err, PIC_EINVAL,
+                      "new token %d: positions must increase strictly within a request", u);
+      } else {
+        pos = next + j;
+        if (pos > kMaxPosition) return fail(err, PIC_ERANGE, "new token %d: position too large", u);
+      }
+      p.new_pos[u] = int32_t(pos);
+      p.new_row[u] = int32_t(row + prefix + j);
+      p.new_req[u] = b;
+      max_pos = std::max<int64_t>(max_pos, pos);
+    }
+    r.first_new_pos = r.n_new > 0 ? p.new_pos[r.new_begin] : 0;
+    r.pad = 0;
+    row += prefix + r.n_new;
+    if (row > INT32_MAX) return fail(err, PIC_ERANGE, "batch has more than 2^31 rows");
+  }
+  p.crow[p.n_spans] = int32_t(crow);
+  p.prefix_rows = crow;
+  p.rows = row;
+  p.max_position = max_pos;
+  if (capacity >= 0 && p.rows > capacity)
+    return fail(err, PIC_ERANGE, "batch needs %lld rows per plane, capacity is %lld",
+                (long long)p.rows, (long long)capacity);
+  *out = std::move(p);
+  return PIC_OK;
+}
+
+void build_attention_work(HostPlan* plan, int32_t kv_heads, int32_t group, int32_t cols_per_wg,
+                          int32_t rows_per_tile, int32_t target_wgs, int32_t max_split,
+                          int32_t min_tiles_per_split) {
+  int64_t base = 0;
+  int32_t max_tiles = 0;
+  for (const ReqRec& r : plan->reqs) {
+    int64_t cols = int64_t(r.n_new) * group;
+    base += kv_heads * ((cols + cols_per_wg - 1) / cols_per_wg);
+    int32_t tiles = (r.prefix_rows + r.n_new + rows_per_tile - 1) / rows_per_tile;
+    max_tiles = std::max(max_tiles, tiles);
+  }
+  int32_t split = 1;
+  if (base > 0 && base < target_wgs) {
+    split = int32_t((target_wgs + base - 1) / base);
+    split = std::min(split, max_split);
+    split = std::min(split, std::max(1, max_tiles / std::max(1, min_tiles_per_split)));
+    split = std::max(split, 1);
+  }
+  plan->n_split = split;
+  plan->work.clear();
+  for (int32_t b = 0; b < int32_t(plan->reqs.size()); ++b) {
+    const ReqRec& r = plan->reqs[b];
+    int64_t cols = int64_t(r.n_new) * group;
+    if (cols == 0) continue;
+    int32_t tiles = (r.prefix_rows + r.n_new + rows_per_tile - 1) / rows_per_tile;
+    for (int32_t h = 0; h < kv_heads; ++h) {
+      for (int32_t sp = 0; sp < split; ++sp) {
+        int32_t t0 = int32_t(int64_t(tiles) * sp / split);
+        int32_t t1 = int32_t(int64_t(tiles) * (sp + 1) / split);
+        for (int64_t c = 0; c < cols; c += cols_per_wg) {
+          AttnWork w;
+          w.req = b;
+          w.head = h;
+          w.col_begin = int32_t(c);
+          w.tile_begin = t0;
+          w.tile_end = t1;
+          w.split = sp;
+          w.pad0 = w.pad1 = 0;
+          plan->work.push_back(w);
+        }
+      }
+    }
+  }
+}
+
+}  // namespace pic

@@ -1,0 +1,110 @@
+// Host-side validation and planning for libpic (pure C++17, no HIP).
+//
+// Everything here is integer arithmetic on the caller's span tables: span
+// lengths, row offsets, resolved targets, rotation deltas (CoinRAG page,
+// section 2.3, Delta equation: a span's new start is the prompt length plus
+// the lengths of the spans before it), new-token positions and the work list
+// of the attention kernel.  The records below are uploaded to the device as
+// they are, so their layouts are shared with the kernels.
+#pragma once
+
+#include <cstdint>
+#include <string>
+#include <vector>
+
+#include "pic.h"
+
+namespace pic {
+
+struct ModelInfo {
+  int32_t layers = 0, q_heads = 0, kv_heads = 0, head_dim = 0, dtype = 0;
+  double theta = 0.0;
+  int32_t elem_bytes = 0;   // 2 (bf16) or 4 (f32)
+  int32_t group = 0;        // q_heads / kv_heads
+  int64_t row_bytes = 0;    // head_dim * elem_bytes
+};
+
+struct PoolInfo {
+  ModelInfo m;
+  void* base = nullptr;
+  int64_t bytes = 0;
+  int32_t page_tokens = 0, page_shift = 0, n_pages = 0, n_chunks = 0;
+  int64_t page_bytes = 0;
+  std::vector<int32_t> chunk_len, chunk_orig, chunk_page_ptr, page_ids;
+};
+
+// Span record as the kernels read it (32 bytes).
+struct SpanRec {
+  int32_t crow;      // first compact prefix row of the span (over the whole batch)
+  int32_t dst_row;   // first assembled row
+  int32_t page_off;  // chunk_page_ptr[chunk]: index of the chunk's first page id
+  int32_t s;         // first source token
+  int32_t n;         // length e - s + 1
+  int32_t target;    // new position of token s
+  int32_t delta;     // rotation applied to every key of the span
+  int32_t req;       // request index
+};
+
+// Request record (32 bytes).
+struct ReqRec {
+  int32_t row_base;     // first assembled row of the request
+  int32_t prefix_rows;  // rows gathered from spans
+  int32_t n_new;        // new tokens
+  int32_t new_begin;    // index of the first new token in the packed arrays
+  int32_t span_begin, span_end;
+  int32_t first_new_pos;
+  int32_t pad;
+};
+
+// Attention work item: one workgroup handles query columns
+// [col_begin, col_begin + cols) of request `req` and kv head `head`, over the
+// request's row tiles [tile_begin, tile_end); split `split` of `n_split`.
+struct AttnWork {
+  int32_t req;
+  int32_t head;
+  int32_t col_begin;
+  int32_t tile_begin;
+  int32_t tile_end;
+  int32_t split;
+  int32_t pad0, pad1;
+};
+
+struct HostPlan {
+  int32_t batch = 0, n_spans = 0, max_position = 0;
+  int64_t prefix_rows = 0, new_rows = 0, rows = 0;
+  std::vector<SpanRec> spans;
+  std::vector<int32_t> crow;        // n_spans + 1 compact-row offsets
+  std::vector<ReqRec> reqs;
+  std::vector<int32_t> new_pos;     // per new token
+  std::vector<int32_t> new_row;     // assembled row of each new token
+  std::vector<int32_t> new_req;     // request of each new token
+  // attention work list (built per kernel tiling)
+  std::vector<AttnWork> work;
+  int32_t n_split = 1;
+};
+
+// Validation helpers return PIC_OK or an error code and fill `err`.
+pic_status check_model(const pic_model* m, ModelInfo* out, std::string* err);
+
+pic_status build_pool(const pic_model* model, void* pool, int64_t pool_bytes, int32_t page_tokens,
+                      int32_t n_pages, int32_t n_chunks, const int32_t* chunk_len,
+                      const int32_t* chunk_orig, const int32_t* chunk_page_ptr,
+                      const int32_t* page_ids, PoolInfo* out, std::string* err);
+
+// Validate a batch and compute its plan.  `capacity` is the rows available in
+// each assembled plane (ignored when < 0).
+pic_status build_plan(const PoolInfo& pool, int32_t batch, const int32_t* span_ptr,
+                      const pic_span* spans, const int32_t* new_ptr, const int32_t* new_pos,
+                      int64_t capacity, HostPlan* out, std::string* err);
+
+// Attention work list for the tiled kernel: `cols_per_wg` query columns
+// (token-major: column j*G + g is token j, head g of the group) and
+// `rows_per_tile` rows per tile.  The kv range of a request is split in
+// n_split parts, chosen so that about `target_wgs` workgroups exist when the
+// batch alone gives fewer (at most `max_split`, and never fewer than
+// `min_tiles_per_split` tiles per part).
+void build_attention_work(HostPlan* plan, int32_t kv_heads, int32_t group, int32_t cols_per_wg,
+                          int32_t rows_per_tile, int32_t target_wgs, int32_t max_split,
+                          int32_t min_tiles_per_split);
+
+}  // namespace pic

@@ -1,0 +1,63 @@
+"""Convenience wrapper: register a pool, keep assembled buffers, run a batch.
+
+Allocation and call sequencing only (torch tensors for device memory, the
+current torch stream for ordering).  All computation happens in libpic.
+"""
+from __future__ import annotations
+
+from typing import Optional
+
+import numpy as np
+
+from .binding import (DRY_RUN, PLAN_ONLY, VARIANT_MATERIALIZED, Plan, Pool, model_struct)
+
+
+class Session:
+    def __init__(self, layers, q_heads, kv_heads, head_dim, theta, dtype, pool_tensor,
+                 page_tokens, chunk_len, chunk_page_ptr, page_ids, chunk_orig=None):
+        import torch
+        self.torch = torch
+        self.layers, self.q_heads, self.kv_heads, self.head_dim = layers, q_heads, kv_heads, head_dim
+        self.dtype = dtype
+        self.tdtype = torch.bfloat16 if dtype == "bf16" else torch.float32
+        self.model = model_struct(layers, q_heads, kv_heads, head_dim, theta, dtype)
+        self.pool_tensor = pool_tensor
+        self.pool = Pool(self.model, pool_tensor, pool_tensor.numel() * pool_tensor.element_size(),
+                         page_tokens, pool_tensor.shape[0], chunk_len, chunk_page_ptr, page_ids,
+                         chunk_orig)
+        self.plan = Plan(self.pool)
+        self.asm_k = None
+        self.asm_v = None
+        self.capacity = 0
+
+    def ensure_capacity(self, rows: int):
+        """(Re)allocate the assembled planes [L][Hkv][rows][d] when too small."""
+        if self.asm_k is not None and self.capacity >= rows:
+            return
+        t = self.torch
+        shape = (self.layers, self.kv_heads, max(rows, 1), self.head_dim)
+        self.asm_k = t.empty(shape, dtype=self.tdtype, device=self.pool_tensor.device)
+        self.asm_v = t.empty(shape, dtype=self.tdtype, device=self.pool_tensor.device)
+        self.capacity = max(rows, 1)
+
+    def assemble(self, span_ptr, spans, new_ptr, new_pos=None, plan_only: bool = False):
+        d = self.plan_host(span_ptr, spans, new_ptr, new_pos)
+        self.ensure_capacity(d["rows"])
+        self.plan.assemble(span_ptr, spans, new_ptr, new_pos, self.asm_k, self.asm_v, self.capacity,
+                           PLAN_ONLY if plan_only else 0, self.torch.cuda.current_stream())
+        return d
+
+    def plan_host(self, span_ptr, spans, new_ptr, new_pos=None) -> dict:
+        """Validate and plan on the host only (no device work)."""
+        self.plan.assemble(span_ptr, spans, new_ptr, new_pos, None, None, 2 ** 62, DRY_RUN, None)
+        return self.plan.summary()
+
+    def prefill_layer(self, layer, q, k_new, v_new, out=None, variant: int = VARIANT_MATERIALIZED):
+        if out is None:
+            out = self.torch.empty_like(q)
+        self.plan.query_prefill(layer, q, k_new, v_new, out, variant, self.torch.cuda.current_stream())
+        return out
+
+    def close(self):
+        self.plan.release()
+        self.pool.release()

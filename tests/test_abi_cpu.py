@@ -1,0 +1,192 @@
+"""CPU checks of the C ABI: exports, host validation, host planning.
+
+No GPU is touched: pool registration copies host tables only, and
+PIC_ASSEMBLE_DRY_RUN plans on the host.  Planning results (targets, deltas,
+rows, new-token positions) are integers and must equal the oracle's exactly.
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import workloads as W
+from oracle import pic_oracle as orc
+from position_independent_kv_pic_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE_POOL = 1 << 40          # aligned fake device address; registration never dereferences it
+
+
+def _header_functions():
+    text = open(os.path.join(ROOT, "include", "pic.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pic_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    lib = B.lib()
+    declared = _header_functions()
+    assert declared, "no declarations parsed"
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert set(declared) == set(B.EXPORTED)
+    assert lib.pic_version().decode().startswith("libpic")
+
+
+def _model(wl):
+    m = wl.model
+    return B.model_struct(m.layers, m.q_heads, m.kv_heads, m.head_dim, m.theta, m.dtype)
+
+
+def _pool(wl, base=FAKE_POOL):
+    p = wl.pool
+    return B.Pool(_model(wl), base, p.n_pages * W.page_bytes(wl.model, p.page_tokens), p.page_tokens,
+                  p.n_pages, p.chunk_len, p.chunk_page_ptr, p.page_ids, p.chunk_orig)
+
+
+def _dry(plan, wl, capacity=2 ** 40):
+    plan.assemble(wl.span_ptr(), wl.spans_flat(), wl.new_ptr(), wl.new_pos_flat(), None, None,
+                  capacity, B.DRY_RUN)
+
+
+@pytest.mark.parametrize("name", W.FULL_SIZE + W.REDUCED)
+def test_host_plan_matches_oracle(name):
+    wl = W.get(name)
+    pool = _pool(wl)
+    plan = B.Plan(pool)
+    _dry(plan, wl)
+    s = plan.summary()
+    assert s["prefix_rows"] == wl.prefix_rows_total and s["new_rows"] == wl.n_new_total
+    assert s["rows"] == wl.rows_total and s["batch"] == wl.batch
+    tgt, dlt, first = plan.spans()
+    rb, pr, fp = plan.requests()
+    npos, nrow = plan.new_tokens()
+    i = u = row = 0
+    for b, r in enumerate(wl.requests):
+        planned = orc.plan_spans([tuple(x) for x in r.spans], wl.pool.chunk_orig)
+        assert rb[b] == row and pr[b] == sum(p.length for p in planned)
+        acc = row
+        for p in planned:
+            assert (tgt[i], dlt[i], first[i]) == (p.target, p.delta, acc)
+            acc += p.length
+            i += 1
+        pos = orc.new_token_positions(planned, r.n_new, r.new_pos)
+        assert np.array_equal(npos[u:u + r.n_new], pos)
+        assert np.array_equal(nrow[u:u + r.n_new], acc + np.arange(r.n_new))
+        if r.n_new:
+            assert fp[b] == pos[0]
+        u += r.n_new
+        row = acc + r.n_new
+    plan.release()
+    pool.release()
+
+
+def _err(fn):
+    with pytest.raises(B.PicError) as ei:
+        fn()
+    return ei.value.name
+
+
+def test_pool_registration_errors():
+    wl = W.get("tiny_f32")
+    p = wl.pool
+    m = _model(wl)
+    pb = p.n_pages * W.page_bytes(wl.model, p.page_tokens)
+    ok = dict(pool=FAKE_POOL, pool_bytes=pb, page_tokens=p.page_tokens, n_pages=p.n_pages,
+              chunk_len=p.chunk_len, chunk_page_ptr=p.chunk_page_ptr, page_ids=p.page_ids)
+
+    def reg(**kw):
+        a = dict(ok)
+        a.update(kw)
+        return lambda: B.Pool(kw.get("model", m), a["pool"], a["pool_bytes"], a["page_tokens"],
+                              a["n_pages"], a["chunk_len"], a["chunk_page_ptr"], a["page_ids"])
+
+    assert _err(reg(pool=0)) == "PIC_EINVAL"
+    assert _err(reg(pool=FAKE_POOL + 8)) == "PIC_EALIGN"
+    assert _err(reg(page_tokens=12)) == "PIC_EINVAL"
+    assert _err(reg(pool_bytes=pb - 1)) == "PIC_ERANGE"
+    bad_ids = p.page_ids.copy()
+    bad_ids[3] = p.n_pages
+    assert _err(reg(page_ids=bad_ids)) == "PIC_ERANGE"
+    short = p.chunk_page_ptr.copy()
+    short[1:] -= 1
+    short[0] = 0
+    assert _err(reg(chunk_page_ptr=short)) == "PIC_EINVAL"
+    bad_len = p.chunk_len.copy()
+    bad_len[0] = -1
+    assert _err(reg(chunk_len=bad_len)) == "PIC_EINVAL"
+    for bad in (B.model_struct(1, 3, 2, 64, 1e4, "f32"), B.model_struct(1, 2, 1, 72, 1e4, "f32"),
+                B.model_struct(1, 2, 1, 64, 0.5, "f32"), B.model_struct(0, 2, 1, 64, 1e4, "f32")):
+        assert _err(lambda: B.Pool(bad, FAKE_POOL, pb, p.page_tokens, p.n_pages, p.chunk_len,
+                                   p.chunk_page_ptr, p.page_ids)) == "PIC_EINVAL"
+
+
+def test_assemble_validation_errors_enqueue_nothing():
+    wl = W.get("tiny_f32")
+    pool = _pool(wl)
+    plan = B.Plan(pool)
+    sp = wl.span_ptr()
+    np_ = wl.new_ptr()
+    good = wl.spans_flat()
+
+    def dry(spans=good, span_ptr=sp, new_ptr=np_, new_pos=None, cap=2 ** 40):
+        return lambda: plan.assemble(span_ptr, spans, new_ptr, new_pos, None, None, cap, B.DRY_RUN)
+
+    def mod(i, col, val):
+        t = good.copy()
+        t[i, col] = val
+        return t
+
+    assert _err(dry(mod(1, 0, 99))) == "PIC_ERANGE"          # chunk id out of range
+    assert _err(dry(mod(1, 0, -1))) == "PIC_ERANGE"
+    assert _err(dry(mod(1, 1, good[1, 2] + 1))) == "PIC_ERANGE"   # s > e
+    assert _err(dry(mod(1, 2, 64))) == "PIC_ERANGE"          # e >= len
+    assert _err(dry(mod(1, 1, -3))) == "PIC_ERANGE"          # s < 0
+    assert _err(dry(mod(2, 3, -7))) == "PIC_EINVAL"          # bad target
+    assert _err(dry(mod(2, 3, 2 ** 31 - 2))) == "PIC_ERANGE"  # positions overflow
+    with pytest.raises(ValueError):                           # table shorter than its CSR
+        dry(span_ptr=np.array([0, 8]))()
+    assert _err(dry(span_ptr=np.array([1, 7]))) == "PIC_EINVAL"
+    assert _err(dry(new_ptr=np.array([0, -1]))) == "PIC_EINVAL"
+    assert _err(dry(new_pos=np.array([70, 71, 72, 72, 73, 74, 75, 76]))) == "PIC_EINVAL"
+    assert _err(dry(new_pos=np.array([-1, 71, 72, 73, 74, 75, 76, 77]))) == "PIC_EINVAL"
+    assert _err(dry(cap=wl.rows_total - 1)) == "PIC_ERANGE"
+    dry(cap=wl.rows_total)()                                  # exactly enough
+    # non-dry calls need device buffers, checked before any device work
+    assert _err(lambda: plan.assemble(sp, good, np_, None, None, None, 100, 0)) == "PIC_EINVAL"
+    assert _err(lambda: plan.assemble(sp, good, np_, None, FAKE_POOL + 4, FAKE_POOL, 100, 0)) == "PIC_EALIGN"
+    assert _err(lambda: plan.assemble(sp, good, np_, None, None, None, 100, 64)) == "PIC_EINVAL"
+    plan.release()
+    pool.release()
+
+
+def test_query_prefill_state_errors():
+    wl = W.get("tiny_f32")
+    pool = _pool(wl)
+    plan = B.Plan(pool)
+    assert _err(lambda: plan.query_prefill(0, FAKE_POOL, FAKE_POOL, FAKE_POOL, FAKE_POOL)) == "PIC_ESTATE"
+    _dry(plan, wl)
+    assert _err(lambda: plan.query_prefill(0, FAKE_POOL, FAKE_POOL, FAKE_POOL, FAKE_POOL)) == "PIC_ESTATE"
+    # releasing a pool that still has a plan is refused
+    assert _err(pool.release) == "PIC_ESTATE"
+    plan.release()
+    pool.release()
+
+
+def test_empty_and_degenerate_batches_plan():
+    wl = W.get("tiny_f32")
+    pool = _pool(wl)
+    plan = B.Plan(pool)
+    plan.assemble(np.array([0]), np.zeros((0, 4)), np.array([0]), None, None, None, 0, B.DRY_RUN)
+    assert plan.summary()["rows"] == 0
+    # requests with no spans (plain causal prefill) and with no new tokens
+    plan.assemble(np.array([0, 0, 1]), np.array([[2, 0, 63, B.TARGET_AUTO]]), np.array([0, 5, 5]),
+                  None, None, None, 100, B.DRY_RUN)
+    npos, nrow = plan.new_tokens()
+    assert npos.tolist() == [0, 1, 2, 3, 4] and nrow.tolist() == [0, 1, 2, 3, 4]
+    rb, pr, _ = plan.requests()
+    assert rb.tolist() == [0, 5] and pr.tolist() == [0, 64]
+    plan.release()
+    pool.release()

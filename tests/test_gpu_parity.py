@@ -1,0 +1,218 @@
+"""GPU parity: libpic's HIP path against the fp64 CPU oracle, through the C ABI.
+
+Reduced workloads (same structure, fewer layers/requests) are compared
+element by element; the full-size workloads run exactly as the benchmark
+launches them (assemble, then every layer's prefill) and are checked on
+requests {0, last}, layers {0, L/2, L-1} and a spread of query tokens.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from oracle import pic_oracle as orc
+from position_independent_kv_pic_amd import VARIANT_FUSED, VARIANT_MATERIALIZED
+from workloads.device import open_workload
+
+import parity as P
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a ROCm device"
+    torch.cuda.init()
+    yield
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+def _np(t):
+    return t.detach().to("cpu").to(torch.float64).numpy()
+
+
+def run_prefill(dw, layers, variant):
+    """Prefill the given layers; returns {layer: (q, k, v, out)}."""
+    res = {}
+    for l in layers:
+        q, k, v = dw.layer_inputs(l)
+        out = dw.session.prefill_layer(l, q, k, v, variant=variant)
+        res[l] = (q, k, v, out)
+    torch.cuda.synchronize()
+    return res
+
+
+def check_request(dw, b, layers, results, token_subset=None, check_tail=True):
+    """Compare request b's assembled rows, new rows and outputs on `layers`."""
+    wl = dw.wl
+    m = wl.model
+    sess = dw.session
+    rb, pr, _ = sess.plan.requests()
+    base, npre = int(rb[b]), int(pr[b])
+    r = wl.requests[b]
+    nb = int(wl.new_ptr()[b])
+    kpre, vpre, ppre = P.request_prefix(wl, dw.pool, b, layers)
+    pos_new = P.request_positions(wl, b)
+    stats = {}
+    for li, l in enumerate(layers):
+        gk = _np(sess.asm_k[l, :, base:base + npre])
+        gv = _np(sess.asm_v[l, :, base:base + npre])
+        assert np.array_equal(gv, vpre[li]), f"values differ (request {b}, layer {l})"
+        planned = orc.plan_spans([tuple(int(x) for x in s) for s in r.spans], wl.pool.chunk_orig)
+        zero = np.concatenate([np.full(p.length, p.delta == 0) for p in planned]) if planned else np.zeros(0, bool)
+        mx, nx = P.compare_keys(gk, kpre[li], m.dtype, exact_mask=zero[None, :, None])
+        q, k, v, out = results[l]
+        sl = slice(nb, nb + r.n_new)
+        qn, kn, vn = _np(q[sl]), _np(k[sl]), _np(v[sl])
+        o_ref, k_rot, v_ref, _ = orc.query_prefill_layer(kpre[li], vpre[li], ppre, qn, kn, vn, pos_new,
+                                                         m.theta, m.dtype, m.kv_heads,
+                                                         query_subset=token_subset)
+        if check_tail and r.n_new:
+            gkt = _np(sess.asm_k[l, :, base + npre:base + npre + r.n_new]).transpose(1, 0, 2)
+            gvt = _np(sess.asm_v[l, :, base + npre:base + npre + r.n_new]).transpose(1, 0, 2)
+            assert np.array_equal(gvt, v_ref), "new values not appended exactly"
+            P.compare_keys(gkt, k_rot, m.dtype, exact_mask=(pos_new == 0)[:, None, None])
+        got = _np(out[sl])
+        if token_subset is not None:
+            got = got[token_subset]
+        amax, rl2 = P.attn_metrics(got, o_ref)
+        stats[l] = dict(key_max=mx, key_not_exact=nx, attn_max_abs=amax, attn_rel_l2=rl2)
+        assert amax <= P.ATOL[m.dtype] and rl2 <= P.RL2[m.dtype], \
+            f"attention off (request {b}, layer {l}): max-abs {amax:.3g}, rel-L2 {rl2:.3g}"
+    return stats
+
+
+def test_tiny_fp32_config_end_to_end():
+    wl = W.get("tiny_f32")
+    _say("case tiny_f32")
+    dw = open_workload(wl)
+    dw.assemble()
+    res = run_prefill(dw, [0], VARIANT_MATERIALIZED)
+    st = check_request(dw, 0, [0], res)
+    _say("tiny_f32", st)
+    dw.close()
+
+
+@pytest.mark.parametrize("name", W.REDUCED)
+def test_reduced_workloads_every_element(name):
+    wl = W.get(name)
+    _say(f"case reduced {name}")
+    dw = open_workload(wl)
+    dw.assemble()
+    layers = list(range(wl.model.layers))
+    res_m = run_prefill(dw, layers, VARIANT_MATERIALIZED)
+    for b in range(wl.batch):
+        st = check_request(dw, b, layers, res_m)
+        _say(name, b, st)
+    # the fused variant reads the pool directly and must give identical bits
+    res_f = run_prefill(dw, layers, VARIANT_FUSED)
+    for l in layers:
+        assert torch.equal(res_m[l][3], res_f[l][3]), f"fused != materialised on layer {l}"
+    # and it also works from a plan-only assembly
+    dw.assemble(plan_only=True)
+    res_p = run_prefill(dw, layers, VARIANT_FUSED)
+    for l in layers:
+        assert torch.equal(res_m[l][3], res_p[l][3]), f"plan-only fused differs on layer {l}"
+    dw.close()
+    del dw
+    torch.cuda.empty_cache()
+
+
+def _token_subset(n, k=16):
+    if n <= k:
+        return None
+    idx = np.unique(np.concatenate([[0, 1, n - 2, n - 1], np.linspace(0, n - 1, k - 4).round().astype(int)]))
+    return idx
+
+
+@pytest.mark.parametrize("name", [n for n in W.FULL_SIZE if n != "tiny_f32"])
+def test_full_size_workloads_sampled(name):
+    wl = W.get(name)
+    _say(f"case full {name}: batch {wl.batch}, rows {wl.rows_total}")
+    dw = open_workload(wl)
+    summ = dw.assemble()
+    L = wl.model.layers
+    checked = sorted({0, L // 2, L - 1})
+    res = run_prefill(dw, list(range(L)), VARIANT_MATERIALIZED)   # whole path, as benchmarked
+    for b in sorted({0, wl.batch - 1}):
+        sub = _token_subset(wl.requests[b].n_new)
+        st = check_request(dw, b, checked, res, token_subset=sub)
+        _say(name, b, st)
+    res_f = run_prefill(dw, checked, VARIANT_FUSED)
+    for l in checked:
+        assert torch.equal(res[l][3], res_f[l][3]), f"fused != materialised on layer {l}"
+    assert summ["rows"] == wl.rows_total
+    dw.close()
+    del dw, res, res_f
+    torch.cuda.empty_cache()
+
+
+def _edge_workload():
+    """Ragged shapes and degenerate spans on Qwen2-like heads, two layers."""
+    rng = np.random.default_rng(77)
+    model = W.ModelShape(2, 28, 4, 128, 1e6, "bf16")
+    pool = W.make_pool(rng, [512, 300, 17, 1, 96], page_tokens=16)
+    pool.chunk_orig = np.array([0, 1000, 5, 0, 70000], np.int32)
+    A = W.TARGET_AUTO
+    reqs = [
+        # 1-token spans, a span at a chunk's end, a repeated span, negative deltas
+        # (target before the original position), an explicit target that
+        # overlaps positions already used, a large original base
+        W.Request(np.array([[0, 511, 511, 0], [3, 0, 0, A], [1, 299, 299, A], [1, 0, 299, A],
+                            [1, 0, 299, A], [2, 3, 9, 2], [4, 0, 95, A]], np.int32), 37,
+                  np.arange(105, 142, dtype=np.int32)),
+        # no spans: plain causal prefill
+        W.Request(np.zeros((0, 4), np.int32), 29, np.arange(29, dtype=np.int32)),
+        # no new tokens
+        W.Request(np.array([[0, 0, 63, A], [0, 64, 127, A]], np.int32), 0, np.zeros(0, np.int32)),
+        # interleaved: new tokens before, between and after the cached spans, one at position 0
+        W.Request(np.array([[0, 5, 70, 10], [2, 0, 16, 300]], np.int32), 9,
+                  np.array([0, 1, 2, 200, 201, 250, 400, 401, 402], np.int32)),
+    ]
+    return W.Workload("edge", 0, model, pool, reqs, W.ValueRecipe("lognormal", "half"), 900)
+
+
+def test_edge_cases_ragged_degenerate_and_canary():
+    wl = _edge_workload()
+    _say("case edge")
+    dw = open_workload(wl)
+    sess = dw.session
+    cap = wl.rows_total + 37
+    sess.ensure_capacity(cap)
+    nan_bits = torch.tensor(-1, dtype=torch.int16)           # 0xFFFF: a NaN bf16 canary
+    sess.asm_k.view(torch.int16).fill_(nan_bits)
+    sess.asm_v.view(torch.int16).fill_(nan_bits)
+    dw.assemble()
+    layers = [0, 1]
+    res = run_prefill(dw, layers, VARIANT_MATERIALIZED)
+    for b in range(wl.batch):
+        _say("edge", b, check_request(dw, b, layers, res))
+    rows = wl.rows_total
+    for t in (sess.asm_k, sess.asm_v):
+        assert not torch.isnan(t[:, :, :rows].float()).any(), "a planned row was not written"
+        assert bool((t[:, :, rows:].view(torch.int16) == -1).all()), "rows beyond the batch were written"
+    res_f = run_prefill(dw, layers, VARIANT_FUSED)
+    for l in layers:
+        assert torch.equal(res[l][3], res_f[l][3])
+    dw.close()
+
+
+def test_plan_reuse_with_smaller_batch():
+    wl = W.get("coinrag_small")
+    _say("case reuse")
+    dw = open_workload(wl)
+    dw.assemble()
+    run_prefill(dw, [0], VARIANT_MATERIALIZED)
+    small = W.Workload("coinrag_small_1", wl.cfg, wl.model, wl.pool, wl.requests[1:2], wl.values, wl.seed)
+    dw2 = type(dw)(small, dw.pool, dw.kscale, dw.vscale, dw.session)
+    dw2.assemble()
+    res = run_prefill(dw2, [0, 1], VARIANT_MATERIALIZED)
+    _say("reuse", check_request(dw2, 0, [0, 1], res))
+    dw.close()

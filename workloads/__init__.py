@@ -6,9 +6,10 @@ attention): it only draws random layouts and values with the shapes and
 distributions of the pages' workloads, builds a paged pool from them, and
 counts algorithmic bytes and FLOPs for the reports.
 
-Layouts use numpy's default_rng(1000 * cfg + stream); large tensors use a
-torch.Generator on the target device seeded the same way.  The oracle reads
-back the exact values that were generated.
+Pool layouts use numpy's default_rng(1000 * cfg), request layouts
+default_rng([1000 * cfg, 1 + layout]) (the tiny configuration: seed 0); large
+tensors use a torch.Generator on the target device seeded from 1000 * cfg.
+The oracle reads back the exact values that were generated.
 
 Stand-ins for the pages' workloads (the public QA suites they evaluate on are
 not used):
@@ -190,15 +191,20 @@ LLAMA31_8B = ModelShape(32, 32, 8, 128, 5e5, "bf16")
 QWEN3_8B = ModelShape(36, 32, 8, 128, 1e6, "bf16")
 
 
+def _layout_rng(seed: int, layout: int) -> np.random.Generator:
+    """Requests draw from their own stream so that layout variants share the pool."""
+    return np.random.default_rng([seed, 1 + layout])
+
+
 def _turborag(batch: int, model: ModelShape = QWEN2_7B, n_chunks: int = 200,
               chunk: int = 512, top: int = 5, prompt_len: int = 32, n_new: int = 64,
-              name: str = "") -> Workload:
+              name: str = "", layout: int = 0) -> Workload:
     """Whole-chunk reuse: a 32-token prompt cache and top-5 whole 512-token
     chunks out of 200, in retrieval order, contiguous; 64 query tokens."""
     seed = 2000
-    rng = np.random.default_rng(seed)
+    pool = make_pool(np.random.default_rng(seed), [chunk] * n_chunks + [prompt_len])
+    rng = _layout_rng(seed, layout)
     prompt = n_chunks
-    pool = make_pool(rng, [chunk] * n_chunks + [prompt_len])
     reqs = []
     for _ in range(batch):
         sel = rng.choice(n_chunks, size=top, replace=False)
@@ -229,14 +235,14 @@ def _nugget_spans(rng, chunks, n_spans, chunk_len, p_geom=1.0 / 15, lo=3, hi=48)
 
 def _coinrag(batch: int, model: ModelShape = QWEN2_7B, n_chunks: int = 2000,
              chunk: int = 512, retrieved: int = 20, n_spans: int = 64,
-             prompt_len: int = 32, n_new: int = 64, name: str = "") -> Workload:
+             prompt_len: int = 32, n_new: int = 64, name: str = "", layout: int = 0) -> Workload:
     """Nugget reuse: 20 retrieved chunks per request, 64 non-overlapping spans
     with geometric lengths (mean 15, clipped to [3, 48]) in shuffled order,
     contiguous after a 32-token prompt cache; 64 query tokens."""
     seed = 3000
-    rng = np.random.default_rng(seed)
+    pool = make_pool(np.random.default_rng(seed), [chunk] * n_chunks + [prompt_len])
+    rng = _layout_rng(seed, layout)
     prompt = n_chunks
-    pool = make_pool(rng, [chunk] * n_chunks + [prompt_len])
     reqs = []
     for _ in range(batch):
         sel = rng.choice(n_chunks, size=retrieved, replace=False)
@@ -250,15 +256,16 @@ def _coinrag(batch: int, model: ModelShape = QWEN2_7B, n_chunks: int = 2000,
 def _sempic(batch: int, model: ModelShape = LLAMA31_8B, n_docs: int = 64,
             doc_lo: int = 1024, doc_hi: int = 4096, per_req: int = 8,
             inline_lo: int = 64, inline_hi: int = 256, n_query: int = 128,
-            name: str = "") -> Workload:
+            name: str = "", layout: int = 0) -> Workload:
     """Document reuse with interleaving: 8 distinct documents per request in
     random order, 7 inline segments of U[64, 256] fresh tokens between them,
     a 128-token query last.  Every item gets its final logical position in
     sequence order; the inline tokens and the query are the new tokens."""
     seed = 4000
-    rng = np.random.default_rng(seed)
-    lens = rng.integers(doc_lo, doc_hi + 1, size=n_docs)
-    pool = make_pool(rng, lens)
+    prng = np.random.default_rng(seed)
+    lens = prng.integers(doc_lo, doc_hi + 1, size=n_docs)
+    pool = make_pool(prng, lens)
+    rng = _layout_rng(seed, layout)
     reqs = []
     for _ in range(batch):
         docs = rng.choice(n_docs, size=per_req, replace=False)
@@ -276,13 +283,13 @@ def _sempic(batch: int, model: ModelShape = LLAMA31_8B, n_docs: int = 64,
 
 
 def _long(batch: int, docs_per_req: int, model: ModelShape = QWEN3_8B, n_docs: int = 64,
-          doc_len: int = 2048, n_new: int = 256, name: str = "") -> Workload:
+          doc_len: int = 2048, n_new: int = 256, name: str = "", layout: int = 0) -> Workload:
     """Long context: 64 documents of 2048 tokens; each request takes
     `docs_per_req` of them in random order, contiguous; a 256-token query.
     K/V ~ N(0, 1) with 1% outlier channels scaled x20."""
     seed = 5000
-    rng = np.random.default_rng(seed)
-    pool = make_pool(rng, [doc_len] * n_docs)
+    pool = make_pool(np.random.default_rng(seed), [doc_len] * n_docs)
+    rng = _layout_rng(seed, layout)
     reqs = []
     for _ in range(batch):
         docs = rng.choice(n_docs, size=docs_per_req, replace=False)
@@ -292,30 +299,33 @@ def _long(batch: int, docs_per_req: int, model: ModelShape = QWEN3_8B, n_docs: i
                     ValueRecipe("outlier", "outlier"), seed)
 
 
-def get(name: str) -> Workload:
+def get(name: str, layout: int = 0) -> Workload:
     """Named workloads: the five full-size configurations and reduced variants
     that the oracle finishes in seconds (same structure, fewer layers or
-    requests)."""
+    requests).  `layout` draws a different batch of requests over the same
+    pool (the tiny configuration has one layout)."""
     small2 = ModelShape(2, 28, 4, 128, 1e6, "bf16")
     small4 = ModelShape(2, 32, 8, 128, 5e5, "bf16")
     small5 = ModelShape(2, 32, 8, 128, 1e6, "bf16")
     table = {
         "tiny_f32": lambda: _tiny(0),
-        "turborag_b1": lambda: _turborag(1),
-        "turborag_b16": lambda: _turborag(16),
-        "coinrag_b32": lambda: _coinrag(32),
-        "sempic_b8": lambda: _sempic(8),
-        "long_131k_b1": lambda: _long(1, 64, name="long_131k_b1"),
-        "long_16k_b32": lambda: _long(32, 8, name="long_16k_b32"),
+        "turborag_b1": lambda: _turborag(1, layout=layout),
+        "turborag_b16": lambda: _turborag(16, layout=layout),
+        "coinrag_b32": lambda: _coinrag(32, layout=layout),
+        "sempic_b8": lambda: _sempic(8, layout=layout),
+        "long_131k_b1": lambda: _long(1, 64, name="long_131k_b1", layout=layout),
+        "long_16k_b32": lambda: _long(32, 8, name="long_16k_b32", layout=layout),
         # reduced variants
-        "turborag_small": lambda: _turborag(3, small2, n_chunks=12, name="turborag_small"),
-        "coinrag_small": lambda: _coinrag(4, small2, n_chunks=40, name="coinrag_small"),
+        "turborag_small": lambda: _turborag(3, small2, n_chunks=12, name="turborag_small", layout=layout),
+        "coinrag_small": lambda: _coinrag(4, small2, n_chunks=40, name="coinrag_small", layout=layout),
         "sempic_small": lambda: _sempic(2, small4, n_docs=6, doc_lo=100, doc_hi=700, per_req=3,
-                                        inline_lo=20, inline_hi=90, n_query=40, name="sempic_small"),
-        "long_small": lambda: _long(2, 2, small5, n_docs=4, doc_len=1000, n_new=100, name="long_small"),
+                                        inline_lo=20, inline_hi=90, n_query=40, name="sempic_small",
+                                        layout=layout),
+        "long_small": lambda: _long(2, 2, small5, n_docs=4, doc_len=1000, n_new=100, name="long_small",
+                                    layout=layout),
     }
     for b in (1, 2, 4, 8, 16):
-        table[f"long_16k_b{b}"] = (lambda b=b: _long(b, 8, name=f"long_16k_b{b}"))
+        table[f"long_16k_b{b}"] = (lambda b=b: _long(b, 8, name=f"long_16k_b{b}", layout=layout))
     if name not in table:
         raise KeyError(f"unknown workload {name!r}; known: {sorted(table)}")
     return table[name]()
