@@ -47,7 +47,23 @@ def parse():
     ap.add_argument("--layouts", type=int, default=8, help="pre-generated batch layouts to cycle through")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="time budget of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy (to scale HBM counters), then exit")
     return ap.parse_args()
+
+
+def copy_calibration():
+    """A plain copy of known size: its FETCH_SIZE / WRITE_SIZE counters give
+    the factor between counter units and bytes."""
+    import torch
+    n = 1 << 30
+    src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_read": n, "copy_calibration_bytes_written": n,
+                      "launches": 5}), flush=True)
 
 
 def percentile(xs, q):
@@ -105,6 +121,9 @@ def main():
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the path would shard "
               f"requests or kv heads across GPUs with no exchange, see the design notes)", file=sys.stderr)
         sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
     import torch
     import workloads as W
     from workloads.device import open_workload

@@ -7,7 +7,11 @@ Tolerances:
     oracle rounded to bf16 (ordinal distance of the bit patterns, +0 == -0);
   * rotated fp32 keys: within 2^-21 * |(x_k, x_{k+d/2})| of the fp64 value;
   * attention: bf16 max-abs <= 1e-2 and relative L2 <= 5e-3 per checked
-    layer; fp32 both <= 1e-5.
+    layer; fp32 both <= 1e-5.  Attention is linear in V channel by channel,
+    so an output channel whose value channel carries a scale s > 1 (the
+    x20 outlier channels of the long-context workloads) is compared after
+    dividing its error by s: one bf16 rounding of an exact output near 40 is
+    already 0.125, which no bf16 result can beat in absolute terms.
 """
 from __future__ import annotations
 
@@ -55,13 +59,26 @@ def request_positions(wl: W.Workload, b: int):
     return orc.new_token_positions(planned, r.n_new, r.new_pos)
 
 
-def attn_metrics(got: np.ndarray, ref: np.ndarray):
+def channel_scale(vscale_layer: np.ndarray, group: int) -> np.ndarray:
+    """[Hq][d] divisor for the max-abs check: max(1, scale of the value
+    channel each output channel averages), query head h reading kv head h // G."""
+    s = np.maximum(1.0, np.asarray(vscale_layer, np.float64))      # [Hkv][d]
+    return np.repeat(s, group, axis=0)
+
+
+def attn_metrics(got: np.ndarray, ref: np.ndarray, scale=None):
+    """(max-abs error, with channels divided by `scale` [Hq][d] if given; relative L2)."""
     err = np.abs(got - ref)
+    if scale is not None:
+        err = err / scale[None]
     return float(err.max(initial=0.0)), float(np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-300))
 
 
 def compare_keys(got: np.ndarray, ref: np.ndarray, dtype: str, exact_mask=None):
     """Return (max ulp or scaled error, count not bit-exact); raises on violation."""
+    assert got.shape == ref.shape, (got.shape, ref.shape)
+    if got.size == 0:
+        return 0, 0
     if dtype == "bf16":
         d = ulp_distance_bf16(torch.from_numpy(got), torch.from_numpy(ref))
         if exact_mask is not None:

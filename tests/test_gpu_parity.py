@@ -82,8 +82,10 @@ def check_request(dw, b, layers, results, token_subset=None, check_tail=True):
         got = _np(out[sl])
         if token_subset is not None:
             got = got[token_subset]
-        amax, rl2 = P.attn_metrics(got, o_ref)
-        stats[l] = dict(key_max=mx, key_not_exact=nx, attn_max_abs=amax, attn_rel_l2=rl2)
+        cs = P.channel_scale(_np(dw.vscale[l]), m.group)
+        amax, rl2 = P.attn_metrics(got, o_ref, cs)
+        stats[l] = dict(key_max=mx, key_not_exact=nx, attn_max_abs=amax, attn_rel_l2=rl2,
+                        attn_max_abs_unscaled=float(np.abs(got - o_ref).max(initial=0.0)))
         assert amax <= P.ATOL[m.dtype] and rl2 <= P.RL2[m.dtype], \
             f"attention off (request {b}, layer {l}): max-abs {amax:.3g}, rel-L2 {rl2:.3g}"
     return stats
