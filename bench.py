@@ -45,7 +45,7 @@ def parse():
     ap.add_argument("--workload", default="turborag_b16")
     ap.add_argument("--variant", default="M", choices=["M", "F"])
     ap.add_argument("--layouts", type=int, default=8, help="pre-generated batch layouts to cycle through")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="time budget of the oracle sample")
+    ap.add_argument("--cpu-seconds", type=float, default=20.0, help="time budget of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (to scale HBM counters), then exit")
@@ -74,45 +74,56 @@ def percentile(xs, q):
 
 
 def cpu_baseline(wl, pool, dw, budget_s: float):
-    """Time the fp64 oracle on a bounded sample of the same workload: request
-    0, one layer after another until the time budget is spent."""
+    """Time the fp64 oracle on a bounded sample of the same workload: requests
+    in order, every layer of each, until the time budget is spent (or the
+    whole batch is done).  Only the oracle's own work is timed, not the
+    read-back of its inputs."""
     import numpy as np
     import threadpoolctl
     from oracle import pic_oracle as orc
     import workloads as W
-    r = wl.requests[0]
     m = wl.model
-    planned = orc.plan_spans([tuple(int(x) for x in s) for s in r.spans], wl.pool.chunk_orig)
-    pos_new = orc.new_token_positions(planned, r.n_new, r.new_pos)
-    nb = int(wl.new_ptr()[0])
     flops = 0
     spent = 0.0
-    layers = 0
-    n_visible = 0
-    for l in range(m.layers):
-        ck, cv = {}, {}
-        for c in sorted(set(int(c) for c in r.spans[:, 0])):
-            k, v = W.chunk_kv(wl, pool, c, [l])
-            ck[c], cv[c] = k.numpy(), v.numpy()
-        q, kn, vn = dw.layer_inputs(l)
-        sl = slice(nb, nb + r.n_new)
-        qn, kk, vv = (t[sl].float().cpu().double().numpy() for t in (q, kn, vn))
-        t0 = time.perf_counter()
-        kp, vp, pp = orc.assemble(ck, cv, [tuple(int(x) for x in s) for s in r.spans], m.theta, m.dtype,
-                                  chunk_orig=wl.pool.chunk_orig)
-        orc.query_prefill_layer(kp[0], vp[0], pp, qn, kk, vv, pos_new, m.theta, m.dtype, m.kv_heads)
-        spent += time.perf_counter() - t0
-        layers += 1
-        if l == 0:
-            rows = np.concatenate([pp, pos_new])
-            n_visible = int(sum(int((rows <= p).sum()) for p in pos_new))
-        flops += 4 * m.head_dim * m.q_heads * n_visible
+    pairs = 0
+    done_reqs = 0
+    cache = {}
+    for b, r in enumerate(wl.requests):
+        spans = [tuple(int(x) for x in s) for s in r.spans]
+        planned = orc.plan_spans(spans, wl.pool.chunk_orig)
+        pos_new = orc.new_token_positions(planned, r.n_new, r.new_pos)
+        nb = int(wl.new_ptr()[b])
+        n_visible = None
+        for l in range(m.layers):
+            ck, cv = {}, {}
+            for c in sorted(set(int(c) for c in r.spans[:, 0])):
+                k, v = W.chunk_kv(wl, pool, c, [l])
+                ck[c], cv[c] = k.numpy(), v.numpy()
+            if l not in cache:
+                cache[l] = dw.layer_inputs(l)
+            q, kn, vn = cache[l]
+            sl = slice(nb, nb + r.n_new)
+            qn, kk, vv = (t[sl].float().cpu().double().numpy() for t in (q, kn, vn))
+            t0 = time.perf_counter()
+            kp, vp, pp = orc.assemble(ck, cv, spans, m.theta, m.dtype, chunk_orig=wl.pool.chunk_orig)
+            orc.query_prefill_layer(kp[0], vp[0], pp, qn, kk, vv, pos_new, m.theta, m.dtype, m.kv_heads)
+            spent += time.perf_counter() - t0
+            pairs += 1
+            if n_visible is None:
+                rows = np.concatenate([pp, pos_new])
+                n_visible = int(sum(int((rows <= p).sum()) for p in pos_new))
+            flops += 4 * m.head_dim * m.q_heads * n_visible
+            if spent >= budget_s:
+                break
+        done_reqs = b + 1
         if spent >= budget_s:
             break
     threads = max((d.get("num_threads", 1) for d in threadpoolctl.threadpool_info()), default=1)
     return {"value": flops / spent / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"request 0 of {wl.name}, {layers} of {m.layers} layers (gather, re-rotation and "
-                      f"attention in fp64 numpy), {spent:.1f} s; host has {os.cpu_count()} logical CPUs"}
+            "sample": f"{pairs} (request, layer) pairs of {wl.name} ({done_reqs} of {wl.batch} requests, "
+                      f"{m.layers} layers each): gather, re-rotation and attention in fp64 numpy, "
+                      f"{spent:.1f} s of oracle time; value = the sample's attention FLOPs / that time; "
+                      f"host has {os.cpu_count()} logical CPUs"}
 
 
 def main():
@@ -183,6 +194,19 @@ def main():
     kt = {k: plan.timing_read(k) for k in (KERNEL_GATHER, KERNEL_PROLOGUE, KERNEL_ATTN, KERNEL_PLAN)}
     plan.timing(False)
 
+    # practical HBM ceiling for reference: a plain device copy of 2 GiB
+    src = torch.empty(1 << 30, dtype=torch.bfloat16, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    ce = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ce[0].record(stream)
+    for _ in range(5):
+        dst.copy_(src)
+    ce[1].record(stream)
+    torch.cuda.synchronize()
+    copy_gbps = 5 * 2 * src.numel() * 2 / (ce[0].elapsed_time(ce[1]) * 1e-3) / 1e9
+    del src, dst
+
     asm_bytes = sum(W.assembly_bytes(w) for w in (wls * args.steps)[:args.steps]) / args.steps
     attn_flops = sum(W.attention_flops(w) for w in (wls * args.steps)[:args.steps]) / args.steps
     ms_step = total_ms / args.steps
@@ -216,6 +240,7 @@ def main():
                    "layouts": args.layouts, "parallelism": "none (1 GPU)"},
         "assembly_GBps": None if asm_gbps is None else round(asm_gbps, 1),
         "assembly_frac_hbm": None if asm_gbps is None else round(asm_gbps / HBM_PEAK_GBPS, 4),
+        "hbm_copy_GBps": round(copy_gbps, 1),
         "attention_TFLOPs": None if attn_tflops is None else round(attn_tflops, 2),
         "attention_frac_peak": None if attn_tflops is None else round(attn_tflops / peak, 4),
         "p50_us_per_request": round(percentile(step_ms, 50) * 1e3, 1),

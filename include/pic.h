@@ -162,9 +162,9 @@ pic_status pic_plan_release(pic_plan* plan);
  * Its prefix rows come first in span-table order (span i, token s_i + t at
  * row row_base_b + sum_{j<i} n_j + t), followed by the new tokens' rows, which
  * pic_query_prefill fills layer by layer.  Prefix keys are rotated by their
- * span's delta in fp32 arithmetic with a phase computed in fp64 and rounded
- * once to the storage type; a span with delta == 0 is copied bit for bit, as
- * are all values.  Overlapping or repeated spans are legal and gathered as
+ * span's delta in fp64 arithmetic (phase cos/sin in fp64) and rounded once,
+ * to nearest even, to the storage type; a span with delta == 0 is copied bit
+ * for bit, as are all values.  Overlapping or repeated spans are legal and gathered as
  * often as they appear.  The call replaces the plan's previous batch.
  */
 pic_status pic_assemble(pic_plan* plan, int32_t batch, const int32_t* span_ptr,
@@ -185,8 +185,8 @@ pic_status pic_assemble(pic_plan* plan, int32_t batch, const int32_t* span_ptr,
  *   out        device [n_new_total][q_heads][head_dim]
  *   variant    PIC_VARIANT_MATERIALIZED or PIC_VARIANT_FUSED
  * New tokens are packed in request order (new_ptr of the assemble call).
- * Steps: rotate q and k_new to the tokens' positions and round them to the
- * storage type; write k' and v_new into the new-token rows of this layer's
+ * Steps: rotate q and k_new to the tokens' positions (fp64 arithmetic, one
+ * rounding to the storage type); write k' and v_new into the new-token rows of this layer's
  * assembled planes (so the planes hold C_ctx (+) KV_M(q; C_ctx) for decoding);
  * then for every new token j and query head h
  *   out[j][h] = sum_r softmax_r(<q'_j,h, k_r> / sqrt(d)) v_r

@@ -65,8 +65,8 @@ struct pic_plan {
   size_t ws_cap = 0;
   size_t off_spans = 0, off_crow = 0, off_reqs = 0, off_new_pos = 0, off_new_row = 0,
          off_new_req = 0, off_work = 0, off_omega = 0, blob_bytes = 0;
-  size_t off_pos = 0, off_rowsrc = 0, off_phase_span = 0, off_phase_new = 0, off_qrot = 0,
-         off_opart = 0, off_ml = 0, ws_bytes = 0;
+  size_t off_pos = 0, off_rowsrc = 0, off_tile_pos = 0, off_phase_span = 0, off_phase_new = 0,
+         off_qrot = 0, off_opart = 0, off_ml = 0, ws_bytes = 0;
 
   // pinned staging for the upload, reused once its copy has completed
   char* staging = nullptr;
@@ -147,6 +147,7 @@ void layout_workspace(pic_plan* p) {
   p->blob_bytes = o;
   p->off_pos = take(size_t(hp.rows) * sizeof(int32_t));
   p->off_rowsrc = take(size_t(hp.rows) * sizeof(int2));
+  p->off_tile_pos = take(size_t(hp.n_tiles) * sizeof(int2));
   p->off_phase_span = take(size_t(hp.n_spans) * half * sizeof(pic::Phase));
   p->off_phase_new = take(size_t(hp.new_rows) * half * sizeof(pic::Phase));
   p->off_qrot = take(size_t(hp.new_rows) * m.q_heads * m.head_dim * m.elem_bytes);
@@ -307,7 +308,7 @@ pic_status pic_assemble(pic_plan* p, int32_t batch, const int32_t* span_ptr, con
   if (st != PIC_OK) return set_err(st, "%s", err.c_str());
   if (pi.m.dtype == PIC_BF16 && pi.m.head_dim == 128)
     pic::build_attention_work(&hp, pi.m.kv_heads, pi.m.group, pic::kAttnColsPerWG,
-                              pic::kAttnRowsPerTile, /*target_wgs=*/512, /*max_split=*/16,
+                              pic::kAttnRowsPerTile, /*target_wgs=*/512, /*max_split=*/pic::kAttnMaxSplit,
                               /*min_tiles_per_split=*/4);
   if (dry) {
     p->hp = std::move(hp);
@@ -381,6 +382,10 @@ pic_status pic_assemble(pic_plan* p, int32_t batch, const int32_t* span_ptr, con
     pa.rowsrc = reinterpret_cast<int2*>(p->ws + p->off_rowsrc);
     pa.phase_span = reinterpret_cast<pic::Phase*>(p->ws + p->off_phase_span);
     pa.phase_new = reinterpret_cast<pic::Phase*>(p->ws + p->off_phase_new);
+    pa.reqs = reinterpret_cast<const pic::ReqRec*>(p->ws + p->off_reqs);
+    pa.batch = h.batch;
+    pa.n_tiles = h.n_tiles;
+    pa.tile_pos = reinterpret_cast<int2*>(p->ws + p->off_tile_pos);
     e = pic::launch_plan(pa, s);
     if (e != hipSuccess) return device_error(p, e, "plan kernels");
   }
@@ -469,6 +474,7 @@ pic_status pic_query_prefill(pic_plan* p, int32_t layer, const void* q, const vo
       aa.v_plane = reinterpret_cast<const uint16_t*>(vpl);
       aa.cap = p->cap;
       aa.pos = reinterpret_cast<const int32_t*>(p->ws + p->off_pos);
+      aa.tile_pos = reinterpret_cast<const int2*>(p->ws + p->off_tile_pos);
       aa.reqs = reinterpret_cast<const pic::ReqRec*>(p->ws + p->off_reqs);
       aa.new_pos = reinterpret_cast<const int32_t*>(p->ws + p->off_new_pos);
       aa.work = reinterpret_cast<const pic::AttnWork*>(p->ws + p->off_work);

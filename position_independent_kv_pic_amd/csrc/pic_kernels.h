@@ -9,9 +9,8 @@
 
 namespace pic {
 
-// Phase of one rotation: (cos, sin) of an fp64 angle, each split into an fp32
-// head and the fp32 remainder: {cos_hi, cos_lo, sin_hi, sin_lo}.
-using Phase = float4;
+// Phase of one rotation: (cos, sin) of the angle, in fp64.
+using Phase = double2;
 
 struct PlanArgs {
   const SpanRec* spans;
@@ -26,6 +25,9 @@ struct PlanArgs {
   int2* rowsrc;             // [rows]: (pool token slot, span or -1)
   Phase* phase_span;        // [n_spans][half_dim]
   Phase* phase_new;         // [n_new][half_dim]
+  const ReqRec* reqs;       // for the tile bounds
+  int32_t batch, n_tiles;
+  int2* tile_pos;           // [n_tiles]: (min, max) row position; max = INT_MAX for a partial tile
 };
 
 struct GatherArgs {
@@ -60,6 +62,7 @@ struct AttnArgs {
   const uint16_t* v_plane;
   int64_t cap;
   const int32_t* pos;
+  const int2* tile_pos;
   const ReqRec* reqs;
   const int32_t* new_pos;
   const AttnWork* work;
@@ -93,6 +96,7 @@ struct AttnF32Args {
 
 constexpr int kAttnColsPerWG = 128;   // 4 waves x 32 query columns
 constexpr int kAttnRowsPerTile = 64;
+constexpr int kAttnMaxSplit = 16;     // merge_kernel handles at most this many row splits
 
 hipError_t launch_plan(const PlanArgs& a, hipStream_t s);
 hipError_t launch_gather(int dtype, int head_dim, const GatherArgs& a, hipStream_t s);

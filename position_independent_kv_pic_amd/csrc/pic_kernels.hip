@@ -1,7 +1,7 @@
 // HIP kernels for position-independent KV-cache reuse on gfx950 (CDNA4).
 //
 //   plan      per-row positions and pool sources, per-span and per-token
-//             RoPE phases (fp64 cos/sin split into fp32 head + remainder)
+//             RoPE phases, per-tile position bounds
 //   gather    assembly: copy every span's cached rows out of the paged pool
 //             into the contiguous prefix, rotating keys by the span's delta
 //             (CoinRAG page, section 2.3, the C_ctx equation and Rot(.; Delta_i);
@@ -15,13 +15,11 @@
 //             32x32x16 with fp32 accumulation and online softmax; optional
 //             split of the rows with a log-sum-exp merge
 //
-// Rotation arithmetic.  Each key pair (x, y) = (k, k + d/2) is rotated by an
-// angle whose cos/sin were computed in fp64 and stored as fp32 head + fp32
-// remainder.  The products are formed exactly with FMA (error-free
-// transformations) and summed with two-sum, so the result carries about 48
-// good bits in two fp32 words; it is then rounded once to bf16 (ties to even,
-// with the remainder breaking exact ties) or to fp32.  A rotation by zero is a
-// bit copy.
+// Rotation arithmetic.  Each key pair (x, y) = (k, k + d/2) is rotated in fp64
+// (fp64 FMA runs at the fp32 rate on CDNA) by an angle whose cos/sin were
+// computed in fp64 once per span or per position.  The fp64 result is rounded
+// once to bf16 (nearest even; see pack_bf16) or to fp32.  A rotation by zero
+// is a bit copy.
 #include "pic_kernels.h"
 
 #include <climits>
@@ -32,59 +30,47 @@ namespace {
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
-
-struct DF {
-  float hi, lo;
-};
+typedef __attribute__((address_space(3))) void* lds_void_ptr;
+typedef __attribute__((address_space(3))) s16x4* lds_s16x4_ptr;
 
 __device__ __forceinline__ float bf16_lo(unsigned w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(unsigned w) { return __uint_as_float(w & 0xffff0000u); }
 
-// Error-free double-float rotation of one pair.
-__device__ __forceinline__ void rotate_pair(float x, float y, Phase ph, DF& xo, DF& yo) {
-#pragma clang fp contract(off)
-  // x' = x cos - y sin
-  float p1 = x * ph.x;
-  float e1 = __builtin_fmaf(x, ph.x, -p1);
-  float p2 = y * ph.z;
-  float e2 = __builtin_fmaf(y, ph.z, -p2);
-  float a = p1 - p2;
-  float av = a - p1;
-  float ea = (p1 - (a - av)) + (-p2 - av);
-  float t = ((e1 - e2) + ea) + (x * ph.y - y * ph.w);
-  float h = a + t;
-  float hv = h - a;
-  xo.hi = h;
-  xo.lo = (a - (h - hv)) + (t - hv);
-  // y' = x sin + y cos
-  float q1 = x * ph.z;
-  float f1 = __builtin_fmaf(x, ph.z, -q1);
-  float q2 = y * ph.x;
-  float f2 = __builtin_fmaf(y, ph.x, -q2);
-  float b = q1 + q2;
-  float bv = b - q1;
-  float eb = (q1 - (b - bv)) + (q2 - bv);
-  float u = ((f1 + f2) + eb) + (x * ph.w + y * ph.y);
-  float g = b + u;
-  float gv = g - b;
-  yo.hi = g;
-  yo.lo = (b - (g - gv)) + (u - gv);
+// fp64 -> fp32 with round-to-odd: truncate toward zero, then set the last bit
+// if anything was lost.
+__device__ __forceinline__ float to_f32_odd(double x) {
+  float r = float(x);  // round to nearest even
+  double back = double(r);
+  unsigned u = __float_as_uint(r);
+  if (back != x) {
+    if (fabs(back) > fabs(x)) u -= 1u;
+    u |= 1u;
+  }
+  return __uint_as_float(u);
 }
 
-// Round a double-float value to bf16 bits, ties to even; an exact tie in the
-// head is broken by the sign of the remainder.
-__device__ __forceinline__ unsigned round_bf16(DF v) {
-  unsigned u = __float_as_uint(v.hi);
-  if ((u & 0x7f800000u) == 0x7f800000u) return (u >> 16) | ((u & 0xffffu) ? 0x40u : 0u);
-  if ((u & 0xffffu) == 0x8000u && v.lo != 0.0f) {
-    bool away = (v.lo > 0.0f) == ((u >> 31) == 0u);
-    return (u >> 16) + (away ? 1u : 0u);
+// Two fp64 values to a packed pair of bf16 (first in the low half), rounded
+// once to nearest even.  Rounding through fp32 first can only differ when the
+// fp32 value lands exactly on a bf16 midpoint (low 16 bits 0x8000): every
+// midpoint is an fp32 number, so otherwise the fp32 value and the fp64 value
+// lie on the same side of all of them.  Those rare cases (any lane of the
+// wave) redo the step with round-to-odd.
+__device__ __forceinline__ unsigned pack_bf16(double a, double b) {
+  float fa = float(a), fb = float(b);
+  const bool tie = ((__float_as_uint(fa) & 0xffffu) == 0x8000u) | ((__float_as_uint(fb) & 0xffffu) == 0x8000u);
+  if (__builtin_amdgcn_ballot_w64(tie)) {
+    fa = to_f32_odd(a);
+    fb = to_f32_odd(b);
   }
-  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+  const __bf16 ha = (__bf16)fa;
+  const __bf16 hb = (__bf16)fb;
+  return unsigned(__builtin_bit_cast(uint16_t, ha)) | (unsigned(__builtin_bit_cast(uint16_t, hb)) << 16);
 }
 
 // Rotate the 16-byte vectors a (elements k) and b (elements k + d/2).
@@ -95,11 +81,13 @@ template <>
 __device__ __forceinline__ void rotate_vec<true>(u32x4& a, u32x4& b, const Phase* ph) {
 #pragma unroll
   for (int w = 0; w < 4; ++w) {
-    DF x0, y0, x1, y1;
-    rotate_pair(bf16_lo(a[w]), bf16_lo(b[w]), ph[2 * w], x0, y0);
-    rotate_pair(bf16_hi(a[w]), bf16_hi(b[w]), ph[2 * w + 1], x1, y1);
-    a[w] = round_bf16(x0) | (round_bf16(x1) << 16);
-    b[w] = round_bf16(y0) | (round_bf16(y1) << 16);
+    const double x0 = bf16_lo(a[w]), x1 = bf16_hi(a[w]);
+    const double y0 = bf16_lo(b[w]), y1 = bf16_hi(b[w]);
+    const Phase p0 = ph[2 * w], p1 = ph[2 * w + 1];
+    const double rx0 = fma(x0, p0.x, -y0 * p0.y), ry0 = fma(x0, p0.y, y0 * p0.x);
+    const double rx1 = fma(x1, p1.x, -y1 * p1.y), ry1 = fma(x1, p1.y, y1 * p1.x);
+    a[w] = pack_bf16(rx0, rx1);
+    b[w] = pack_bf16(ry0, ry1);
   }
 }
 
@@ -107,22 +95,22 @@ template <>
 __device__ __forceinline__ void rotate_vec<false>(u32x4& a, u32x4& b, const Phase* ph) {
 #pragma unroll
   for (int w = 0; w < 4; ++w) {
-    DF x, y;
-    rotate_pair(__uint_as_float(a[w]), __uint_as_float(b[w]), ph[w], x, y);
-    a[w] = __float_as_uint(x.hi);
-    b[w] = __float_as_uint(y.hi);
+    const double x = __uint_as_float(a[w]), y = __uint_as_float(b[w]);
+    const Phase p = ph[w];
+    a[w] = __float_as_uint(float(fma(x, p.x, -y * p.y)));
+    b[w] = __float_as_uint(float(fma(x, p.y, y * p.x)));
   }
 }
 
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 __device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
 
-// Last span whose first compact row is <= u (spans are never empty).
-__device__ __forceinline__ int find_span(const int32_t* crow, int n_spans, int64_t u) {
-  int lo = 0, hi = n_spans;
+// Last entry of a non-decreasing table whose value is <= u.
+__device__ __forceinline__ int find_le(const int32_t* tbl, int n, int64_t u) {
+  int lo = 0, hi = n;
   while (hi - lo > 1) {
     int mid = (lo + hi) >> 1;
-    if (crow[mid] <= u)
+    if (tbl[mid] <= u)
       lo = mid;
     else
       hi = mid;
@@ -139,14 +127,28 @@ __device__ __forceinline__ int xcd_remap(int bid, int n) {
   return x * q + min(x, r) + k;
 }
 
+// max(a, b, c) as one instruction.  fmaxf in IEEE mode first quiets each
+// MFMA result (one extra instruction per input); scores are never NaN here.
+__device__ __forceinline__ float max3(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
+// Max of a value and its copy in the lane 32 away.
+__device__ __forceinline__ float max_halves(float v) {
+  auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return max3(__uint_as_float(s[0]), __uint_as_float(s[1]), __uint_as_float(s[1]));
+}
+
 // ---------------------------------------------------------------------------
-// plan: positions, pool sources, phases
+// plan: positions, pool sources, phases, tile bounds
 // ---------------------------------------------------------------------------
 
 __global__ __launch_bounds__(256) void plan_rows_kernel(PlanArgs a) {
   int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
   if (i < a.prefix_rows) {
-    int sp = find_span(a.crow, a.n_spans, i);
+    int sp = find_le(a.crow, a.n_spans, i);
     SpanRec s = a.spans[sp];
     int t = int(i - s.crow);
     int tok = s.s + t;
@@ -180,9 +182,36 @@ __global__ __launch_bounds__(256) void plan_phase_kernel(PlanArgs a) {
     dst = a.phase_new + int64_t(u) * a.half_dim + k;
   }
   double ang = p * a.omega[k];
-  double c = cos(ang), s = sin(ang);
-  float ch = float(c), sh = float(s);
-  *dst = make_float4(ch, float(c - double(ch)), sh, float(s - double(sh)));
+  *dst = make_double2(cos(ang), sin(ang));
+}
+
+// One thread per 64-row tile: the smallest and largest row position, with the
+// largest replaced by INT_MAX when the tile runs past the request's rows.
+__global__ __launch_bounds__(256) void plan_tiles_kernel(PlanArgs a) {
+  int tix = int(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (tix >= a.n_tiles) return;
+  int lo = 0, hi = a.batch;
+  while (hi - lo > 1) {
+    int mid = (lo + hi) >> 1;
+    if (a.reqs[mid].tile_base <= tix)
+      lo = mid;
+    else
+      hi = mid;
+  }
+  // requests without rows own no tiles: step to the last one starting here
+  while (lo + 1 < a.batch && a.reqs[lo + 1].tile_base <= tix) ++lo;
+  const ReqRec r = a.reqs[lo];
+  const int rows = r.prefix_rows + r.n_new;
+  const int r0 = (tix - r.tile_base) * kAttnRowsPerTile;
+  const int r1 = min(r0 + kAttnRowsPerTile, rows);
+  int mn = INT_MAX, mx = INT_MIN;
+  for (int rr = r0; rr < r1; ++rr) {
+    int p = a.pos[r.row_base + rr];
+    mn = min(mn, p);
+    mx = max(mx, p);
+  }
+  if (r1 - r0 < kAttnRowsPerTile) mx = INT_MAX;
+  a.tile_pos[tix] = make_int2(mn, mx);
 }
 
 // ---------------------------------------------------------------------------
@@ -205,13 +234,13 @@ __global__ __launch_bounds__(256) void gather_kernel(GatherArgs a) {
   const int j = threadIdx.x % LPR;
   const int64_t u = int64_t(blockIdx.x) * RPB + rl;
   if (u >= a.prefix_rows) return;
-  const int sp = find_span(a.crow, a.n_spans, u);
+  const int sp = find_le(a.crow, a.n_spans, u);
   const SpanRec s = a.spans[sp];
   const int t = int(u - s.crow);
   const int tok = s.s + t;
   const int page = a.page_ids[s.page_off + (tok >> a.page_shift)];
   const int slot = tok & (a.page_tokens - 1);
-  const char* src_row = a.pool + int64_t(page) * a.page_bytes + int64_t(slot) * RB;
+  const char* __restrict__ src_row = a.pool + int64_t(page) * a.page_bytes + int64_t(slot) * RB;
   const int64_t dst_row = int64_t(s.dst_row) + t;
   const bool rot = s.delta != 0;
   Phase ph[EPV];
@@ -224,21 +253,34 @@ __global__ __launch_bounds__(256) void gather_kernel(GatherArgs a) {
   const int p0 = blockIdx.y * a.planes_per_block;
   const int p1 = min(p0 + a.planes_per_block, n_planes);
   const int64_t plane_stride = int64_t(a.page_tokens) * RB;  // one (layer, K/V, head) run
-  for (int pl = p0; pl < p1; ++pl) {
-    const int l = pl / a.kv_heads;
-    const int h = pl - l * a.kv_heads;
-    const char* ks = src_row + (int64_t(l) * 2 * a.kv_heads + h) * plane_stride;
-    const char* vs = ks + int64_t(a.kv_heads) * plane_stride;
-    u32x4 k0 = ld16(ks + j * 16);
-    u32x4 k1 = ld16(ks + RB / 2 + j * 16);
-    u32x4 v0 = ld16(vs + j * 16);
-    u32x4 v1 = ld16(vs + RB / 2 + j * 16);
-    const int64_t off = (int64_t(pl) * a.cap + dst_row) * RB;
-    if (rot) rotate_vec<BF16>(k0, k1, ph);
-    st16(a.asm_k + off + j * 16, k0);
-    st16(a.asm_k + off + RB / 2 + j * 16, k1);
-    st16(a.asm_v + off + j * 16, v0);
-    st16(a.asm_v + off + RB / 2 + j * 16, v1);
+  char* __restrict__ ak = a.asm_k;
+  char* __restrict__ av = a.asm_v;
+  // two planes per iteration: all eight loads are in flight before any store
+  for (int pl = p0; pl < p1; pl += 2) {
+    const bool two = pl + 1 < p1;
+    u32x4 k0[2], k1[2], v0[2], v1[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int pq = two ? pl + q : pl;
+      const int l = pq / a.kv_heads;
+      const int h = pq - l * a.kv_heads;
+      const char* ks = src_row + (int64_t(l) * 2 * a.kv_heads + h) * plane_stride;
+      const char* vs = ks + int64_t(a.kv_heads) * plane_stride;
+      k0[q] = ld16(ks + j * 16);
+      k1[q] = ld16(ks + RB / 2 + j * 16);
+      v0[q] = ld16(vs + j * 16);
+      v1[q] = ld16(vs + RB / 2 + j * 16);
+    }
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      if (q == 1 && !two) break;
+      const int64_t off = (int64_t(pl + q) * a.cap + dst_row) * RB;
+      if (rot) rotate_vec<BF16>(k0[q], k1[q], ph);
+      st16(ak + off + j * 16, k0[q]);
+      st16(ak + off + RB / 2 + j * 16, k1[q]);
+      st16(av + off + j * 16, v0[q]);
+      st16(av + off + RB / 2 + j * 16, v1[q]);
+    }
   }
 }
 
@@ -246,50 +288,69 @@ __global__ __launch_bounds__(256) void gather_kernel(GatherArgs a) {
 // new-token prologue
 // ---------------------------------------------------------------------------
 
-// Row units: for each new token u, Hq query rows, Hkv key rows, Hkv value rows.
+// Each token owns Hq query rows, Hkv key rows and Hkv value rows.  A group of
+// LPR lanes takes one token and kPrologueRows consecutive rows of it, so the
+// token's phases are loaded once per group and reused for every row.
+constexpr int kPrologueRows = 4;
+
 template <bool BF16, int D>
 __global__ __launch_bounds__(256) void prologue_kernel(PrologueArgs a) {
   constexpr int ES = BF16 ? 2 : 4;
   constexpr int EPV = 16 / ES;
   constexpr int LPR = D / (2 * EPV);
-  constexpr int RPB = 256 / LPR;
+  constexpr int GPB = 256 / LPR;   // lane groups per block
   constexpr int64_t RB = int64_t(D) * ES;
   const int per_tok = a.q_heads + 2 * a.kv_heads;
-  const int64_t unit = int64_t(blockIdx.x) * RPB + threadIdx.x / LPR;
+  const int chunks = (per_tok + kPrologueRows - 1) / kPrologueRows;
+  const int64_t grp = int64_t(blockIdx.x) * GPB + threadIdx.x / LPR;
   const int j = threadIdx.x % LPR;
-  if (unit >= int64_t(a.n_new) * per_tok) return;
-  const int u = int(unit / per_tok);
-  const int w = int(unit - int64_t(u) * per_tok);
-  const char* src;
-  char* dst;
-  bool rot;
-  if (w < a.q_heads) {
-    src = a.q + (int64_t(u) * a.q_heads + w) * RB;
-    dst = a.q_rot + (int64_t(u) * a.q_heads + w) * RB;
-    rot = true;
-  } else if (w < a.q_heads + a.kv_heads) {
-    int h = w - a.q_heads;
-    src = a.k_new + (int64_t(u) * a.kv_heads + h) * RB;
-    dst = a.asm_k + (int64_t(h) * a.cap + a.new_row[u]) * RB;
-    rot = true;
-  } else {
-    int h = w - a.q_heads - a.kv_heads;
-    src = a.v_new + (int64_t(u) * a.kv_heads + h) * RB;
-    dst = a.asm_v + (int64_t(h) * a.cap + a.new_row[u]) * RB;
-    rot = false;
-  }
-  rot = rot && a.new_pos[u] != 0;
-  u32x4 x0 = ld16(src + j * 16);
-  u32x4 x1 = ld16(src + RB / 2 + j * 16);
-  if (rot) {
-    Phase ph[EPV];
+  if (grp >= int64_t(a.n_new) * chunks) return;
+  const int u = int(grp / chunks);
+  const int w0 = int(grp - int64_t(u) * chunks) * kPrologueRows;
+  const int w1 = min(w0 + kPrologueRows, per_tok);
+  const bool rot_tok = a.new_pos[u] != 0;
+  Phase ph[EPV];
+  if (rot_tok && w0 < a.q_heads + a.kv_heads) {
     const Phase* pp = a.phase_new + int64_t(u) * (D / 2) + j * EPV;
 #pragma unroll
     for (int e = 0; e < EPV; ++e) ph[e] = pp[e];
-    rotate_vec<BF16>(x0, x1, ph);
   }
-  st16(dst + j * 16, x0);
-  st16(dst + RB / 2 + j * 16, x1);
+  const int row = a.new_row[u];
+  // issue every row's loads before any rotation or store
+  u32x4 x0[kPrologueRows], x1[kPrologueRows];
+  char* dst[kPrologueRows];
+  bool rot[kPrologueRows];
+#pragma unroll
+  for (int i = 0; i < kPrologueRows; ++i) {
+    const int w = w0 + i;
+    dst[i] = nullptr;
+    rot[i] = false;
+    if (w >= w1) continue;
+    const char* src;
+    if (w < a.q_heads) {
+      src = a.q + (int64_t(u) * a.q_heads + w) * RB;
+      dst[i] = a.q_rot + (int64_t(u) * a.q_heads + w) * RB;
+      rot[i] = rot_tok;
+    } else if (w < a.q_heads + a.kv_heads) {
+      const int h = w - a.q_heads;
+      src = a.k_new + (int64_t(u) * a.kv_heads + h) * RB;
+      dst[i] = a.asm_k + (int64_t(h) * a.cap + row) * RB;
+      rot[i] = rot_tok;
+    } else {
+      const int h = w - a.q_heads - a.kv_heads;
+      src = a.v_new + (int64_t(u) * a.kv_heads + h) * RB;
+      dst[i] = a.asm_v + (int64_t(h) * a.cap + row) * RB;
+    }
+    x0[i] = ld16(src + j * 16);
+    x1[i] = ld16(src + RB / 2 + j * 16);
+  }
+#pragma unroll
+  for (int i = 0; i < kPrologueRows; ++i) {
+    if (!dst[i]) continue;
+    if (rot[i]) rotate_vec<BF16>(x0[i], x1[i], ph);
+    st16(dst[i] + j * 16, x0[i]);
+    st16(dst[i] + RB / 2 + j * 16, x1[i]);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -300,146 +361,183 @@ __global__ __launch_bounds__(256) void prologue_kernel(PrologueArgs a) {
 // range of 64-row tiles.  Column c of a request is token c / G, query head
 // c % G of the group, so the G heads that share a kv head share every K/V
 // tile.  Per wave, with its 32 columns as the MFMA N dimension:
-//   S^T = K Q^T   (A = K rows from LDS, B = the wave's rotated queries held in
-//                  registers), 2 x 8 MFMA 32x32x16 per tile;
-//   O^T += V^T P^T (A = V^T from LDS, B = the wave's own probabilities: the
-//                  S^T accumulator layout puts each column's 16 row values of
-//                  a 32-row block in one lane, which is the B layout needed
-//                  here once the row order inside a k-step is permuted the
-//                  same way for A), 4 x 2 x 2 MFMA per tile.
+//   S^T = K Q^T   (A = 32-row K fragments from LDS, B = the wave's rotated
+//                  queries, held in registers), 2 x 8 MFMA 32x32x16 per tile;
+//   O^T += V^T P^T (A = V^T fragments read with the LDS transpose load,
+//                  B = the wave's own probabilities: the S^T accumulator puts
+//                  each column's 16 row values of a 32-row block in one lane,
+//                  which is the B layout needed here once the row order inside
+//                  a k-step is permuted identically for A), 4 x 2 x 2 MFMA.
 // Each lane therefore owns one query column: the softmax statistics are
 // lane-local plus one exchange with the lane 32 away.
 //
-// LDS per stage: K tile [64 rows][128] with 16-byte granules XOR-swizzled by
-// row (conflict-free row-strided reads), V^T tile [128][64 rows] in 8-byte
-// granules of 4 rows rotated by (d + d/16) mod 16 (conflict-free transposed
-// writes and reads), 64 row positions and the tile's min/max position.
-// Two stages: the next tile is fetched into registers while the current one
-// is consumed.
+// Tiles: K and V, 64 rows x 256 bytes each, row-major with 16-byte granules
+// XOR-swizzled by row, are copied global -> LDS directly (no registers) by
+// 16-byte lane loads whose source addresses apply the swizzle.  Two stages:
+// the next tile streams in while the current one is consumed; one barrier per
+// tile.  Rows past the request's end repeat its last row and are masked by
+// position.
+//
+// Softmax: scores are kept relative to a reference maximum that is raised
+// only when a tile's maximum exceeds it by more than 8 (log2 units), so the
+// accumulator rescale is rare; probabilities stay below 2^8.
 
-constexpr int kStageBytes = 33280;  // 16384 K + 16384 V^T + 272 pos, padded
-constexpr int kPosOff = 32768;
+constexpr int kTileBytes = 16384;
+constexpr int kPosOffset = 2 * kTileBytes;          // 64 row positions after K and V
+constexpr int kStageBytes = 2 * kTileBytes + 256;
+constexpr float kRescaleSlack = 8.0f;
 
-__device__ __forceinline__ int vt_offset(int d, int gran) {
-  return d * 128 + 8 * ((gran + ((d + (d >> 4)) & 15)) & 15);
+// LDS swizzles of the 16-byte granules of a tile row.  Keys are read as one
+// 16-byte granule per lane from 32 consecutive rows, so granules are XORed
+// with the row index (mod 16); values are read with the transpose load, whose
+// 16-lane groups touch 4 consecutive rows x 2 granules x 2 halves, so their
+// granules are XORed with 2 * (row mod 4).  Either way each 16-lane group hits
+// distinct banks.
+__device__ __forceinline__ int k_swz(int r) { return r & 15; }
+__device__ __forceinline__ int v_swz(int r) { return 2 * (r & 3); }
+
+// Copy one 64-row tile of one plane into LDS.  `base` is the request's row 0,
+// `wave` the wave index (scalar).  Rows past the request's end repeat its
+// last row (only the request's last tile has any).
+template <bool VALUE>
+__device__ __forceinline__ void tile_to_lds(const char* base, int t0, int rows, char* lds, int wave) {
+  const int lane = threadIdx.x & 63;
+  const bool full = t0 + kAttnRowsPerTile <= rows;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int blk = wave * 4 + i;                 // 1 KB block = 4 rows
+    const int r = blk * 4 + (lane >> 4);
+    const int rr = full ? t0 + r : min(t0 + r, rows - 1);
+    const int gran = (lane & 15) ^ (VALUE ? v_swz(r) : k_swz(r));
+    __builtin_amdgcn_global_load_lds(base + int64_t(rr) * 256 + gran * 16,
+                                     (lds_void_ptr)(lds + blk * 1024), 16, 0, 0);
+  }
 }
 
-template <bool FUSED>
-struct TileRegs {
-  u32x4 k[2][2];   // [unit][half]
-  u32x4 v[4];      // rows 4*kv4 + 0..3, granule c
-  int pos;
+// Row positions of one tile into LDS (wave 0, one 4-byte lane load each).
+// Rows past the request's end repeat its last row; readers mask them by index.
+__device__ __forceinline__ void pos_to_lds(const int32_t* pos_row0, int t0, int rows, char* lds) {
+  if ((threadIdx.x >> 6) == 0) {
+    const int rr = min(t0 + int(threadIdx.x), rows - 1);
+    __builtin_amdgcn_global_load_lds(pos_row0 + rr, (lds_void_ptr)lds, 4, 0, 0);
+  }
+}
+
+// Fused variant: value rows straight from the pool pages (prefix rows) or the
+// assembled tail (new rows).
+__device__ __forceinline__ const char* fused_row(const AttnArgs& a, const ReqRec& rq, int head,
+                                                 int rr, bool value, int2* src_out) {
+  if (rr < rq.prefix_rows) {
+    const int2 src = a.rowsrc[rq.row_base + rr];
+    if (src_out) *src_out = src;
+    return a.pool + int64_t(src.x >> a.page_shift) * a.page_bytes + a.kv_plane_off +
+           (value ? a.v_off : 0) + (int64_t(head) * a.page_tokens + (src.x & (a.page_tokens - 1))) * 256;
+  }
+  if (src_out) *src_out = make_int2(-1, -1);
+  const uint16_t* plane = value ? a.v_plane : a.k_plane;
+  return reinterpret_cast<const char*>(plane + (int64_t(head) * a.cap + rq.row_base + rr) * 128);
+}
+
+__device__ __forceinline__ void fused_v_to_lds(const AttnArgs& a, const ReqRec& rq, int head, int t0,
+                                               int rows, char* lds) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int blk = wave * 4 + i;
+    const int r = blk * 4 + (lane >> 4);
+    const int rr = min(t0 + r, rows - 1);
+    const int gran = (lane & 15) ^ v_swz(r);
+    const char* row = fused_row(a, rq, head, rr, true, nullptr);
+    __builtin_amdgcn_global_load_lds(row + gran * 16, (lds_void_ptr)(lds + blk * 1024), 16, 0, 0);
+  }
+}
+
+// Fused variant: keys through registers (rotated on the way) into the same
+// swizzled layout.  Thread units: rows (tid >> 3) + 32 i, pair vector j = tid & 7.
+struct FusedK {
+  u32x4 k[2][2];
+  int span[2];
 };
 
-template <bool FUSED>
-__device__ __forceinline__ void load_tile(const AttnArgs& a, int row_base, int prefix_rows,
-                                          int rows, int head, int tile, TileRegs<FUSED>& r) {
+__device__ __forceinline__ void fused_k_load(const AttnArgs& a, const ReqRec& rq, int head, int t0,
+                                             int rows, FusedK& f) {
   const int tid = threadIdx.x;
-  const int t0 = tile * kAttnRowsPerTile;
-  // keys: units (row, j) with j = tid & 7 and rows (tid >> 3) + 32 i
+  const int j = tid & 7;
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
-    const int rr = t0 + (tid >> 3) + 32 * i;
-    const int j = tid & 7;
-    if (rr < rows) {
-      if (FUSED && rr < prefix_rows) {
-        const int2 src = a.rowsrc[row_base + rr];
-        const char* p = a.pool + int64_t(src.x >> a.page_shift) * a.page_bytes + a.kv_plane_off +
-                        (int64_t(head) * a.page_tokens + (src.x & (a.page_tokens - 1))) * 256;
-        r.k[i][0] = ld16(p + j * 16);
-        r.k[i][1] = ld16(p + 128 + j * 16);
-        if (src.y >= 0) {
-          Phase ph[8];
-          const Phase* pp = a.phase_span + int64_t(src.y) * 64 + j * 8;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) ph[e] = pp[e];
-          rotate_vec<true>(r.k[i][0], r.k[i][1], ph);
-        }
-      } else {
-        const uint16_t* p = a.k_plane + (int64_t(head) * a.cap + row_base + rr) * 128;
-        r.k[i][0] = ld16(p + j * 8);
-        r.k[i][1] = ld16(p + 64 + j * 8);
-      }
-    } else {
-      r.k[i][0] = u32x4{0, 0, 0, 0};
-      r.k[i][1] = u32x4{0, 0, 0, 0};
-    }
-  }
-  // values: rows 4 * (tid >> 4) + 0..3, granule tid & 15
-  const int c = tid & 15;
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int rr = t0 + 4 * (tid >> 4) + q;
-    if (rr < rows) {
-      if (FUSED && rr < prefix_rows) {
-        const int2 src = a.rowsrc[row_base + rr];
-        const char* p = a.pool + int64_t(src.x >> a.page_shift) * a.page_bytes + a.kv_plane_off +
-                        a.v_off + (int64_t(head) * a.page_tokens + (src.x & (a.page_tokens - 1))) * 256;
-        r.v[q] = ld16(p + c * 16);
-      } else {
-        r.v[q] = ld16(a.v_plane + (int64_t(head) * a.cap + row_base + rr) * 128 + c * 8);
-      }
-    } else {
-      r.v[q] = u32x4{0, 0, 0, 0};
-    }
-  }
-  if (tid < 64) {
-    const int rr = t0 + tid;
-    r.pos = rr < rows ? a.pos[row_base + rr] : INT_MAX;
+    const int r = (tid >> 3) + 32 * i;
+    const int rr = min(t0 + r, rows - 1);
+    int2 src;
+    const char* row = fused_row(a, rq, head, rr, false, &src);
+    f.k[i][0] = ld16(row + j * 16);
+    f.k[i][1] = ld16(row + 128 + j * 16);
+    f.span[i] = src.y;
   }
 }
 
-template <bool FUSED>
-__device__ __forceinline__ void store_tile(char* st, const TileRegs<FUSED>& r) {
+__device__ __forceinline__ void fused_k_store(const AttnArgs& a, FusedK& f, char* lds) {
   const int tid = threadIdx.x;
+  const int j = tid & 7;
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
-    const int row = (tid >> 3) + 32 * i;
-    const int j = tid & 7;
-    st16(st + row * 256 + 16 * (j ^ (row & 15)), r.k[i][0]);
-    st16(st + row * 256 + 16 * ((j + 8) ^ (row & 15)), r.k[i][1]);
-  }
-  // transpose 4 rows x 8 d into 8 granules of 4 rows (one per d)
-  const int kv4 = tid >> 4;
-  const int c = tid & 15;
-  char* vt = st + 16384;
+    const int r = (tid >> 3) + 32 * i;
+    if (f.span[i] >= 0) {
+      Phase ph[8];
+      const Phase* pp = a.phase_span + int64_t(f.span[i]) * 64 + j * 8;
 #pragma unroll
-  for (int w = 0; w < 4; ++w) {
-    const unsigned a0 = r.v[0][w], a1 = r.v[1][w], a2 = r.v[2][w], a3 = r.v[3][w];
-    const int d0 = 8 * c + 2 * w;
-    u32x2 lo, hi;
-    lo[0] = (a0 & 0xffffu) | (a1 << 16);
-    lo[1] = (a2 & 0xffffu) | (a3 << 16);
-    hi[0] = (a0 >> 16) | (a1 & 0xffff0000u);
-    hi[1] = (a2 >> 16) | (a3 & 0xffff0000u);
-    *reinterpret_cast<u32x2*>(vt + vt_offset(d0, kv4)) = lo;
-    *reinterpret_cast<u32x2*>(vt + vt_offset(d0 + 1, kv4)) = hi;
-  }
-  if (tid < 64) {
-    int* ps = reinterpret_cast<int*>(st + kPosOff);
-    ps[tid] = r.pos;
-    int mn = r.pos, mx = r.pos;
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-      mn = min(mn, __shfl_xor(mn, o));
-      mx = max(mx, __shfl_xor(mx, o));
+      for (int e = 0; e < 8; ++e) ph[e] = pp[e];
+      rotate_vec<true>(f.k[i][0], f.k[i][1], ph);
     }
-    if (tid == 0) {
-      ps[64] = mn;
-      ps[65] = mx;
-    }
+    st16(lds + r * 256 + 16 * (j ^ k_swz(r)), f.k[i][0]);
+    st16(lds + r * 256 + 16 * ((j + 8) ^ k_swz(r)), f.k[i][1]);
   }
+}
+
+__device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// LDS transpose read (ds_read_b64_tr_b16) issued as inline asm.  The
+// intrinsic form makes the compiler wait for every outstanding global->LDS
+// copy before it (it cannot tell that they target the other stage); here the
+// caller waits with lds_wait() instead, which also orders the results.
+template <int OFF>
+__device__ __forceinline__ s16x4 tr_read(unsigned addr) {
+  s16x4 r;
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
+  return r;
+}
+
+struct TrBlock {
+  s16x4 x[8];   // [kb][s2][half] of one 32-wide d block
+};
+
+__device__ __forceinline__ void tr_block_read(unsigned a0, unsigned a1, TrBlock& b) {
+  b.x[0] = tr_read<0>(a0);
+  b.x[1] = tr_read<0>(a1);
+  b.x[2] = tr_read<16 * 256>(a0);
+  b.x[3] = tr_read<16 * 256>(a1);
+  b.x[4] = tr_read<32 * 256>(a0);
+  b.x[5] = tr_read<32 * 256>(a1);
+  b.x[6] = tr_read<48 * 256>(a0);
+  b.x[7] = tr_read<48 * 256>(a1);
+}
+
+// Wait for every LDS read of this wave; the block's registers are tied to the
+// wait so no use can move above it.
+__device__ __forceinline__ void lds_wait(TrBlock& b) {
+  asm volatile("s_waitcnt lgkmcnt(0)"
+               : "+v"(b.x[0]), "+v"(b.x[1]), "+v"(b.x[2]), "+v"(b.x[3]), "+v"(b.x[4]), "+v"(b.x[5]),
+                 "+v"(b.x[6]), "+v"(b.x[7]));
 }
 
 template <bool FUSED>
 __global__ __launch_bounds__(256, 2) void attention_bf16_kernel(AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) char smem[2 * kStageBytes];
+  __shared__ __attribute__((aligned(1024))) char smem[2 * kStageBytes];
   const int bid = xcd_remap(blockIdx.x, gridDim.x);
   const AttnWork w = a.work[bid];
   const ReqRec rq = a.reqs[w.req];
   const int rows = rq.prefix_rows + rq.n_new;
   const int ncols = rq.n_new * a.group;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int g2 = lane >> 5;
   const int lq = lane & 31;
@@ -467,157 +565,242 @@ __global__ __launch_bounds__(256, 2) void attention_bf16_kernel(AttnArgs a) {
     for (int s = 0; s < 8; ++s) qb[s] = __builtin_bit_cast(bf16x8, qp[2 * s + g2]);
   }
 
-  f32x16 o[4];
+  // per-lane LDS offsets (the tile row block and stage fold into immediates)
+  int koff[8];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) o[i] = f32x16{};
-  float m = -INFINITY, l = 0.0f;
-
-  const int tb = w.tile_begin, te = w.tile_end;
-  if (tb < te) {
-    TileRegs<FUSED> regs;
-    load_tile<FUSED>(a, rq.row_base, rq.prefix_rows, rows, w.head, tb, regs);
-    store_tile<FUSED>(smem, regs);
-    __syncthreads();
-    for (int t = tb; t < te; ++t) {
-      const int stage = (t - tb) & 1;
-      if (t + 1 < te) load_tile<FUSED>(a, rq.row_base, rq.prefix_rows, rows, w.head, t + 1, regs);
-      const char* st = smem + stage * kStageBytes;
-      const int* ps = reinterpret_cast<const int*>(st + kPosOff);
-      const int tmin = ps[64], tmax = ps[65];
-      if (tmin <= wq_max) {
-        // S^T = K Q^T
-        f32x16 sacc[2];
+  for (int s = 0; s < 8; ++s) koff[s] = lq * 256 + 16 * ((2 * s + g2) ^ k_swz(lq));
+  int voff[4][2];
+  {
+    const int l16 = lane & 15, gm = (lane >> 4) & 1;
+    const int c = 2 * gm + ((l16 & 3) >> 1);
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          sacc[kb] = f32x16{};
-          const int row = 32 * kb + lq;
-          const char* kr = st + row * 256;
+    for (int h = 0; h < 2; ++h) {
+      const int rowi = 8 * h + 4 * g2 + (l16 >> 2);
 #pragma unroll
-          for (int s = 0; s < 8; ++s) {
-            const bf16x8 kf = __builtin_bit_cast(bf16x8, ld16(kr + 16 * ((2 * s + g2) ^ (row & 15))));
-            sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qb[s], sacc[kb], 0, 0, 0);
-          }
-        }
-        if (tmax > wq_min) {
-          // rows of this tile may be later than some query: mask pos_row > pos_q
-#pragma unroll
-          for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-            for (int qq = 0; qq < 4; ++qq) {
-              const i32x4 p4 = *reinterpret_cast<const i32x4*>(ps + 32 * kb + 8 * qq + 4 * g2);
-#pragma unroll
-              for (int e = 0; e < 4; ++e)
-                if (p4[e] > qpos) sacc[kb][4 * qq + e] = -INFINITY;
-            }
-          }
-        }
-        float mx = -INFINITY;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb][i]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float mnew = fmaxf(m, mx * a.scale_log2);
-        const float mb = mnew == -INFINITY ? 0.0f : mnew;
-        const float alpha = __builtin_amdgcn_exp2f(m - mb);
-        float rs = 0.0f;
-        bf16x8 pb[2][2];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][i], a.scale_log2, -mb));
-            rs += p;
-            pb[kb][i >> 3][i & 7] = (__bf16)p;
-          }
-        }
-        l = l * alpha + rs;
-        m = mnew;
-#pragma unroll
-        for (int db = 0; db < 4; ++db) o[db] *= alpha;
-        // O^T += V^T P^T
-        const char* vt = st + 16384;
-#pragma unroll
-        for (int db = 0; db < 4; ++db) {
-          const int d = 32 * db + lq;
-#pragma unroll
-          for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-            for (int s2 = 0; s2 < 2; ++s2) {
-              const int ga = 8 * kb + 4 * s2 + g2;
-              const u32x2 x0 = *reinterpret_cast<const u32x2*>(vt + vt_offset(d, ga));
-              const u32x2 x1 = *reinterpret_cast<const u32x2*>(vt + vt_offset(d, ga + 2));
-              const u32x4 xv = {x0[0], x0[1], x1[0], x1[1]};
-              o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, xv),
-                                                              pb[kb][s2], o[db], 0, 0, 0);
-            }
-          }
-        }
-      }
-      if (t + 1 < te) store_tile<FUSED>(smem + (stage ^ 1) * kStageBytes, regs);
-      __syncthreads();
+      for (int db = 0; db < 4; ++db)
+        voff[db][h] = kTileBytes + rowi * 256 + 16 * ((4 * db + c) ^ v_swz(rowi)) + 8 * (l16 & 1);
     }
   }
 
-  const float lt = l + __shfl_xor(l, 32);
-  if (!col_ok) return;
-  if (a.n_split == 1) {
-    const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
-    uint16_t* op = a.out + (int64_t(u) * a.q_heads + hq) * 128;
+  f32x16 o[4];
 #pragma unroll
-    for (int db = 0; db < 4; ++db) {
+  for (int i = 0; i < 4; ++i) o[i] = f32x16{};
+  f32x16 lacc = f32x16{};   // every row holds the column's running sum of weights
+  float m = -INFINITY;
+  const bf16x8 ones = __builtin_bit_cast(bf16x8, u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
+
+  const char* kbase = reinterpret_cast<const char*>(a.k_plane + (int64_t(w.head) * a.cap + rq.row_base) * 128);
+  const char* vbase = reinterpret_cast<const char*>(a.v_plane + (int64_t(w.head) * a.cap + rq.row_base) * 128);
+  const int32_t* pbase = a.pos + rq.row_base;
+  const int tb = w.tile_begin, te = w.tile_end;
+  FusedK fk;
+  int2 tp_next = make_int2(INT_MAX, INT_MAX);
+  if (tb < te) {
+    tp_next = a.tile_pos[rq.tile_base + tb];
+    if (FUSED) {
+      fused_k_load(a, rq, w.head, tb * kAttnRowsPerTile, rows, fk);
+      fused_v_to_lds(a, rq, w.head, tb * kAttnRowsPerTile, rows, smem + kTileBytes);
+      fused_k_store(a, fk, smem);
+    } else {
+      tile_to_lds<false>(kbase, tb * kAttnRowsPerTile, rows, smem, wave);
+      tile_to_lds<true>(vbase, tb * kAttnRowsPerTile, rows, smem + kTileBytes, wave);
+    }
+    pos_to_lds(pbase, tb * kAttnRowsPerTile, rows, smem + kPosOffset);
+  }
+  for (int t = tb; t < te; ++t) {
+    const int stage = (t - tb) & 1;
+    wait_vm();
+    __syncthreads();
+    const bool more = t + 1 < te;
+    char* nxt = smem + (stage ^ 1) * kStageBytes;
+    // this tile's bounds were fetched before the next tile's copies were issued,
+    // so reading them never waits on those copies
+    const int2 tp = tp_next;
+    if (more) {
+      tp_next = a.tile_pos[rq.tile_base + t + 1];
+      const int t1 = (t + 1) * kAttnRowsPerTile;
+      if (FUSED) {
+        fused_k_load(a, rq, w.head, t1, rows, fk);
+        fused_v_to_lds(a, rq, w.head, t1, rows, nxt + kTileBytes);
+      } else {
+        tile_to_lds<false>(kbase, t1, rows, nxt, wave);
+        tile_to_lds<true>(vbase, t1, rows, nxt + kTileBytes, wave);
+      }
+      pos_to_lds(pbase, t1, rows, nxt + kPosOffset);
+    }
+    const char* st = smem + stage * kStageBytes;
+    if (tp.x <= wq_max) {
+      // S^T = K Q^T
+      bf16x8 kf[2][8];
 #pragma unroll
-      for (int qq = 0; qq < 4; ++qq) {
-        const int d0 = 32 * db + 8 * qq + 4 * g2;
-        u32x2 pk;
-        const __bf16 b0 = (__bf16)(o[db][4 * qq + 0] * inv), b1 = (__bf16)(o[db][4 * qq + 1] * inv);
-        const __bf16 b2 = (__bf16)(o[db][4 * qq + 2] * inv), b3 = (__bf16)(o[db][4 * qq + 3] * inv);
-        pk[0] = unsigned(__builtin_bit_cast(uint16_t, b0)) | (unsigned(__builtin_bit_cast(uint16_t, b1)) << 16);
-        pk[1] = unsigned(__builtin_bit_cast(uint16_t, b2)) | (unsigned(__builtin_bit_cast(uint16_t, b3)) << 16);
-        *reinterpret_cast<u32x2*>(op + d0) = pk;
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int s = 0; s < 8; ++s) kf[kb][s] = __builtin_bit_cast(bf16x8, ld16(st + kb * 8192 + koff[s]));
+      f32x16 sacc[2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        sacc[kb] = f32x16{};
+#pragma unroll
+        for (int s = 0; s < 8; ++s)
+          sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kb][s], qb[s], sacc[kb], 0, 0, 0);
+      }
+      if (tp.y > wq_min) {
+        // rows of this tile may be later than some query (or past the end of
+        // the request): mask pos_row > pos_q
+        const int t0 = t * kAttnRowsPerTile;
+        const int* ps = reinterpret_cast<const int*>(st + kPosOffset);
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+          for (int qq = 0; qq < 4; ++qq) {
+            const int r4 = 32 * kb + 8 * qq + 4 * g2;
+            const i32x4 p4 = *reinterpret_cast<const i32x4*>(ps + r4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const bool hide = p4[e] > qpos || t0 + r4 + e >= rows;
+              if (hide) sacc[kb][4 * qq + e] = -INFINITY;
+            }
+          }
+        }
+      }
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; i += 2) mx = max3(mx, sacc[kb][i], sacc[kb][i + 1]);
+      const float mt = max_halves(mx) * a.scale_log2;
+      const bool raise = mt > m + kRescaleSlack;
+      if (__builtin_amdgcn_ballot_w64(raise)) {
+        // only raising lanes rescale: a lane whose maximum is still -inf
+        // must not form exp2(-inf - -inf)
+        const float alpha = raise ? __builtin_amdgcn_exp2f(m - mt) : 1.0f;
+#pragma unroll
+        for (int db = 0; db < 4; ++db) o[db] *= alpha;
+        lacc *= alpha;
+        m = raise ? mt : m;
+      }
+      const float mb = m == -INFINITY ? 0.0f : m;
+      bf16x8 pb[2][2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][i], a.scale_log2, -mb));
+          pb[kb][i >> 3][i & 7] = (__bf16)p;
+        }
+      }
+      // the denominator: ones^T P^T on the matrix core sums exactly the bf16
+      // weights the PV product uses, so the output is an exact weighted mean
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2)
+          lacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones, pb[kb][s2], lacc, 0, 0, 0);
+      // O^T += V^T P^T.  Block db+1's transpose reads are issued before
+      // block db's MFMAs, and waited for while those run.
+      // LDS-local byte address of this stage (not its flat address)
+      const unsigned sbase =
+          unsigned(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const char*)st));
+      TrBlock vb[2];
+      tr_block_read(sbase + voff[0][0], sbase + voff[0][1], vb[0]);
+      lds_wait(vb[0]);
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        TrBlock& cur = vb[db & 1];
+        if (db + 1 < 4) tr_block_read(sbase + voff[db + 1][0], sbase + voff[db + 1][1], vb[(db + 1) & 1]);
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+          for (int s2 = 0; s2 < 2; ++s2) {
+            const s16x8 xv = __builtin_shufflevector(cur.x[4 * kb + 2 * s2], cur.x[4 * kb + 2 * s2 + 1], 0, 1, 2,
+                                                     3, 4, 5, 6, 7);
+            o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, xv), pb[kb][s2], o[db],
+                                                            0, 0, 0);
+          }
+        }
+        if (db + 1 < 4) lds_wait(vb[(db + 1) & 1]);
       }
     }
-  } else {
+    if (FUSED && more) fused_k_store(a, fk, nxt);
+  }
+
+  // rows of lacc are identical: each lane already holds its column's full sum
+  const float lt = lacc[0];
+  if (!col_ok) return;
+  if (a.n_split > 1) {
+    // this split's partial (unnormalised O, max, sum); merge_kernel combines them
     const int64_t idx = (int64_t(w.split) * a.n_new + u) * a.q_heads + hq;
-    float* op = a.opart + idx * 128;
+    float* pp = a.opart + idx * 128;
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
 #pragma unroll
       for (int qq = 0; qq < 4; ++qq) {
         const int d0 = 32 * db + 8 * qq + 4 * g2;
         const f32x4 v = {o[db][4 * qq], o[db][4 * qq + 1], o[db][4 * qq + 2], o[db][4 * qq + 3]};
-        *reinterpret_cast<f32x4*>(op + d0) = v;
+        *reinterpret_cast<f32x4*>(pp + d0) = v;
       }
     }
     if (g2 == 0) a.ml[idx] = make_float2(m, lt);
+    return;
+  }
+  const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
+  uint16_t* op = a.out + (int64_t(u) * a.q_heads + hq) * 128;
+#pragma unroll
+  for (int db = 0; db < 4; ++db) {
+#pragma unroll
+    for (int qq = 0; qq < 4; ++qq) {
+      const int d0 = 32 * db + 8 * qq + 4 * g2;
+      u32x2 pk;
+      const __bf16 b0 = (__bf16)(o[db][4 * qq + 0] * inv), b1 = (__bf16)(o[db][4 * qq + 1] * inv);
+      const __bf16 b2 = (__bf16)(o[db][4 * qq + 2] * inv), b3 = (__bf16)(o[db][4 * qq + 3] * inv);
+      pk[0] = unsigned(__builtin_bit_cast(uint16_t, b0)) | (unsigned(__builtin_bit_cast(uint16_t, b1)) << 16);
+      pk[1] = unsigned(__builtin_bit_cast(uint16_t, b2)) | (unsigned(__builtin_bit_cast(uint16_t, b3)) << 16);
+      *reinterpret_cast<u32x2*>(op + d0) = pk;
+    }
   }
 }
 
-// Log-sum-exp merge of the row splits: one wave per (new token, query head).
+// Log-sum-exp merge of the row splits, in split order.  32 threads per
+// (new token, query head), 4 output values each; every split's partial is
+// requested before any is combined.
+constexpr int kMaxSplit = 16;
+
 __global__ __launch_bounds__(256) void merge_kernel(AttnArgs a) {
-  const int64_t item = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  if (item >= int64_t(a.n_new) * a.q_heads) return;
-  float mmax = -INFINITY;
-  for (int s = 0; s < a.n_split; ++s) {
-    const float2 v = a.ml[int64_t(s) * a.n_new * a.q_heads + item];
-    if (v.y > 0.0f) mmax = fmaxf(mmax, v.x);
+  const int64_t item = int64_t(blockIdx.x) * 8 + (threadIdx.x >> 5);
+  const int d0 = (threadIdx.x & 31) * 4;
+  const int64_t n_items = int64_t(a.n_new) * a.q_heads;
+  if (item >= n_items) return;
+  float2 ml[kMaxSplit];
+  f32x4 part[kMaxSplit];
+#pragma unroll
+  for (int sp = 0; sp < kMaxSplit; ++sp) {
+    if (sp < a.n_split) {
+      const int64_t idx = int64_t(sp) * n_items + item;
+      ml[sp] = a.ml[idx];
+      part[sp] = *reinterpret_cast<const f32x4*>(a.opart + idx * 128 + d0);
+    }
   }
-  float den = 0.0f, n0 = 0.0f, n1 = 0.0f;
-  for (int s = 0; s < a.n_split; ++s) {
-    const int64_t idx = int64_t(s) * a.n_new * a.q_heads + item;
-    const float2 v = a.ml[idx];
-    if (!(v.y > 0.0f)) continue;
-    const float wgt = __builtin_amdgcn_exp2f(v.x - mmax);
-    den += wgt * v.y;
-    const float* op = a.opart + idx * 128;
-    n0 += wgt * op[2 * lane];
-    n1 += wgt * op[2 * lane + 1];
+  float mmax = -INFINITY;
+#pragma unroll
+  for (int sp = 0; sp < kMaxSplit; ++sp)
+    if (sp < a.n_split && ml[sp].y > 0.0f) mmax = fmaxf(mmax, ml[sp].x);
+  float den = 0.0f;
+  f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int sp = 0; sp < kMaxSplit; ++sp) {
+    if (sp < a.n_split && ml[sp].y > 0.0f) {
+      const float wgt = __builtin_amdgcn_exp2f(ml[sp].x - mmax);
+      den += wgt * ml[sp].y;
+      acc += wgt * part[sp];
+    }
   }
   const float inv = den > 0.0f ? 1.0f / den : 0.0f;
-  const __bf16 b0 = (__bf16)(n0 * inv), b1 = (__bf16)(n1 * inv);
-  reinterpret_cast<unsigned*>(a.out + item * 128)[lane] =
-      unsigned(__builtin_bit_cast(uint16_t, b0)) | (unsigned(__builtin_bit_cast(uint16_t, b1)) << 16);
+  const __bf16 b0 = (__bf16)(acc[0] * inv), b1 = (__bf16)(acc[1] * inv);
+  const __bf16 b2 = (__bf16)(acc[2] * inv), b3 = (__bf16)(acc[3] * inv);
+  u32x2 pk;
+  pk[0] = unsigned(__builtin_bit_cast(uint16_t, b0)) | (unsigned(__builtin_bit_cast(uint16_t, b1)) << 16);
+  pk[1] = unsigned(__builtin_bit_cast(uint16_t, b2)) | (unsigned(__builtin_bit_cast(uint16_t, b3)) << 16);
+  *reinterpret_cast<u32x2*>(a.out + item * 128 + d0) = pk;
 }
 
 // ---------------------------------------------------------------------------
@@ -683,6 +866,9 @@ hipError_t launch_plan(const PlanArgs& a, hipStream_t s) {
   if (n2 > 0) {
     hipLaunchKernelGGL(plan_phase_kernel, dim3(unsigned((n2 + 255) / 256)), dim3(256), 0, s, a);
   }
+  if (a.n_tiles > 0) {
+    hipLaunchKernelGGL(plan_tiles_kernel, dim3(unsigned((a.n_tiles + 255) / 256)), dim3(256), 0, s, a);
+  }
   return hipGetLastError();
 }
 
@@ -718,9 +904,10 @@ template <bool BF16, int D>
 static void prologue_launch(const PrologueArgs& a, hipStream_t s) {
   constexpr int ES = BF16 ? 2 : 4;
   constexpr int LPR = D / (2 * (16 / ES));
-  constexpr int RPB = 256 / LPR;
-  const int64_t units = int64_t(a.n_new) * (a.q_heads + 2 * a.kv_heads);
-  hipLaunchKernelGGL((prologue_kernel<BF16, D>), dim3(unsigned((units + RPB - 1) / RPB)), dim3(256), 0,
+  constexpr int GPB = 256 / LPR;
+  const int per_tok = a.q_heads + 2 * a.kv_heads;
+  const int64_t groups = int64_t(a.n_new) * ((per_tok + kPrologueRows - 1) / kPrologueRows);
+  hipLaunchKernelGGL((prologue_kernel<BF16, D>), dim3(unsigned((groups + GPB - 1) / GPB)), dim3(256), 0,
                      s, a);
 }
 
@@ -749,7 +936,7 @@ hipError_t launch_attention_bf16(const AttnArgs& a, bool fused, hipStream_t s) {
     hipLaunchKernelGGL(attention_bf16_kernel<false>, dim3(unsigned(a.n_work)), dim3(256), 0, s, a);
   if (a.n_split > 1) {
     const int64_t items = int64_t(a.n_new) * a.q_heads;
-    hipLaunchKernelGGL(merge_kernel, dim3(unsigned((items + 3) / 4)), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(merge_kernel, dim3(unsigned((items + 7) / 8)), dim3(256), 0, s, a);
   }
   return hipGetLastError();
 }

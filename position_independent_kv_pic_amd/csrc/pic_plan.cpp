@@ -29,6 +29,9 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 // attention kernel marks rows past the end of a request with it.
 constexpr int64_t kMaxPosition = INT32_MAX - 1;
 
+// rows per attention tile (the kernels' tile height)
+constexpr int64_t kTileRows = 64;
+
 }  // namespace
 
 pic_status check_model(const pic_model* m, ModelInfo* out, std::string* err) {
@@ -143,7 +146,7 @@ pic_status build_plan(const PoolInfo& pool, int32_t batch, const int32_t* span_p
   p.new_row.resize(size_t(p.new_rows));
   p.new_req.resize(size_t(p.new_rows));
 
-  int64_t row = 0, crow = 0;
+  int64_t row = 0, crow = 0, tiles = 0;
   int32_t max_pos = 0;
   for (int32_t b = 0; b < batch; ++b) {
     ReqRec& r = p.reqs[b];
@@ -208,13 +211,15 @@ pic_status build_plan(const PoolInfo& pool, int32_t batch, const int32_t* span_p
       max_pos = std::max<int64_t>(max_pos, pos);
     }
     r.first_new_pos = r.n_new > 0 ? p.new_pos[r.new_begin] : 0;
-    r.pad = 0;
+    r.tile_base = int32_t(tiles);
+    tiles += (prefix + r.n_new + kTileRows - 1) / kTileRows;
     row += prefix + r.n_new;
     if (row > INT32_MAX) return fail(err, PIC_ERANGE, "batch has more than 2^31 rows");
   }
   p.crow[p.n_spans] = int32_t(crow);
   p.prefix_rows = crow;
   p.rows = row;
+  p.n_tiles = int32_t(tiles);
   p.max_position = max_pos;
   if (capacity >= 0 && p.rows > capacity)
     return fail(err, PIC_ERANGE, "batch needs %lld rows per plane, capacity is %lld",
@@ -243,29 +248,34 @@ void build_attention_work(HostPlan* plan, int32_t kv_heads, int32_t group, int32
   }
   plan->n_split = split;
   plan->work.clear();
+  int32_t groups = 0;
   for (int32_t b = 0; b < int32_t(plan->reqs.size()); ++b) {
     const ReqRec& r = plan->reqs[b];
     int64_t cols = int64_t(r.n_new) * group;
     if (cols == 0) continue;
     int32_t tiles = (r.prefix_rows + r.n_new + rows_per_tile - 1) / rows_per_tile;
+    int32_t ncb = int32_t((cols + cols_per_wg - 1) / cols_per_wg);
     for (int32_t h = 0; h < kv_heads; ++h) {
       for (int32_t sp = 0; sp < split; ++sp) {
         int32_t t0 = int32_t(int64_t(tiles) * sp / split);
         int32_t t1 = int32_t(int64_t(tiles) * (sp + 1) / split);
-        for (int64_t c = 0; c < cols; c += cols_per_wg) {
+        for (int32_t c = 0; c < ncb; ++c) {
           AttnWork w;
           w.req = b;
           w.head = h;
-          w.col_begin = int32_t(c);
+          w.col_begin = c * cols_per_wg;
           w.tile_begin = t0;
           w.tile_end = t1;
           w.split = sp;
-          w.pad0 = w.pad1 = 0;
+          w.group = groups + c;
+          w.pad = 0;
           plan->work.push_back(w);
         }
       }
+      groups += ncb;
     }
   }
+  plan->n_groups = groups;
 }
 
 }  // namespace pic

@@ -53,7 +53,7 @@ struct ReqRec {
   int32_t new_begin;    // index of the first new token in the packed arrays
   int32_t span_begin, span_end;
   int32_t first_new_pos;
-  int32_t pad;
+  int32_t tile_base;    // index of the request's first 64-row attention tile
 };
 
 // Attention work item: one workgroup handles query columns
@@ -66,12 +66,14 @@ struct AttnWork {
   int32_t tile_begin;
   int32_t tile_end;
   int32_t split;
-  int32_t pad0, pad1;
+  int32_t group;     // index of the (req, head, col_begin) group the splits share
+  int32_t pad;
 };
 
 struct HostPlan {
   int32_t batch = 0, n_spans = 0, max_position = 0;
   int64_t prefix_rows = 0, new_rows = 0, rows = 0;
+  int32_t n_tiles = 0;              // 64-row attention tiles over all requests
   std::vector<SpanRec> spans;
   std::vector<int32_t> crow;        // n_spans + 1 compact-row offsets
   std::vector<ReqRec> reqs;
@@ -81,6 +83,7 @@ struct HostPlan {
   // attention work list (built per kernel tiling)
   std::vector<AttnWork> work;
   int32_t n_split = 1;
+  int32_t n_groups = 0;             // work items / n_split
 };
 
 // Validation helpers return PIC_OK or an error code and fill `err`.
