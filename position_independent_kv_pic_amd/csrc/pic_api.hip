@@ -306,10 +306,13 @@ pic_status pic_assemble(pic_plan* p, int32_t batch, const int32_t* span_ptr, con
   pic_status st = pic::build_plan(pi, batch, span_ptr, spans, new_ptr, new_pos, asm_rows_capacity,
                                   &hp, &err);
   if (st != PIC_OK) return set_err(st, "%s", err.c_str());
-  if (pi.m.dtype == PIC_BF16 && pi.m.head_dim == 128)
-    pic::build_attention_work(&hp, pi.m.kv_heads, pi.m.group, pic::kAttnColsPerWG,
-                              pic::kAttnRowsPerTile, /*target_wgs=*/512, /*max_split=*/pic::kAttnMaxSplit,
-                              /*min_tiles_per_split=*/4);
+  if (pi.m.dtype == PIC_BF16 && pi.m.head_dim == 128) {
+    hp.n_split = pic::choose_attention_split(hp, pi.m.kv_heads, pi.m.group, pic::kAttnColsPerWG,
+                                             pic::kAttnRowsPerTile, pic::kAttnTargetWGs,
+                                             pic::kAttnMaxSplit, /*min_tiles_per_split=*/4);
+    pic::build_attention_work(hp, pi.m.kv_heads, pi.m.group, pic::kAttnColsPerWG, pic::kAttnRowsPerTile,
+                              hp.n_split, &hp.work);
+  }
   if (dry) {
     p->hp = std::move(hp);
     p->has_batch = true;

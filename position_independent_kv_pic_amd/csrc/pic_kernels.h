@@ -94,8 +94,9 @@ struct AttnF32Args {
   char* out;
 };
 
-constexpr int kAttnColsPerWG = 128;   // 4 waves x 32 query columns
 constexpr int kAttnRowsPerTile = 64;
+constexpr int kAttnColsPerWG = 128;   // 4 waves x 32 query columns
+constexpr int kAttnTargetWGs = 512;   // two workgroups per CU
 constexpr int kAttnMaxSplit = 16;     // merge_kernel handles at most this many row splits
 
 hipError_t launch_plan(const PlanArgs& a, hipStream_t s);

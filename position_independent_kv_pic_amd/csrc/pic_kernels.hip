@@ -24,6 +24,7 @@
 
 #include <climits>
 #include <cmath>
+#include <type_traits>
 
 namespace pic {
 namespace {
@@ -357,10 +358,9 @@ __global__ __launch_bounds__(256) void prologue_kernel(PrologueArgs a) {
 // bf16 query-prefill attention, head_dim 128
 // ---------------------------------------------------------------------------
 //
-// One workgroup = 4 waves = 128 query columns of one (request, kv head) and a
-// range of 64-row tiles.  Column c of a request is token c / G, query head
-// c % G of the group, so the G heads that share a kv head share every K/V
-// tile.  Per wave, with its 32 columns as the MFMA N dimension:
+// Query columns.  Column c of a request is token c / G, query head c % G of
+// the group, so the G heads that share a kv head share every K/V tile.  A
+// wave owns 32 consecutive columns; with them as the MFMA N dimension
 //   S^T = K Q^T   (A = 32-row K fragments from LDS, B = the wave's rotated
 //                  queries, held in registers), 2 x 8 MFMA 32x32x16 per tile;
 //   O^T += V^T P^T (A = V^T fragments read with the LDS transpose load,
@@ -373,49 +373,337 @@ __global__ __launch_bounds__(256) void prologue_kernel(PrologueArgs a) {
 //
 // Tiles: K and V, 64 rows x 256 bytes each, row-major with 16-byte granules
 // XOR-swizzled by row, are copied global -> LDS directly (no registers) by
-// 16-byte lane loads whose source addresses apply the swizzle.  Two stages:
-// the next tile streams in while the current one is consumed; one barrier per
-// tile.  Rows past the request's end repeat its last row and are masked by
-// position.
+// 16-byte lane loads whose source addresses apply the swizzle, together with
+// the rows' positions.  Rows past the request's end repeat its last row and
+// are masked by index.
 //
 // Softmax: scores are kept relative to a reference maximum that is raised
 // only when a tile's maximum exceeds it by more than 8 (log2 units), so the
-// accumulator rescale is rare; probabilities stay below 2^8.
+// accumulator rescale is rare; probabilities stay below 2^8.  The denominator
+// is summed on the matrix core from the same bf16 probabilities the PV
+// product uses, so the output is an exact weighted mean of the values.
 
 constexpr int kTileBytes = 16384;
 constexpr int kPosOffset = 2 * kTileBytes;          // 64 row positions after K and V
-constexpr int kStageBytes = 2 * kTileBytes + 256;
 constexpr float kRescaleSlack = 8.0f;
 
 // LDS swizzles of the 16-byte granules of a tile row.  Keys are read as one
 // 16-byte granule per lane from 32 consecutive rows, so granules are XORed
 // with the row index (mod 16); values are read with the transpose load, whose
 // 16-lane groups touch 4 consecutive rows x 2 granules x 2 halves, so their
-// granules are XORed with 2 * (row mod 4).  Either way each 16-lane group hits
-// distinct banks.
+// granules are XORed with 2 * (row mod 4).
 __device__ __forceinline__ int k_swz(int r) { return r & 15; }
 __device__ __forceinline__ int v_swz(int r) { return 2 * (r & 3); }
 
-// Copy one 64-row tile of one plane into LDS.  `base` is the request's row 0,
-// `wave` the wave index (scalar).  Rows past the request's end repeat its
-// last row (only the request's last tile has any).
-template <bool VALUE>
-__device__ __forceinline__ void tile_to_lds(const char* base, int t0, int rows, char* lds, int wave) {
+__device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// LDS-local byte address (not the flat address) of a shared-memory pointer.
+__device__ __forceinline__ unsigned lds_addr(const char* p) {
+  return unsigned(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const char*)p));
+}
+
+// LDS reads as inline asm.  The intrinsic forms make the compiler wait for
+// every outstanding global->LDS copy before them (it cannot tell that those
+// target another stage); the callers wait with an explicit lgkmcnt(0) whose
+// operands are the results, so no use can move above it.
+template <int OFF>
+__device__ __forceinline__ u32x4 lds_read16(unsigned addr) {
+  u32x4 r;
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
+  return r;
+}
+
+template <int OFF>
+__device__ __forceinline__ s16x4 tr_read(unsigned addr) {
+  s16x4 r;
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
+  return r;
+}
+
+struct KFrags {
+  u32x4 x[8];   // the k steps of one 32-row block
+};
+
+__device__ __forceinline__ void kfrag_wait(KFrags& f) {
+  asm volatile("s_waitcnt lgkmcnt(0)"
+               : "+v"(f.x[0]), "+v"(f.x[1]), "+v"(f.x[2]), "+v"(f.x[3]), "+v"(f.x[4]), "+v"(f.x[5]),
+                 "+v"(f.x[6]), "+v"(f.x[7]));
+}
+
+struct TrBlock {
+  s16x4 x[8];   // [kb][s2][half] of one 32-wide d block
+};
+
+template <int OFF>
+__device__ __forceinline__ void tr_block_read(unsigned a0, unsigned a1, TrBlock& b) {
+  b.x[0] = tr_read<OFF>(a0);
+  b.x[1] = tr_read<OFF>(a1);
+  b.x[2] = tr_read<OFF + 16 * 256>(a0);
+  b.x[3] = tr_read<OFF + 16 * 256>(a1);
+  b.x[4] = tr_read<OFF + 32 * 256>(a0);
+  b.x[5] = tr_read<OFF + 32 * 256>(a1);
+  b.x[6] = tr_read<OFF + 48 * 256>(a0);
+  b.x[7] = tr_read<OFF + 48 * 256>(a1);
+}
+
+__device__ __forceinline__ void lds_wait(TrBlock& b) {
+  asm volatile("s_waitcnt lgkmcnt(0)"
+               : "+v"(b.x[0]), "+v"(b.x[1]), "+v"(b.x[2]), "+v"(b.x[3]), "+v"(b.x[4]), "+v"(b.x[5]),
+                 "+v"(b.x[6]), "+v"(b.x[7]));
+}
+
+// Max of the 32 scores a lane holds, as a depth-4 tree of 3-input maxima.
+__device__ __forceinline__ float max32(const f32x16& a, const f32x16& b) {
+  const float t0 = max3(a[0], a[1], a[2]), t1 = max3(a[3], a[4], a[5]), t2 = max3(a[6], a[7], a[8]);
+  const float t3 = max3(a[9], a[10], a[11]), t4 = max3(a[12], a[13], a[14]), t5 = max3(a[15], b[0], b[1]);
+  const float t6 = max3(b[2], b[3], b[4]), t7 = max3(b[5], b[6], b[7]), t8 = max3(b[8], b[9], b[10]);
+  const float t9 = max3(b[11], b[12], b[13]);
+  const float u0 = max3(t0, t1, t2), u1 = max3(t3, t4, t5), u2 = max3(t6, t7, t8);
+  const float u3 = max3(t9, b[14], b[15]);
+  return max3(max3(u0, u1, u2), u3, u3);
+}
+
+// Per-lane state of one query column and its wave.
+struct Col {
+  bool ok;          // the column exists
+  int u;            // packed index of its new token
+  int hq;           // its query head
+  int qpos;         // its position
+  int wq_min, wq_max;  // range of the wave's query positions (empty: INT_MAX, INT_MIN)
+  unsigned kaddr[8];     // LDS addresses of the lane's K fragments in stage 0
+  unsigned vaddr[4][2];  // LDS addresses of the lane's V^T transpose reads in stage 0
+};
+
+// `lds` is the LDS address of stage 0; later stages are reached through the
+// instructions' immediate offsets.
+__device__ __forceinline__ void col_setup(const AttnArgs& a, const AttnWork& w, const ReqRec& rq,
+                                          int wave, unsigned lds, Col& c, bf16x8 qb[8]) {
   const int lane = threadIdx.x & 63;
-  const bool full = t0 + kAttnRowsPerTile <= rows;
+  const int g2 = lane >> 5, lq = lane & 31;
+  const int ncols = rq.n_new * a.group;
+  const int col = w.col_begin + wave * 32 + lq;
+  c.ok = col < ncols;
+  const int colc = c.ok ? col : ncols - 1;
+  const int tokj = colc / a.group;
+  c.hq = w.head * a.group + (colc - tokj * a.group);
+  c.u = rq.new_begin + tokj;
+  c.qpos = a.new_pos[c.u];
+  int lo = c.ok ? c.qpos : INT_MAX;
+  int hi = c.ok ? c.qpos : INT_MIN;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    lo = min(lo, __shfl_xor(lo, o));
+    hi = max(hi, __shfl_xor(hi, o));
+  }
+  c.wq_min = lo;
+  c.wq_max = hi;
+  const u32x4* qp = reinterpret_cast<const u32x4*>(a.q_rot + (int64_t(c.u) * a.q_heads + c.hq) * 128);
+#pragma unroll
+  for (int s = 0; s < 8; ++s) qb[s] = __builtin_bit_cast(bf16x8, qp[2 * s + g2]);
+#pragma unroll
+  for (int s = 0; s < 8; ++s) c.kaddr[s] = lds + lq * 256 + 16 * ((2 * s + g2) ^ k_swz(lq));
+  const int l16 = lane & 15, gm = (lane >> 4) & 1;
+  const int cc = 2 * gm + ((l16 & 3) >> 1);
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int rowi = 8 * h + 4 * g2 + (l16 >> 2);
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+      c.vaddr[db][h] = lds + kTileBytes + rowi * 256 + 16 * ((4 * db + cc) ^ v_swz(rowi)) + 8 * (l16 & 1);
+  }
+}
+
+// S^T = K Q^T for the tile in the stage at byte offset STAGE from stage 0,
+// one 32-row block at a time (its 8 fragment reads in flight before one wait).
+template <int OFF>
+__device__ __forceinline__ void s_block(const Col& c, const bf16x8 qb[8], f32x16& acc) {
+  KFrags kf;
+#pragma unroll
+  for (int s = 0; s < 8; ++s) kf.x[s] = lds_read16<OFF>(c.kaddr[s]);
+  kfrag_wait(kf);
+  acc = f32x16{};
+#pragma unroll
+  for (int s = 0; s < 8; ++s)
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kf.x[s]), qb[s], acc, 0, 0, 0);
+}
+
+template <int STAGE>
+__device__ __forceinline__ void s_product(const Col& c, const bf16x8 qb[8], f32x16 sacc[2]) {
+  s_block<STAGE>(c, qb, sacc[0]);
+  s_block<STAGE + 8192>(c, qb, sacc[1]);
+}
+
+// Softmax of one tile's scores: mask (when the tile's rows are not all at or
+// before every query of the wave), raise the reference maximum if needed,
+// and form the bf16 probabilities.  `ps` are the tile's row positions in LDS,
+// `r0` its first row, `rows` the request's rows.
+__device__ __forceinline__ void softmax_tile(f32x16 sacc[2], int2 bnd, const int* ps, int r0, int rows,
+                                             const Col& c, float scale_log2, float& m, f32x16 o[4],
+                                             f32x16& lacc, bf16x8 pb[2][2]) {
+  const int g2 = (threadIdx.x & 63) >> 5;
+  if (bnd.y > c.wq_min) {
+    // rows of this tile may be later than some query (or past the end of
+    // the request): mask pos_row > pos_q
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int qq = 0; qq < 4; ++qq) {
+        const int r4 = 32 * kb + 8 * qq + 4 * g2;
+        const i32x4 p4 = *reinterpret_cast<const i32x4*>(ps + r4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const bool hide = p4[e] > c.qpos || r0 + r4 + e >= rows;
+          if (hide) sacc[kb][4 * qq + e] = -INFINITY;
+        }
+      }
+    }
+  }
+  const float mt = max_halves(max32(sacc[0], sacc[1])) * scale_log2;
+  const bool raise = mt > m + kRescaleSlack;
+  if (__builtin_amdgcn_ballot_w64(raise)) {
+    // only raising lanes rescale: a lane whose maximum is still -inf must not
+    // form exp2(-inf - -inf)
+    const float alpha = raise ? __builtin_amdgcn_exp2f(m - mt) : 1.0f;
+#pragma unroll
+    for (int db = 0; db < 4; ++db) o[db] *= alpha;
+    lacc *= alpha;
+    m = raise ? mt : m;
+  }
+  const float mb = m == -INFINITY ? 0.0f : m;
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][i], scale_log2, -mb));
+      pb[kb][i >> 3][i & 7] = (__bf16)p;
+    }
+  }
+}
+
+// O^T += V^T P^T and the denominator (ones^T P^T) for the tile in the stage
+// at byte offset STAGE from stage 0.  Block db+1's transpose reads are issued before
+// block db's products, and waited for while those run.
+template <int STAGE>
+__device__ __forceinline__ void pv_product(const Col& c, const bf16x8 pb[2][2], f32x16 o[4],
+                                           f32x16& lacc) {
+  const bf16x8 ones = __builtin_bit_cast(bf16x8, u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) lacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones, pb[kb][s2], lacc, 0, 0, 0);
+  TrBlock vb[2];
+  tr_block_read<STAGE>(c.vaddr[0][0], c.vaddr[0][1], vb[0]);
+  lds_wait(vb[0]);
+#pragma unroll
+  for (int db = 0; db < 4; ++db) {
+    TrBlock& cur = vb[db & 1];
+    if (db + 1 < 4) tr_block_read<STAGE>(c.vaddr[db + 1][0], c.vaddr[db + 1][1], vb[(db + 1) & 1]);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        const s16x8 xv =
+            __builtin_shufflevector(cur.x[4 * kb + 2 * s2], cur.x[4 * kb + 2 * s2 + 1], 0, 1, 2, 3, 4, 5, 6, 7);
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, xv), pb[kb][s2], o[db], 0, 0,
+                                                        0);
+      }
+    }
+    if (db + 1 < 4) lds_wait(vb[(db + 1) & 1]);
+  }
+}
+
+// Write a column's result: the split's partial (unnormalised O, reference
+// maximum, sum) for merge_kernel, or the normalised bf16 output.
+__device__ __forceinline__ void store_column(const AttnArgs& a, const AttnWork& w, const Col& c, const f32x16 o[4],
+                                             const f32x16& lacc, float m) {
+  // rows of lacc are identical: each lane already holds its column's full sum
+  const float lt = lacc[0];
+  if (!c.ok) return;
+  const int g2 = (threadIdx.x & 63) >> 5;
+  if (a.n_split > 1) {
+    const int64_t idx = (int64_t(w.split) * a.n_new + c.u) * a.q_heads + c.hq;
+    float* pp = a.opart + idx * 128;
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+#pragma unroll
+      for (int qq = 0; qq < 4; ++qq) {
+        const int d0 = 32 * db + 8 * qq + 4 * g2;
+        const f32x4 v = {o[db][4 * qq], o[db][4 * qq + 1], o[db][4 * qq + 2], o[db][4 * qq + 3]};
+        *reinterpret_cast<f32x4*>(pp + d0) = v;
+      }
+    }
+    if (g2 == 0) a.ml[idx] = make_float2(m, lt);
+    return;
+  }
+  const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
+  uint16_t* op = a.out + (int64_t(c.u) * a.q_heads + c.hq) * 128;
+#pragma unroll
+  for (int db = 0; db < 4; ++db) {
+#pragma unroll
+    for (int qq = 0; qq < 4; ++qq) {
+      const int d0 = 32 * db + 8 * qq + 4 * g2;
+      u32x2 pk;
+      const __bf16 b0 = (__bf16)(o[db][4 * qq + 0] * inv), b1 = (__bf16)(o[db][4 * qq + 1] * inv);
+      const __bf16 b2 = (__bf16)(o[db][4 * qq + 2] * inv), b3 = (__bf16)(o[db][4 * qq + 3] * inv);
+      pk[0] = unsigned(__builtin_bit_cast(uint16_t, b0)) | (unsigned(__builtin_bit_cast(uint16_t, b1)) << 16);
+      pk[1] = unsigned(__builtin_bit_cast(uint16_t, b2)) | (unsigned(__builtin_bit_cast(uint16_t, b3)) << 16);
+      *reinterpret_cast<u32x2*>(op + d0) = pk;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// attention kernel
+// ---------------------------------------------------------------------------
+// One workgroup = 4 waves = 128 query columns of one (request, kv head) and a
+// range of tiles; two workgroups per CU.  Two stages: the next tile streams in
+// while the current one is consumed, one barrier per tile.  The fused variant
+// reads prefix rows straight from the pool: values with direct copies, keys
+// through registers, rotated on the way.
+
+constexpr int kStageBytes = 2 * kTileBytes + 256;
+
+// Per-lane byte offsets, inside a 64-row tile of one plane, of the 16-byte
+// granules a lane copies: 4 blocks of 1 KB (4 rows) per wave, the granule
+// order swizzled as the readers expect.
+struct TileLanes {
+  unsigned k[4], v[4];
+};
+
+__device__ __forceinline__ void tile_lanes(int wave, TileLanes& tl) {
+  const int lane = threadIdx.x & 63;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int blk = wave * 4 + i;                 // 1 KB block = 4 rows
-    const int r = blk * 4 + (lane >> 4);
-    const int rr = full ? t0 + r : min(t0 + r, rows - 1);
-    const int gran = (lane & 15) ^ (VALUE ? v_swz(r) : k_swz(r));
-    __builtin_amdgcn_global_load_lds(base + int64_t(rr) * 256 + gran * 16,
-                                     (lds_void_ptr)(lds + blk * 1024), 16, 0, 0);
+    const int r = (wave * 4 + i) * 4 + (lane >> 4);
+    tl.k[i] = r * 256 + ((lane & 15) ^ k_swz(r)) * 16;
+    tl.v[i] = r * 256 + ((lane & 15) ^ v_swz(r)) * 16;
+  }
+}
+
+// Copy one 64-row tile of one plane into LDS.  `base` is the request's row 0,
+// `t0` the tile's first row.  A full tile is addressed as one uniform base
+// plus the fixed lane offsets; the request's last tile repeats its last row
+// past the end.
+template <bool VALUE>
+__device__ __forceinline__ void tile_to_lds(const char* base, int t0, int rows, const TileLanes& tl, char* lds,
+                                            int wave) {
+  const unsigned* off = VALUE ? tl.v : tl.k;
+  if (t0 + kAttnRowsPerTile <= rows) {
+    const char* tbase = base + int64_t(t0) * 256;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      __builtin_amdgcn_global_load_lds(tbase + off[i], (lds_void_ptr)(lds + (wave * 4 + i) * 1024), 16, 0, 0);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int rr = min(t0 + int(off[i] >> 8), rows - 1);
+      __builtin_amdgcn_global_load_lds(base + int64_t(rr) * 256 + (off[i] & 255u),
+                                       (lds_void_ptr)(lds + (wave * 4 + i) * 1024), 16, 0, 0);
+    }
   }
 }
 
 // Row positions of one tile into LDS (wave 0, one 4-byte lane load each).
-// Rows past the request's end repeat its last row; readers mask them by index.
 __device__ __forceinline__ void pos_to_lds(const int32_t* pos_row0, int t0, int rows, char* lds) {
   if ((threadIdx.x >> 6) == 0) {
     const int rr = min(t0 + int(threadIdx.x), rows - 1);
@@ -493,42 +781,6 @@ __device__ __forceinline__ void fused_k_store(const AttnArgs& a, FusedK& f, char
   }
 }
 
-__device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-
-// LDS transpose read (ds_read_b64_tr_b16) issued as inline asm.  The
-// intrinsic form makes the compiler wait for every outstanding global->LDS
-// copy before it (it cannot tell that they target the other stage); here the
-// caller waits with lds_wait() instead, which also orders the results.
-template <int OFF>
-__device__ __forceinline__ s16x4 tr_read(unsigned addr) {
-  s16x4 r;
-  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
-  return r;
-}
-
-struct TrBlock {
-  s16x4 x[8];   // [kb][s2][half] of one 32-wide d block
-};
-
-__device__ __forceinline__ void tr_block_read(unsigned a0, unsigned a1, TrBlock& b) {
-  b.x[0] = tr_read<0>(a0);
-  b.x[1] = tr_read<0>(a1);
-  b.x[2] = tr_read<16 * 256>(a0);
-  b.x[3] = tr_read<16 * 256>(a1);
-  b.x[4] = tr_read<32 * 256>(a0);
-  b.x[5] = tr_read<32 * 256>(a1);
-  b.x[6] = tr_read<48 * 256>(a0);
-  b.x[7] = tr_read<48 * 256>(a1);
-}
-
-// Wait for every LDS read of this wave; the block's registers are tied to the
-// wait so no use can move above it.
-__device__ __forceinline__ void lds_wait(TrBlock& b) {
-  asm volatile("s_waitcnt lgkmcnt(0)"
-               : "+v"(b.x[0]), "+v"(b.x[1]), "+v"(b.x[2]), "+v"(b.x[3]), "+v"(b.x[4]), "+v"(b.x[5]),
-                 "+v"(b.x[6]), "+v"(b.x[7]));
-}
-
 template <bool FUSED>
 __global__ __launch_bounds__(256, 2) void attention_bf16_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(1024))) char smem[2 * kStageBytes];
@@ -536,244 +788,90 @@ __global__ __launch_bounds__(256, 2) void attention_bf16_kernel(AttnArgs a) {
   const AttnWork w = a.work[bid];
   const ReqRec rq = a.reqs[w.req];
   const int rows = rq.prefix_rows + rq.n_new;
-  const int ncols = rq.n_new * a.group;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  const int g2 = lane >> 5;
-  const int lq = lane & 31;
-  const int col = w.col_begin + wave * 32 + lq;
-  const bool col_ok = col < ncols;
-  const int colc = col_ok ? col : ncols - 1;
-  const int tokj = colc / a.group;
-  const int hq = w.head * a.group + (colc - tokj * a.group);
-  const int u = rq.new_begin + tokj;
-  const int qpos = a.new_pos[u];
 
-  // the wave's query range decides per tile whether to skip or mask
-  int wq_min = col_ok ? qpos : INT_MAX;
-  int wq_max = col_ok ? qpos : INT_MIN;
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-    wq_min = min(wq_min, __shfl_xor(wq_min, o));
-    wq_max = max(wq_max, __shfl_xor(wq_max, o));
-  }
-
+  Col c;
   bf16x8 qb[8];
-  {
-    const u32x4* qp = reinterpret_cast<const u32x4*>(a.q_rot + (int64_t(u) * a.q_heads + hq) * 128);
-#pragma unroll
-    for (int s = 0; s < 8; ++s) qb[s] = __builtin_bit_cast(bf16x8, qp[2 * s + g2]);
-  }
-
-  // per-lane LDS offsets (the tile row block and stage fold into immediates)
-  int koff[8];
-#pragma unroll
-  for (int s = 0; s < 8; ++s) koff[s] = lq * 256 + 16 * ((2 * s + g2) ^ k_swz(lq));
-  int voff[4][2];
-  {
-    const int l16 = lane & 15, gm = (lane >> 4) & 1;
-    const int c = 2 * gm + ((l16 & 3) >> 1);
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int rowi = 8 * h + 4 * g2 + (l16 >> 2);
-#pragma unroll
-      for (int db = 0; db < 4; ++db)
-        voff[db][h] = kTileBytes + rowi * 256 + 16 * ((4 * db + c) ^ v_swz(rowi)) + 8 * (l16 & 1);
-    }
-  }
+  col_setup(a, w, rq, wave, lds_addr(smem), c, qb);
+  TileLanes tl;
+  tile_lanes(wave, tl);
 
   f32x16 o[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) o[i] = f32x16{};
-  f32x16 lacc = f32x16{};   // every row holds the column's running sum of weights
+  f32x16 lacc = f32x16{};
   float m = -INFINITY;
-  const bf16x8 ones = __builtin_bit_cast(bf16x8, u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
 
   const char* kbase = reinterpret_cast<const char*>(a.k_plane + (int64_t(w.head) * a.cap + rq.row_base) * 128);
   const char* vbase = reinterpret_cast<const char*>(a.v_plane + (int64_t(w.head) * a.cap + rq.row_base) * 128);
   const int32_t* pbase = a.pos + rq.row_base;
   const int tb = w.tile_begin, te = w.tile_end;
   FusedK fk;
+
+  // copies of tile t into stage S (0 or 1)
+  auto issue = [&](auto stage_c, int t) {
+    constexpr int S = decltype(stage_c)::value;
+    char* st = smem + S * kStageBytes;
+    const int t0 = t * kAttnRowsPerTile;
+    if (FUSED) {
+      fused_k_load(a, rq, w.head, t0, rows, fk);
+      fused_v_to_lds(a, rq, w.head, t0, rows, st + kTileBytes);
+    } else {
+      tile_to_lds<false>(kbase, t0, rows, tl, st, wave);
+      tile_to_lds<true>(vbase, t0, rows, tl, st + kTileBytes, wave);
+    }
+    pos_to_lds(pbase, t0, rows, st + kPosOffset);
+  };
+
   int2 tp_next = make_int2(INT_MAX, INT_MAX);
   if (tb < te) {
     tp_next = a.tile_pos[rq.tile_base + tb];
-    if (FUSED) {
-      fused_k_load(a, rq, w.head, tb * kAttnRowsPerTile, rows, fk);
-      fused_v_to_lds(a, rq, w.head, tb * kAttnRowsPerTile, rows, smem + kTileBytes);
-      fused_k_store(a, fk, smem);
-    } else {
-      tile_to_lds<false>(kbase, tb * kAttnRowsPerTile, rows, smem, wave);
-      tile_to_lds<true>(vbase, tb * kAttnRowsPerTile, rows, smem + kTileBytes, wave);
-    }
-    pos_to_lds(pbase, tb * kAttnRowsPerTile, rows, smem + kPosOffset);
+    issue(std::integral_constant<int, 0>{}, tb);
+    if (FUSED) fused_k_store(a, fk, smem);
   }
-  for (int t = tb; t < te; ++t) {
-    const int stage = (t - tb) & 1;
+  // one tile in stage S: wait for its copies, start the next tile's copies
+  // into the other stage, then consume it
+  auto step = [&](auto stage_c, int t) {
+    constexpr int S = decltype(stage_c)::value;
     wait_vm();
     __syncthreads();
     const bool more = t + 1 < te;
-    char* nxt = smem + (stage ^ 1) * kStageBytes;
-    // this tile's bounds were fetched before the next tile's copies were issued,
-    // so reading them never waits on those copies
+    // this tile's bounds were fetched before the next tile's copies were
+    // issued, so reading them never waits on those copies
     const int2 tp = tp_next;
     if (more) {
       tp_next = a.tile_pos[rq.tile_base + t + 1];
-      const int t1 = (t + 1) * kAttnRowsPerTile;
-      if (FUSED) {
-        fused_k_load(a, rq, w.head, t1, rows, fk);
-        fused_v_to_lds(a, rq, w.head, t1, rows, nxt + kTileBytes);
-      } else {
-        tile_to_lds<false>(kbase, t1, rows, nxt, wave);
-        tile_to_lds<true>(vbase, t1, rows, nxt + kTileBytes, wave);
-      }
-      pos_to_lds(pbase, t1, rows, nxt + kPosOffset);
+      issue(std::integral_constant<int, 1 - S>{}, t + 1);
     }
-    const char* st = smem + stage * kStageBytes;
-    if (tp.x <= wq_max) {
-      // S^T = K Q^T
-      bf16x8 kf[2][8];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int s = 0; s < 8; ++s) kf[kb][s] = __builtin_bit_cast(bf16x8, ld16(st + kb * 8192 + koff[s]));
+    if (tp.x <= c.wq_max) {
       f32x16 sacc[2];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        sacc[kb] = f32x16{};
-#pragma unroll
-        for (int s = 0; s < 8; ++s)
-          sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kb][s], qb[s], sacc[kb], 0, 0, 0);
-      }
-      if (tp.y > wq_min) {
-        // rows of this tile may be later than some query (or past the end of
-        // the request): mask pos_row > pos_q
-        const int t0 = t * kAttnRowsPerTile;
-        const int* ps = reinterpret_cast<const int*>(st + kPosOffset);
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-          for (int qq = 0; qq < 4; ++qq) {
-            const int r4 = 32 * kb + 8 * qq + 4 * g2;
-            const i32x4 p4 = *reinterpret_cast<const i32x4*>(ps + r4);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const bool hide = p4[e] > qpos || t0 + r4 + e >= rows;
-              if (hide) sacc[kb][4 * qq + e] = -INFINITY;
-            }
-          }
-        }
-      }
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; i += 2) mx = max3(mx, sacc[kb][i], sacc[kb][i + 1]);
-      const float mt = max_halves(mx) * a.scale_log2;
-      const bool raise = mt > m + kRescaleSlack;
-      if (__builtin_amdgcn_ballot_w64(raise)) {
-        // only raising lanes rescale: a lane whose maximum is still -inf
-        // must not form exp2(-inf - -inf)
-        const float alpha = raise ? __builtin_amdgcn_exp2f(m - mt) : 1.0f;
-#pragma unroll
-        for (int db = 0; db < 4; ++db) o[db] *= alpha;
-        lacc *= alpha;
-        m = raise ? mt : m;
-      }
-      const float mb = m == -INFINITY ? 0.0f : m;
       bf16x8 pb[2][2];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][i], a.scale_log2, -mb));
-          pb[kb][i >> 3][i & 7] = (__bf16)p;
-        }
-      }
-      // the denominator: ones^T P^T on the matrix core sums exactly the bf16
-      // weights the PV product uses, so the output is an exact weighted mean
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2)
-          lacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones, pb[kb][s2], lacc, 0, 0, 0);
-      // O^T += V^T P^T.  Block db+1's transpose reads are issued before
-      // block db's MFMAs, and waited for while those run.
-      // LDS-local byte address of this stage (not its flat address)
-      const unsigned sbase =
-          unsigned(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const char*)st));
-      TrBlock vb[2];
-      tr_block_read(sbase + voff[0][0], sbase + voff[0][1], vb[0]);
-      lds_wait(vb[0]);
-#pragma unroll
-      for (int db = 0; db < 4; ++db) {
-        TrBlock& cur = vb[db & 1];
-        if (db + 1 < 4) tr_block_read(sbase + voff[db + 1][0], sbase + voff[db + 1][1], vb[(db + 1) & 1]);
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-          for (int s2 = 0; s2 < 2; ++s2) {
-            const s16x8 xv = __builtin_shufflevector(cur.x[4 * kb + 2 * s2], cur.x[4 * kb + 2 * s2 + 1], 0, 1, 2,
-                                                     3, 4, 5, 6, 7);
-            o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, xv), pb[kb][s2], o[db],
-                                                            0, 0, 0);
-          }
-        }
-        if (db + 1 < 4) lds_wait(vb[(db + 1) & 1]);
-      }
+      s_product<S * kStageBytes>(c, qb, sacc);
+      softmax_tile(sacc, tp, reinterpret_cast<const int*>(smem + S * kStageBytes + kPosOffset),
+                   t * kAttnRowsPerTile, rows, c, a.scale_log2, m, o, lacc, pb);
+      pv_product<S * kStageBytes>(c, pb, o, lacc);
     }
-    if (FUSED && more) fused_k_store(a, fk, nxt);
+    if (FUSED && more) fused_k_store(a, fk, smem + (1 - S) * kStageBytes);
+  };
+  for (int t = tb; t < te; t += 2) {
+    step(std::integral_constant<int, 0>{}, t);
+    if (t + 1 < te) step(std::integral_constant<int, 1>{}, t + 1);
   }
-
-  // rows of lacc are identical: each lane already holds its column's full sum
-  const float lt = lacc[0];
-  if (!col_ok) return;
-  if (a.n_split > 1) {
-    // this split's partial (unnormalised O, max, sum); merge_kernel combines them
-    const int64_t idx = (int64_t(w.split) * a.n_new + u) * a.q_heads + hq;
-    float* pp = a.opart + idx * 128;
-#pragma unroll
-    for (int db = 0; db < 4; ++db) {
-#pragma unroll
-      for (int qq = 0; qq < 4; ++qq) {
-        const int d0 = 32 * db + 8 * qq + 4 * g2;
-        const f32x4 v = {o[db][4 * qq], o[db][4 * qq + 1], o[db][4 * qq + 2], o[db][4 * qq + 3]};
-        *reinterpret_cast<f32x4*>(pp + d0) = v;
-      }
-    }
-    if (g2 == 0) a.ml[idx] = make_float2(m, lt);
-    return;
-  }
-  const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
-  uint16_t* op = a.out + (int64_t(u) * a.q_heads + hq) * 128;
-#pragma unroll
-  for (int db = 0; db < 4; ++db) {
-#pragma unroll
-    for (int qq = 0; qq < 4; ++qq) {
-      const int d0 = 32 * db + 8 * qq + 4 * g2;
-      u32x2 pk;
-      const __bf16 b0 = (__bf16)(o[db][4 * qq + 0] * inv), b1 = (__bf16)(o[db][4 * qq + 1] * inv);
-      const __bf16 b2 = (__bf16)(o[db][4 * qq + 2] * inv), b3 = (__bf16)(o[db][4 * qq + 3] * inv);
-      pk[0] = unsigned(__builtin_bit_cast(uint16_t, b0)) | (unsigned(__builtin_bit_cast(uint16_t, b1)) << 16);
-      pk[1] = unsigned(__builtin_bit_cast(uint16_t, b2)) | (unsigned(__builtin_bit_cast(uint16_t, b3)) << 16);
-      *reinterpret_cast<u32x2*>(op + d0) = pk;
-    }
-  }
+  store_column(a, w, c, o, lacc, m);
 }
 
 // Log-sum-exp merge of the row splits, in split order.  32 threads per
 // (new token, query head), 4 output values each; every split's partial is
 // requested before any is combined.
-constexpr int kMaxSplit = 16;
-
 __global__ __launch_bounds__(256) void merge_kernel(AttnArgs a) {
   const int64_t item = int64_t(blockIdx.x) * 8 + (threadIdx.x >> 5);
   const int d0 = (threadIdx.x & 31) * 4;
   const int64_t n_items = int64_t(a.n_new) * a.q_heads;
   if (item >= n_items) return;
-  float2 ml[kMaxSplit];
-  f32x4 part[kMaxSplit];
+  float2 ml[kAttnMaxSplit];
+  f32x4 part[kAttnMaxSplit];
 #pragma unroll
-  for (int sp = 0; sp < kMaxSplit; ++sp) {
+  for (int sp = 0; sp < kAttnMaxSplit; ++sp) {
     if (sp < a.n_split) {
       const int64_t idx = int64_t(sp) * n_items + item;
       ml[sp] = a.ml[idx];
@@ -782,12 +880,12 @@ __global__ __launch_bounds__(256) void merge_kernel(AttnArgs a) {
   }
   float mmax = -INFINITY;
 #pragma unroll
-  for (int sp = 0; sp < kMaxSplit; ++sp)
+  for (int sp = 0; sp < kAttnMaxSplit; ++sp)
     if (sp < a.n_split && ml[sp].y > 0.0f) mmax = fmaxf(mmax, ml[sp].x);
   float den = 0.0f;
   f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-  for (int sp = 0; sp < kMaxSplit; ++sp) {
+  for (int sp = 0; sp < kAttnMaxSplit; ++sp) {
     if (sp < a.n_split && ml[sp].y > 0.0f) {
       const float wgt = __builtin_amdgcn_exp2f(ml[sp].x - mmax);
       den += wgt * ml[sp].y;

@@ -228,12 +228,12 @@ pic_status build_plan(const PoolInfo& pool, int32_t batch, const int32_t* span_p
   return PIC_OK;
 }
 
-void build_attention_work(HostPlan* plan, int32_t kv_heads, int32_t group, int32_t cols_per_wg,
-                          int32_t rows_per_tile, int32_t target_wgs, int32_t max_split,
-                          int32_t min_tiles_per_split) {
+int32_t choose_attention_split(const HostPlan& plan, int32_t kv_heads, int32_t group, int32_t cols_per_wg,
+                               int32_t rows_per_tile, int32_t target_wgs, int32_t max_split,
+                               int32_t min_tiles_per_split) {
   int64_t base = 0;
   int32_t max_tiles = 0;
-  for (const ReqRec& r : plan->reqs) {
+  for (const ReqRec& r : plan.reqs) {
     int64_t cols = int64_t(r.n_new) * group;
     base += kv_heads * ((cols + cols_per_wg - 1) / cols_per_wg);
     int32_t tiles = (r.prefix_rows + r.n_new + rows_per_tile - 1) / rows_per_tile;
@@ -246,11 +246,14 @@ void build_attention_work(HostPlan* plan, int32_t kv_heads, int32_t group, int32
     split = std::min(split, std::max(1, max_tiles / std::max(1, min_tiles_per_split)));
     split = std::max(split, 1);
   }
-  plan->n_split = split;
-  plan->work.clear();
-  int32_t groups = 0;
-  for (int32_t b = 0; b < int32_t(plan->reqs.size()); ++b) {
-    const ReqRec& r = plan->reqs[b];
+  return split;
+}
+
+void build_attention_work(const HostPlan& plan, int32_t kv_heads, int32_t group, int32_t cols_per_wg,
+                          int32_t rows_per_tile, int32_t split, std::vector<AttnWork>* out) {
+  out->clear();
+  for (int32_t b = 0; b < int32_t(plan.reqs.size()); ++b) {
+    const ReqRec& r = plan.reqs[b];
     int64_t cols = int64_t(r.n_new) * group;
     if (cols == 0) continue;
     int32_t tiles = (r.prefix_rows + r.n_new + rows_per_tile - 1) / rows_per_tile;
@@ -267,15 +270,13 @@ void build_attention_work(HostPlan* plan, int32_t kv_heads, int32_t group, int32
           w.tile_begin = t0;
           w.tile_end = t1;
           w.split = sp;
-          w.group = groups + c;
-          w.pad = 0;
-          plan->work.push_back(w);
+          w.pad0 = 0;
+          w.pad1 = 0;
+          out->push_back(w);
         }
       }
-      groups += ncb;
     }
   }
-  plan->n_groups = groups;
 }
 
 }  // namespace pic

@@ -66,8 +66,7 @@ struct AttnWork {
   int32_t tile_begin;
   int32_t tile_end;
   int32_t split;
-  int32_t group;     // index of the (req, head, col_begin) group the splits share
-  int32_t pad;
+  int32_t pad0, pad1;
 };
 
 struct HostPlan {
@@ -80,10 +79,9 @@ struct HostPlan {
   std::vector<int32_t> new_pos;     // per new token
   std::vector<int32_t> new_row;     // assembled row of each new token
   std::vector<int32_t> new_req;     // request of each new token
-  // attention work list (built per kernel tiling)
+  // attention work list
   std::vector<AttnWork> work;
   int32_t n_split = 1;
-  int32_t n_groups = 0;             // work items / n_split
 };
 
 // Validation helpers return PIC_OK or an error code and fill `err`.
@@ -100,14 +98,18 @@ pic_status build_plan(const PoolInfo& pool, int32_t batch, const int32_t* span_p
                       const pic_span* spans, const int32_t* new_ptr, const int32_t* new_pos,
                       int64_t capacity, HostPlan* out, std::string* err);
 
-// Attention work list for the tiled kernel: `cols_per_wg` query columns
-// (token-major: column j*G + g is token j, head g of the group) and
-// `rows_per_tile` rows per tile.  The kv range of a request is split in
-// n_split parts, chosen so that about `target_wgs` workgroups exist when the
-// batch alone gives fewer (at most `max_split`, and never fewer than
-// `min_tiles_per_split` tiles per part).
-void build_attention_work(HostPlan* plan, int32_t kv_heads, int32_t group, int32_t cols_per_wg,
-                          int32_t rows_per_tile, int32_t target_wgs, int32_t max_split,
-                          int32_t min_tiles_per_split);
+// Row split for the attention kernels: about `target_wgs` workgroups of
+// `cols_per_wg` query columns when the batch alone gives fewer (at most
+// `max_split` parts, and never fewer than `min_tiles_per_split` tiles per part).
+int32_t choose_attention_split(const HostPlan& plan, int32_t kv_heads, int32_t group, int32_t cols_per_wg,
+                               int32_t rows_per_tile, int32_t target_wgs, int32_t max_split,
+                               int32_t min_tiles_per_split);
+
+// Attention work list: `cols_per_wg` query columns (token-major: column
+// j*G + g is token j, head g of the group) per item, `rows_per_tile` rows per
+// tile, each request's tiles cut into `split` contiguous ranges.  Items are
+// ordered (request, kv head, split, column block).
+void build_attention_work(const HostPlan& plan, int32_t kv_heads, int32_t group, int32_t cols_per_wg,
+                          int32_t rows_per_tile, int32_t split, std::vector<AttnWork>* out);
 
 }  // namespace pic
