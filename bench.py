@@ -26,6 +26,7 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
+HERE = os.path.dirname(os.path.abspath(__file__))
 METRIC = "assembly GB/s + query-prefill attn TFLOP/s (% roofline), p99 µs/request"
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
@@ -126,6 +127,40 @@ def cpu_baseline(wl, pool, dw, budget_s: float):
                       f"host has {os.cpu_count()} logical CPUs"}
 
 
+def kernel_source_hash() -> str:
+    """sha256 of the HIP kernel sources; counter-based traffic figures are only
+    valid for the kernels they were taken on."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in ("pic_kernels.hip", "pic_kernels.h"):
+        with open(os.path.join(HERE, "position_independent_kv_pic_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload: str, variant: str) -> dict:
+    """HBM bytes per launch measured with rocprofv3 counters (FETCH_SIZE,
+    WRITE_SIZE, scaled by a plain copy of known size), read from the committed
+    profile summary of this workload; empty when none exists or the kernels
+    changed since it was taken."""
+    path = os.path.join(HERE, "profiles", f"traffic_{workload}_{variant}.txt")
+    if not os.path.exists(path):
+        return {}
+    vals = {}
+    with open(path) as fh:
+        for line in fh:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                vals[k.strip()] = v.strip()
+    if vals.get("kernel_source_sha256") != kernel_source_hash():
+        return {}
+    out = {}
+    for key in ("attention", "gather"):
+        if f"{key}_bytes_per_launch" in vals:
+            out[key] = int(vals[f"{key}_bytes_per_launch"])
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -185,7 +220,9 @@ def main():
     total_ms = ev[0].elapsed_time(ev[-1])
     log(f"[bench] timed {args.steps} steps: {total_ms:.2f} ms (host wall {wall * 1e3:.2f} ms)")
 
-    # per-kernel durations: a second pass with the library's event brackets on
+    # per-kernel durations: the same K steps again with the library's HIP-event
+    # brackets around each kernel class on the launch stream (kept out of the
+    # timed region: about a hundred extra event records per step lengthen it)
     plan.timing(True)
     plan.timing_reset()
     for i in range(args.steps):
@@ -220,6 +257,7 @@ def main():
     attn_tflops = attn_launch_flops / (attn_ms * 1e-3) / 1e12 if n_a else None
     value = attn_flops / (ms_step * 1e-3) / 1e12
     peak = BF16_PEAK_TFLOPS if m.dtype == "bf16" else FP32_PEAK_TFLOPS
+    traffic = measured_traffic(wl.name, args.variant)
 
     res = {
         "metric": METRIC,
@@ -252,12 +290,13 @@ def main():
         "roofline": {"bound": "mfma", "achieved": None if attn_tflops is None else round(attn_tflops, 2),
                      "peak": peak, "unit": "TFLOP/s",
                      "frac": None if attn_tflops is None else round(attn_tflops / peak, 4),
-                     "traffic": None, "kernel": "attention_bf16_kernel (+ split merge)",
+                     "traffic": traffic.get("attention"), "kernel": "attention_bf16_kernel (+ merge_kernel when split)",
                      "per_launch_flops": int(attn_launch_flops)},
         "roofline_assembly": {"bound": "hbm", "achieved": None if asm_gbps is None else round(asm_gbps, 1),
                               "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                               "frac": None if asm_gbps is None else round(asm_gbps / HBM_PEAK_GBPS, 4),
-                              "traffic": None, "kernel": "gather_kernel", "per_launch_bytes": int(asm_bytes)},
+                              "traffic": traffic.get("gather"), "kernel": "gather_kernel",
+                              "per_launch_bytes": int(asm_bytes)},
         "not_ttft": "assembly + per-layer attention only; no projections, MLP or sampling",
     }
     if variant == VARIANT_FUSED:

@@ -291,8 +291,10 @@ __global__ __launch_bounds__(256) void gather_kernel(GatherArgs a) {
 
 // Each token owns Hq query rows, Hkv key rows and Hkv value rows.  A group of
 // LPR lanes takes one token and kPrologueRows consecutive rows of it, so the
-// token's phases are loaded once per group and reused for every row.
-constexpr int kPrologueRows = 4;
+// token's phases are loaded once per group and reused for every row.  The
+// phases, the rows and the token's position are requested together (nothing
+// waits on another load before its own loads are issued).
+constexpr int kPrologueRows = 2;
 
 template <bool BF16, int D>
 __global__ __launch_bounds__(256) void prologue_kernel(PrologueArgs a) {
@@ -309,14 +311,15 @@ __global__ __launch_bounds__(256) void prologue_kernel(PrologueArgs a) {
   const int u = int(grp / chunks);
   const int w0 = int(grp - int64_t(u) * chunks) * kPrologueRows;
   const int w1 = min(w0 + kPrologueRows, per_tok);
-  const bool rot_tok = a.new_pos[u] != 0;
+  const int pos = a.new_pos[u];
+  const int row = a.new_row[u];
   Phase ph[EPV];
-  if (rot_tok && w0 < a.q_heads + a.kv_heads) {
+  if (w0 < a.q_heads + a.kv_heads) {
     const Phase* pp = a.phase_new + int64_t(u) * (D / 2) + j * EPV;
 #pragma unroll
     for (int e = 0; e < EPV; ++e) ph[e] = pp[e];
   }
-  const int row = a.new_row[u];
+  const bool rot_tok = pos != 0;
   // issue every row's loads before any rotation or store
   u32x4 x0[kPrologueRows], x1[kPrologueRows];
   char* dst[kPrologueRows];
