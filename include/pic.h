@@ -21,10 +21,14 @@
  *   new tokens  the request's fresh tokens (query, inline segments) that are
  *               prefilled against the prefix: KV_M(q; C_ctx).
  *
- * Conventions: positions are 0-based.  Cached keys are stored rotated by
- * standard half-split RoPE (pairs (k, k + d/2), omega_k = theta^(-2k/d)) at
- * their original position orig_c + t.  A span is moved by rotating each of its
- * keys by delta = target - (orig_c + s); values are copied.  A new token at
+ * Conventions: positions are 0-based.  RoPE is the standard half-split form
+ * (pairs (k, k + d/2), omega_k = theta^(-2k/d)).  Cached keys are stored
+ * either rotated at their original position orig_c + t (PIC_KEYS_ROTATED: the
+ * CoinRAG and SemPIC pages' caches) or before RoPE (PIC_KEYS_UNROTATED: the
+ * TurboRAG review page's alternative, Reordered Positions paragraph).  A span
+ * placed at `target` rotates each rotated key by delta = target - (orig_c + s)
+ * (the same for the whole span), or each un-rotated key by its new position
+ * target + t; values are copied.  A new token at
  * position P sees every row, cached or new, whose position is <= P: this is
  * the TurboRAG review page's independent attention (Figure 4: the query sees
  * all chunks and itself, chunks never see each other) and the SemPIC page's
@@ -58,6 +62,12 @@ typedef enum {
 
 typedef enum { PIC_F32 = 0, PIC_BF16 = 1 } pic_dtype;
 
+/* How the pool stores keys. */
+typedef enum {
+  PIC_KEYS_ROTATED = 0,   /* RoPE already applied at the original position orig_c + t */
+  PIC_KEYS_UNROTATED = 1  /* raw keys; RoPE is applied at the new position on assembly */
+} pic_key_storage;
+
 /* Model shape.  head_dim even, a multiple of 16, at most 256; q_heads a
  * multiple of kv_heads (query head h reads kv head h / (q_heads / kv_heads)). */
 typedef struct {
@@ -67,13 +77,19 @@ typedef struct {
   int32_t head_dim;
   double rope_theta;
   int32_t dtype;          /* pic_dtype: storage and I/O type of every tensor */
+  int32_t key_storage;    /* pic_key_storage of the pool's keys (0 = rotated) */
 } pic_model;
 
 /* One span of a request's span table.  e is inclusive.  target is the new
- * position of token s, or PIC_TARGET_AUTO: right after the previous span of
- * the same request (0 for the first).  With the prompt cache as span 0 and
- * every other span AUTO this is CoinRAG's Delta_i = |p| + sum_{j<i}(e_j-s_j+1)
- * (section 2.3, Delta equation; TurboRAG's Reordered Positions). */
+ * position of token s, or
+ *   PIC_TARGET_AUTO:     right after the previous span of the same request
+ *                        (0 for the first).  With the prompt cache as span 0
+ *                        and every other span AUTO this is CoinRAG's
+ *                        Delta_i = |p| + sum_{j<i}(e_j-s_j+1) (section 2.3,
+ *                        Delta equation; TurboRAG's Reordered Positions);
+ *   PIC_TARGET_ORIGINAL: where the span was encoded, orig_c + s (delta 0):
+ *                        TurboRAG's Composite Positions (Figure 5), every
+ *                        chunk restarting at its own base. */
 typedef struct {
   int32_t chunk;
   int32_t s;
@@ -82,6 +98,7 @@ typedef struct {
 } pic_span;
 
 #define PIC_TARGET_AUTO (-1)
+#define PIC_TARGET_ORIGINAL (-2)
 
 /* pic_assemble flags */
 #define PIC_ASSEMBLE_PLAN_ONLY 1  /* plan on host and device, gather nothing (variant F) */
@@ -149,8 +166,11 @@ pic_status pic_plan_release(pic_plan* plan);
  *   new_ptr        host int32[batch + 1], CSR offsets of the new tokens
  *   new_pos        host int32[new_ptr[batch]] explicit positions, strictly
  *                  increasing within a request, or NULL: the new tokens of a
- *                  request then follow its last span (P_j = target_last +
- *                  len_last + j; j if the request has no spans)
+ *                  request then follow its whole prefix, P_j = max(sum of
+ *                  span lengths, furthest span end target_i + len_i) + j
+ *                  (for a contiguous prefix of n rows: n + j; TurboRAG Figure
+ *                  5 also puts the query after the concatenated chunks when
+ *                  their positions restart)
  *   asm_k, asm_v   device buffers [layers][kv_heads][asm_rows_capacity][head_dim]
  *                  of the model dtype, 16-byte aligned (may be NULL with DRY_RUN)
  *   asm_rows_capacity  rows per (layer, kv head) plane
@@ -161,10 +181,10 @@ pic_status pic_plan_release(pic_plan* plan);
  * of every plane, row_base_b = sum over earlier requests of (prefix + n_new).
  * Its prefix rows come first in span-table order (span i, token s_i + t at
  * row row_base_b + sum_{j<i} n_j + t), followed by the new tokens' rows, which
- * pic_query_prefill fills layer by layer.  Prefix keys are rotated by their
- * span's delta in fp64 arithmetic (phase cos/sin in fp64) and rounded once,
- * to nearest even, to the storage type; a span with delta == 0 is copied bit
- * for bit, as are all values.  Overlapping or repeated spans are legal and gathered as
+ * pic_query_prefill fills layer by layer.  Prefix keys are rotated (by their
+ * span's delta, or for un-rotated pools by their new position) in fp64
+ * arithmetic with fp64 cos/sin, and rounded once, to nearest even, to the
+ * storage type; a rotation by 0 is a bit copy, as are all values.  Overlapping or repeated spans are legal and gathered as
  * often as they appear.  The call replaces the plan's previous batch.
  */
 pic_status pic_assemble(pic_plan* plan, int32_t batch, const int32_t* span_ptr,

@@ -26,9 +26,18 @@ Readings of points the pages leave open (each listed in the design notes):
   - RoPE is the standard half-split form, omega_k = theta^(-2k/d), no
     frequency scaling; the pages never write the formula out;
   - positions are 0-based; cached keys are stored already rotated at their
-    original position o_c + t (o_c = 0 unless registered otherwise);
+    original position o_c + t (o_c = 0 unless registered otherwise), or, for a
+    cache built the TurboRAG review page's alternative way (Reordered
+    Positions paragraph), stored un-rotated;
   - a span moved from original start o_c + s to target T is rotated by
-    delta = T - (o_c + s), the same delta for every token of the span;
+    delta = T - (o_c + s), the same delta for every token of the span; an
+    un-rotated key is rotated by its new position T + t;
+  - a span may keep its original positions (target o_c + s, delta 0): the
+    page's composite positions, where every chunk restarts at 0;
+  - new tokens without explicit positions start right after the whole
+    prefix: at the larger of the total span length and the furthest span
+    end (Figure 5 puts the query after the concatenated chunks even when
+    their positions restart);
   - a rotation by angle zero is the identity (values copied, not recomputed);
   - softmax scale 1/sqrt(d); query head h reads kv head floor(h / G);
   - a new token at position P sees every row (cached or new) whose position
@@ -53,6 +62,12 @@ import numpy as np
 
 # span target meaning "continue right after the previous span"
 TARGET_AUTO = -1
+# span target meaning "keep the span's original positions" (delta = 0)
+TARGET_ORIGINAL = -2
+
+# how the pool stores keys
+KEYS_ROTATED = "rotated"       # RoPE applied at the original position o_c + t
+KEYS_UNROTATED = "unrotated"   # raw keys; RoPE applied at the new position
 
 STORAGE_TYPES = ("bf16", "f32", "f64")
 
@@ -167,6 +182,8 @@ def plan_spans(spans: Sequence[Tuple[int, int, int, int]],
     places the span right after the previous one (at 0 for the first):
     with the prompt cache as span 0 and every other span AUTO this is the
     CoinRAG Delta equation, Delta_i = |p| + sum_{j<i} (e_j - s_j + 1).
+    target == TARGET_ORIGINAL keeps the span where it was encoded, o_c + s
+    (TurboRAG review page, Figure 5: composite positions).
     delta = target - (o_c + s), where o_c is the chunk's original base.
     """
     out: List[PlannedSpan] = []
@@ -175,8 +192,13 @@ def plan_spans(spans: Sequence[Tuple[int, int, int, int]],
         if e < s:
             raise ValueError("span end before start")
         n = e - s + 1
-        target = nxt if t == TARGET_AUTO else int(t)
         o = 0 if chunk_orig is None else int(chunk_orig[c])
+        if t == TARGET_AUTO:
+            target = nxt
+        elif t == TARGET_ORIGINAL:
+            target = o + int(s)
+        else:
+            target = int(t)
         out.append(PlannedSpan(int(c), int(s), int(e), target, target - (o + int(s))))
         nxt = target + n
     return out
@@ -187,17 +209,20 @@ def new_token_positions(planned: Sequence[PlannedSpan], n_new: int,
     """Positions of the request's new tokens.
 
     Explicit positions are taken as given (SemPIC: final logical positions).
-    Otherwise they continue right after the last span, which for a contiguous
-    prefix of length n is n, n+1, ... (TurboRAG Figure 5: the query follows
-    the last chunk).
+    Otherwise they start right after the whole prefix: at the larger of the
+    total span length and the furthest span end.  For a contiguous prefix of
+    length n both are n; with composite positions (every chunk restarting at
+    0) the first is larger, and TurboRAG Figure 5 indeed places the query
+    after the concatenated chunks (13..16 after three 4-token chunks).
     """
     if explicit is not None:
         p = np.asarray(explicit, dtype=np.int64)
         if p.shape != (n_new,):
             raise ValueError("explicit positions have the wrong length")
         return p
-    start = planned[-1].target + planned[-1].length if planned else 0
-    return start + np.arange(n_new, dtype=np.int64)
+    total = sum(sp.length for sp in planned)
+    furthest = max((sp.target + sp.length for sp in planned), default=0)
+    return max(total, furthest) + np.arange(n_new, dtype=np.int64)
 
 
 # ---------------------------------------------------------------------------
@@ -206,26 +231,37 @@ def new_token_positions(planned: Sequence[PlannedSpan], n_new: int,
 
 def assemble(chunk_k: Sequence[np.ndarray], chunk_v: Sequence[np.ndarray],
              spans: Sequence[Tuple[int, int, int, int]], theta: float, dtype: str,
-             chunk_orig: Optional[Sequence[int]] = None):
+             chunk_orig: Optional[Sequence[int]] = None, keys: str = KEYS_ROTATED):
     """Gather every span's cached K/V rows into one contiguous prefix.
 
-    chunk_k[c], chunk_v[c]: arrays [L][Hkv][len_c][d] of stored values (keys
-    already rotated at their original positions).  Returns
-    (K [L][Hkv][rows][d], V [L][Hkv][rows][d], pos [rows]) with rows in span
-    order: for span i and t = 0 .. e_i - s_i the row holds position target_i + t,
-    key R(delta_i) K_c[s_i + t] rounded to the storage type, and value
-    V_c[s_i + t] copied.
+    chunk_k[c], chunk_v[c]: arrays [L][Hkv][len_c][d] of stored values.
+    Returns (K [L][Hkv][rows][d], V [L][Hkv][rows][d], pos [rows]) with rows
+    in span order: for span i and t = 0 .. e_i - s_i the row holds position
+    target_i + t and value V_c[s_i + t] copied.  Its key, rounded to the
+    storage type, is
+      keys == KEYS_ROTATED:   R(delta_i) K_c[s_i + t]  (CoinRAG section 2.3,
+                              Rot(.; Delta_i): one rotation per span);
+      keys == KEYS_UNROTATED: R(target_i + t) K_c[s_i + t]  (TurboRAG review
+                              page, Reordered Positions: RoPE applied once, at
+                              the token's new position).
     """
+    if keys not in (KEYS_ROTATED, KEYS_UNROTATED):
+        raise ValueError(f"unknown key storage {keys!r}")
     planned = plan_spans(spans, chunk_orig)
     ks, vs, pos = [], [], []
     for sp in planned:
         k = np.asarray(chunk_k[sp.chunk], dtype=np.float64)[:, :, sp.s:sp.e + 1, :]
         v = np.asarray(chunk_v[sp.chunk], dtype=np.float64)[:, :, sp.s:sp.e + 1, :]
-        if sp.delta != 0:
+        p = sp.target + np.arange(sp.length, dtype=np.int64)
+        if keys == KEYS_UNROTATED:
+            angle = np.broadcast_to(p, k.shape[:-1])
+            if np.any(p != 0):
+                k = to_storage(rotate(k, angle, theta), dtype)
+        elif sp.delta != 0:
             k = to_storage(rotate(k, sp.delta, theta), dtype)
         ks.append(k)
         vs.append(v)
-        pos.append(sp.target + np.arange(sp.length, dtype=np.int64))
+        pos.append(p)
     if not ks:
         raise ValueError("assemble() needs at least one span; use empty_prefix()")
     return np.concatenate(ks, axis=2), np.concatenate(vs, axis=2), np.concatenate(pos)

@@ -6,6 +6,7 @@ marshals arguments and raises on error codes; every step of the hot path runs
 in the library's kernels.  PyTorch supplies device memory and streams only.
 """
 from .binding import (  # noqa: F401
-    PIC_BF16, PIC_F32, TARGET_AUTO, VARIANT_FUSED, VARIANT_MATERIALIZED,
+    PIC_BF16, PIC_F32, TARGET_AUTO, TARGET_ORIGINAL, KEYS_ROTATED, KEYS_UNROTATED, VARIANT_FUSED,
+    VARIANT_MATERIALIZED,
     PLAN_ONLY, DRY_RUN, PicError, Plan, Pool, lib, library_path, model_struct,
 )

@@ -18,6 +18,9 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 PIC_F32 = 0
 PIC_BF16 = 1
 TARGET_AUTO = -1
+TARGET_ORIGINAL = -2
+KEYS_ROTATED = 0
+KEYS_UNROTATED = 1
 PLAN_ONLY = 1
 DRY_RUN = 2
 VARIANT_MATERIALIZED = 0
@@ -44,7 +47,8 @@ class PicError(RuntimeError):
 class PicModel(ctypes.Structure):
     _fields_ = [("layers", ctypes.c_int32), ("q_heads", ctypes.c_int32),
                 ("kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
-                ("rope_theta", ctypes.c_double), ("dtype", ctypes.c_int32)]
+                ("rope_theta", ctypes.c_double), ("dtype", ctypes.c_int32),
+                ("key_storage", ctypes.c_int32)]
 
 
 class PicSpan(ctypes.Structure):
@@ -139,9 +143,10 @@ def _p32(a: Optional[np.ndarray]):
     return a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
 
 
-def model_struct(layers, q_heads, kv_heads, head_dim, theta, dtype) -> PicModel:
+def model_struct(layers, q_heads, kv_heads, head_dim, theta, dtype, keys="rotated") -> PicModel:
     dt = {"bf16": PIC_BF16, "f32": PIC_F32}.get(dtype, dtype)
-    return PicModel(int(layers), int(q_heads), int(kv_heads), int(head_dim), float(theta), int(dt))
+    ks = {"rotated": KEYS_ROTATED, "unrotated": KEYS_UNROTATED}.get(keys, keys)
+    return PicModel(int(layers), int(q_heads), int(kv_heads), int(head_dim), float(theta), int(dt), int(ks))
 
 
 class Pool:
@@ -153,6 +158,13 @@ class Pool:
         self._keep = (_i32(chunk_len), _i32(chunk_page_ptr), _i32(page_ids),
                       None if chunk_orig is None else _i32(chunk_orig))
         cl, cp, pg, co = self._keep
+        # the library reads n_chunks (+ 1) entries of these tables
+        if cp.shape[0] != cl.shape[0] + 1:
+            raise ValueError("chunk_page_ptr needs len(chunk_len) + 1 entries")
+        if co is not None and co.shape[0] != cl.shape[0]:
+            raise ValueError("chunk_orig needs len(chunk_len) entries")
+        if cp.shape[0] and pg.shape[0] < int(cp[-1]):
+            raise ValueError("page_ids is shorter than chunk_page_ptr[-1]")
         h = ctypes.c_void_p()
         _check(lib().pic_pool_register(ctypes.byref(model), ctypes.c_void_p(_ptr(pool)), int(pool_bytes),
                                        int(page_tokens), int(n_pages), int(cl.shape[0]), _p32(cl),

@@ -65,7 +65,7 @@ struct pic_plan {
   size_t ws_cap = 0;
   size_t off_spans = 0, off_crow = 0, off_reqs = 0, off_new_pos = 0, off_new_row = 0,
          off_new_req = 0, off_work = 0, off_omega = 0, blob_bytes = 0;
-  size_t off_pos = 0, off_rowsrc = 0, off_tile_pos = 0, off_phase_span = 0, off_phase_new = 0,
+  size_t off_pos = 0, off_rowsrc = 0, off_tile_pos = 0, off_phase_tab = 0, off_phase_new = 0,
          off_qrot = 0, off_opart = 0, off_ml = 0, ws_bytes = 0;
 
   // pinned staging for the upload, reused once its copy has completed
@@ -148,7 +148,7 @@ void layout_workspace(pic_plan* p) {
   p->off_pos = take(size_t(hp.rows) * sizeof(int32_t));
   p->off_rowsrc = take(size_t(hp.rows) * sizeof(int2));
   p->off_tile_pos = take(size_t(hp.n_tiles) * sizeof(int2));
-  p->off_phase_span = take(size_t(hp.n_spans) * half * sizeof(pic::Phase));
+  p->off_phase_tab = take(size_t(hp.phase_rows) * half * sizeof(pic::Phase));
   p->off_phase_new = take(size_t(hp.new_rows) * half * sizeof(pic::Phase));
   p->off_qrot = take(size_t(hp.new_rows) * m.q_heads * m.head_dim * m.elem_bytes);
   const size_t nsplit = hp.n_split > 1 ? size_t(hp.n_split) : 0;
@@ -383,7 +383,9 @@ pic_status pic_assemble(pic_plan* p, int32_t batch, const int32_t* span_ptr, con
     pa.prefix_rows = h.prefix_rows;
     pa.pos = reinterpret_cast<int32_t*>(p->ws + p->off_pos);
     pa.rowsrc = reinterpret_cast<int2*>(p->ws + p->off_rowsrc);
-    pa.phase_span = reinterpret_cast<pic::Phase*>(p->ws + p->off_phase_span);
+    pa.phase_tab = reinterpret_cast<pic::Phase*>(p->ws + p->off_phase_tab);
+    pa.per_position = pi.m.key_storage == PIC_KEYS_UNROTATED;
+    pa.phase_rows = h.phase_rows;
     pa.phase_new = reinterpret_cast<pic::Phase*>(p->ws + p->off_phase_new);
     pa.reqs = reinterpret_cast<const pic::ReqRec*>(p->ws + p->off_reqs);
     pa.batch = h.batch;
@@ -398,7 +400,8 @@ pic_status pic_assemble(pic_plan* p, int32_t batch, const int32_t* span_ptr, con
     ga.spans = reinterpret_cast<const pic::SpanRec*>(p->ws + p->off_spans);
     ga.crow = reinterpret_cast<const int32_t*>(p->ws + p->off_crow);
     ga.page_ids = p->pool->d_page_ids;
-    ga.phase_span = reinterpret_cast<const pic::Phase*>(p->ws + p->off_phase_span);
+    ga.phase_tab = reinterpret_cast<const pic::Phase*>(p->ws + p->off_phase_tab);
+    ga.per_position = pi.m.key_storage == PIC_KEYS_UNROTATED;
     ga.pool = static_cast<const char*>(pi.base);
     ga.asm_k = p->asm_k;
     ga.asm_v = p->asm_v;
@@ -492,7 +495,7 @@ pic_status pic_query_prefill(pic_plan* p, int32_t layer, const void* q, const vo
       aa.ml = reinterpret_cast<float2*>(p->ws + p->off_ml);
       aa.pool = static_cast<const char*>(pi.base);
       aa.rowsrc = reinterpret_cast<const int2*>(p->ws + p->off_rowsrc);
-      aa.phase_span = reinterpret_cast<const pic::Phase*>(p->ws + p->off_phase_span);
+      aa.phase_tab = reinterpret_cast<const pic::Phase*>(p->ws + p->off_phase_tab);
       aa.page_bytes = pi.page_bytes;
       aa.kv_plane_off = int64_t(layer) * 2 * m.kv_heads * pi.page_tokens * m.row_bytes;
       aa.v_off = int64_t(m.kv_heads) * pi.page_tokens * m.row_bytes;

@@ -20,10 +20,12 @@ struct PlanArgs {
   const int32_t* page_ids;
   const double* omega;      // [head_dim / 2]
   int32_t n_spans, n_new, page_shift, half_dim;
+  int32_t per_position;     // keys stored un-rotated: the prefix phases are per position
+  int32_t phase_rows;       // rows of phase_tab: n_spans, or largest prefix position + 1
   int64_t prefix_rows;
   int32_t* pos;             // [rows]
-  int2* rowsrc;             // [rows]: (pool token slot, span or -1)
-  Phase* phase_span;        // [n_spans][half_dim]
+  int2* rowsrc;             // [rows]: (pool token slot, phase_tab row or -1 for no rotation)
+  Phase* phase_tab;         // [phase_rows][half_dim]: per span delta, or per position
   Phase* phase_new;         // [n_new][half_dim]
   const ReqRec* reqs;       // for the tile bounds
   int32_t batch, n_tiles;
@@ -34,12 +36,13 @@ struct GatherArgs {
   const SpanRec* spans;
   const int32_t* crow;
   const int32_t* page_ids;
-  const Phase* phase_span;
+  const Phase* phase_tab;   // per span (rotated keys) or per position (un-rotated keys)
   const char* pool;
   char* asm_k;
   char* asm_v;
   int64_t prefix_rows, cap, page_bytes;
   int32_t n_spans, page_shift, page_tokens, layers, kv_heads, planes_per_block;
+  int32_t per_position;     // keys stored un-rotated: rotate each row by its new position
 };
 
 struct PrologueArgs {
@@ -73,8 +76,8 @@ struct AttnArgs {
   float2* ml;               // [n_split][n_new][Hq]: (max in log2 units, sum)
   // fused variant: prefix rows come from the pool
   const char* pool;
-  const int2* rowsrc;
-  const Phase* phase_span;
+  const int2* rowsrc;       // (pool slot, phase_tab row or -1)
+  const Phase* phase_tab;
   int64_t page_bytes;
   int64_t kv_plane_off;     // byte offset of (layer, K, head 0) inside a page
   int64_t v_off;            // byte offset from a K row to its V row inside a page

@@ -156,8 +156,12 @@ __global__ __launch_bounds__(256) void plan_rows_kernel(PlanArgs a) {
     int page = a.page_ids[s.page_off + (tok >> a.page_shift)];
     int slot = (page << a.page_shift) | (tok & ((1 << a.page_shift) - 1));
     int row = s.dst_row + t;
-    a.pos[row] = s.target + t;
-    a.rowsrc[row] = make_int2(slot, s.delta != 0 ? sp : -1);
+    const int p = s.target + t;
+    a.pos[row] = p;
+    // phase row: the span's delta, or for un-rotated keys the row's position;
+    // -1 where the rotation is by 0 (a bit copy)
+    const int ph = a.per_position ? (p != 0 ? p : -1) : (s.delta != 0 ? sp : -1);
+    a.rowsrc[row] = make_int2(slot, ph);
   } else if (i < a.prefix_rows + a.n_new) {
     int u = int(i - a.prefix_rows);
     int row = a.new_row[u];
@@ -168,17 +172,17 @@ __global__ __launch_bounds__(256) void plan_rows_kernel(PlanArgs a) {
 
 __global__ __launch_bounds__(256) void plan_phase_kernel(PlanArgs a) {
   int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
-  int64_t total = int64_t(a.n_spans + a.n_new) * a.half_dim;
+  int64_t total = (int64_t(a.phase_rows) + a.n_new) * a.half_dim;
   if (i >= total) return;
-  int which = int(i / a.half_dim);
+  int64_t which = i / a.half_dim;
   int k = int(i % a.half_dim);
   double p;
   Phase* dst;
-  if (which < a.n_spans) {
-    p = double(a.spans[which].delta);
-    dst = a.phase_span + int64_t(which) * a.half_dim + k;
+  if (which < a.phase_rows) {
+    p = a.per_position ? double(which) : double(a.spans[which].delta);
+    dst = a.phase_tab + which * a.half_dim + k;
   } else {
-    int u = which - a.n_spans;
+    int u = int(which - a.phase_rows);
     p = double(a.new_pos[u]);
     dst = a.phase_new + int64_t(u) * a.half_dim + k;
   }
@@ -243,10 +247,13 @@ __global__ __launch_bounds__(256) void gather_kernel(GatherArgs a) {
   const int slot = tok & (a.page_tokens - 1);
   const char* __restrict__ src_row = a.pool + int64_t(page) * a.page_bytes + int64_t(slot) * RB;
   const int64_t dst_row = int64_t(s.dst_row) + t;
-  const bool rot = s.delta != 0;
+  // rotation: the span's delta, or for un-rotated keys the row's new position
+  const int newpos = s.target + t;
+  const bool rot = a.per_position ? newpos != 0 : s.delta != 0;
+  const int64_t prow = a.per_position ? newpos : sp;
   Phase ph[EPV];
   if (rot) {
-    const Phase* pp = a.phase_span + int64_t(sp) * (D / 2) + j * EPV;
+    const Phase* pp = a.phase_tab + prow * (D / 2) + j * EPV;
 #pragma unroll
     for (int e = 0; e < EPV; ++e) ph[e] = pp[e];
   }
@@ -747,7 +754,7 @@ __device__ __forceinline__ void fused_v_to_lds(const AttnArgs& a, const ReqRec& 
 // swizzled layout.  Thread units: rows (tid >> 3) + 32 i, pair vector j = tid & 7.
 struct FusedK {
   u32x4 k[2][2];
-  int span[2];
+  int phase[2];   // phase_tab row of each key, -1 for none
 };
 
 __device__ __forceinline__ void fused_k_load(const AttnArgs& a, const ReqRec& rq, int head, int t0,
@@ -762,7 +769,7 @@ __device__ __forceinline__ void fused_k_load(const AttnArgs& a, const ReqRec& rq
     const char* row = fused_row(a, rq, head, rr, false, &src);
     f.k[i][0] = ld16(row + j * 16);
     f.k[i][1] = ld16(row + 128 + j * 16);
-    f.span[i] = src.y;
+    f.phase[i] = src.y;
   }
 }
 
@@ -772,9 +779,9 @@ __device__ __forceinline__ void fused_k_store(const AttnArgs& a, FusedK& f, char
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int r = (tid >> 3) + 32 * i;
-    if (f.span[i] >= 0) {
+    if (f.phase[i] >= 0) {
       Phase ph[8];
-      const Phase* pp = a.phase_span + int64_t(f.span[i]) * 64 + j * 8;
+      const Phase* pp = a.phase_tab + int64_t(f.phase[i]) * 64 + j * 8;
 #pragma unroll
       for (int e = 0; e < 8; ++e) ph[e] = pp[e];
       rotate_vec<true>(f.k[i][0], f.k[i][1], ph);
@@ -963,7 +970,7 @@ hipError_t launch_plan(const PlanArgs& a, hipStream_t s) {
   if (n1 > 0) {
     hipLaunchKernelGGL(plan_rows_kernel, dim3(unsigned((n1 + 255) / 256)), dim3(256), 0, s, a);
   }
-  const int64_t n2 = int64_t(a.n_spans + a.n_new) * a.half_dim;
+  const int64_t n2 = (int64_t(a.phase_rows) + a.n_new) * a.half_dim;
   if (n2 > 0) {
     hipLaunchKernelGGL(plan_phase_kernel, dim3(unsigned((n2 + 255) / 256)), dim3(256), 0, s, a);
   }

@@ -48,12 +48,15 @@ pic_status check_model(const pic_model* m, ModelInfo* out, std::string* err) {
     return fail(err, PIC_EINVAL, "rope_theta must be finite and > 1");
   if (m->dtype != PIC_F32 && m->dtype != PIC_BF16)
     return fail(err, PIC_EINVAL, "dtype must be PIC_F32 or PIC_BF16");
+  if (m->key_storage != PIC_KEYS_ROTATED && m->key_storage != PIC_KEYS_UNROTATED)
+    return fail(err, PIC_EINVAL, "key_storage must be PIC_KEYS_ROTATED or PIC_KEYS_UNROTATED");
   ModelInfo mi;
   mi.layers = m->layers;
   mi.q_heads = m->q_heads;
   mi.kv_heads = m->kv_heads;
   mi.head_dim = m->head_dim;
   mi.dtype = m->dtype;
+  mi.key_storage = m->key_storage;
   mi.theta = m->rope_theta;
   mi.elem_bytes = m->dtype == PIC_BF16 ? 2 : 4;
   mi.group = m->q_heads / m->kv_heads;
@@ -148,6 +151,7 @@ pic_status build_plan(const PoolInfo& pool, int32_t batch, const int32_t* span_p
 
   int64_t row = 0, crow = 0, tiles = 0;
   int32_t max_pos = 0;
+  int64_t max_prefix_pos = -1;
   for (int32_t b = 0; b < batch; ++b) {
     ReqRec& r = p.reqs[b];
     r.row_base = int32_t(row);  // range-checked below before it can overflow
@@ -155,7 +159,8 @@ pic_status build_plan(const PoolInfo& pool, int32_t batch, const int32_t* span_p
     r.span_end = span_ptr[b + 1];
     r.new_begin = new_ptr[b];
     r.n_new = new_ptr[b + 1] - new_ptr[b];
-    int64_t next = 0;  // AUTO continuation position
+    int64_t next = 0;      // AUTO continuation position
+    int64_t furthest = 0;  // largest span end (target + n)
     int64_t prefix = 0;
     for (int32_t i = span_ptr[b]; i < span_ptr[b + 1]; ++i) {
       const pic_span& sp = spans[i];
@@ -165,14 +170,19 @@ pic_status build_plan(const PoolInfo& pool, int32_t batch, const int32_t* span_p
       if (sp.s < 0 || sp.s > sp.e || sp.e >= len)
         return fail(err, PIC_ERANGE, "span %d: need 0 <= s <= e < len, got s=%d e=%d len=%d", i,
                     sp.s, sp.e, len);
-      if (sp.target < 0 && sp.target != PIC_TARGET_AUTO)
-        return fail(err, PIC_EINVAL, "span %d: target %d is neither >= 0 nor PIC_TARGET_AUTO", i,
+      if (sp.target < 0 && sp.target != PIC_TARGET_AUTO && sp.target != PIC_TARGET_ORIGINAL)
+        return fail(err, PIC_EINVAL,
+                    "span %d: target %d is neither >= 0 nor PIC_TARGET_AUTO / PIC_TARGET_ORIGINAL", i,
                     sp.target);
       int64_t n = int64_t(sp.e) - sp.s + 1;
-      int64_t target = sp.target == PIC_TARGET_AUTO ? next : int64_t(sp.target);
+      const int64_t orig = int64_t(pool.chunk_orig[sp.chunk]) + sp.s;
+      int64_t target = sp.target == PIC_TARGET_AUTO       ? next
+                       : sp.target == PIC_TARGET_ORIGINAL ? orig
+                                                          : int64_t(sp.target);
+      if (target < 0) return fail(err, PIC_ERANGE, "span %d: original position is negative", i);
       if (target + n - 1 > kMaxPosition)
         return fail(err, PIC_ERANGE, "span %d: positions exceed %lld", i, (long long)kMaxPosition);
-      int64_t delta = target - (int64_t(pool.chunk_orig[sp.chunk]) + sp.s);
+      int64_t delta = target - orig;
       SpanRec& s = p.spans[i];
       s.crow = int32_t(crow);
       s.dst_row = int32_t(row + prefix);
@@ -184,6 +194,8 @@ pic_status build_plan(const PoolInfo& pool, int32_t batch, const int32_t* span_p
       s.req = b;
       p.crow[i] = int32_t(crow);
       max_pos = std::max<int64_t>(max_pos, target + n - 1);
+      max_prefix_pos = std::max<int64_t>(max_prefix_pos, target + n - 1);
+      furthest = std::max<int64_t>(furthest, target + n);
       next = target + n;
       prefix += n;
       crow += n;
@@ -202,7 +214,8 @@ pic_status build_plan(const PoolInfo& pool, int32_t batch, const int32_t* span_p
           return fail(err, PIC_EINVAL,
                       "new token %d: positions must increase strictly within a request", u);
       } else {
-        pos = next + j;
+        // after the whole prefix: the larger of its length and its furthest end
+        pos = std::max(prefix, furthest) + j;
         if (pos > kMaxPosition) return fail(err, PIC_ERANGE, "new token %d: position too large", u);
       }
       p.new_pos[u] = int32_t(pos);
@@ -221,6 +234,9 @@ pic_status build_plan(const PoolInfo& pool, int32_t batch, const int32_t* span_p
   p.rows = row;
   p.n_tiles = int32_t(tiles);
   p.max_position = max_pos;
+  // rows of the prefix phase table: one per span (rotated keys, one delta per
+  // span) or one per position 0 .. largest prefix position (un-rotated keys)
+  p.phase_rows = pool.m.key_storage == PIC_KEYS_UNROTATED ? int32_t(max_prefix_pos + 1) : p.n_spans;
   if (capacity >= 0 && p.rows > capacity)
     return fail(err, PIC_ERANGE, "batch needs %lld rows per plane, capacity is %lld",
                 (long long)p.rows, (long long)capacity);

@@ -1,10 +1,11 @@
 // Host-side validation and planning for libpic (pure C++17, no HIP).
 //
 // Everything here is integer arithmetic on the caller's span tables: span
-// lengths, row offsets, resolved targets, rotation deltas (CoinRAG page,
-// section 2.3, Delta equation: a span's new start is the prompt length plus
-// the lengths of the spans before it), new-token positions and the work list
-// of the attention kernel.  The records below are uploaded to the device as
+// lengths, row offsets, resolved targets (CoinRAG page, section 2.3, Delta
+// equation: a span's new start is the prompt length plus the lengths of the
+// spans before it; TurboRAG review page, Figure 5: composite positions keep
+// each chunk where it was encoded), rotation deltas, new-token positions and
+// the work list of the attention kernel.  The records below are uploaded to the device as
 // they are, so their layouts are shared with the kernels.
 #pragma once
 
@@ -18,6 +19,7 @@ namespace pic {
 
 struct ModelInfo {
   int32_t layers = 0, q_heads = 0, kv_heads = 0, head_dim = 0, dtype = 0;
+  int32_t key_storage = PIC_KEYS_ROTATED;
   double theta = 0.0;
   int32_t elem_bytes = 0;   // 2 (bf16) or 4 (f32)
   int32_t group = 0;        // q_heads / kv_heads
@@ -73,6 +75,7 @@ struct HostPlan {
   int32_t batch = 0, n_spans = 0, max_position = 0;
   int64_t prefix_rows = 0, new_rows = 0, rows = 0;
   int32_t n_tiles = 0;              // 64-row attention tiles over all requests
+  int32_t phase_rows = 0;           // rows of the prefix phase table (spans or positions)
   std::vector<SpanRec> spans;
   std::vector<int32_t> crow;        // n_spans + 1 compact-row offsets
   std::vector<ReqRec> reqs;

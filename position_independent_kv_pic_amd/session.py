@@ -14,13 +14,13 @@ from .binding import (DRY_RUN, PLAN_ONLY, VARIANT_MATERIALIZED, Plan, Pool, mode
 
 class Session:
     def __init__(self, layers, q_heads, kv_heads, head_dim, theta, dtype, pool_tensor,
-                 page_tokens, chunk_len, chunk_page_ptr, page_ids, chunk_orig=None):
+                 page_tokens, chunk_len, chunk_page_ptr, page_ids, chunk_orig=None, keys="rotated"):
         import torch
         self.torch = torch
         self.layers, self.q_heads, self.kv_heads, self.head_dim = layers, q_heads, kv_heads, head_dim
         self.dtype = dtype
         self.tdtype = torch.bfloat16 if dtype == "bf16" else torch.float32
-        self.model = model_struct(layers, q_heads, kv_heads, head_dim, theta, dtype)
+        self.model = model_struct(layers, q_heads, kv_heads, head_dim, theta, dtype, keys)
         self.pool_tensor = pool_tensor
         self.pool = Pool(self.model, pool_tensor, pool_tensor.numel() * pool_tensor.element_size(),
                          page_tokens, pool_tensor.shape[0], chunk_len, chunk_page_ptr, page_ids,

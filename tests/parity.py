@@ -50,7 +50,7 @@ def request_prefix(wl: W.Workload, pool, b: int, layers):
         ck[c] = k.numpy()
         cv[c] = v.numpy()
     return orc.assemble(ck, cv, [tuple(int(x) for x in s) for s in r.spans], wl.model.theta,
-                        wl.model.dtype, chunk_orig=wl.pool.chunk_orig)
+                        wl.model.dtype, chunk_orig=wl.pool.chunk_orig, keys=wl.keys)
 
 
 def request_positions(wl: W.Workload, b: int):

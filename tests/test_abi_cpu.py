@@ -37,7 +37,7 @@ def test_library_exports_every_declared_function():
 
 def _model(wl):
     m = wl.model
-    return B.model_struct(m.layers, m.q_heads, m.kv_heads, m.head_dim, m.theta, m.dtype)
+    return B.model_struct(m.layers, m.q_heads, m.kv_heads, m.head_dim, m.theta, m.dtype, wl.keys)
 
 
 def _pool(wl, base=FAKE_POOL):
@@ -51,7 +51,8 @@ def _dry(plan, wl, capacity=2 ** 40):
                   capacity, B.DRY_RUN)
 
 
-@pytest.mark.parametrize("name", W.FULL_SIZE + W.REDUCED)
+@pytest.mark.parametrize("name", W.FULL_SIZE + W.REDUCED + W.REDUCED_NEXT +
+                         ("turborag_b16_unrot", "turborag_b16_composite"))
 def test_host_plan_matches_oracle(name):
     wl = W.get(name)
     pool = _pool(wl)
@@ -81,6 +82,40 @@ def test_host_plan_matches_oracle(name):
         row = acc + r.n_new
     plan.release()
     pool.release()
+
+
+def test_original_targets_and_new_positions_after_the_whole_prefix():
+    # composite positions with non-zero chunk bases: each span stays where it
+    # was encoded (delta 0) and the new tokens follow the whole prefix
+    wl = W.get("tiny_f32")
+    p = wl.pool
+    orig = np.zeros(p.n_chunks, np.int32)
+    orig[:3] = [100, 0, 7]
+    pool = B.Pool(_model(wl), FAKE_POOL, p.n_pages * W.page_bytes(wl.model, p.page_tokens), p.page_tokens,
+                  p.n_pages, p.chunk_len, p.chunk_page_ptr, p.page_ids, orig)
+    plan = B.Plan(pool)
+    spans = np.array([[0, 2, 5, B.TARGET_ORIGINAL], [2, 0, 9, B.TARGET_ORIGINAL], [1, 3, 4, B.TARGET_AUTO]],
+                     np.int32)
+    plan.assemble(np.array([0, 3]), spans, np.array([0, 4]), None, None, None, 2 ** 40, B.DRY_RUN)
+    tgt, dlt, _ = plan.spans()
+    want = orc.plan_spans([tuple(int(x) for x in r) for r in spans], orig)
+    assert tgt.tolist() == [sp.target for sp in want] == [102, 7, 17]
+    assert dlt.tolist() == [sp.delta for sp in want] == [0, 0, 14]
+    npos, _ = plan.new_tokens()
+    assert npos.tolist() == orc.new_token_positions(want, 4).tolist() == [106, 107, 108, 109]
+    plan.release()
+    pool.release()
+
+
+def test_key_storage_is_validated():
+    wl = W.get("tiny_f32")
+    p = wl.pool
+    m = _model(wl)
+    m.key_storage = 7
+    with pytest.raises(B.PicError) as ei:
+        B.Pool(m, FAKE_POOL, p.n_pages * W.page_bytes(wl.model, p.page_tokens), p.page_tokens, p.n_pages,
+               p.chunk_len, p.chunk_page_ptr, p.page_ids)
+    assert ei.value.name == "PIC_EINVAL"
 
 
 def _err(fn):

@@ -102,7 +102,7 @@ def test_tiny_fp32_config_end_to_end():
     dw.close()
 
 
-@pytest.mark.parametrize("name", W.REDUCED)
+@pytest.mark.parametrize("name", W.REDUCED + W.REDUCED_NEXT)
 def test_reduced_workloads_every_element(name):
     wl = W.get(name)
     _say(f"case reduced {name}")
@@ -139,7 +139,8 @@ def _token_subset(n, k=16):
     return idx
 
 
-@pytest.mark.parametrize("name", [n for n in W.FULL_SIZE if n != "tiny_f32"])
+@pytest.mark.parametrize("name", [n for n in W.FULL_SIZE if n != "tiny_f32"] +
+                         ["turborag_b16_unrot", "turborag_b16_composite"])
 def test_full_size_workloads_sampled(name):
     wl = W.get(name)
     _say(f"case full {name}: batch {wl.batch}, rows {wl.rows_total}")
@@ -161,7 +162,7 @@ def test_full_size_workloads_sampled(name):
     torch.cuda.empty_cache()
 
 
-def _edge_workload():
+def _edge_workload(keys="rotated"):
     """Ragged shapes and degenerate spans on Qwen2-like heads, two layers."""
     rng = np.random.default_rng(77)
     model = W.ModelShape(2, 28, 4, 128, 1e6, "bf16")
@@ -171,9 +172,11 @@ def _edge_workload():
     reqs = [
         # 1-token spans, a span at a chunk's end, a repeated span, negative deltas
         # (target before the original position), an explicit target that
-        # overlaps positions already used, a large original base
+        # overlaps positions already used, a large original base, a span kept
+        # at its original positions (later than every query: fully masked)
         W.Request(np.array([[0, 511, 511, 0], [3, 0, 0, A], [1, 299, 299, A], [1, 0, 299, A],
-                            [1, 0, 299, A], [2, 3, 9, 2], [4, 0, 95, A]], np.int32), 37,
+                            [1, 0, 299, A], [2, 3, 9, 2], [4, 0, 95, A],
+                            [4, 10, 20, W.TARGET_ORIGINAL]], np.int32), 37,
                   np.arange(105, 142, dtype=np.int32)),
         # no spans: plain causal prefill
         W.Request(np.zeros((0, 4), np.int32), 29, np.arange(29, dtype=np.int32)),
@@ -183,12 +186,13 @@ def _edge_workload():
         W.Request(np.array([[0, 5, 70, 10], [2, 0, 16, 300]], np.int32), 9,
                   np.array([0, 1, 2, 200, 201, 250, 400, 401, 402], np.int32)),
     ]
-    return W.Workload("edge", 0, model, pool, reqs, W.ValueRecipe("lognormal", "half"), 900)
+    return W.Workload("edge", 0, model, pool, reqs, W.ValueRecipe("lognormal", "half"), 900, keys=keys)
 
 
-def test_edge_cases_ragged_degenerate_and_canary():
-    wl = _edge_workload()
-    _say("case edge")
+@pytest.mark.parametrize("keys", ["rotated", "unrotated"])
+def test_edge_cases_ragged_degenerate_and_canary(keys):
+    wl = _edge_workload(keys)
+    _say(f"case edge, keys {keys}")
     dw = open_workload(wl)
     sess = dw.session
     cap = wl.rows_total + 37

@@ -109,7 +109,34 @@ def _bf16_truncate(x):
 
 _ORIG = {n: getattr(orc, n) for n in ("rotate", "rope_frequencies", "plan_spans", "attention", "round_bf16")}
 
+_orig_assemble = orc.assemble
+_orig_new_positions = orc.new_token_positions
+_orig_plan_spans = orc.plan_spans
+
+
+def _assemble_unrotated_by_span_delta(chunk_k, chunk_v, spans, theta, dtype, chunk_orig=None,
+                                      keys=orc.KEYS_ROTATED):
+    # un-rotated keys moved by the span's delta, as if they were stored rotated
+    return _orig_assemble(chunk_k, chunk_v, spans, theta, dtype, chunk_orig=chunk_orig)
+
+
+def _new_positions_after_last_span(planned, n_new, explicit=None):
+    if explicit is not None:
+        return _orig_new_positions(planned, n_new, explicit)
+    start = planned[-1].target + planned[-1].length if planned else 0
+    return start + np.arange(n_new, dtype=np.int64)
+
+
+def _plan_original_ignores_base(spans, chunk_orig=None):
+    # TARGET_ORIGINAL resolved to s, forgetting the chunk's original base
+    fixed = [(c, s, e, s if t == orc.TARGET_ORIGINAL else t) for (c, s, e, t) in spans]
+    return _orig_plan_spans(fixed, chunk_orig)
+
+
 MUTANTS = [
+    ("assemble", _assemble_unrotated_by_span_delta),
+    ("new_token_positions", _new_positions_after_last_span),
+    ("plan_spans", _plan_original_ignores_base),
     ("rotate", _rotate_wrong_sign),
     ("rotate", _rotate_interleaved),
     ("rope_frequencies", _freq_wrong_exponent),

@@ -183,6 +183,29 @@ def test_worked_example_positions():
     assert qpos - pos_r[pr["chunk"] * l + pr["token_in_chunk"]] == g["true_distance"]
 
 
+def test_worked_example_composite_query_follows_the_concatenated_chunks():
+    # TurboRAG Figure 5: with composite positions every chunk restarts at 0
+    # (kept where it was encoded: TARGET_ORIGINAL), yet the query sits after
+    # the concatenated chunks (13..16 in the figure's 1-based labels)
+    with open(os.path.join(GOLDEN, "turborag_fig5_positions.json")) as f:
+        g = json.load(f)
+    l, k = g["chunk_length"], g["n_chunks"]
+    composite = orc.plan_spans([(c, 0, l - 1, orc.TARGET_ORIGINAL) for c in range(k)])
+    pos_c = np.concatenate([sp.target + np.arange(sp.length) for sp in composite])
+    assert pos_c.tolist() == g["composite_positions"]
+    assert all(sp.delta == 0 for sp in composite)
+    assert orc.new_token_positions(composite, 4).tolist() == g["query_positions"]
+
+
+def test_target_original_keeps_encoded_positions():
+    plan = orc.plan_spans([(0, 3, 7, orc.TARGET_ORIGINAL), (1, 0, 2, orc.TARGET_ORIGINAL),
+                           (1, 5, 6, orc.TARGET_AUTO)], chunk_orig=[10, 0])
+    assert [sp.target for sp in plan] == [13, 0, 3]
+    assert [sp.delta for sp in plan] == [0, 0, 3 - 5]
+    # new tokens follow the whole prefix: 5 + 3 + 2 rows, furthest end 18
+    assert orc.new_token_positions(plan, 2).tolist() == [18, 19]
+
+
 def test_delta_equation_with_prompt_and_nuggets():
     # CoinRAG section 2.3: Delta_i = |p| + sum_{j<i} (e_j - s_j + 1)
     prompt = (9, 0, 31, 0)
@@ -232,6 +255,50 @@ def test_assembled_keys_equal_keys_encoded_at_new_positions():
             assert np.array_equal(v[:, :, row, :], vals[c][:, :, s + t, :])
             row += 1
     assert row == k.shape[2]
+
+
+def test_unrotated_keys_are_rotated_at_their_new_positions():
+    # TurboRAG review page, Reordered Positions: store keys before RoPE and
+    # apply it at the new position when the caches are concatenated
+    rng = np.random.default_rng(16)
+    theta, d = 1e4, 16
+    orig = [0, 40, 7]
+    raw, stored, vals = _pool(rng, 3, 24, 2, 2, d, theta, orig)
+    spans = [(1, 0, 3, 0), (0, 5, 9, orc.TARGET_AUTO), (2, 23, 23, orc.TARGET_ORIGINAL),
+             (0, 5, 9, orc.TARGET_AUTO), (1, 10, 20, 100)]
+    k, v, pos = orc.assemble(raw, vals, spans, theta, "f64", chunk_orig=orig, keys=orc.KEYS_UNROTATED)
+    assert pos.tolist() == list(range(9)) + [30] + list(range(31, 36)) + list(range(100, 111))
+    row = 0
+    for (c, s, e, _) in spans:
+        for t in range(e - s + 1):
+            want_k = rope_ref(raw[c][:, :, s + t, :], theta, pos[row])
+            assert np.allclose(k[:, :, row, :], want_k, atol=1e-9)
+            assert np.array_equal(v[:, :, row, :], vals[c][:, :, s + t, :])
+            row += 1
+    assert row == k.shape[2]
+    # the same prefix as from keys stored rotated at their original positions
+    k2, _, pos2 = orc.assemble(stored, vals, spans, theta, "f64", chunk_orig=orig)
+    assert np.array_equal(pos, pos2)
+    assert np.allclose(k, k2, atol=1e-9)
+
+
+def test_unrotated_unit_keys_give_cos_sin_of_the_new_position():
+    d, theta, T = 8, 1e4, 37
+    h = d // 2
+    chunk = np.zeros((1, 1, h, d))
+    for t in range(h):
+        chunk[0, 0, t, t] = 1.0          # token t holds the unit vector e_t
+    k, _, pos = orc.assemble([chunk], [chunk], [(0, 0, h - 1, T)], theta, "f64",
+                             keys=orc.KEYS_UNROTATED)
+    for t in range(h):
+        w = math.exp(-(2.0 * t / d) * math.log(theta))
+        ang = (T + t) * w
+        want = np.zeros(d)
+        want[t], want[t + h] = math.cos(ang), math.sin(ang)
+        assert np.allclose(k[0, 0, t], want, atol=1e-12)
+    # a token that lands at position 0 is copied unchanged (R(0) = I)
+    k0, _, _ = orc.assemble([chunk], [chunk], [(0, 0, 0, 0)], theta, "f64", keys=orc.KEYS_UNROTATED)
+    assert np.array_equal(k0[0, 0, 0], chunk[0, 0, 0])
 
 
 def test_zero_delta_is_an_exact_copy_and_rounding_applies_otherwise():

@@ -30,6 +30,7 @@ from typing import Dict, List, Optional
 import numpy as np
 
 TARGET_AUTO = -1
+TARGET_ORIGINAL = -2   # keep the span where it was encoded (composite positions)
 
 
 # ---------------------------------------------------------------------------
@@ -105,6 +106,7 @@ class Workload:
     seed: int
     notes: str = ""
     extra: Dict = field(default_factory=dict)
+    keys: str = "rotated"        # "rotated" (at the original position) or "unrotated"
 
     @property
     def batch(self) -> int:
@@ -198,20 +200,25 @@ def _layout_rng(seed: int, layout: int) -> np.random.Generator:
 
 def _turborag(batch: int, model: ModelShape = QWEN2_7B, n_chunks: int = 200,
               chunk: int = 512, top: int = 5, prompt_len: int = 32, n_new: int = 64,
-              name: str = "", layout: int = 0) -> Workload:
+              name: str = "", layout: int = 0, keys: str = "rotated",
+              positions: str = "reordered") -> Workload:
     """Whole-chunk reuse: a 32-token prompt cache and top-5 whole 512-token
-    chunks out of 200, in retrieval order, contiguous; 64 query tokens."""
+    chunks out of 200, in retrieval order; 64 query tokens.  Reordered
+    positions make the chunks contiguous; composite positions keep every chunk
+    where it was encoded (each restarting at 0).  Keys are stored rotated at
+    their original positions or un-rotated."""
     seed = 2000
     pool = make_pool(np.random.default_rng(seed), [chunk] * n_chunks + [prompt_len])
     rng = _layout_rng(seed, layout)
     prompt = n_chunks
+    tgt = TARGET_ORIGINAL if positions == "composite" else TARGET_AUTO
     reqs = []
     for _ in range(batch):
         sel = rng.choice(n_chunks, size=top, replace=False)
-        rows = [(prompt, 0, prompt_len - 1, 0)] + [(int(c), 0, chunk - 1, TARGET_AUTO) for c in sel]
+        rows = [(prompt, 0, prompt_len - 1, 0)] + [(int(c), 0, chunk - 1, tgt) for c in sel]
         reqs.append(Request(_spans(rows), n_new))
     return Workload(name or f"turborag_b{batch}", 2, model, pool, reqs,
-                    ValueRecipe("lognormal", "half"), seed)
+                    ValueRecipe("lognormal", "half"), seed, keys=keys)
 
 
 def _nugget_spans(rng, chunks, n_spans, chunk_len, p_geom=1.0 / 15, lo=3, hi=48):
@@ -235,7 +242,8 @@ def _nugget_spans(rng, chunks, n_spans, chunk_len, p_geom=1.0 / 15, lo=3, hi=48)
 
 def _coinrag(batch: int, model: ModelShape = QWEN2_7B, n_chunks: int = 2000,
              chunk: int = 512, retrieved: int = 20, n_spans: int = 64,
-             prompt_len: int = 32, n_new: int = 64, name: str = "", layout: int = 0) -> Workload:
+             prompt_len: int = 32, n_new: int = 64, name: str = "", layout: int = 0,
+             keys: str = "rotated") -> Workload:
     """Nugget reuse: 20 retrieved chunks per request, 64 non-overlapping spans
     with geometric lengths (mean 15, clipped to [3, 48]) in shuffled order,
     contiguous after a 32-token prompt cache; 64 query tokens."""
@@ -250,7 +258,7 @@ def _coinrag(batch: int, model: ModelShape = QWEN2_7B, n_chunks: int = 2000,
         rows = [(prompt, 0, prompt_len - 1, 0)] + [(c, s, e, TARGET_AUTO) for c, s, e in spans]
         reqs.append(Request(_spans(rows), n_new))
     return Workload(name or f"coinrag_b{batch}", 3, model, pool, reqs,
-                    ValueRecipe("lognormal", "half"), seed)
+                    ValueRecipe("lognormal", "half"), seed, keys=keys)
 
 
 def _sempic(batch: int, model: ModelShape = LLAMA31_8B, n_docs: int = 64,
@@ -311,6 +319,11 @@ def get(name: str, layout: int = 0) -> Workload:
         "tiny_f32": lambda: _tiny(0),
         "turborag_b1": lambda: _turborag(1, layout=layout),
         "turborag_b16": lambda: _turborag(16, layout=layout),
+        # the TurboRAG review page's other two layouts: keys stored un-rotated
+        # (RoPE applied at the new position), and composite positions
+        "turborag_b16_unrot": lambda: _turborag(16, name="turborag_b16_unrot", layout=layout, keys="unrotated"),
+        "turborag_b16_composite": lambda: _turborag(16, name="turborag_b16_composite", layout=layout,
+                                                    positions="composite"),
         "coinrag_b32": lambda: _coinrag(32, layout=layout),
         "sempic_b8": lambda: _sempic(8, layout=layout),
         "long_131k_b1": lambda: _long(1, 64, name="long_131k_b1", layout=layout),
@@ -318,6 +331,12 @@ def get(name: str, layout: int = 0) -> Workload:
         # reduced variants
         "turborag_small": lambda: _turborag(3, small2, n_chunks=12, name="turborag_small", layout=layout),
         "coinrag_small": lambda: _coinrag(4, small2, n_chunks=40, name="coinrag_small", layout=layout),
+        "turborag_small_unrot": lambda: _turborag(3, small2, n_chunks=12, name="turborag_small_unrot",
+                                                  layout=layout, keys="unrotated"),
+        "coinrag_small_unrot": lambda: _coinrag(4, small2, n_chunks=40, name="coinrag_small_unrot",
+                                                layout=layout, keys="unrotated"),
+        "turborag_small_composite": lambda: _turborag(3, small2, n_chunks=12, name="turborag_small_composite",
+                                                      layout=layout, positions="composite"),
         "sempic_small": lambda: _sempic(2, small4, n_docs=6, doc_lo=100, doc_hi=700, per_req=3,
                                         inline_lo=20, inline_hi=90, n_query=40, name="sempic_small",
                                         layout=layout),
@@ -334,6 +353,7 @@ def get(name: str, layout: int = 0) -> Workload:
 FULL_SIZE = ("tiny_f32", "turborag_b1", "turborag_b16", "coinrag_b32", "sempic_b8",
              "long_131k_b1", "long_16k_b32")
 REDUCED = ("turborag_small", "coinrag_small", "sempic_small", "long_small")
+REDUCED_NEXT = ("turborag_small_unrot", "coinrag_small_unrot", "turborag_small_composite")
 
 
 # ---------------------------------------------------------------------------

@@ -40,5 +40,5 @@ def open_workload(wl: Workload, device="cuda") -> DeviceWorkload:
     torch.cuda.synchronize()
     m, p = wl.model, wl.pool
     sess = Session(m.layers, m.q_heads, m.kv_heads, m.head_dim, m.theta, m.dtype, pool, p.page_tokens,
-                   p.chunk_len, p.chunk_page_ptr, p.page_ids, p.chunk_orig)
+                   p.chunk_len, p.chunk_page_ptr, p.page_ids, p.chunk_orig, keys=wl.keys)
     return DeviceWorkload(wl, pool, ks, vs, sess)
