@@ -151,7 +151,7 @@ void layout_workspace(pic_plan* p) {
   p->off_phase_tab = take(size_t(hp.phase_rows) * half * sizeof(pic::Phase));
   p->off_phase_new = take(size_t(hp.new_rows) * half * sizeof(pic::Phase));
   p->off_qrot = take(size_t(hp.new_rows) * m.q_heads * m.head_dim * m.elem_bytes);
-  const size_t nsplit = hp.n_split > 1 ? size_t(hp.n_split) : 0;
+  const size_t nsplit = hp.n_split_out > 1 ? size_t(hp.n_split_out) : 0;
   p->off_opart = take(nsplit * size_t(hp.new_rows) * m.q_heads * m.head_dim * sizeof(float));
   p->off_ml = take(nsplit * size_t(hp.new_rows) * m.q_heads * sizeof(float2));
   p->ws_bytes = o;
@@ -310,8 +310,8 @@ pic_status pic_assemble(pic_plan* p, int32_t batch, const int32_t* span_ptr, con
     hp.n_split = pic::choose_attention_split(hp, pi.m.kv_heads, pi.m.group, pic::kAttnColsPerWG,
                                              pic::kAttnRowsPerTile, pic::kAttnTargetWGs,
                                              pic::kAttnMaxSplit, /*min_tiles_per_split=*/4);
-    pic::build_attention_work(hp, pi.m.kv_heads, pi.m.group, pic::kAttnColsPerWG, pic::kAttnRowsPerTile,
-                              hp.n_split, &hp.work);
+    hp.n_split_out = pic::build_attention_work(hp, pi.m.kv_heads, pi.m.group, pic::kAttnColsPerWG,
+                                               pic::kAttnRowsPerTile, hp.n_split, &hp.work);
   }
   if (dry) {
     p->hp = std::move(hp);
@@ -488,7 +488,7 @@ pic_status pic_query_prefill(pic_plan* p, int32_t layer, const void* q, const vo
       aa.q_heads = m.q_heads;
       aa.group = m.group;
       aa.n_new = int32_t(h.new_rows);
-      aa.n_split = h.n_split;
+      aa.n_split_out = h.n_split_out;
       aa.scale_log2 = float(1.4426950408889634 / std::sqrt(double(m.head_dim)));
       aa.out = static_cast<uint16_t*>(out);
       aa.opart = reinterpret_cast<float*>(p->ws + p->off_opart);

@@ -69,11 +69,12 @@ struct AttnArgs {
   const ReqRec* reqs;
   const int32_t* new_pos;
   const AttnWork* work;
-  int32_t n_work, q_heads, group, n_new, n_split;
+  int32_t n_work, q_heads, group, n_new;
+  int32_t n_split_out;      // partials written for merge_kernel (1: outputs written directly)
   float scale_log2;         // log2(e) / sqrt(head_dim)
   uint16_t* out;            // n_split == 1
-  float* opart;             // [n_split][n_new][Hq][128]
-  float2* ml;               // [n_split][n_new][Hq]: (max in log2 units, sum)
+  float* opart;             // [n_split_out][n_new][Hq][128]
+  float2* ml;               // [n_split_out][n_new][Hq]: (max in log2 units, sum)
   // fused variant: prefix rows come from the pool
   const char* pool;
   const int2* rowsrc;       // (pool slot, phase_tab row or -1)
@@ -98,8 +99,8 @@ struct AttnF32Args {
 };
 
 constexpr int kAttnRowsPerTile = 64;
-constexpr int kAttnColsPerWG = 128;   // 4 waves x 32 query columns
-constexpr int kAttnTargetWGs = 512;   // two workgroups per CU
+constexpr int kAttnColsPerWG = 128;   // work item: 4 waves x 32 query columns
+constexpr int kAttnTargetWGs = 512;   // work items: two per CU (one workgroup of two items)
 constexpr int kAttnMaxSplit = 16;     // merge_kernel handles at most this many row splits
 
 hipError_t launch_plan(const PlanArgs& a, hipStream_t s);

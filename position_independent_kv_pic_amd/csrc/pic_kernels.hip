@@ -622,16 +622,15 @@ __device__ __forceinline__ void pv_product(const Col& c, const bf16x8 pb[2][2], 
   }
 }
 
-// Write a column's result: the split's partial (unnormalised O, reference
-// maximum, sum) for merge_kernel, or the normalised bf16 output.
-__device__ __forceinline__ void store_column(const AttnArgs& a, const AttnWork& w, const Col& c, const f32x16 o[4],
-                                             const f32x16& lacc, float m) {
-  // rows of lacc are identical: each lane already holds its column's full sum
-  const float lt = lacc[0];
+// Write a column's result: a partial (unnormalised O, reference maximum m,
+// sum lt) at partial index `part` for merge_kernel, or the normalised bf16
+// output.
+__device__ __forceinline__ void store_column(const AttnArgs& a, const Col& c, const f32x16 o[4], float lt,
+                                             float m, bool partial, int part) {
   if (!c.ok) return;
   const int g2 = (threadIdx.x & 63) >> 5;
-  if (a.n_split > 1) {
-    const int64_t idx = (int64_t(w.split) * a.n_new + c.u) * a.q_heads + c.hq;
+  if (partial) {
+    const int64_t idx = (int64_t(part) * a.n_new + c.u) * a.q_heads + c.hq;
     float* pp = a.opart + idx * 128;
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
@@ -665,13 +664,20 @@ __device__ __forceinline__ void store_column(const AttnArgs& a, const AttnWork& 
 // ---------------------------------------------------------------------------
 // attention kernel
 // ---------------------------------------------------------------------------
-// One workgroup = 4 waves = 128 query columns of one (request, kv head) and a
-// range of tiles; two workgroups per CU.  Two stages: the next tile streams in
-// while the current one is consumed, one barrier per tile.  The fused variant
+// One workgroup = 8 waves = two work items, one per group of 4 waves, one
+// workgroup per CU.  An item is 128 query columns of one (request, kv head)
+// over a range of tiles.  Each group streams its own tiles through its own
+// two LDS stages (the next tile streams in while the current one is
+// consumed); the groups share the per-tile barrier.  When the two items are
+// the two row splits of one column block, the second group hands its
+// (O, m, sum) to the first through LDS after the last tile, and the first
+// writes the merged result: no partials leave the CU.  The fused variant
 // reads prefix rows straight from the pool: values with direct copies, keys
 // through registers, rotated on the way.
 
 constexpr int kStageBytes = 2 * kTileBytes + 256;
+constexpr int kGroupLdsBytes = 2 * kStageBytes;
+constexpr int kAttnLdsBytes = 2 * kGroupLdsBytes;
 
 // Per-lane byte offsets, inside a 64-row tile of one plane, of the 16-byte
 // granules a lane copies: 4 blocks of 1 KB (4 rows) per wave, the granule
@@ -713,10 +719,11 @@ __device__ __forceinline__ void tile_to_lds(const char* base, int t0, int rows, 
   }
 }
 
-// Row positions of one tile into LDS (wave 0, one 4-byte lane load each).
-__device__ __forceinline__ void pos_to_lds(const int32_t* pos_row0, int t0, int rows, char* lds) {
-  if ((threadIdx.x >> 6) == 0) {
-    const int rr = min(t0 + int(threadIdx.x), rows - 1);
+// Row positions of one tile into LDS (wave 0 of the group, one 4-byte lane
+// load each).
+__device__ __forceinline__ void pos_to_lds(const int32_t* pos_row0, int t0, int rows, char* lds, int wave) {
+  if (wave == 0) {
+    const int rr = min(t0 + int(threadIdx.x & 63), rows - 1);
     __builtin_amdgcn_global_load_lds(pos_row0 + rr, (lds_void_ptr)lds, 4, 0, 0);
   }
 }
@@ -737,8 +744,8 @@ __device__ __forceinline__ const char* fused_row(const AttnArgs& a, const ReqRec
 }
 
 __device__ __forceinline__ void fused_v_to_lds(const AttnArgs& a, const ReqRec& rq, int head, int t0,
-                                               int rows, char* lds) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+                                               int rows, char* lds, int wave) {
+  const int lane = threadIdx.x & 63;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int blk = wave * 4 + i;
@@ -751,7 +758,8 @@ __device__ __forceinline__ void fused_v_to_lds(const AttnArgs& a, const ReqRec& 
 }
 
 // Fused variant: keys through registers (rotated on the way) into the same
-// swizzled layout.  Thread units: rows (tid >> 3) + 32 i, pair vector j = tid & 7.
+// swizzled layout.  Thread units (tid: the thread within its 4-wave group):
+// rows (tid >> 3) + 32 i, pair vector j = tid & 7.
 struct FusedK {
   u32x4 k[2][2];
   int phase[2];   // phase_tab row of each key, -1 for none
@@ -759,7 +767,7 @@ struct FusedK {
 
 __device__ __forceinline__ void fused_k_load(const AttnArgs& a, const ReqRec& rq, int head, int t0,
                                              int rows, FusedK& f) {
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x & 255;
   const int j = tid & 7;
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
@@ -774,7 +782,7 @@ __device__ __forceinline__ void fused_k_load(const AttnArgs& a, const ReqRec& rq
 }
 
 __device__ __forceinline__ void fused_k_store(const AttnArgs& a, FusedK& f, char* lds) {
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x & 255;
   const int j = tid & 7;
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
@@ -792,13 +800,26 @@ __device__ __forceinline__ void fused_k_store(const AttnArgs& a, FusedK& f, char
 }
 
 template <bool FUSED>
-__global__ __launch_bounds__(256, 2) void attention_bf16_kernel(AttnArgs a) {
-  __shared__ __attribute__((aligned(1024))) char smem[2 * kStageBytes];
-  const int bid = xcd_remap(blockIdx.x, gridDim.x);
-  const AttnWork w = a.work[bid];
+__global__ __launch_bounds__(512, 1) void attention_bf16_kernel(AttnArgs a) {
+  extern __shared__ __attribute__((aligned(1024))) char lds_all[];
+  const int pair = xcd_remap(blockIdx.x, gridDim.x);
+  const int wave8 = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int grp = wave8 >> 2;
+  const int wave = wave8 & 3;                 // wave within the group
+  const int item = 2 * pair + grp;
+  const bool has = item < a.n_work;
+  const AttnWork w = a.work[has ? item : 2 * pair];
+  const int T = has ? w.tile_end - w.tile_begin : 0;
+  // both groups pass the same number of barriers
+  const AttnWork w0 = a.work[2 * pair];
+  const int T_other = grp == 0 ? (2 * pair + 1 < a.n_work ? a.work[2 * pair + 1].tile_end -
+                                                                a.work[2 * pair + 1].tile_begin
+                                                          : 0)
+                               : w0.tile_end - w0.tile_begin;
+  const int steps = max(T, T_other);
+  char* smem = lds_all + grp * kGroupLdsBytes;
   const ReqRec rq = a.reqs[w.req];
   const int rows = rq.prefix_rows + rq.n_new;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
   Col c;
   bf16x8 qb[8];
@@ -815,7 +836,7 @@ __global__ __launch_bounds__(256, 2) void attention_bf16_kernel(AttnArgs a) {
   const char* kbase = reinterpret_cast<const char*>(a.k_plane + (int64_t(w.head) * a.cap + rq.row_base) * 128);
   const char* vbase = reinterpret_cast<const char*>(a.v_plane + (int64_t(w.head) * a.cap + rq.row_base) * 128);
   const int32_t* pbase = a.pos + rq.row_base;
-  const int tb = w.tile_begin, te = w.tile_end;
+  const int tb = w.tile_begin;
   FusedK fk;
 
   // copies of tile t into stage S (0 or 1)
@@ -825,27 +846,29 @@ __global__ __launch_bounds__(256, 2) void attention_bf16_kernel(AttnArgs a) {
     const int t0 = t * kAttnRowsPerTile;
     if (FUSED) {
       fused_k_load(a, rq, w.head, t0, rows, fk);
-      fused_v_to_lds(a, rq, w.head, t0, rows, st + kTileBytes);
+      fused_v_to_lds(a, rq, w.head, t0, rows, st + kTileBytes, wave);
     } else {
       tile_to_lds<false>(kbase, t0, rows, tl, st, wave);
       tile_to_lds<true>(vbase, t0, rows, tl, st + kTileBytes, wave);
     }
-    pos_to_lds(pbase, t0, rows, st + kPosOffset);
+    pos_to_lds(pbase, t0, rows, st + kPosOffset, wave);
   };
 
   int2 tp_next = make_int2(INT_MAX, INT_MAX);
-  if (tb < te) {
+  if (T > 0) {
     tp_next = a.tile_pos[rq.tile_base + tb];
     issue(std::integral_constant<int, 0>{}, tb);
     if (FUSED) fused_k_store(a, fk, smem);
   }
-  // one tile in stage S: wait for its copies, start the next tile's copies
-  // into the other stage, then consume it
-  auto step = [&](auto stage_c, int t) {
+  // step i: the group's tile tb + i sits in stage S (i even: 0); wait for its
+  // copies, start the next tile's copies into the other stage, consume it
+  auto step = [&](auto stage_c, int i) {
     constexpr int S = decltype(stage_c)::value;
     wait_vm();
     __syncthreads();
-    const bool more = t + 1 < te;
+    if (i >= T) return;
+    const int t = tb + i;
+    const bool more = i + 1 < T;
     // this tile's bounds were fetched before the next tile's copies were
     // issued, so reading them never waits on those copies
     const int2 tp = tp_next;
@@ -863,11 +886,53 @@ __global__ __launch_bounds__(256, 2) void attention_bf16_kernel(AttnArgs a) {
     }
     if (FUSED && more) fused_k_store(a, fk, smem + (1 - S) * kStageBytes);
   };
-  for (int t = tb; t < te; t += 2) {
-    step(std::integral_constant<int, 0>{}, t);
-    if (t + 1 < te) step(std::integral_constant<int, 1>{}, t + 1);
+  for (int i = 0; i < steps; i += 2) {
+    step(std::integral_constant<int, 0>{}, i);
+    if (i + 1 < steps) step(std::integral_constant<int, 1>{}, i + 1);
   }
-  store_column(a, w, c, o, lacc, m);
+
+  // rows of lacc are identical: each lane already holds its column's full sum
+  float lt = lacc[0];
+  if (w0.merge_pair) {
+    // the second split of the pair hands (O, m, sum) to the first through LDS,
+    // laid out [wave][16-byte chunk][lane] so that both sides are
+    // conflict-free; split order is kept: first + second
+    __syncthreads();
+    const int lane = threadIdx.x & 63;
+    f32x4* xo = reinterpret_cast<f32x4*>(lds_all) + wave * 16 * 64 + lane;
+    float2* xml = reinterpret_cast<float2*>(lds_all + 4 * 16 * 64 * 16) + wave * 64 + lane;
+    if (grp == 1) {
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq)
+          xo[(db * 4 + qq) * 64] = f32x4{o[db][4 * qq], o[db][4 * qq + 1], o[db][4 * qq + 2], o[db][4 * qq + 3]};
+      *xml = make_float2(m, lt);
+    }
+    __syncthreads();
+    if (grp == 1) return;
+    const float2 ml1 = *xml;
+    const bool l0 = lt > 0.0f, l1 = ml1.y > 0.0f;
+    const float mm = l0 ? (l1 ? fmaxf(m, ml1.x) : m) : ml1.x;
+    const float w0f = l0 ? __builtin_amdgcn_exp2f(m - mm) : 0.0f;
+    const float w1f = l1 ? __builtin_amdgcn_exp2f(ml1.x - mm) : 0.0f;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int qq = 0; qq < 4; ++qq) {
+        const f32x4 x = xo[(db * 4 + qq) * 64];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[db][4 * qq + e] = w0f * o[db][4 * qq + e] + w1f * x[e];
+      }
+    lt = w0f * lt + w1f * ml1.y;
+    m = (l0 || l1) ? mm : -INFINITY;
+  } else if (!has) {
+    return;
+  }
+  // merged pairs write partial split/2 (or the output when that was the only
+  // pair); unpaired items write partial `split` (or the output)
+  const int part = w0.merge_pair ? w.split / 2 : w.split;
+  store_column(a, c, o, lt, m, a.n_split_out > 1, part);
 }
 
 // Log-sum-exp merge of the row splits, in split order.  32 threads per
@@ -882,7 +947,7 @@ __global__ __launch_bounds__(256) void merge_kernel(AttnArgs a) {
   f32x4 part[kAttnMaxSplit];
 #pragma unroll
   for (int sp = 0; sp < kAttnMaxSplit; ++sp) {
-    if (sp < a.n_split) {
+    if (sp < a.n_split_out) {
       const int64_t idx = int64_t(sp) * n_items + item;
       ml[sp] = a.ml[idx];
       part[sp] = *reinterpret_cast<const f32x4*>(a.opart + idx * 128 + d0);
@@ -891,12 +956,12 @@ __global__ __launch_bounds__(256) void merge_kernel(AttnArgs a) {
   float mmax = -INFINITY;
 #pragma unroll
   for (int sp = 0; sp < kAttnMaxSplit; ++sp)
-    if (sp < a.n_split && ml[sp].y > 0.0f) mmax = fmaxf(mmax, ml[sp].x);
+    if (sp < a.n_split_out && ml[sp].y > 0.0f) mmax = fmaxf(mmax, ml[sp].x);
   float den = 0.0f;
   f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
   for (int sp = 0; sp < kAttnMaxSplit; ++sp) {
-    if (sp < a.n_split && ml[sp].y > 0.0f) {
+    if (sp < a.n_split_out && ml[sp].y > 0.0f) {
       const float wgt = __builtin_amdgcn_exp2f(ml[sp].x - mmax);
       den += wgt * ml[sp].y;
       acc += wgt * part[sp];
@@ -1038,11 +1103,20 @@ bool attention_supported(int dtype, int head_dim, bool fused) {
 
 hipError_t launch_attention_bf16(const AttnArgs& a, bool fused, hipStream_t s) {
   if (a.n_work <= 0) return hipSuccess;
+  static const hipError_t attr_f = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(attention_bf16_kernel<true>), hipFuncAttributeMaxDynamicSharedMemorySize,
+      kAttnLdsBytes);
+  static const hipError_t attr_m = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(attention_bf16_kernel<false>), hipFuncAttributeMaxDynamicSharedMemorySize,
+      kAttnLdsBytes);
+  if (attr_f != hipSuccess) return attr_f;
+  if (attr_m != hipSuccess) return attr_m;
+  const unsigned pairs = unsigned((a.n_work + 1) / 2);
   if (fused)
-    hipLaunchKernelGGL(attention_bf16_kernel<true>, dim3(unsigned(a.n_work)), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(attention_bf16_kernel<true>, dim3(pairs), dim3(512), kAttnLdsBytes, s, a);
   else
-    hipLaunchKernelGGL(attention_bf16_kernel<false>, dim3(unsigned(a.n_work)), dim3(256), 0, s, a);
-  if (a.n_split > 1) {
+    hipLaunchKernelGGL(attention_bf16_kernel<false>, dim3(pairs), dim3(512), kAttnLdsBytes, s, a);
+  if (a.n_split_out > 1) {
     const int64_t items = int64_t(a.n_new) * a.q_heads;
     hipLaunchKernelGGL(merge_kernel, dim3(unsigned((items + 7) / 8)), dim3(256), 0, s, a);
   }

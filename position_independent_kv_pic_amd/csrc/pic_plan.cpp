@@ -261,13 +261,15 @@ int32_t choose_attention_split(const HostPlan& plan, int32_t kv_heads, int32_t g
     split = std::min(split, max_split);
     split = std::min(split, std::max(1, max_tiles / std::max(1, min_tiles_per_split)));
     split = std::max(split, 1);
+    if (split > 1 && (split & 1)) split = std::min(split + 1, max_split & ~1);
   }
   return split;
 }
 
-void build_attention_work(const HostPlan& plan, int32_t kv_heads, int32_t group, int32_t cols_per_wg,
-                          int32_t rows_per_tile, int32_t split, std::vector<AttnWork>* out) {
+int32_t build_attention_work(const HostPlan& plan, int32_t kv_heads, int32_t group, int32_t cols_per_wg,
+                             int32_t rows_per_tile, int32_t split, std::vector<AttnWork>* out) {
   out->clear();
+  const bool pairs = split > 1 && (split % 2) == 0;
   for (int32_t b = 0; b < int32_t(plan.reqs.size()); ++b) {
     const ReqRec& r = plan.reqs[b];
     int64_t cols = int64_t(r.n_new) * group;
@@ -275,24 +277,23 @@ void build_attention_work(const HostPlan& plan, int32_t kv_heads, int32_t group,
     int32_t tiles = (r.prefix_rows + r.n_new + rows_per_tile - 1) / rows_per_tile;
     int32_t ncb = int32_t((cols + cols_per_wg - 1) / cols_per_wg);
     for (int32_t h = 0; h < kv_heads; ++h) {
-      for (int32_t sp = 0; sp < split; ++sp) {
-        int32_t t0 = int32_t(int64_t(tiles) * sp / split);
-        int32_t t1 = int32_t(int64_t(tiles) * (sp + 1) / split);
-        for (int32_t c = 0; c < ncb; ++c) {
+      for (int32_t c = 0; c < ncb; ++c) {
+        for (int32_t sp = 0; sp < split; ++sp) {
           AttnWork w;
           w.req = b;
           w.head = h;
           w.col_begin = c * cols_per_wg;
-          w.tile_begin = t0;
-          w.tile_end = t1;
+          w.tile_begin = int32_t(int64_t(tiles) * sp / split);
+          w.tile_end = int32_t(int64_t(tiles) * (sp + 1) / split);
           w.split = sp;
-          w.pad0 = 0;
-          w.pad1 = 0;
+          w.merge_pair = pairs && (sp % 2) == 0;
+          w.pad = 0;
           out->push_back(w);
         }
       }
     }
   }
+  return pairs ? split / 2 : split;
 }
 
 }  // namespace pic

@@ -58,9 +58,11 @@ struct ReqRec {
   int32_t tile_base;    // index of the request's first 64-row attention tile
 };
 
-// Attention work item: one workgroup handles query columns
-// [col_begin, col_begin + cols) of request `req` and kv head `head`, over the
-// request's row tiles [tile_begin, tile_end); split `split` of `n_split`.
+// Attention work item: query columns [col_begin, col_begin + cols) of
+// request `req` and kv head `head`, over the request's row tiles
+// [tile_begin, tile_end); split `split` of `n_split`.  Items 2p and 2p + 1
+// share a workgroup; `merge_pair` (set on item 2p) marks them as splits 2j and
+// 2j + 1 of one column block, merged inside the workgroup.
 struct AttnWork {
   int32_t req;
   int32_t head;
@@ -68,7 +70,8 @@ struct AttnWork {
   int32_t tile_begin;
   int32_t tile_end;
   int32_t split;
-  int32_t pad0, pad1;
+  int32_t merge_pair;
+  int32_t pad;
 };
 
 struct HostPlan {
@@ -85,6 +88,7 @@ struct HostPlan {
   // attention work list
   std::vector<AttnWork> work;
   int32_t n_split = 1;
+  int32_t n_split_out = 1;          // partials left after the in-workgroup pair merge
 };
 
 // Validation helpers return PIC_OK or an error code and fill `err`.
@@ -101,9 +105,10 @@ pic_status build_plan(const PoolInfo& pool, int32_t batch, const int32_t* span_p
                       const pic_span* spans, const int32_t* new_ptr, const int32_t* new_pos,
                       int64_t capacity, HostPlan* out, std::string* err);
 
-// Row split for the attention kernels: about `target_wgs` workgroups of
+// Row split for the attention kernel: about `target_wgs` work items of
 // `cols_per_wg` query columns when the batch alone gives fewer (at most
-// `max_split` parts, and never fewer than `min_tiles_per_split` tiles per part).
+// `max_split` parts, never fewer than `min_tiles_per_split` tiles per part,
+// and an even count so that splits pair up inside workgroups).
 int32_t choose_attention_split(const HostPlan& plan, int32_t kv_heads, int32_t group, int32_t cols_per_wg,
                                int32_t rows_per_tile, int32_t target_wgs, int32_t max_split,
                                int32_t min_tiles_per_split);
@@ -111,8 +116,10 @@ int32_t choose_attention_split(const HostPlan& plan, int32_t kv_heads, int32_t g
 // Attention work list: `cols_per_wg` query columns (token-major: column
 // j*G + g is token j, head g of the group) per item, `rows_per_tile` rows per
 // tile, each request's tiles cut into `split` contiguous ranges.  Items are
-// ordered (request, kv head, split, column block).
-void build_attention_work(const HostPlan& plan, int32_t kv_heads, int32_t group, int32_t cols_per_wg,
-                          int32_t rows_per_tile, int32_t split, std::vector<AttnWork>* out);
+// ordered (request, kv head, column block, split), so with an even split the
+// two splits of a pair are adjacent at an even index (merge_pair set).
+// Returns the partials left for merge_kernel (split / 2, or 1).
+int32_t build_attention_work(const HostPlan& plan, int32_t kv_heads, int32_t group, int32_t cols_per_wg,
+                             int32_t rows_per_tile, int32_t split, std::vector<AttnWork>* out);
 
 }  // namespace pic
