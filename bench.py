@@ -48,6 +48,8 @@ def parse():
     ap.add_argument("--layouts", type=int, default=8, help="pre-generated batch layouts to cycle through")
     ap.add_argument("--cpu-seconds", type=float, default=20.0, help="time budget of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--decode-steps", type=int, default=0,
+                    help="also time this many decode steps (every layer, one token per request) after a prefill")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (to scale HBM counters), then exit")
     return ap.parse_args()
@@ -161,6 +163,48 @@ def measured_traffic(workload: str, variant: str) -> dict:
     return out
 
 
+def decode_bench(args, wl, dw, inputs, variant, stream) -> dict:
+    """Decode after a prefill of layout 0: K steps of one token per request over
+    every layer, timed with events on the launch stream.  The rows a step
+    reads (K and V of every earlier row of every request, all layers and kv
+    heads) give the effective HBM rate of this HBM-bound step."""
+    import torch
+    import workloads as W
+    m = wl.model
+    sess = dw.session
+    plan = sess.plan
+    K = args.decode_steps
+    plan.set_decode_rows(K)
+    sess.ensure_capacity(wl.rows_total + K * wl.batch)
+    plan_flag = 1 if variant == 1 else 0
+    plan.assemble(wl.span_ptr(), wl.spans_flat(), wl.new_ptr(), wl.new_pos_flat(), sess.asm_k, sess.asm_v,
+                  sess.capacity, plan_flag, stream)
+    n = wl.n_new_total
+    for l in range(m.layers):
+        q, k, v = inputs[l]
+        plan.query_prefill(l, q[:n], k[:n], v[:n], torch.empty_like(q[:n]), variant, stream)
+    dec_in = [[W.decode_tokens(wl, l, st, dw.kscale, dw.vscale, dw.pool.device) for l in range(m.layers)]
+              for st in range(K)]
+    dout = torch.empty_like(dec_in[0][0][0])
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
+    torch.cuda.synchronize()
+    ev[0].record(stream)
+    for st in range(K):
+        for l in range(m.layers):
+            q, k, v = dec_in[st][l]
+            plan.decode_layer(l, st, q, k, v, dout, variant, stream)
+        ev[st + 1].record(stream)
+    torch.cuda.synchronize()
+    ms = [ev[i].elapsed_time(ev[i + 1]) for i in range(K)]
+    plan.set_decode_rows(0)
+    rows = wl.rows_total
+    bytes_step = (rows + wl.batch * (K + 1) / 2) * 2 * m.layers * m.kv_heads * m.head_dim * m.elem_bytes
+    ms_med = sorted(ms)[len(ms) // 2]
+    return {"steps": K, "ms_per_step_median": round(ms_med, 4), "tokens_per_s": round(wl.batch / (ms_med * 1e-3), 1),
+            "kv_read_GBps": round(bytes_step / (ms_med * 1e-3) / 1e9, 1),
+            "note": "one token per request per step over all layers; kv_read counts each earlier row's K and V once"}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -185,21 +229,22 @@ def main():
     sess = dw.session
     cap = max(w.rows_total for w in wls)
     sess.ensure_capacity(cap)
-    n_new = max(w.n_new_total for w in wls)
-    assert all(w.n_new_total == n_new for w in wls), "layouts must share the new-token count"
-    inputs = [dw.layer_inputs(l) for l in range(m.layers)]
+    # inputs sized for the layout with the most new tokens; each step passes
+    # the leading rows its own layout needs
+    wl_max = max(wls, key=lambda w: w.n_new_total)
+    inputs = [W.new_tokens(wl_max, l, dw.kscale, dw.vscale, dw.pool.device) for l in range(m.layers)]
     outs = [torch.empty_like(inputs[l][0]) for l in range(m.layers)]
-    tables = [(w.span_ptr(), w.spans_flat(), w.new_ptr(), w.new_pos_flat()) for w in wls]
+    tables = [(w.span_ptr(), w.spans_flat(), w.new_ptr(), w.new_pos_flat(), w.n_new_total) for w in wls]
     stream = torch.cuda.current_stream()
     plan = sess.plan
     plan_flag = 1 if variant == VARIANT_FUSED else 0
 
     def step(i):
-        sp, spans, npt, npos = tables[i % len(tables)]
+        sp, spans, npt, npos, n = tables[i % len(tables)]
         plan.assemble(sp, spans, npt, npos, sess.asm_k, sess.asm_v, sess.capacity, plan_flag, stream)
         for l in range(m.layers):
             q, k, v = inputs[l]
-            plan.query_prefill(l, q, k, v, outs[l], variant, stream)
+            plan.query_prefill(l, q[:n], k[:n], v[:n], outs[l][:n], variant, stream)
 
     for i in range(args.warmup):
         step(i)
@@ -303,6 +348,8 @@ def main():
         res["roofline_assembly"]["achieved"] = None
         res["assembly_GBps"] = None
         res["roofline_assembly"]["note"] = "fused variant gathers inside attention; no gather kernel"
+    if args.decode_steps > 0:
+        res["decode"] = decode_bench(args, wl, dw, inputs, variant, stream)
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle sample")
         res["cpu_baseline"] = cpu_baseline(wl, dw.pool, dw, args.cpu_seconds)

@@ -219,6 +219,45 @@ pic_status pic_assemble(pic_plan* plan, int32_t batch, const int32_t* span_ptr,
 pic_status pic_query_prefill(pic_plan* plan, int32_t layer, const void* q, const void* k_new,
                              const void* v_new, void* out, int32_t variant, void* stream);
 
+/*
+ * Decode over the assembled cache (the step after the prefill: ordinary
+ * autoregressive decoding; CoinRAG page section 2.3 after KV_M(q; C_ctx),
+ * SemPIC page's hit path).
+ *
+ * pic_plan_set_decode_rows reserves `rows` assembled rows after each
+ * request's new tokens at the NEXT pic_assemble (0 by default).  The row
+ * layout becomes: request b owns rows [row_base_b, row_base_b + prefix_b +
+ * n_new_b + rows), row_base_b = sum over earlier requests of (prefix + n_new
+ * + rows); asm_rows_capacity must cover the reserve.
+ */
+pic_status pic_plan_set_decode_rows(pic_plan* plan, int32_t rows);
+
+/*
+ * One decode step of one layer: every request of the batch gets one token.
+ *   layer     in [0, layers)
+ *   step      0-based decode index, in [0, reserved rows).  The token of
+ *             request b sits at position last_b + 1 + step (last_b: the
+ *             largest position among the request's spans and new tokens; -1
+ *             if it has none) and at assembled row prefix_b + n_new_b + step.
+ *   q         device [batch][Hq][head_dim], un-rotated
+ *   k_new     device [batch][Hkv][head_dim], un-rotated
+ *   v_new     device [batch][Hkv][head_dim]
+ *   out       device [batch][Hq][head_dim]
+ *   variant   PIC_VARIANT_MATERIALIZED or PIC_VARIANT_FUSED (prefix rows
+ *             straight from the pool; works after a PLAN_ONLY assemble)
+ * Steps: rotate q and k_new to the token's position (fp64, one rounding),
+ * write k' and v_new at the token's row of this layer's planes, then
+ *   out[b][h] = sum_r softmax_r(<q'_b,h, k_r> / sqrt(d)) v_r
+ * over all of request b's rows up to and including the token (every earlier
+ * row has a smaller position).  The rows are split across workgroups
+ * (split-KV) and merged by log-sum-exp.  Requires that this layer was
+ * prefilled (pic_query_prefill) and decoded for steps 0 .. step-1 of the
+ * current batch, in order.  Implemented for bf16 with head_dim 128
+ * (PIC_EUNSUPPORTED otherwise).
+ */
+pic_status pic_decode_layer(pic_plan* plan, int32_t layer, int32_t step, const void* q, const void* k_new,
+                            const void* v_new, void* out, int32_t variant, void* stream);
+
 /* Host-side description of the plan's current batch. */
 typedef struct {
   int32_t batch;

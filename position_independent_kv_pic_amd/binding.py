@@ -33,7 +33,7 @@ EXPORTED = (
     "pic_pool_register", "pic_pool_release", "pic_plan_create", "pic_plan_release",
     "pic_assemble", "pic_query_prefill", "pic_plan_get_summary", "pic_plan_get_requests",
     "pic_plan_get_spans", "pic_plan_get_new_tokens", "pic_timing_enable", "pic_timing_read",
-    "pic_timing_reset", "pic_last_error", "pic_version",
+    "pic_timing_reset", "pic_last_error", "pic_version", "pic_plan_set_decode_rows", "pic_decode_layer",
 )
 
 
@@ -92,6 +92,8 @@ def lib() -> ctypes.CDLL:
         "pic_plan_release": [P],
         "pic_assemble": [P, I32, pi32, ctypes.POINTER(PicSpan), pi32, pi32, P, P, I64, I32, P],
         "pic_query_prefill": [P, I32, P, P, P, P, I32, P],
+        "pic_plan_set_decode_rows": [P, I32],
+        "pic_decode_layer": [P, I32, I32, P, P, P, P, I32, P],
         "pic_plan_get_summary": [P, ctypes.POINTER(PicPlanSummary)],
         "pic_plan_get_requests": [P, pi64, pi32, pi32],
         "pic_plan_get_spans": [P, pi32, pi32, pi64],
@@ -223,6 +225,17 @@ class Plan:
                                        ctypes.c_void_p(_ptr(k_new)), ctypes.c_void_p(_ptr(v_new)),
                                        ctypes.c_void_p(_ptr(out)), int(variant),
                                        ctypes.c_void_p(_stream(stream))))
+
+    def set_decode_rows(self, rows: int):
+        """Rows reserved per request for decode tokens at the next assemble."""
+        _check(lib().pic_plan_set_decode_rows(self.handle, int(rows)))
+
+    def decode_layer(self, layer: int, step: int, q, k_new, v_new, out, variant: int = VARIANT_MATERIALIZED,
+                     stream=None):
+        _check(lib().pic_decode_layer(self.handle, int(layer), int(step), ctypes.c_void_p(_ptr(q)),
+                                      ctypes.c_void_p(_ptr(k_new)), ctypes.c_void_p(_ptr(v_new)),
+                                      ctypes.c_void_p(_ptr(out)), int(variant),
+                                      ctypes.c_void_p(_stream(stream))))
 
     def summary(self) -> dict:
         s = PicPlanSummary()

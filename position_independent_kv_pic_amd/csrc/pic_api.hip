@@ -74,6 +74,15 @@ struct pic_plan {
   hipEvent_t staging_ev = nullptr;
   bool staging_pending = false;
 
+  // decode: rows reserved per request at the next assemble, and the tables of
+  // the current decode step (uploaded blob followed by generated tables)
+  int32_t decode_rows_next = 0;
+  pic::DecodePlan dec;
+  char* dws = nullptr;
+  size_t dws_cap = 0;
+  size_t d_pos = 0, d_row = 0, d_reqs = 0, d_work = 0, d_blob = 0, d_phase = 0, d_qrot = 0, d_opart = 0,
+         d_ml = 0, d_bytes = 0;
+
   // optional kernel timing
   bool timing = false;
   std::vector<std::pair<hipEvent_t, hipEvent_t>> events[kTimedKernels];
@@ -157,6 +166,8 @@ void layout_workspace(pic_plan* p) {
   p->ws_bytes = o;
 }
 
+pic_status ensure_staging(pic_plan* p, size_t bytes);
+
 pic_status ensure_capacity(pic_plan* p) {
   if (p->ws_bytes > p->ws_cap) {
     if (p->ws) {
@@ -175,7 +186,11 @@ pic_status ensure_capacity(pic_plan* p) {
     }
     p->ws_cap = want;
   }
-  if (p->blob_bytes > p->staging_cap) {
+  return ensure_staging(p, p->blob_bytes);
+}
+
+pic_status ensure_staging(pic_plan* p, size_t bytes) {
+  if (bytes > p->staging_cap) {
     if (p->staging_pending) {
       hipError_t e = hipEventSynchronize(p->staging_ev);
       if (e != hipSuccess) return device_error(p, e, "wait for the previous plan upload");
@@ -184,7 +199,7 @@ pic_status ensure_capacity(pic_plan* p) {
     if (p->staging) (void)hipHostFree(p->staging);
     p->staging = nullptr;
     p->staging_cap = 0;
-    size_t want = align256(p->blob_bytes + p->blob_bytes / 4);
+    size_t want = align256(bytes + bytes / 4);
     hipError_t e = hipHostMalloc(reinterpret_cast<void**>(&p->staging), want, hipHostMallocDefault);
     if (e != hipSuccess) {
       p->staging = nullptr;
@@ -273,6 +288,7 @@ pic_status pic_plan_release(pic_plan* p) {
   if (!p) return set_err(PIC_EINVAL, "plan is NULL");
   if (p->ws || p->staging || p->staging_ev) (void)hipDeviceSynchronize();
   if (p->ws) (void)hipFree(p->ws);
+  if (p->dws) (void)hipFree(p->dws);
   if (p->staging) (void)hipHostFree(p->staging);
   if (p->staging_ev) (void)hipEventDestroy(p->staging_ev);
   for (auto& v : p->events)
@@ -304,7 +320,7 @@ pic_status pic_assemble(pic_plan* p, int32_t batch, const int32_t* span_ptr, con
   pic::HostPlan hp;
   std::string err;
   pic_status st = pic::build_plan(pi, batch, span_ptr, spans, new_ptr, new_pos, asm_rows_capacity,
-                                  &hp, &err);
+                                  p->decode_rows_next, &hp, &err);
   if (st != PIC_OK) return set_err(st, "%s", err.c_str());
   if (pi.m.dtype == PIC_BF16 && pi.m.head_dim == 128) {
     hp.n_split = pic::choose_attention_split(hp, pi.m.kv_heads, pi.m.group, pic::kAttnColsPerWG,
@@ -313,6 +329,7 @@ pic_status pic_assemble(pic_plan* p, int32_t batch, const int32_t* span_ptr, con
     hp.n_split_out = pic::build_attention_work(hp, pi.m.kv_heads, pi.m.group, pic::kAttnColsPerWG,
                                                pic::kAttnRowsPerTile, hp.n_split, &hp.work);
   }
+  p->dec.step = -1;  // decode tables describe the previous batch
   if (dry) {
     p->hp = std::move(hp);
     p->has_batch = true;
@@ -489,6 +506,8 @@ pic_status pic_query_prefill(pic_plan* p, int32_t layer, const void* q, const vo
       aa.group = m.group;
       aa.n_new = int32_t(h.new_rows);
       aa.n_split_out = h.n_split_out;
+      aa.paired = h.n_split_out < h.n_split;
+      aa.decode = 0;
       aa.scale_log2 = float(1.4426950408889634 / std::sqrt(double(m.head_dim)));
       aa.out = static_cast<uint16_t*>(out);
       aa.opart = reinterpret_cast<float*>(p->ws + p->off_opart);
@@ -520,6 +539,167 @@ pic_status pic_query_prefill(pic_plan* p, int32_t layer, const void* q, const vo
       e = pic::launch_attention_f32(m.head_dim, aa, s);
     }
     if (e != hipSuccess) return device_error(p, e, "attention kernel");
+  }
+  return ok();
+}
+
+pic_status pic_plan_set_decode_rows(pic_plan* p, int32_t rows) {
+  if (!p) return set_err(PIC_EINVAL, "plan is NULL");
+  if (rows < 0) return set_err(PIC_EINVAL, "decode rows must be >= 0");
+  p->decode_rows_next = rows;
+  return ok();
+}
+
+pic_status pic_decode_layer(pic_plan* p, int32_t layer, int32_t step, const void* q, const void* k_new,
+                            const void* v_new, void* out, int32_t variant, void* stream) {
+  if (!p) return set_err(PIC_EINVAL, "plan is NULL");
+  if (p->failed) return set_err(PIC_ESTATE, "plan is unusable after a device error");
+  if (!p->has_batch || !p->asm_k) return set_err(PIC_ESTATE, "no assembled batch");
+  const pic::HostPlan& h = p->hp;
+  const pic::PoolInfo& pi = p->pool->info;
+  const pic::ModelInfo& m = pi.m;
+  if (layer < 0 || layer >= m.layers) return set_err(PIC_ERANGE, "layer %d outside [0, %d)", layer, m.layers);
+  if (step < 0 || step >= h.decode_rows)
+    return set_err(PIC_ERANGE, "decode step %d outside the %d reserved rows", step, h.decode_rows);
+  if (variant != PIC_VARIANT_MATERIALIZED && variant != PIC_VARIANT_FUSED)
+    return set_err(PIC_EINVAL, "unknown variant %d", variant);
+  const bool fused = variant == PIC_VARIANT_FUSED;
+  if (!fused && !p->materialized) return set_err(PIC_ESTATE, "variant M needs a full assemble");
+  if (m.dtype != PIC_BF16 || m.head_dim != 128)
+    return set_err(PIC_EUNSUPPORTED, "decode is implemented for bf16 with head_dim 128");
+  if (h.batch == 0) return ok();
+  if (!q || !k_new || !v_new || !out) return set_err(PIC_EINVAL, "q, k_new, v_new and out are required");
+  if (!aligned16(q) || !aligned16(k_new) || !aligned16(v_new) || !aligned16(out))
+    return set_err(PIC_EALIGN, "q, k_new, v_new and out must be 16-byte aligned");
+  pic_status st = check_device(p);
+  if (st != PIC_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+
+  if (p->dec.step != step) {
+    pic::build_decode(h, m.kv_heads, step, pic::kAttnRowsPerTile, pic::kAttnTargetWGs, pic::kAttnMaxSplit,
+                      /*min_tiles_per_split=*/2, &p->dec);
+    const pic::DecodePlan& d = p->dec;
+    size_t o = 0;
+    auto take = [&o](size_t bytes) {
+      size_t at = o;
+      o = align256(o + bytes);
+      return at;
+    };
+    const size_t nb = size_t(h.batch);
+    p->d_pos = take(nb * sizeof(int32_t));
+    p->d_row = take(nb * sizeof(int32_t));
+    p->d_reqs = take(nb * sizeof(pic::ReqRec));
+    p->d_work = take(d.work.size() * sizeof(pic::AttnWork));
+    p->d_blob = o;
+    p->d_phase = take(nb * (m.head_dim / 2) * sizeof(pic::Phase));
+    p->d_qrot = take(nb * m.q_heads * m.row_bytes);
+    const size_t np = d.n_split_out > 1 ? size_t(d.n_split_out) : 0;
+    p->d_opart = take(np * nb * m.q_heads * m.head_dim * sizeof(float));
+    p->d_ml = take(np * nb * m.q_heads * sizeof(float2));
+    p->d_bytes = o;
+    if (p->d_bytes > p->dws_cap) {
+      if (p->dws) {
+        hipError_t e = hipDeviceSynchronize();
+        if (e != hipSuccess) return device_error(p, e, "synchronise before growing the decode tables");
+        (void)hipFree(p->dws);
+        p->dws = nullptr;
+        p->dws_cap = 0;
+      }
+      hipError_t e = hipMalloc(reinterpret_cast<void**>(&p->dws), p->d_bytes);
+      if (e != hipSuccess) {
+        p->dws = nullptr;
+        p->dec.step = -1;
+        return set_err(PIC_ENOMEM, "hipMalloc of %zu decode bytes failed: %s", p->d_bytes, hipGetErrorString(e));
+      }
+      p->dws_cap = p->d_bytes;
+    }
+    if (p->staging_pending) {
+      hipError_t e = hipEventSynchronize(p->staging_ev);
+      if (e != hipSuccess) return device_error(p, e, "wait for the previous upload");
+      p->staging_pending = false;
+    }
+    st = ensure_staging(p, p->d_blob);
+    if (st != PIC_OK) {
+      p->dec.step = -1;
+      return st;
+    }
+    put(p->staging, p->d_pos, d.pos);
+    put(p->staging, p->d_row, d.row);
+    put(p->staging, p->d_reqs, d.reqs);
+    put(p->staging, p->d_work, d.work);
+    hipError_t e = hipMemcpyAsync(p->dws, p->staging, p->d_blob, hipMemcpyHostToDevice, s);
+    if (e != hipSuccess) return device_error(p, e, "decode table upload");
+    e = hipEventRecord(p->staging_ev, s);
+    if (e != hipSuccess) return device_error(p, e, "record the upload event");
+    p->staging_pending = true;
+    pic::DecodePlanArgs da;
+    da.dec_pos = reinterpret_cast<const int32_t*>(p->dws + p->d_pos);
+    da.dec_row = reinterpret_cast<const int32_t*>(p->dws + p->d_row);
+    da.omega = reinterpret_cast<const double*>(p->ws + p->off_omega);
+    da.batch = h.batch;
+    da.half_dim = m.head_dim / 2;
+    da.phase = reinterpret_cast<pic::Phase*>(p->dws + p->d_phase);
+    da.pos = reinterpret_cast<int32_t*>(p->ws + p->off_pos);
+    e = pic::launch_decode_plan(da, s);
+    if (e != hipSuccess) return device_error(p, e, "decode plan kernel");
+  }
+  const pic::DecodePlan& d = p->dec;
+  const int64_t plane_bytes = p->cap * m.row_bytes;
+  char* kpl = p->asm_k + int64_t(layer) * m.kv_heads * plane_bytes;
+  char* vpl = p->asm_v + int64_t(layer) * m.kv_heads * plane_bytes;
+  {
+    Timed tm(p, 1, s);
+    pic::PrologueArgs pa;
+    pa.q = static_cast<const char*>(q);
+    pa.k_new = static_cast<const char*>(k_new);
+    pa.v_new = static_cast<const char*>(v_new);
+    pa.new_pos = reinterpret_cast<const int32_t*>(p->dws + p->d_pos);
+    pa.new_row = reinterpret_cast<const int32_t*>(p->dws + p->d_row);
+    pa.phase_new = reinterpret_cast<const pic::Phase*>(p->dws + p->d_phase);
+    pa.q_rot = p->dws + p->d_qrot;
+    pa.asm_k = kpl;
+    pa.asm_v = vpl;
+    pa.cap = p->cap;
+    pa.n_new = h.batch;
+    pa.q_heads = m.q_heads;
+    pa.kv_heads = m.kv_heads;
+    hipError_t e = pic::launch_prologue(m.dtype, m.head_dim, pa, s);
+    if (e != hipSuccess) return device_error(p, e, "decode prologue kernel");
+  }
+  {
+    Timed tm(p, 2, s);
+    pic::AttnArgs aa;
+    aa.q_rot = reinterpret_cast<const uint16_t*>(p->dws + p->d_qrot);
+    aa.k_plane = reinterpret_cast<const uint16_t*>(kpl);
+    aa.v_plane = reinterpret_cast<const uint16_t*>(vpl);
+    aa.cap = p->cap;
+    aa.pos = reinterpret_cast<const int32_t*>(p->ws + p->off_pos);
+    aa.tile_pos = nullptr;
+    aa.reqs = reinterpret_cast<const pic::ReqRec*>(p->dws + p->d_reqs);
+    aa.new_pos = reinterpret_cast<const int32_t*>(p->dws + p->d_pos);
+    aa.work = reinterpret_cast<const pic::AttnWork*>(p->dws + p->d_work);
+    aa.n_work = int32_t(d.work.size());
+    aa.q_heads = m.q_heads;
+    aa.group = m.group;
+    aa.n_new = h.batch;
+    aa.n_split_out = d.n_split_out;
+    aa.paired = d.n_split_out < d.n_split;
+    aa.decode = 1;
+    aa.scale_log2 = float(1.4426950408889634 / std::sqrt(double(m.head_dim)));
+    aa.out = static_cast<uint16_t*>(out);
+    aa.opart = reinterpret_cast<float*>(p->dws + p->d_opart);
+    aa.ml = reinterpret_cast<float2*>(p->dws + p->d_ml);
+    aa.pool = static_cast<const char*>(pi.base);
+    aa.rowsrc = reinterpret_cast<const int2*>(p->ws + p->off_rowsrc);
+    aa.phase_tab = reinterpret_cast<const pic::Phase*>(p->ws + p->off_phase_tab);
+    aa.page_bytes = pi.page_bytes;
+    aa.kv_plane_off = int64_t(layer) * 2 * m.kv_heads * pi.page_tokens * m.row_bytes;
+    aa.v_off = int64_t(m.kv_heads) * pi.page_tokens * m.row_bytes;
+    aa.page_shift = pi.page_shift;
+    aa.page_tokens = pi.page_tokens;
+    aa.kv_heads = m.kv_heads;
+    hipError_t e = pic::launch_attention_bf16(aa, fused, s);
+    if (e != hipSuccess) return device_error(p, e, "decode attention kernel");
   }
   return ok();
 }

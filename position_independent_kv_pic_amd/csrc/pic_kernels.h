@@ -71,6 +71,9 @@ struct AttnArgs {
   const AttnWork* work;
   int32_t n_work, q_heads, group, n_new;
   int32_t n_split_out;      // partials written for merge_kernel (1: outputs written directly)
+  int32_t paired;           // work items 2p, 2p + 1 are the row splits of one column block
+  int32_t decode;           // one query per request (new_begin = its index), every row visible:
+                            // tile bounds are not read, rows past the end are masked
   float scale_log2;         // log2(e) / sqrt(head_dim)
   uint16_t* out;            // n_split == 1
   float* opart;             // [n_split_out][n_new][Hq][128]
@@ -103,7 +106,19 @@ constexpr int kAttnColsPerWG = 128;   // work item: 4 waves x 32 query columns
 constexpr int kAttnTargetWGs = 512;   // work items: two per CU (one workgroup of two items)
 constexpr int kAttnMaxSplit = 16;     // merge_kernel handles at most this many row splits
 
+// Decode step tables: per request, the phases of its decode position and the
+// position of its decode row.
+struct DecodePlanArgs {
+  const int32_t* dec_pos;   // [batch]
+  const int32_t* dec_row;   // [batch]
+  const double* omega;      // [half_dim]
+  int32_t batch, half_dim;
+  Phase* phase;             // [batch][half_dim]
+  int32_t* pos;             // assembled row positions
+};
+
 hipError_t launch_plan(const PlanArgs& a, hipStream_t s);
+hipError_t launch_decode_plan(const DecodePlanArgs& a, hipStream_t s);
 hipError_t launch_gather(int dtype, int head_dim, const GatherArgs& a, hipStream_t s);
 hipError_t launch_prologue(int dtype, int head_dim, const PrologueArgs& a, hipStream_t s);
 hipError_t launch_attention_bf16(const AttnArgs& a, bool fused, hipStream_t s);

@@ -190,6 +190,15 @@ __global__ __launch_bounds__(256) void plan_phase_kernel(PlanArgs a) {
   *dst = make_double2(cos(ang), sin(ang));
 }
 
+__global__ __launch_bounds__(256) void decode_plan_kernel(DecodePlanArgs a) {
+  const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i >= int64_t(a.batch) * a.half_dim) return;
+  const int b = int(i / a.half_dim), k = int(i % a.half_dim);
+  const double ang = double(a.dec_pos[b]) * a.omega[k];
+  a.phase[i] = make_double2(cos(ang), sin(ang));
+  if (k == 0) a.pos[a.dec_row[b]] = a.dec_pos[b];
+}
+
 // One thread per 64-row tile: the smallest and largest row position, with the
 // largest replaced by INT_MAX when the tile runs past the request's rows.
 __global__ __launch_bounds__(256) void plan_tiles_kernel(PlanArgs a) {
@@ -490,7 +499,7 @@ __device__ __forceinline__ void col_setup(const AttnArgs& a, const AttnWork& w, 
                                           int wave, unsigned lds, Col& c, bf16x8 qb[8]) {
   const int lane = threadIdx.x & 63;
   const int g2 = lane >> 5, lq = lane & 31;
-  const int ncols = rq.n_new * a.group;
+  const int ncols = (a.decode ? 1 : rq.n_new) * a.group;
   const int col = w.col_begin + wave * 32 + lq;
   c.ok = col < ncols;
   const int colc = c.ok ? col : ncols - 1;
@@ -664,14 +673,15 @@ __device__ __forceinline__ void store_column(const AttnArgs& a, const Col& c, co
 // ---------------------------------------------------------------------------
 // attention kernel
 // ---------------------------------------------------------------------------
-// One workgroup = 8 waves = two work items, one per group of 4 waves, one
-// workgroup per CU.  An item is 128 query columns of one (request, kv head)
-// over a range of tiles.  Each group streams its own tiles through its own
-// two LDS stages (the next tile streams in while the current one is
-// consumed); the groups share the per-tile barrier.  When the two items are
-// the two row splits of one column block, the second group hands its
-// (O, m, sum) to the first through LDS after the last tile, and the first
-// writes the merged result: no partials leave the CU.  The fused variant
+// A work item is 128 query columns of one (request, kv head) over a range of
+// tiles, run by a group of 4 waves that streams its tiles through its own two
+// LDS stages (the next tile streams in while the current one is consumed),
+// one barrier per tile.  Unpaired: one item per workgroup, two workgroups per
+// CU, independent of each other.  Paired (row splits): one workgroup of 8
+// waves per CU runs the two splits of one column block; they share the
+// per-tile barrier, and after the last tile the second group hands its
+// (O, m, sum) to the first through LDS, which writes the merged result, so
+// no partials leave the CU.  The fused variant
 // reads prefix rows straight from the pool: values with direct copies, keys
 // through registers, rotated on the way.
 
@@ -799,24 +809,26 @@ __device__ __forceinline__ void fused_k_store(const AttnArgs& a, FusedK& f, char
   }
 }
 
-template <bool FUSED>
-__global__ __launch_bounds__(512, 1) void attention_bf16_kernel(AttnArgs a) {
+template <bool FUSED, bool PAIRED>
+__global__ __launch_bounds__(PAIRED ? 512 : 256, PAIRED ? 1 : 2) void attention_bf16_kernel(AttnArgs a) {
   extern __shared__ __attribute__((aligned(1024))) char lds_all[];
-  const int pair = xcd_remap(blockIdx.x, gridDim.x);
+  constexpr int G = PAIRED ? 2 : 1;           // work items per workgroup
+  const int blk = xcd_remap(blockIdx.x, gridDim.x);
   const int wave8 = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int grp = wave8 >> 2;
+  const int grp = PAIRED ? wave8 >> 2 : 0;
   const int wave = wave8 & 3;                 // wave within the group
-  const int item = 2 * pair + grp;
+  const int item = G * blk + grp;
   const bool has = item < a.n_work;
-  const AttnWork w = a.work[has ? item : 2 * pair];
+  const AttnWork w = a.work[has ? item : G * blk];
   const int T = has ? w.tile_end - w.tile_begin : 0;
-  // both groups pass the same number of barriers
-  const AttnWork w0 = a.work[2 * pair];
-  const int T_other = grp == 0 ? (2 * pair + 1 < a.n_work ? a.work[2 * pair + 1].tile_end -
-                                                                a.work[2 * pair + 1].tile_begin
-                                                          : 0)
-                               : w0.tile_end - w0.tile_begin;
-  const int steps = max(T, T_other);
+  // both groups of a pair pass the same number of barriers
+  const AttnWork w0 = a.work[G * blk];
+  int steps = T;
+  if (PAIRED) {
+    const int T_other = grp == 0 ? (item + 1 < a.n_work ? a.work[item + 1].tile_end - a.work[item + 1].tile_begin : 0)
+                                 : w0.tile_end - w0.tile_begin;
+    steps = max(T, T_other);
+  }
   char* smem = lds_all + grp * kGroupLdsBytes;
   const ReqRec rq = a.reqs[w.req];
   const int rows = rq.prefix_rows + rq.n_new;
@@ -854,9 +866,15 @@ __global__ __launch_bounds__(512, 1) void attention_bf16_kernel(AttnArgs a) {
     pos_to_lds(pbase, t0, rows, st + kPosOffset, wave);
   };
 
+  // position bounds of tile t; in decode mode every row is visible and only
+  // the last tile (rows past the end) needs the mask
+  auto bounds = [&](int t) {
+    if (a.decode) return make_int2(INT_MIN, (t + 1) * kAttnRowsPerTile > rows ? INT_MAX : INT_MIN);
+    return a.tile_pos[rq.tile_base + t];
+  };
   int2 tp_next = make_int2(INT_MAX, INT_MAX);
   if (T > 0) {
-    tp_next = a.tile_pos[rq.tile_base + tb];
+    tp_next = bounds(tb);
     issue(std::integral_constant<int, 0>{}, tb);
     if (FUSED) fused_k_store(a, fk, smem);
   }
@@ -873,7 +891,7 @@ __global__ __launch_bounds__(512, 1) void attention_bf16_kernel(AttnArgs a) {
     // issued, so reading them never waits on those copies
     const int2 tp = tp_next;
     if (more) {
-      tp_next = a.tile_pos[rq.tile_base + t + 1];
+      tp_next = bounds(t + 1);
       issue(std::integral_constant<int, 1 - S>{}, t + 1);
     }
     if (tp.x <= c.wq_max) {
@@ -893,7 +911,7 @@ __global__ __launch_bounds__(512, 1) void attention_bf16_kernel(AttnArgs a) {
 
   // rows of lacc are identical: each lane already holds its column's full sum
   float lt = lacc[0];
-  if (w0.merge_pair) {
+  if (PAIRED && w0.merge_pair) {
     // the second split of the pair hands (O, m, sum) to the first through LDS,
     // laid out [wave][16-byte chunk][lane] so that both sides are
     // conflict-free; split order is kept: first + second
@@ -931,7 +949,7 @@ __global__ __launch_bounds__(512, 1) void attention_bf16_kernel(AttnArgs a) {
   }
   // merged pairs write partial split/2 (or the output when that was the only
   // pair); unpaired items write partial `split` (or the output)
-  const int part = w0.merge_pair ? w.split / 2 : w.split;
+  const int part = PAIRED && w0.merge_pair ? w.split / 2 : w.split;
   store_column(a, c, o, lt, m, a.n_split_out > 1, part);
 }
 
@@ -1030,6 +1048,12 @@ __global__ __launch_bounds__(256) void attention_f32_kernel(AttnF32Args a) {
 // launchers
 // ---------------------------------------------------------------------------
 
+hipError_t launch_decode_plan(const DecodePlanArgs& a, hipStream_t s) {
+  const int64_t n = int64_t(a.batch) * a.half_dim;
+  if (n > 0) hipLaunchKernelGGL(decode_plan_kernel, dim3(unsigned((n + 255) / 256)), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_plan(const PlanArgs& a, hipStream_t s) {
   const int64_t n1 = a.prefix_rows + a.n_new;
   if (n1 > 0) {
@@ -1103,19 +1127,34 @@ bool attention_supported(int dtype, int head_dim, bool fused) {
 
 hipError_t launch_attention_bf16(const AttnArgs& a, bool fused, hipStream_t s) {
   if (a.n_work <= 0) return hipSuccess;
-  static const hipError_t attr_f = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(attention_bf16_kernel<true>), hipFuncAttributeMaxDynamicSharedMemorySize,
-      kAttnLdsBytes);
-  static const hipError_t attr_m = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(attention_bf16_kernel<false>), hipFuncAttributeMaxDynamicSharedMemorySize,
-      kAttnLdsBytes);
-  if (attr_f != hipSuccess) return attr_f;
-  if (attr_m != hipSuccess) return attr_m;
-  const unsigned pairs = unsigned((a.n_work + 1) / 2);
-  if (fused)
-    hipLaunchKernelGGL(attention_bf16_kernel<true>, dim3(pairs), dim3(512), kAttnLdsBytes, s, a);
-  else
-    hipLaunchKernelGGL(attention_bf16_kernel<false>, dim3(pairs), dim3(512), kAttnLdsBytes, s, a);
+  // dynamic LDS above 64 KB has to be allowed per kernel, once
+  static const hipError_t attr = [] {
+    const void* fns[4] = {reinterpret_cast<const void*>(attention_bf16_kernel<true, true>),
+                          reinterpret_cast<const void*>(attention_bf16_kernel<false, true>),
+                          reinterpret_cast<const void*>(attention_bf16_kernel<true, false>),
+                          reinterpret_cast<const void*>(attention_bf16_kernel<false, false>)};
+    const int bytes[4] = {kAttnLdsBytes, kAttnLdsBytes, kGroupLdsBytes, kGroupLdsBytes};
+    for (int i = 0; i < 4; ++i) {
+      hipError_t e = hipFuncSetAttribute(fns[i], hipFuncAttributeMaxDynamicSharedMemorySize, bytes[i]);
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+  }();
+  if (attr != hipSuccess) return attr;
+  if (a.paired) {
+    const unsigned pairs = unsigned((a.n_work + 1) / 2);
+    if (fused)
+      hipLaunchKernelGGL((attention_bf16_kernel<true, true>), dim3(pairs), dim3(512), kAttnLdsBytes, s, a);
+    else
+      hipLaunchKernelGGL((attention_bf16_kernel<false, true>), dim3(pairs), dim3(512), kAttnLdsBytes, s, a);
+  } else {
+    if (fused)
+      hipLaunchKernelGGL((attention_bf16_kernel<true, false>), dim3(unsigned(a.n_work)), dim3(256), kGroupLdsBytes,
+                         s, a);
+    else
+      hipLaunchKernelGGL((attention_bf16_kernel<false, false>), dim3(unsigned(a.n_work)), dim3(256), kGroupLdsBytes,
+                         s, a);
+  }
   if (a.n_split_out > 1) {
     const int64_t items = int64_t(a.n_new) * a.q_heads;
     hipLaunchKernelGGL(merge_kernel, dim3(unsigned((items + 7) / 8)), dim3(256), 0, s, a);

@@ -125,7 +125,8 @@ pic_status build_pool(const pic_model* model, void* pool, int64_t pool_bytes, in
 
 pic_status build_plan(const PoolInfo& pool, int32_t batch, const int32_t* span_ptr,
                       const pic_span* spans, const int32_t* new_ptr, const int32_t* new_pos,
-                      int64_t capacity, HostPlan* out, std::string* err) {
+                      int64_t capacity, int32_t decode_rows, HostPlan* out, std::string* err) {
+  if (decode_rows < 0) return fail(err, PIC_EINVAL, "decode_rows must be >= 0");
   if (batch < 0) return fail(err, PIC_EINVAL, "batch must be >= 0");
   if (batch > 0 && (!span_ptr || !new_ptr))
     return fail(err, PIC_EINVAL, "span_ptr and new_ptr are required");
@@ -148,6 +149,8 @@ pic_status build_plan(const PoolInfo& pool, int32_t batch, const int32_t* span_p
   p.new_pos.resize(size_t(p.new_rows));
   p.new_row.resize(size_t(p.new_rows));
   p.new_req.resize(size_t(p.new_rows));
+  p.req_last_pos.assign(size_t(batch), -1);
+  p.decode_rows = decode_rows;
 
   int64_t row = 0, crow = 0, tiles = 0;
   int32_t max_pos = 0;
@@ -161,6 +164,7 @@ pic_status build_plan(const PoolInfo& pool, int32_t batch, const int32_t* span_p
     r.n_new = new_ptr[b + 1] - new_ptr[b];
     int64_t next = 0;      // AUTO continuation position
     int64_t furthest = 0;  // largest span end (target + n)
+    int64_t max_req_span_pos = -1;
     int64_t prefix = 0;
     for (int32_t i = span_ptr[b]; i < span_ptr[b + 1]; ++i) {
       const pic_span& sp = spans[i];
@@ -195,6 +199,7 @@ pic_status build_plan(const PoolInfo& pool, int32_t batch, const int32_t* span_p
       p.crow[i] = int32_t(crow);
       max_pos = std::max<int64_t>(max_pos, target + n - 1);
       max_prefix_pos = std::max<int64_t>(max_prefix_pos, target + n - 1);
+      max_req_span_pos = std::max<int64_t>(max_req_span_pos, target + n - 1);
       furthest = std::max<int64_t>(furthest, target + n);
       next = target + n;
       prefix += n;
@@ -226,7 +231,13 @@ pic_status build_plan(const PoolInfo& pool, int32_t batch, const int32_t* span_p
     r.first_new_pos = r.n_new > 0 ? p.new_pos[r.new_begin] : 0;
     r.tile_base = int32_t(tiles);
     tiles += (prefix + r.n_new + kTileRows - 1) / kTileRows;
-    row += prefix + r.n_new;
+    row += prefix + r.n_new + decode_rows;
+    int64_t last = prefix > 0 ? max_req_span_pos : -1;
+    if (r.n_new > 0) last = std::max<int64_t>(last, p.new_pos[r.new_begin + r.n_new - 1]);
+    if (last + int64_t(decode_rows) > kMaxPosition)
+      return fail(err, PIC_ERANGE, "request %d: decode positions would exceed %lld", b,
+                  (long long)kMaxPosition);
+    p.req_last_pos[b] = int32_t(last);
     if (row > INT32_MAX) return fail(err, PIC_ERANGE, "batch has more than 2^31 rows");
   }
   p.crow[p.n_spans] = int32_t(crow);
@@ -294,6 +305,59 @@ int32_t build_attention_work(const HostPlan& plan, int32_t kv_heads, int32_t gro
     }
   }
   return pairs ? split / 2 : split;
+}
+
+void build_decode(const HostPlan& plan, int32_t kv_heads, int32_t step, int32_t rows_per_tile,
+                  int32_t target_items, int32_t max_split, int32_t min_tiles_per_split, DecodePlan* out) {
+  const int32_t batch = plan.batch;
+  out->step = step;
+  out->pos.assign(size_t(batch), 0);
+  out->row.assign(size_t(batch), 0);
+  out->reqs.assign(size_t(batch), ReqRec{});
+  int32_t max_tiles = 0;
+  for (int32_t b = 0; b < batch; ++b) {
+    const ReqRec& r = plan.reqs[b];
+    ReqRec& d = out->reqs[b];
+    d = r;
+    d.n_new = r.n_new + step + 1;   // plane rows after the pool rows, this token last
+    d.new_begin = b;                // query b of the decode batch
+    d.tile_base = 0;
+    out->pos[b] = plan.req_last_pos[b] + 1 + step;
+    out->row[b] = r.row_base + r.prefix_rows + r.n_new + step;
+    d.first_new_pos = out->pos[b];
+    max_tiles = std::max(max_tiles, (d.prefix_rows + d.n_new + rows_per_tile - 1) / rows_per_tile);
+  }
+  const int64_t base = int64_t(batch) * kv_heads;
+  int32_t split = 1;
+  if (base > 0 && base < target_items) {
+    split = int32_t((target_items + base - 1) / base);
+    split = std::min(split, max_split);
+    split = std::min(split, std::max(1, max_tiles / std::max(1, min_tiles_per_split)));
+    split = std::max(split, 1);
+    if (split > 1 && (split & 1)) split = std::min(split + 1, max_split & ~1);
+  }
+  const bool pairs = split > 1 && (split % 2) == 0;
+  out->n_split = split;
+  out->n_split_out = pairs ? split / 2 : split;
+  out->work.clear();
+  for (int32_t b = 0; b < batch; ++b) {
+    const ReqRec& d = out->reqs[b];
+    const int32_t tiles = (d.prefix_rows + d.n_new + rows_per_tile - 1) / rows_per_tile;
+    for (int32_t h = 0; h < kv_heads; ++h) {
+      for (int32_t sp = 0; sp < split; ++sp) {
+        AttnWork w;
+        w.req = b;
+        w.head = h;
+        w.col_begin = 0;
+        w.tile_begin = int32_t(int64_t(tiles) * sp / split);
+        w.tile_end = int32_t(int64_t(tiles) * (sp + 1) / split);
+        w.split = sp;
+        w.merge_pair = pairs && (sp % 2) == 0;
+        w.pad = 0;
+        out->work.push_back(w);
+      }
+    }
+  }
 }
 
 }  // namespace pic

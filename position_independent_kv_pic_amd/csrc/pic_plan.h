@@ -85,6 +85,8 @@ struct HostPlan {
   std::vector<int32_t> new_pos;     // per new token
   std::vector<int32_t> new_row;     // assembled row of each new token
   std::vector<int32_t> new_req;     // request of each new token
+  std::vector<int32_t> req_last_pos;  // per request: largest position of its rows (-1: none)
+  int32_t decode_rows = 0;          // rows reserved after each request's new tokens
   // attention work list
   std::vector<AttnWork> work;
   int32_t n_split = 1;
@@ -100,10 +102,30 @@ pic_status build_pool(const pic_model* model, void* pool, int64_t pool_bytes, in
                       const int32_t* page_ids, PoolInfo* out, std::string* err);
 
 // Validate a batch and compute its plan.  `capacity` is the rows available in
-// each assembled plane (ignored when < 0).
+// each assembled plane (ignored when < 0); `decode_rows` rows are left free
+// after each request's new tokens for decode tokens.
 pic_status build_plan(const PoolInfo& pool, int32_t batch, const int32_t* span_ptr,
                       const pic_span* spans, const int32_t* new_ptr, const int32_t* new_pos,
-                      int64_t capacity, HostPlan* out, std::string* err);
+                      int64_t capacity, int32_t decode_rows, HostPlan* out, std::string* err);
+
+// One decode step over a planned (and prefilled) batch: every request gets one
+// token at position last_pos + 1 + step, stored at its row
+// prefix + n_new + step.  The attention records describe, per request, the
+// pool rows (prefix), the rows after them in the planes (new tokens, earlier
+// decode tokens and this one) and the single query.
+struct DecodePlan {
+  int32_t step = -1;
+  std::vector<int32_t> pos;     // per request: the token's position
+  std::vector<int32_t> row;     // per request: its assembled row
+  std::vector<ReqRec> reqs;     // per request, for the attention kernel in decode mode
+  std::vector<AttnWork> work;   // one column block per (request, kv head), split over rows
+  int32_t n_split = 1, n_split_out = 1;
+};
+
+// `target_items`: about this many work items (row splits of at least
+// `min_tiles_per_split` tiles, at most `max_split`, even).
+void build_decode(const HostPlan& plan, int32_t kv_heads, int32_t step, int32_t rows_per_tile,
+                  int32_t target_items, int32_t max_split, int32_t min_tiles_per_split, DecodePlan* out);
 
 // Row split for the attention kernel: about `target_wgs` work items of
 // `cols_per_wg` query columns when the batch alone gives fewer (at most

@@ -52,6 +52,16 @@ class Session:
         self.plan.assemble(span_ptr, spans, new_ptr, new_pos, None, None, 2 ** 62, DRY_RUN, None)
         return self.plan.summary()
 
+    def set_decode_rows(self, rows: int):
+        """Reserve rows for decode tokens after each request (takes effect at the next assemble)."""
+        self.plan.set_decode_rows(rows)
+
+    def decode_layer(self, layer, step, q, k_new, v_new, out=None, variant: int = VARIANT_MATERIALIZED):
+        if out is None:
+            out = self.torch.empty_like(q)
+        self.plan.decode_layer(layer, step, q, k_new, v_new, out, variant, self.torch.cuda.current_stream())
+        return out
+
     def prefill_layer(self, layer, q, k_new, v_new, out=None, variant: int = VARIANT_MATERIALIZED):
         if out is None:
             out = self.torch.empty_like(q)

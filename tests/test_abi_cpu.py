@@ -107,6 +107,35 @@ def test_original_targets_and_new_positions_after_the_whole_prefix():
     pool.release()
 
 
+@pytest.mark.parametrize("name", ["turborag_small", "sempic_small"])
+def test_decode_reserve_row_layout(name):
+    # each request owns prefix + n_new + reserve rows; the plan keeps the
+    # request's positions and rows otherwise unchanged
+    wl = W.get(name)
+    pool = _pool(wl)
+    plan = B.Plan(pool)
+    reserve = 5
+    plan.set_decode_rows(reserve)
+    _dry(plan, wl)
+    s = plan.summary()
+    assert s["rows"] == wl.rows_total + reserve * wl.batch
+    rb, pr, _ = plan.requests()
+    acc = 0
+    for b, r in enumerate(wl.requests):
+        assert rb[b] == acc and pr[b] == r.prefix_rows
+        acc += r.prefix_rows + r.n_new + reserve
+    # a capacity that does not cover the reserve is rejected
+    with pytest.raises(B.PicError) as ei:
+        plan.assemble(wl.span_ptr(), wl.spans_flat(), wl.new_ptr(), wl.new_pos_flat(), None, None,
+                      wl.rows_total, B.DRY_RUN)
+    assert ei.value.name == "PIC_ERANGE"
+    assert _err(lambda: plan.set_decode_rows(-1)) == "PIC_EINVAL"
+    # decoding needs an assembled batch (a dry run has none)
+    assert _err(lambda: plan.decode_layer(0, 0, FAKE_POOL, FAKE_POOL, FAKE_POOL, FAKE_POOL)) == "PIC_ESTATE"
+    plan.release()
+    pool.release()
+
+
 def test_key_storage_is_validated():
     wl = W.get("tiny_f32")
     p = wl.pool

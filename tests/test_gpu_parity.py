@@ -132,6 +132,105 @@ def test_reduced_workloads_every_element(name):
     torch.cuda.empty_cache()
 
 
+DECODE_STEPS = 3
+
+
+def run_decode(dw, layers, steps, variant):
+    """Decode `steps` tokens per request on the given layers, step by step;
+    returns {layer: [(q, k, v, out) per step]}."""
+    res = {l: [] for l in layers}
+    for st in range(steps):
+        for l in layers:
+            q, k, v = dw.decode_inputs(l, st)
+            out = dw.session.decode_layer(l, st, q, k, v, variant=variant)
+            res[l].append((q, k, v, out))
+    torch.cuda.synchronize()
+    return res
+
+
+def check_decode(dw, b, layers, prefill, decoded):
+    """Request b after its prefill: every decoded token's output, and the rows
+    it appended, against the oracle over the rows so far."""
+    wl = dw.wl
+    m = wl.model
+    sess = dw.session
+    rb, pr, _ = sess.plan.requests()
+    base, npre = int(rb[b]), int(pr[b])
+    r = wl.requests[b]
+    nb = int(wl.new_ptr()[b])
+    kpre, vpre, ppre = P.request_prefix(wl, dw.pool, b, layers)
+    pos_new = P.request_positions(wl, b)
+    last = int(max(ppre.max(initial=-1), pos_new.max(initial=-1)))
+    cs_worst = dict(attn_max_abs=0.0, attn_rel_l2=0.0)
+    for li, l in enumerate(layers):
+        q, k, v, _ = prefill[l]
+        sl = slice(nb, nb + r.n_new)
+        _, kr, vr = orc.prologue(_np(q[sl]), _np(k[sl]), _np(v[sl]), pos_new, m.theta, m.dtype)
+        ks = np.concatenate([kpre[li], kr.transpose(1, 0, 2)], axis=1)
+        vs = np.concatenate([vpre[li], vr.transpose(1, 0, 2)], axis=1)
+        ps = np.concatenate([ppre, pos_new])
+        cs = P.channel_scale(_np(dw.vscale[l]), m.group)
+        for st, (qd, kd, vd, od) in enumerate(decoded[l]):
+            p_tok = np.array([last + 1 + st])
+            o_ref, k1, v1, _ = orc.query_prefill_layer(ks, vs, ps, _np(qd[b:b + 1]), _np(kd[b:b + 1]),
+                                                       _np(vd[b:b + 1]), p_tok, m.theta, m.dtype, m.kv_heads)
+            row = base + npre + r.n_new + st
+            gk = _np(sess.asm_k[l, :, row:row + 1]).transpose(1, 0, 2)
+            gv = _np(sess.asm_v[l, :, row:row + 1]).transpose(1, 0, 2)
+            assert np.array_equal(gv, v1), f"decode value row differs (request {b}, layer {l}, step {st})"
+            P.compare_keys(gk, k1, m.dtype, exact_mask=(p_tok == 0)[:, None, None])
+            amax, rl2 = P.attn_metrics(_np(od[b:b + 1]), o_ref, cs)
+            cs_worst["attn_max_abs"] = max(cs_worst["attn_max_abs"], amax)
+            cs_worst["attn_rel_l2"] = max(cs_worst["attn_rel_l2"], rl2)
+            assert amax <= P.ATOL[m.dtype] and rl2 <= P.RL2[m.dtype], \
+                f"decode attention off (request {b}, layer {l}, step {st}): max-abs {amax:.3g}, rel-L2 {rl2:.3g}"
+            ks = np.concatenate([ks, k1.transpose(1, 0, 2)], axis=1)
+            vs = np.concatenate([vs, v1.transpose(1, 0, 2)], axis=1)
+            ps = np.concatenate([ps, p_tok])
+    return cs_worst
+
+
+@pytest.mark.parametrize("name", ["turborag_small", "coinrag_small", "sempic_small", "long_small",
+                                  "turborag_small_unrot"])
+def test_decode_after_prefill_reduced(name):
+    wl = W.get(name)
+    _say(f"case decode {name}")
+    dw = open_workload(wl)
+    dw.session.set_decode_rows(DECODE_STEPS + 2)
+    dw.assemble()
+    layers = list(range(wl.model.layers))
+    pre = run_prefill(dw, layers, VARIANT_MATERIALIZED)
+    dec = run_decode(dw, layers, DECODE_STEPS, VARIANT_MATERIALIZED)
+    for b in range(wl.batch):
+        _say(name, b, check_decode(dw, b, layers, pre, dec))
+    # the fused variant decodes to identical bits (same split, same rows)
+    dec_f = run_decode(dw, layers, DECODE_STEPS, VARIANT_FUSED)
+    for l in layers:
+        for st in range(DECODE_STEPS):
+            assert torch.equal(dec[l][st][3], dec_f[l][st][3]), f"fused decode differs (layer {l}, step {st})"
+    dw.close()
+    del dw
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("name", ["turborag_b16", "long_16k_b32"])
+def test_decode_after_prefill_full_size(name):
+    wl = W.get(name)
+    _say(f"case decode full {name}")
+    dw = open_workload(wl)
+    dw.session.set_decode_rows(4)
+    dw.assemble()
+    L = wl.model.layers
+    checked = sorted({0, L - 1})
+    pre = run_prefill(dw, list(range(L)), VARIANT_MATERIALIZED)
+    dec = run_decode(dw, checked, 2, VARIANT_MATERIALIZED)
+    for b in sorted({0, wl.batch - 1}):
+        _say(name, b, check_decode(dw, b, checked, pre, dec))
+    dw.close()
+    del dw, pre, dec
+    torch.cuda.empty_cache()
+
+
 def _token_subset(n, k=16):
     if n <= k:
         return None

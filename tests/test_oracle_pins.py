@@ -396,6 +396,38 @@ def test_interleaved_layout_is_causal_prefill_in_position_order():
     assert np.allclose(o, ref[pos_new], rtol=0, atol=1e-11)
 
 
+def test_decoding_one_token_at_a_time_equals_prefilling_them_together():
+    # the step after the prefill is ordinary autoregressive decoding: a token
+    # decoded after the earlier ones (their rotated keys appended as rows)
+    # sees exactly what it would see had all been prefilled at once
+    rng = np.random.default_rng(21)
+    theta, d, hkv, hq = 1e4, 16, 2, 6
+    rows = 13
+    kp = orc.round_bf16(rng.standard_normal((hkv, rows, d)))
+    vp = orc.round_bf16(rng.standard_normal((hkv, rows, d)))
+    pp = np.array([0, 1, 2, 7, 8, 9, 10, 3, 4, 5, 6, 11, 12])
+    n, steps = 4, 5
+    tot = n + steps
+    q = orc.round_bf16(rng.standard_normal((tot, hq, d)))
+    k = orc.round_bf16(rng.standard_normal((tot, hkv, d)))
+    v = orc.round_bf16(rng.standard_normal((tot, hkv, d)))
+    pos = 13 + np.arange(tot)
+    o_all, _, _, _ = orc.query_prefill_layer(kp, vp, pp, q, k, v, pos, theta, "bf16", hkv)
+    o_pre, kr, vr, _ = orc.query_prefill_layer(kp, vp, pp, q[:n], k[:n], v[:n], pos[:n], theta, "bf16", hkv)
+    assert np.allclose(o_pre, o_all[:n], atol=1e-13)
+    ks = np.concatenate([kp, kr.transpose(1, 0, 2)], axis=1)
+    vs = np.concatenate([vp, vr.transpose(1, 0, 2)], axis=1)
+    ps = np.concatenate([pp, pos[:n]])
+    for s_ in range(steps):
+        j = n + s_
+        o1, k1, v1, _ = orc.query_prefill_layer(ks, vs, ps, q[j:j + 1], k[j:j + 1], v[j:j + 1], pos[j:j + 1],
+                                                theta, "bf16", hkv)
+        assert np.allclose(o1[0], o_all[j], atol=1e-13)
+        ks = np.concatenate([ks, k1.transpose(1, 0, 2)], axis=1)
+        vs = np.concatenate([vs, v1.transpose(1, 0, 2)], axis=1)
+        ps = np.concatenate([ps, pos[j:j + 1]])
+
+
 def test_attention_weight_properties():
     rng = np.random.default_rng(12)
     d, hq, hkv, r, n = 8, 4, 2, 30, 5

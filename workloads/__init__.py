@@ -443,6 +443,20 @@ def new_tokens(wl: Workload, layer: int, kscale, vscale, device):
     return q.to(dt), k.to(dt), v.to(dt)
 
 
+def decode_tokens(wl: Workload, layer: int, step: int, kscale, vscale, device):
+    """Un-rotated q [batch][Hq][d], k [batch][Hkv][d], v [batch][Hkv][d] of decode
+    step `step` (one token per request) for one layer."""
+    torch = _torch()
+    m = wl.model
+    n = wl.batch
+    g = _generator(device, wl.seed * 7 + 500000 + 1000 * step + layer)
+    dt = torch_dtype(m)
+    q = torch.randn((n, m.q_heads, m.head_dim), generator=g, device=device)
+    k = torch.randn((n, m.kv_heads, m.head_dim), generator=g, device=device) * kscale[layer][None]
+    v = torch.randn((n, m.kv_heads, m.head_dim), generator=g, device=device) * vscale[layer][None]
+    return q.to(dt), k.to(dt), v.to(dt)
+
+
 def chunk_kv(wl: Workload, pool, c: int, layers=None):
     """Read chunk c's stored K and V back out of the pages: two CPU float64
     tensors [L'][Hkv][len][d] (L' = the selected layers)."""

@@ -9,7 +9,7 @@ from dataclasses import dataclass
 
 import numpy as np
 
-from . import (Workload, alloc_pool, channel_scales, fill_pool, new_tokens)
+from . import (Workload, alloc_pool, channel_scales, decode_tokens, fill_pool, new_tokens)
 
 
 @dataclass
@@ -22,6 +22,9 @@ class DeviceWorkload:
 
     def layer_inputs(self, layer: int):
         return new_tokens(self.wl, layer, self.kscale, self.vscale, self.pool.device)
+
+    def decode_inputs(self, layer: int, step: int):
+        return decode_tokens(self.wl, layer, step, self.kscale, self.vscale, self.pool.device)
 
     def assemble(self, plan_only: bool = False):
         wl = self.wl
