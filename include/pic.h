@@ -101,8 +101,9 @@ typedef struct {
 #define PIC_TARGET_ORIGINAL (-2)
 
 /* pic_assemble flags */
-#define PIC_ASSEMBLE_PLAN_ONLY 1  /* plan on host and device, gather nothing (variant F) */
-#define PIC_ASSEMBLE_DRY_RUN   2  /* validate and plan on the host only; touch no device */
+#define PIC_ASSEMBLE_PLAN_ONLY 1     /* plan on host and device, gather nothing (variant F) */
+#define PIC_ASSEMBLE_DRY_RUN   2     /* validate and plan on the host only; touch no device */
+#define PIC_ASSEMBLE_DEFER_GATHER 4  /* plan now; gather layers later with pic_gather_layers */
 
 /* pic_query_prefill variants */
 #define PIC_VARIANT_MATERIALIZED 0  /* read keys/values from the assembled buffers */
@@ -141,6 +142,23 @@ pic_status pic_pool_register(const pic_model* model, void* pool, int64_t pool_by
                              const int32_t* chunk_len, const int32_t* chunk_orig,
                              const int32_t* chunk_page_ptr, const int32_t* page_ids,
                              pic_pool** out);
+
+/*
+ * The same for a pool that lives in pinned host memory (hipHostMalloc): the
+ * staging tier in front of HBM.  Assembly then reads only the rows the spans
+ * cover, over the host link (CoinRAG page section 3.3 loads only the
+ * selected slices; the TurboRAG review page's batch-scaling discussion names
+ * this transfer as the cost that remains).  Combined with
+ * PIC_ASSEMBLE_DEFER_GATHER and pic_gather_layers on a second stream, layer
+ * l + 1 is transferred while layer l's attention runs.  PIC_EINVAL if `pool`
+ * is not pinned host memory.  Needs a device (it asks the runtime for the
+ * memory's device address).
+ */
+pic_status pic_pool_register_host(const pic_model* model, void* pool, int64_t pool_bytes,
+                                  int32_t page_tokens, int32_t n_pages, int32_t n_chunks,
+                                  const int32_t* chunk_len, const int32_t* chunk_orig,
+                                  const int32_t* chunk_page_ptr, const int32_t* page_ids,
+                                  pic_pool** out);
 
 /* Release a pool handle (not the pool memory).  Plans made from it must be
  * released first (PIC_ESTATE otherwise).  Synchronises the device if device
@@ -193,6 +211,18 @@ pic_status pic_assemble(pic_plan* plan, int32_t batch, const int32_t* span_ptr,
                         void* stream);
 
 /*
+ * Gather layers [layer_begin, layer_end) of the current batch into the
+ * assembled planes on `stream` (after an assemble with
+ * PIC_ASSEMBLE_DEFER_GATHER; re-gathering is allowed).  The stream first
+ * waits for the batch's plan kernels.  A later pic_query_prefill or
+ * pic_decode_layer (variant M) of such a layer, on any stream, waits for this
+ * gather to complete, so an engine can gather layer l + 1 on one stream while
+ * layer l's attention runs on another (the per-layer dependency of a real
+ * prefill: each layer's KV_M needs that layer's C_ctx only).
+ */
+pic_status pic_gather_layers(pic_plan* plan, int32_t layer_begin, int32_t layer_end, void* stream);
+
+/*
  * One layer of the query prefill, KV_M(q; C_ctx) (CoinRAG section 2.3, last
  * equation; TurboRAG: only the query is prefilled online; SemPIC: inline
  * tokens run through the decoder and interleave with compiled caches under a
@@ -212,8 +242,8 @@ pic_status pic_assemble(pic_plan* plan, int32_t batch, const int32_t* span_ptr,
  *   out[j][h] = sum_r softmax_r(<q'_j,h, k_r> / sqrt(d)) v_r
  * over the request's rows r with pos_r <= pos_j.  Variant FUSED reads the
  * prefix rows straight from the pool (its plan may come from PLAN_ONLY) and
- * is implemented for bf16 with head_dim 128; MATERIALIZED needs a full
- * assemble.  bf16 attention uses bf16 MFMA products with fp32 accumulation
+ * is implemented for bf16 with head_dim 128; MATERIALIZED needs the layer
+ * gathered (a full assemble, or pic_gather_layers after a deferred one).  bf16 attention uses bf16 MFMA products with fp32 accumulation
  * and an fp32 online softmax; f32 attention computes in fp32.
  */
 pic_status pic_query_prefill(pic_plan* plan, int32_t layer, const void* q, const void* k_new,

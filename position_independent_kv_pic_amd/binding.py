@@ -23,6 +23,7 @@ KEYS_ROTATED = 0
 KEYS_UNROTATED = 1
 PLAN_ONLY = 1
 DRY_RUN = 2
+DEFER_GATHER = 4
 VARIANT_MATERIALIZED = 0
 VARIANT_FUSED = 1
 
@@ -34,6 +35,7 @@ EXPORTED = (
     "pic_assemble", "pic_query_prefill", "pic_plan_get_summary", "pic_plan_get_requests",
     "pic_plan_get_spans", "pic_plan_get_new_tokens", "pic_timing_enable", "pic_timing_read",
     "pic_timing_reset", "pic_last_error", "pic_version", "pic_plan_set_decode_rows", "pic_decode_layer",
+    "pic_pool_register_host", "pic_gather_layers",
 )
 
 
@@ -87,6 +89,9 @@ def lib() -> ctypes.CDLL:
     sig = {
         "pic_pool_register": [ctypes.POINTER(PicModel), P, I64, I32, I32, I32, pi32, pi32, pi32, pi32,
                               ctypes.POINTER(P)],
+        "pic_pool_register_host": [ctypes.POINTER(PicModel), P, I64, I32, I32, I32, pi32, pi32, pi32, pi32,
+                                   ctypes.POINTER(P)],
+        "pic_gather_layers": [P, I32, I32, P],
         "pic_pool_release": [P],
         "pic_plan_create": [P, ctypes.POINTER(P)],
         "pic_plan_release": [P],
@@ -155,7 +160,7 @@ class Pool:
     """A registered paged chunk-KV pool (the memory stays the caller's)."""
 
     def __init__(self, model: PicModel, pool, pool_bytes: int, page_tokens: int, n_pages: int,
-                 chunk_len, chunk_page_ptr, page_ids, chunk_orig=None):
+                 chunk_len, chunk_page_ptr, page_ids, chunk_orig=None, host: bool = False):
         self.model = model
         self._keep = (_i32(chunk_len), _i32(chunk_page_ptr), _i32(page_ids),
                       None if chunk_orig is None else _i32(chunk_orig))
@@ -168,9 +173,9 @@ class Pool:
         if cp.shape[0] and pg.shape[0] < int(cp[-1]):
             raise ValueError("page_ids is shorter than chunk_page_ptr[-1]")
         h = ctypes.c_void_p()
-        _check(lib().pic_pool_register(ctypes.byref(model), ctypes.c_void_p(_ptr(pool)), int(pool_bytes),
-                                       int(page_tokens), int(n_pages), int(cl.shape[0]), _p32(cl),
-                                       _p32(co), _p32(cp), _p32(pg), ctypes.byref(h)))
+        reg = lib().pic_pool_register_host if host else lib().pic_pool_register
+        _check(reg(ctypes.byref(model), ctypes.c_void_p(_ptr(pool)), int(pool_bytes), int(page_tokens),
+                   int(n_pages), int(cl.shape[0]), _p32(cl), _p32(co), _p32(cp), _p32(pg), ctypes.byref(h)))
         self.handle = h
 
     def release(self):
@@ -224,6 +229,11 @@ class Plan:
         _check(lib().pic_query_prefill(self.handle, int(layer), ctypes.c_void_p(_ptr(q)),
                                        ctypes.c_void_p(_ptr(k_new)), ctypes.c_void_p(_ptr(v_new)),
                                        ctypes.c_void_p(_ptr(out)), int(variant),
+                                       ctypes.c_void_p(_stream(stream))))
+
+    def gather_layers(self, layer_begin: int, layer_end: int, stream=None):
+        """Gather layers [layer_begin, layer_end) after a DEFER_GATHER assemble."""
+        _check(lib().pic_gather_layers(self.handle, int(layer_begin), int(layer_end),
                                        ctypes.c_void_p(_stream(stream))))
 
     def set_decode_rows(self, rows: int):

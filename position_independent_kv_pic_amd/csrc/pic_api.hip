@@ -53,7 +53,11 @@ struct pic_plan {
   pic_pool* pool = nullptr;
   pic::HostPlan hp;
   bool has_batch = false;
-  bool materialized = false;
+  bool materialized = false;         // every layer's prefix rows are gathered
+  std::vector<char> gathered;        // per layer: prefix rows gathered into the planes
+  std::vector<hipEvent_t> layer_ev;  // per layer: completion of a deferred gather
+  std::vector<char> layer_ev_live;   // per layer: layer_ev was recorded for this batch
+  hipEvent_t plan_ev = nullptr;      // the batch's plan kernels have been enqueued before it
   bool failed = false;
   char* asm_k = nullptr;
   char* asm_v = nullptr;
@@ -234,6 +238,63 @@ pic_status check_device(pic_plan* p) {
   return PIC_OK;
 }
 
+// Gather the prefix rows of layers [l0, l1) into the planes on stream s.  A
+// deferred gather records each layer's completion so that the layer's
+// prefill, on any stream, waits for it.
+pic_status gather_layers(pic_plan* p, int32_t l0, int32_t l1, hipStream_t s, bool deferred) {
+  const pic::HostPlan& h = p->hp;
+  const pic::PoolInfo& pi = p->pool->info;
+  if (h.prefix_rows > 0 && l1 > l0) {
+    Timed tm(p, 0, s);
+    pic::GatherArgs ga;
+    ga.spans = reinterpret_cast<const pic::SpanRec*>(p->ws + p->off_spans);
+    ga.crow = reinterpret_cast<const int32_t*>(p->ws + p->off_crow);
+    ga.page_ids = p->pool->d_page_ids;
+    ga.phase_tab = reinterpret_cast<const pic::Phase*>(p->ws + p->off_phase_tab);
+    ga.per_position = pi.m.key_storage == PIC_KEYS_UNROTATED;
+    ga.pool = static_cast<const char*>(pi.device_base);
+    ga.asm_k = p->asm_k;
+    ga.asm_v = p->asm_v;
+    ga.prefix_rows = h.prefix_rows;
+    ga.cap = p->cap;
+    ga.page_bytes = pi.page_bytes;
+    ga.n_spans = h.n_spans;
+    ga.page_shift = pi.page_shift;
+    ga.page_tokens = pi.page_tokens;
+    ga.layers = pi.m.layers;
+    ga.kv_heads = pi.m.kv_heads;
+    ga.planes_per_block = 8;
+    ga.plane_begin = l0 * pi.m.kv_heads;
+    ga.plane_end = l1 * pi.m.kv_heads;
+    hipError_t e = pic::launch_gather(pi.m.dtype, pi.m.head_dim, ga, s);
+    if (e != hipSuccess) return device_error(p, e, "gather kernel");
+  }
+  if (p->layer_ev.size() != size_t(pi.m.layers)) p->layer_ev.resize(size_t(pi.m.layers), nullptr);
+  for (int32_t l = l0; l < l1; ++l) {
+    p->gathered[size_t(l)] = 1;
+    if (!deferred) continue;
+    if (!p->layer_ev[size_t(l)]) {
+      hipError_t e = hipEventCreateWithFlags(&p->layer_ev[size_t(l)], hipEventDisableTiming);
+      if (e != hipSuccess) return device_error(p, e, "create a layer event");
+    }
+    hipError_t e = hipEventRecord(p->layer_ev[size_t(l)], s);
+    if (e != hipSuccess) return device_error(p, e, "record a layer event");
+    p->layer_ev_live[size_t(l)] = 1;
+  }
+  return PIC_OK;
+}
+
+// Before using layer `layer`'s planes on stream s: it must be gathered, and a
+// deferred gather on another stream must have completed.
+pic_status await_layer(pic_plan* p, int32_t layer, hipStream_t s) {
+  if (!p->gathered[size_t(layer)]) return set_err(PIC_ESTATE, "layer %d was not gathered", layer);
+  if (p->layer_ev_live[size_t(layer)]) {
+    hipError_t e = hipStreamWaitEvent(s, p->layer_ev[size_t(layer)], 0);
+    if (e != hipSuccess) return device_error(p, e, "wait for the layer's gather");
+  }
+  return PIC_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -258,6 +319,32 @@ pic_status pic_pool_register(const pic_model* model, void* pool, int64_t pool_by
   if (!p) return set_err(PIC_ENOMEM, "out of host memory");
   p->info = std::move(info);
   *out = p;
+  return ok();
+}
+
+pic_status pic_pool_register_host(const pic_model* model, void* pool, int64_t pool_bytes,
+                                  int32_t page_tokens, int32_t n_pages, int32_t n_chunks,
+                                  const int32_t* chunk_len, const int32_t* chunk_orig,
+                                  const int32_t* chunk_page_ptr, const int32_t* page_ids,
+                                  pic_pool** out) {
+  if (!out) return set_err(PIC_EINVAL, "out is NULL");
+  *out = nullptr;
+  if (!pool) return set_err(PIC_EINVAL, "pool pointer is NULL");
+  // the memory must be pinned host memory the device can address
+  hipPointerAttribute_t attr;
+  hipError_t e = hipPointerGetAttributes(&attr, pool);
+  if (e != hipSuccess || attr.type != hipMemoryTypeHost) {
+    (void)hipGetLastError();
+    return set_err(PIC_EINVAL, "pool is not pinned host memory (allocate it with hipHostMalloc)");
+  }
+  void* dev = nullptr;
+  e = hipHostGetDevicePointer(&dev, pool, 0);
+  if (e != hipSuccess || !dev) return set_err(PIC_EDEVICE, "hipHostGetDevicePointer: %s", hipGetErrorString(e));
+  pic_status st = pic_pool_register(model, pool, pool_bytes, page_tokens, n_pages, n_chunks, chunk_len,
+                                    chunk_orig, chunk_page_ptr, page_ids, out);
+  if (st != PIC_OK) return st;
+  (*out)->info.device_base = dev;
+  (*out)->info.host = true;
   return ok();
 }
 
@@ -291,6 +378,9 @@ pic_status pic_plan_release(pic_plan* p) {
   if (p->dws) (void)hipFree(p->dws);
   if (p->staging) (void)hipHostFree(p->staging);
   if (p->staging_ev) (void)hipEventDestroy(p->staging_ev);
+  if (p->plan_ev) (void)hipEventDestroy(p->plan_ev);
+  for (hipEvent_t e : p->layer_ev)
+    if (e) (void)hipEventDestroy(e);
   for (auto& v : p->events)
     for (auto& pr : v) {
       (void)hipEventDestroy(pr.first);
@@ -306,8 +396,11 @@ pic_status pic_assemble(pic_plan* p, int32_t batch, const int32_t* span_ptr, con
                         int64_t asm_rows_capacity, int32_t flags, void* stream) {
   if (!p) return set_err(PIC_EINVAL, "plan is NULL");
   if (p->failed) return set_err(PIC_ESTATE, "plan is unusable after a device error");
-  if (flags & ~(PIC_ASSEMBLE_PLAN_ONLY | PIC_ASSEMBLE_DRY_RUN))
+  if (flags & ~(PIC_ASSEMBLE_PLAN_ONLY | PIC_ASSEMBLE_DRY_RUN | PIC_ASSEMBLE_DEFER_GATHER))
     return set_err(PIC_EINVAL, "unknown flags 0x%x", flags);
+  if ((flags & PIC_ASSEMBLE_PLAN_ONLY) && (flags & PIC_ASSEMBLE_DEFER_GATHER))
+    return set_err(PIC_EINVAL, "PIC_ASSEMBLE_PLAN_ONLY and PIC_ASSEMBLE_DEFER_GATHER exclude each other");
+  const bool defer = (flags & PIC_ASSEMBLE_DEFER_GATHER) != 0;
   const bool dry = (flags & PIC_ASSEMBLE_DRY_RUN) != 0;
   const bool plan_only = (flags & PIC_ASSEMBLE_PLAN_ONLY) != 0;
   if (asm_rows_capacity < 0) return set_err(PIC_EINVAL, "asm_rows_capacity must be >= 0");
@@ -348,6 +441,8 @@ pic_status pic_assemble(pic_plan* p, int32_t batch, const int32_t* span_ptr, con
 
   p->hp = std::move(hp);
   p->has_batch = false;
+  p->gathered.assign(size_t(pi.m.layers), 0);
+  p->layer_ev_live.assign(size_t(pi.m.layers), 0);
   p->asm_k = static_cast<char*>(asm_k);
   p->asm_v = static_cast<char*>(asm_v);
   p->cap = asm_rows_capacity;
@@ -355,7 +450,8 @@ pic_status pic_assemble(pic_plan* p, int32_t batch, const int32_t* span_ptr, con
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (batch == 0 || h.rows == 0) {
     p->has_batch = true;
-    p->materialized = !plan_only;
+    p->materialized = !plan_only && !defer;
+    if (!plan_only) p->gathered.assign(size_t(pi.m.layers), 1);
     return ok();
   }
 
@@ -411,31 +507,42 @@ pic_status pic_assemble(pic_plan* p, int32_t batch, const int32_t* span_ptr, con
     e = pic::launch_plan(pa, s);
     if (e != hipSuccess) return device_error(p, e, "plan kernels");
   }
-  if (!plan_only && h.prefix_rows > 0) {
-    Timed tm(p, 0, s);
-    pic::GatherArgs ga;
-    ga.spans = reinterpret_cast<const pic::SpanRec*>(p->ws + p->off_spans);
-    ga.crow = reinterpret_cast<const int32_t*>(p->ws + p->off_crow);
-    ga.page_ids = p->pool->d_page_ids;
-    ga.phase_tab = reinterpret_cast<const pic::Phase*>(p->ws + p->off_phase_tab);
-    ga.per_position = pi.m.key_storage == PIC_KEYS_UNROTATED;
-    ga.pool = static_cast<const char*>(pi.base);
-    ga.asm_k = p->asm_k;
-    ga.asm_v = p->asm_v;
-    ga.prefix_rows = h.prefix_rows;
-    ga.cap = p->cap;
-    ga.page_bytes = pi.page_bytes;
-    ga.n_spans = h.n_spans;
-    ga.page_shift = pi.page_shift;
-    ga.page_tokens = pi.page_tokens;
-    ga.layers = pi.m.layers;
-    ga.kv_heads = pi.m.kv_heads;
-    ga.planes_per_block = 8;
-    hipError_t e = pic::launch_gather(pi.m.dtype, pi.m.head_dim, ga, s);
-    if (e != hipSuccess) return device_error(p, e, "gather kernel");
+  if (!p->plan_ev) {
+    hipError_t e = hipEventCreateWithFlags(&p->plan_ev, hipEventDisableTiming);
+    if (e != hipSuccess) return device_error(p, e, "create the plan event");
+  }
+  {
+    hipError_t e = hipEventRecord(p->plan_ev, s);
+    if (e != hipSuccess) return device_error(p, e, "record the plan event");
   }
   p->has_batch = true;
-  p->materialized = !plan_only;
+  if (!plan_only && !defer) {
+    st = gather_layers(p, 0, pi.m.layers, s, /*deferred=*/false);
+    if (st != PIC_OK) return st;
+  }
+  p->materialized = !plan_only && !defer;
+  return ok();
+}
+
+pic_status pic_gather_layers(pic_plan* p, int32_t layer_begin, int32_t layer_end, void* stream) {
+  if (!p) return set_err(PIC_EINVAL, "plan is NULL");
+  if (p->failed) return set_err(PIC_ESTATE, "plan is unusable after a device error");
+  if (!p->has_batch || !p->asm_k) return set_err(PIC_ESTATE, "no assembled batch with planes");
+  const int32_t L = p->pool->info.m.layers;
+  if (layer_begin < 0 || layer_end > L || layer_begin > layer_end)
+    return set_err(PIC_ERANGE, "layer range [%d, %d) outside [0, %d)", layer_begin, layer_end, L);
+  pic_status st = check_device(p);
+  if (st != PIC_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (p->plan_ev) {
+    hipError_t e = hipStreamWaitEvent(s, p->plan_ev, 0);
+    if (e != hipSuccess) return device_error(p, e, "wait for the plan kernels");
+  }
+  st = gather_layers(p, layer_begin, layer_end, s, /*deferred=*/true);
+  if (st != PIC_OK) return st;
+  bool all = true;
+  for (char g : p->gathered) all = all && g;
+  p->materialized = all;
   return ok();
 }
 
@@ -452,8 +559,9 @@ pic_status pic_query_prefill(pic_plan* p, int32_t layer, const void* q, const vo
   if (variant != PIC_VARIANT_MATERIALIZED && variant != PIC_VARIANT_FUSED)
     return set_err(PIC_EINVAL, "unknown variant %d", variant);
   const bool fused = variant == PIC_VARIANT_FUSED;
-  if (!fused && !p->materialized)
-    return set_err(PIC_ESTATE, "the materialised variant needs an assemble without PLAN_ONLY");
+  if (!fused && (p->gathered.empty() || !p->gathered[size_t(layer)]))
+    return set_err(PIC_ESTATE, "the materialised variant needs layer %d gathered (an assemble without "
+                   "PLAN_ONLY or DEFER_GATHER, or pic_gather_layers)", layer);
   if (!pic::attention_supported(m.dtype, m.head_dim, fused))
     return set_err(PIC_EUNSUPPORTED, "attention variant %d is not implemented for dtype %d, head_dim %d",
                    variant, m.dtype, m.head_dim);
@@ -465,6 +573,10 @@ pic_status pic_query_prefill(pic_plan* p, int32_t layer, const void* q, const vo
   pic_status st = check_device(p);
   if (st != PIC_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (!fused) {
+    st = await_layer(p, layer, s);
+    if (st != PIC_OK) return st;
+  }
   const int64_t plane_bytes = p->cap * m.row_bytes;
   char* kpl = p->asm_k + int64_t(layer) * m.kv_heads * plane_bytes;
   char* vpl = p->asm_v + int64_t(layer) * m.kv_heads * plane_bytes;
@@ -512,7 +624,7 @@ pic_status pic_query_prefill(pic_plan* p, int32_t layer, const void* q, const vo
       aa.out = static_cast<uint16_t*>(out);
       aa.opart = reinterpret_cast<float*>(p->ws + p->off_opart);
       aa.ml = reinterpret_cast<float2*>(p->ws + p->off_ml);
-      aa.pool = static_cast<const char*>(pi.base);
+      aa.pool = static_cast<const char*>(pi.device_base);
       aa.rowsrc = reinterpret_cast<const int2*>(p->ws + p->off_rowsrc);
       aa.phase_tab = reinterpret_cast<const pic::Phase*>(p->ws + p->off_phase_tab);
       aa.page_bytes = pi.page_bytes;
@@ -564,7 +676,8 @@ pic_status pic_decode_layer(pic_plan* p, int32_t layer, int32_t step, const void
   if (variant != PIC_VARIANT_MATERIALIZED && variant != PIC_VARIANT_FUSED)
     return set_err(PIC_EINVAL, "unknown variant %d", variant);
   const bool fused = variant == PIC_VARIANT_FUSED;
-  if (!fused && !p->materialized) return set_err(PIC_ESTATE, "variant M needs a full assemble");
+  if (!fused && (p->gathered.empty() || !p->gathered[size_t(layer)]))
+    return set_err(PIC_ESTATE, "variant M needs layer %d gathered", layer);
   if (m.dtype != PIC_BF16 || m.head_dim != 128)
     return set_err(PIC_EUNSUPPORTED, "decode is implemented for bf16 with head_dim 128");
   if (h.batch == 0) return ok();
@@ -574,6 +687,10 @@ pic_status pic_decode_layer(pic_plan* p, int32_t layer, int32_t step, const void
   pic_status st = check_device(p);
   if (st != PIC_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (!fused) {
+    st = await_layer(p, layer, s);
+    if (st != PIC_OK) return st;
+  }
 
   if (p->dec.step != step) {
     pic::build_decode(h, m.kv_heads, step, pic::kAttnRowsPerTile, pic::kAttnTargetWGs, pic::kAttnMaxSplit,
@@ -689,7 +806,7 @@ pic_status pic_decode_layer(pic_plan* p, int32_t layer, int32_t step, const void
     aa.out = static_cast<uint16_t*>(out);
     aa.opart = reinterpret_cast<float*>(p->dws + p->d_opart);
     aa.ml = reinterpret_cast<float2*>(p->dws + p->d_ml);
-    aa.pool = static_cast<const char*>(pi.base);
+    aa.pool = static_cast<const char*>(pi.device_base);
     aa.rowsrc = reinterpret_cast<const int2*>(p->ws + p->off_rowsrc);
     aa.phase_tab = reinterpret_cast<const pic::Phase*>(p->ws + p->off_phase_tab);
     aa.page_bytes = pi.page_bytes;

@@ -43,6 +43,7 @@ struct GatherArgs {
   int64_t prefix_rows, cap, page_bytes;
   int32_t n_spans, page_shift, page_tokens, layers, kv_heads, planes_per_block;
   int32_t per_position;     // keys stored un-rotated: rotate each row by its new position
+  int32_t plane_begin, plane_end;  // (layer, kv head) planes l * Hkv + h to gather
 };
 
 struct PrologueArgs {

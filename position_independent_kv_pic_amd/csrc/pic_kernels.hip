@@ -266,9 +266,8 @@ __global__ __launch_bounds__(256) void gather_kernel(GatherArgs a) {
 #pragma unroll
     for (int e = 0; e < EPV; ++e) ph[e] = pp[e];
   }
-  const int n_planes = a.layers * a.kv_heads;
-  const int p0 = blockIdx.y * a.planes_per_block;
-  const int p1 = min(p0 + a.planes_per_block, n_planes);
+  const int p0 = a.plane_begin + blockIdx.y * a.planes_per_block;
+  const int p1 = min(p0 + a.planes_per_block, a.plane_end);
   const int64_t plane_stride = int64_t(a.page_tokens) * RB;  // one (layer, K/V, head) run
   char* __restrict__ ak = a.asm_k;
   char* __restrict__ av = a.asm_v;
@@ -1079,14 +1078,14 @@ static void gather_launch(const GatherArgs& a, hipStream_t s) {
   constexpr int ES = BF16 ? 2 : 4;
   constexpr int LPR = D / (2 * (16 / ES));
   constexpr int RPB = 256 / LPR;
-  const int n_planes = a.layers * a.kv_heads;
+  const int n_planes = a.plane_end - a.plane_begin;
   dim3 grid(unsigned((a.prefix_rows + RPB - 1) / RPB),
             unsigned((n_planes + a.planes_per_block - 1) / a.planes_per_block));
   hipLaunchKernelGGL((gather_kernel<BF16, D>), grid, dim3(256), 0, s, a);
 }
 
 hipError_t launch_gather(int dtype, int head_dim, const GatherArgs& a, hipStream_t s) {
-  if (a.prefix_rows <= 0) return hipSuccess;
+  if (a.prefix_rows <= 0 || a.plane_end <= a.plane_begin) return hipSuccess;
   if (dtype == PIC_BF16) {
     if (head_dim == 128) gather_launch<true, 128>(a, s);
     else gather_launch<true, 64>(a, s);

@@ -81,6 +81,7 @@ pic_status build_pool(const pic_model* model, void* pool, int64_t pool_bytes, in
   if (n_chunks > 0 && (!chunk_len || !chunk_page_ptr))
     return fail(err, PIC_EINVAL, "chunk_len and chunk_page_ptr are required");
   p.base = pool;
+  p.device_base = pool;
   p.bytes = pool_bytes;
   p.page_tokens = page_tokens;
   p.page_shift = 0;

@@ -28,7 +28,9 @@ struct ModelInfo {
 
 struct PoolInfo {
   ModelInfo m;
-  void* base = nullptr;
+  void* base = nullptr;         // as registered (device memory or pinned host memory)
+  void* device_base = nullptr;  // the same memory as kernels address it
+  bool host = false;            // the pool lives in pinned host memory
   int64_t bytes = 0;
   int32_t page_tokens = 0, page_shift = 0, n_pages = 0, n_chunks = 0;
   int64_t page_bytes = 0;

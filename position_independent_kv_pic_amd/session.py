@@ -9,7 +9,7 @@ from typing import Optional
 
 import numpy as np
 
-from .binding import (DRY_RUN, PLAN_ONLY, VARIANT_MATERIALIZED, Plan, Pool, model_struct)
+from .binding import (DEFER_GATHER, DRY_RUN, PLAN_ONLY, VARIANT_MATERIALIZED, Plan, Pool, model_struct)
 
 
 class Session:
@@ -22,9 +22,12 @@ class Session:
         self.tdtype = torch.bfloat16 if dtype == "bf16" else torch.float32
         self.model = model_struct(layers, q_heads, kv_heads, head_dim, theta, dtype, keys)
         self.pool_tensor = pool_tensor
+        # a pool in pinned host memory is the staging tier: the planes stay on the GPU
+        self.host_pool = not pool_tensor.is_cuda
+        self.device = torch.device("cuda") if self.host_pool else pool_tensor.device
         self.pool = Pool(self.model, pool_tensor, pool_tensor.numel() * pool_tensor.element_size(),
                          page_tokens, pool_tensor.shape[0], chunk_len, chunk_page_ptr, page_ids,
-                         chunk_orig)
+                         chunk_orig, host=self.host_pool)
         self.plan = Plan(self.pool)
         self.asm_k = None
         self.asm_v = None
@@ -36,15 +39,16 @@ class Session:
             return
         t = self.torch
         shape = (self.layers, self.kv_heads, max(rows, 1), self.head_dim)
-        self.asm_k = t.empty(shape, dtype=self.tdtype, device=self.pool_tensor.device)
-        self.asm_v = t.empty(shape, dtype=self.tdtype, device=self.pool_tensor.device)
+        self.asm_k = t.empty(shape, dtype=self.tdtype, device=self.device)
+        self.asm_v = t.empty(shape, dtype=self.tdtype, device=self.device)
         self.capacity = max(rows, 1)
 
-    def assemble(self, span_ptr, spans, new_ptr, new_pos=None, plan_only: bool = False):
+    def assemble(self, span_ptr, spans, new_ptr, new_pos=None, plan_only: bool = False, defer: bool = False):
         d = self.plan_host(span_ptr, spans, new_ptr, new_pos)
         self.ensure_capacity(d["rows"])
+        flags = (PLAN_ONLY if plan_only else 0) | (DEFER_GATHER if defer else 0)
         self.plan.assemble(span_ptr, spans, new_ptr, new_pos, self.asm_k, self.asm_v, self.capacity,
-                           PLAN_ONLY if plan_only else 0, self.torch.cuda.current_stream())
+                           flags, self.torch.cuda.current_stream())
         return d
 
     def plan_host(self, span_ptr, spans, new_ptr, new_pos=None) -> dict:

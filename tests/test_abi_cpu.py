@@ -136,6 +136,22 @@ def test_decode_reserve_row_layout(name):
     pool.release()
 
 
+def test_deferred_gather_flags_and_states():
+    wl = W.get("turborag_small")
+    pool = _pool(wl)
+    plan = B.Plan(pool)
+    sp, spans, npt = wl.span_ptr(), wl.spans_flat(), wl.new_ptr()
+    # PLAN_ONLY and DEFER_GATHER exclude each other
+    assert _err(lambda: plan.assemble(sp, spans, npt, None, None, None, 2 ** 40,
+                                      B.DRY_RUN | B.PLAN_ONLY | B.DEFER_GATHER)) == "PIC_EINVAL"
+    # no planes yet: nothing to gather into
+    assert _err(lambda: plan.gather_layers(0, 1)) == "PIC_ESTATE"
+    _dry(plan, wl)
+    assert _err(lambda: plan.gather_layers(0, 1)) == "PIC_ESTATE"
+    plan.release()
+    pool.release()
+
+
 def test_key_storage_is_validated():
     wl = W.get("tiny_f32")
     p = wl.pool

@@ -261,6 +261,51 @@ def test_full_size_workloads_sampled(name):
     torch.cuda.empty_cache()
 
 
+def test_layer_pipelined_gather_matches_one_gather():
+    # plan first, then gather each layer on a second stream right before the
+    # layer's prefill on the main stream: the same bits as one full gather
+    wl = W.get("coinrag_small")
+    _say("case pipelined gather")
+    dw = open_workload(wl)
+    dw.assemble()
+    layers = list(range(wl.model.layers))
+    ref = run_prefill(dw, layers, VARIANT_MATERIALIZED)
+    dw.assemble(defer=True)
+    with pytest.raises(Exception):
+        dw.session.prefill_layer(0, *dw.layer_inputs(0))          # layer 0 not gathered yet
+    side = torch.cuda.Stream()
+    res = {}
+    dw.session.plan.gather_layers(0, 1, side)
+    for l in layers:
+        if l + 1 < wl.model.layers:
+            dw.session.plan.gather_layers(l + 1, l + 2, side)
+        q, k, v = dw.layer_inputs(l)
+        res[l] = dw.session.prefill_layer(l, q, k, v)
+    torch.cuda.synchronize()
+    for l in layers:
+        assert torch.equal(ref[l][3], res[l]), f"pipelined gather differs on layer {l}"
+    dw.close()
+
+
+@pytest.mark.parametrize("name", ["turborag_small", "coinrag_small_unrot"])
+def test_pool_in_pinned_host_memory(name):
+    # the staging tier: the pool in pinned host memory, only covered rows read
+    wl = W.get(name)
+    _say(f"case host pool {name}")
+    dw = open_workload(wl, host_pool=True)
+    assert not dw.pool.is_cuda
+    dw.assemble()
+    layers = list(range(wl.model.layers))
+    res_m = run_prefill(dw, layers, VARIANT_MATERIALIZED)
+    for b in range(wl.batch):
+        _say(name, b, check_request(dw, b, layers, res_m))
+    dw.assemble(plan_only=True)
+    res_f = run_prefill(dw, layers, VARIANT_FUSED)
+    for l in layers:
+        assert torch.equal(res_m[l][3], res_f[l][3]), f"fused from host pool differs on layer {l}"
+    dw.close()
+
+
 def _edge_workload(keys="rotated"):
     """Ragged shapes and degenerate spans on Qwen2-like heads, two layers."""
     rng = np.random.default_rng(77)

@@ -21,26 +21,34 @@ class DeviceWorkload:
     session: object       # position_independent_kv_pic_amd.session.Session
 
     def layer_inputs(self, layer: int):
-        return new_tokens(self.wl, layer, self.kscale, self.vscale, self.pool.device)
+        return new_tokens(self.wl, layer, self.kscale, self.vscale, self.kscale.device)
 
     def decode_inputs(self, layer: int, step: int):
-        return decode_tokens(self.wl, layer, step, self.kscale, self.vscale, self.pool.device)
+        return decode_tokens(self.wl, layer, step, self.kscale, self.vscale, self.kscale.device)
 
-    def assemble(self, plan_only: bool = False):
+    def assemble(self, plan_only: bool = False, defer: bool = False):
         wl = self.wl
         return self.session.assemble(wl.span_ptr(), wl.spans_flat(), wl.new_ptr(), wl.new_pos_flat(),
-                                     plan_only=plan_only)
+                                     plan_only=plan_only, defer=defer)
 
     def close(self):
         self.session.close()
 
 
-def open_workload(wl: Workload, device="cuda") -> DeviceWorkload:
+def open_workload(wl: Workload, device="cuda", host_pool: bool = False) -> DeviceWorkload:
+    """Fill the pool on the device; with host_pool it is then moved to pinned
+    host memory (the staging tier) and the device copy freed."""
     import torch
     from position_independent_kv_pic_amd.session import Session
     ks, vs = channel_scales(wl, device)
     pool = fill_pool(wl, alloc_pool(wl, device), ks, vs)
     torch.cuda.synchronize()
+    if host_pool:
+        host = torch.empty(pool.shape, dtype=pool.dtype, pin_memory=True)
+        host.copy_(pool)
+        del pool
+        torch.cuda.empty_cache()
+        pool = host
     m, p = wl.model, wl.pool
     sess = Session(m.layers, m.q_heads, m.kv_heads, m.head_dim, m.theta, m.dtype, pool, p.page_tokens,
                    p.chunk_len, p.chunk_page_ptr, p.page_ids, p.chunk_orig, keys=wl.keys)
