@@ -405,13 +405,15 @@ constexpr int kTileBytes = 16384;
 constexpr int kPosOffset = 2 * kTileBytes;          // 64 row positions after K and V
 constexpr float kRescaleSlack = 8.0f;
 
-// LDS swizzles of the 16-byte granules of a tile row.  Keys are read as one
-// 16-byte granule per lane from 32 consecutive rows, so granules are XORed
-// with the row index (mod 16); values are read with the transpose load, whose
-// 16-lane groups touch 4 consecutive rows x 2 granules x 2 halves, so their
-// granules are XORed with 2 * (row mod 4).
+// LDS swizzles of the 16-byte granules of a tile row (64 banks of 4 bytes:
+// one 256-byte row spans every bank once).  Keys are read as one 16-byte
+// granule per lane from 32 consecutive rows, so granules are XORed with the
+// row index (mod 16).  Values are read with the transpose load: each group of
+// 32 lanes touches 4 consecutive rows x 2 granule pairs, so rows r mod 4 take
+// disjoint quarters of the granules (XOR with 4 * (row mod 4)) and the group
+// hits every bank once.
 __device__ __forceinline__ int k_swz(int r) { return r & 15; }
-__device__ __forceinline__ int v_swz(int r) { return 2 * (r & 3); }
+__device__ __forceinline__ int v_swz(int r) { return 4 * (r & 3); }
 
 __device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
