@@ -697,35 +697,38 @@ struct TileLanes {
   unsigned k[4], v[4];
 };
 
-__device__ __forceinline__ void tile_lanes(int wave, TileLanes& tl) {
+// Blocks b0 .. b0 + 3 (a group's wave w copies b0 = 4 w; with rows shared
+// by both groups of a workgroup, wave w8 of the 8 copies b0 = 2 w8, 2 blocks).
+__device__ __forceinline__ void tile_lanes(int b0, TileLanes& tl) {
   const int lane = threadIdx.x & 63;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int r = (wave * 4 + i) * 4 + (lane >> 4);
+    const int r = (b0 + i) * 4 + (lane >> 4);
     tl.k[i] = r * 256 + ((lane & 15) ^ k_swz(r)) * 16;
     tl.v[i] = r * 256 + ((lane & 15) ^ v_swz(r)) * 16;
   }
 }
 
-// Copy one 64-row tile of one plane into LDS.  `base` is the request's row 0,
-// `t0` the tile's first row.  A full tile is addressed as one uniform base
-// plus the fixed lane offsets; the request's last tile repeats its last row
-// past the end.
-template <bool VALUE>
+// Copy NB blocks (b0 .. b0 + NB - 1, 4 rows of 256 bytes each) of one
+// 64-row tile of one plane into LDS.  `base` is the request's row 0, `t0` the
+// tile's first row.  A full tile is addressed as one uniform base plus the
+// fixed lane offsets; the request's last tile repeats its last row past the
+// end.
+template <bool VALUE, int NB>
 __device__ __forceinline__ void tile_to_lds(const char* base, int t0, int rows, const TileLanes& tl, char* lds,
-                                            int wave) {
+                                            int b0) {
   const unsigned* off = VALUE ? tl.v : tl.k;
   if (t0 + kAttnRowsPerTile <= rows) {
     const char* tbase = base + int64_t(t0) * 256;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      __builtin_amdgcn_global_load_lds(tbase + off[i], (lds_void_ptr)(lds + (wave * 4 + i) * 1024), 16, 0, 0);
+    for (int i = 0; i < NB; ++i)
+      __builtin_amdgcn_global_load_lds(tbase + off[i], (lds_void_ptr)(lds + (b0 + i) * 1024), 16, 0, 0);
   } else {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < NB; ++i) {
       const int rr = min(t0 + int(off[i] >> 8), rows - 1);
       __builtin_amdgcn_global_load_lds(base + int64_t(rr) * 256 + (off[i] & 255u),
-                                       (lds_void_ptr)(lds + (wave * 4 + i) * 1024), 16, 0, 0);
+                                       (lds_void_ptr)(lds + (b0 + i) * 1024), 16, 0, 0);
     }
   }
 }
@@ -824,13 +827,15 @@ __global__ __launch_bounds__(PAIRED ? 512 : 256, PAIRED ? 1 : 2) void attention_
   const int T = has ? w.tile_end - w.tile_begin : 0;
   // both groups of a pair pass the same number of barriers
   const AttnWork w0 = a.work[G * blk];
+  // the pair covers the same rows: one stream of copies shared by all 8 waves
+  const bool shared = PAIRED && !FUSED && w0.share_rows != 0;
   int steps = T;
   if (PAIRED) {
     const int T_other = grp == 0 ? (item + 1 < a.n_work ? a.work[item + 1].tile_end - a.work[item + 1].tile_begin : 0)
                                  : w0.tile_end - w0.tile_begin;
     steps = max(T, T_other);
   }
-  char* smem = lds_all + grp * kGroupLdsBytes;
+  char* smem = lds_all + (shared ? 0 : grp * kGroupLdsBytes);
   const ReqRec rq = a.reqs[w.req];
   const int rows = rq.prefix_rows + rq.n_new;
 
@@ -838,7 +843,7 @@ __global__ __launch_bounds__(PAIRED ? 512 : 256, PAIRED ? 1 : 2) void attention_
   bf16x8 qb[8];
   col_setup(a, w, rq, wave, lds_addr(smem), c, qb);
   TileLanes tl;
-  tile_lanes(wave, tl);
+  tile_lanes(shared ? 2 * wave8 : 4 * wave, tl);
 
   f32x16 o[4];
 #pragma unroll
@@ -861,10 +866,15 @@ __global__ __launch_bounds__(PAIRED ? 512 : 256, PAIRED ? 1 : 2) void attention_
       fused_k_load(a, rq, w.head, t0, rows, fk);
       fused_v_to_lds(a, rq, w.head, t0, rows, st + kTileBytes, wave);
     } else {
-      tile_to_lds<false>(kbase, t0, rows, tl, st, wave);
-      tile_to_lds<true>(vbase, t0, rows, tl, st + kTileBytes, wave);
+      if (shared) {
+        tile_to_lds<false, 2>(kbase, t0, rows, tl, st, 2 * wave8);
+        tile_to_lds<true, 2>(vbase, t0, rows, tl, st + kTileBytes, 2 * wave8);
+      } else {
+        tile_to_lds<false, 4>(kbase, t0, rows, tl, st, 4 * wave);
+        tile_to_lds<true, 4>(vbase, t0, rows, tl, st + kTileBytes, 4 * wave);
+      }
     }
-    pos_to_lds(pbase, t0, rows, st + kPosOffset, wave);
+    pos_to_lds(pbase, t0, rows, st + kPosOffset, shared ? wave8 : wave);
   };
 
   // position bounds of tile t; in decode mode every row is visible and only
@@ -1130,32 +1140,28 @@ hipError_t launch_attention_bf16(const AttnArgs& a, bool fused, hipStream_t s) {
   if (a.n_work <= 0) return hipSuccess;
   // dynamic LDS above 64 KB has to be allowed per kernel, once
   static const hipError_t attr = [] {
-    const void* fns[4] = {reinterpret_cast<const void*>(attention_bf16_kernel<true, true>),
+    const void* fns[3] = {reinterpret_cast<const void*>(attention_bf16_kernel<true, true>),
                           reinterpret_cast<const void*>(attention_bf16_kernel<false, true>),
-                          reinterpret_cast<const void*>(attention_bf16_kernel<true, false>),
-                          reinterpret_cast<const void*>(attention_bf16_kernel<false, false>)};
-    const int bytes[4] = {kAttnLdsBytes, kAttnLdsBytes, kGroupLdsBytes, kGroupLdsBytes};
-    for (int i = 0; i < 4; ++i) {
+                          reinterpret_cast<const void*>(attention_bf16_kernel<true, false>)};
+    const int bytes[3] = {kAttnLdsBytes, kAttnLdsBytes, kGroupLdsBytes};
+    for (int i = 0; i < 3; ++i) {
       hipError_t e = hipFuncSetAttribute(fns[i], hipFuncAttributeMaxDynamicSharedMemorySize, bytes[i]);
       if (e != hipSuccess) return e;
     }
     return hipSuccess;
   }();
   if (attr != hipSuccess) return attr;
-  if (a.paired) {
-    const unsigned pairs = unsigned((a.n_work + 1) / 2);
-    if (fused)
-      hipLaunchKernelGGL((attention_bf16_kernel<true, true>), dim3(pairs), dim3(512), kAttnLdsBytes, s, a);
-    else
-      hipLaunchKernelGGL((attention_bf16_kernel<false, true>), dim3(pairs), dim3(512), kAttnLdsBytes, s, a);
-  } else {
-    if (fused)
-      hipLaunchKernelGGL((attention_bf16_kernel<true, false>), dim3(unsigned(a.n_work)), dim3(256), kGroupLdsBytes,
-                         s, a);
-    else
-      hipLaunchKernelGGL((attention_bf16_kernel<false, false>), dim3(unsigned(a.n_work)), dim3(256), kGroupLdsBytes,
-                         s, a);
-  }
+  // the assembled-plane variant always runs two items per workgroup: row
+  // splits merged in LDS, or neighbouring column blocks sharing their rows'
+  // copies; the fused variant pairs only the row splits it merges
+  const unsigned pairs = unsigned((a.n_work + 1) / 2);
+  if (!fused)
+    hipLaunchKernelGGL((attention_bf16_kernel<false, true>), dim3(pairs), dim3(512), kAttnLdsBytes, s, a);
+  else if (a.paired)
+    hipLaunchKernelGGL((attention_bf16_kernel<true, true>), dim3(pairs), dim3(512), kAttnLdsBytes, s, a);
+  else
+    hipLaunchKernelGGL((attention_bf16_kernel<true, false>), dim3(unsigned(a.n_work)), dim3(256), kGroupLdsBytes,
+                       s, a);
   if (a.n_split_out > 1) {
     const int64_t items = int64_t(a.n_new) * a.q_heads;
     hipLaunchKernelGGL(merge_kernel, dim3(unsigned((items + 7) / 8)), dim3(256), 0, s, a);

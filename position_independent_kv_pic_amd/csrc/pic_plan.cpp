@@ -299,11 +299,32 @@ int32_t build_attention_work(const HostPlan& plan, int32_t kv_heads, int32_t gro
           w.tile_end = int32_t(int64_t(tiles) * (sp + 1) / split);
           w.split = sp;
           w.merge_pair = pairs && (sp % 2) == 0;
-          w.pad = 0;
+          w.share_rows = 0;
           out->push_back(w);
         }
       }
+      // unsplit: neighbouring column blocks pair up and share their rows; an
+      // odd count gets an empty partner (no rows, no valid columns) so that
+      // pairs never straddle two (request, kv head)s
+      if (split == 1 && (ncb & 1) && (out->size() & 1)) {
+        AttnWork w;
+        w.req = b;
+        w.head = h;
+        w.col_begin = ncb * cols_per_wg;
+        w.tile_begin = w.tile_end = 0;
+        w.split = 0;
+        w.merge_pair = 0;
+        w.share_rows = 0;
+        out->push_back(w);
+      }
     }
+  }
+  for (size_t i = 0; i + 1 < out->size(); i += 2) {
+    AttnWork& x = (*out)[i];
+    AttnWork& y = (*out)[i + 1];
+    if (!x.merge_pair && x.req == y.req && x.head == y.head && x.tile_begin == y.tile_begin &&
+        x.tile_end == y.tile_end && x.tile_end > x.tile_begin)
+      x.share_rows = y.share_rows = 1;
   }
   return pairs ? split / 2 : split;
 }
@@ -354,7 +375,7 @@ void build_decode(const HostPlan& plan, int32_t kv_heads, int32_t step, int32_t 
         w.tile_end = int32_t(int64_t(tiles) * (sp + 1) / split);
         w.split = sp;
         w.merge_pair = pairs && (sp % 2) == 0;
-        w.pad = 0;
+        w.share_rows = 0;
         out->work.push_back(w);
       }
     }

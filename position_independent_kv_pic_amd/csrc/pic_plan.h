@@ -73,7 +73,7 @@ struct AttnWork {
   int32_t tile_end;
   int32_t split;
   int32_t merge_pair;
-  int32_t pad;
+  int32_t share_rows;   // items 2p and 2p + 1 cover the same rows of one (request, kv head)
 };
 
 struct HostPlan {
