@@ -70,7 +70,8 @@ struct pic_plan {
   size_t off_spans = 0, off_crow = 0, off_reqs = 0, off_new_pos = 0, off_new_row = 0,
          off_new_req = 0, off_work = 0, off_omega = 0, blob_bytes = 0;
   size_t off_pos = 0, off_rowsrc = 0, off_tile_pos = 0, off_phase_tab = 0, off_phase_new = 0,
-         off_qrot = 0, off_opart = 0, off_ml = 0, ws_bytes = 0;
+         off_qrot = 0, off_opart = 0, off_ml = 0, off_spart = 0, off_sml = 0, off_count = 0,
+         ws_bytes = 0;
 
   // pinned staging for the upload, reused once its copy has completed
   char* staging = nullptr;
@@ -167,6 +168,12 @@ void layout_workspace(pic_plan* p) {
   const size_t nsplit = hp.n_split_out > 1 ? size_t(hp.n_split_out) : 0;
   p->off_opart = take(nsplit * size_t(hp.new_rows) * m.q_heads * m.head_dim * sizeof(float));
   p->off_ml = take(nsplit * size_t(hp.new_rows) * m.q_heads * sizeof(float2));
+  // row splits merged inside the attention kernel: per column block and
+  // split, 4 waves of 64 lanes x (64 floats of O + (m, sum)), and a counter
+  const size_t split_waves = size_t(hp.n_slots) * size_t(hp.n_split_wg > 1 ? hp.n_split_wg : 0) * 4;
+  p->off_spart = take(split_waves * 64 * 64 * sizeof(float));
+  p->off_sml = take(split_waves * 64 * 2 * sizeof(float));
+  p->off_count = take(size_t(hp.n_slots) * sizeof(int32_t));
   p->ws_bytes = o;
 }
 
@@ -416,11 +423,10 @@ pic_status pic_assemble(pic_plan* p, int32_t batch, const int32_t* span_ptr, con
                                   p->decode_rows_next, &hp, &err);
   if (st != PIC_OK) return set_err(st, "%s", err.c_str());
   if (pi.m.dtype == PIC_BF16 && pi.m.head_dim == 128) {
-    hp.n_split = pic::choose_attention_split(hp, pi.m.kv_heads, pi.m.group, pic::kAttnColsPerWG,
-                                             pic::kAttnRowsPerTile, pic::kAttnTargetWGs,
-                                             pic::kAttnMaxSplit, /*min_tiles_per_split=*/4);
-    hp.n_split_out = pic::build_attention_work(hp, pi.m.kv_heads, pi.m.group, pic::kAttnColsPerWG,
-                                               pic::kAttnRowsPerTile, hp.n_split, &hp.work);
+    const pic::AttnSplit sp = pic::choose_attention_split(
+        hp, pi.m.kv_heads, pi.m.group, pic::kAttnColsPerWG, pic::kAttnRowsPerTile, pic::kAttnTargetWGs,
+        pic::kAttnMaxSplit, /*min_tiles_per_split=*/4, pic::kAttnMinTilesAcross);
+    pic::build_attention_work(&hp, pi.m.kv_heads, pi.m.group, pic::kAttnColsPerWG, pic::kAttnRowsPerTile, sp);
   }
   p->dec.step = -1;  // decode tables describe the previous batch
   if (dry) {
@@ -504,6 +510,8 @@ pic_status pic_assemble(pic_plan* p, int32_t batch, const int32_t* span_ptr, con
     pa.batch = h.batch;
     pa.n_tiles = h.n_tiles;
     pa.tile_pos = reinterpret_cast<int2*>(p->ws + p->off_tile_pos);
+    pa.split_count = reinterpret_cast<int32_t*>(p->ws + p->off_count);
+    pa.n_slots = h.n_slots;
     e = pic::launch_plan(pa, s);
     if (e != hipSuccess) return device_error(p, e, "plan kernels");
   }
@@ -618,7 +626,11 @@ pic_status pic_query_prefill(pic_plan* p, int32_t layer, const void* q, const vo
       aa.group = m.group;
       aa.n_new = int32_t(h.new_rows);
       aa.n_split_out = h.n_split_out;
-      aa.paired = h.n_split_out < h.n_split;
+      aa.paired = h.n_split > 1;
+      aa.n_split_wg = h.n_split_wg;
+      aa.split_count = reinterpret_cast<int32_t*>(p->ws + p->off_count);
+      aa.spart = reinterpret_cast<float*>(p->ws + p->off_spart);
+      aa.sml = reinterpret_cast<float*>(p->ws + p->off_sml);
       aa.decode = 0;
       aa.scale_log2 = float(1.4426950408889634 / std::sqrt(double(m.head_dim)));
       aa.out = static_cast<uint16_t*>(out);
@@ -693,7 +705,7 @@ pic_status pic_decode_layer(pic_plan* p, int32_t layer, int32_t step, const void
   }
 
   if (p->dec.step != step) {
-    pic::build_decode(h, m.kv_heads, step, pic::kAttnRowsPerTile, pic::kAttnTargetWGs, pic::kAttnMaxSplit,
+    pic::build_decode(h, m.kv_heads, step, pic::kAttnRowsPerTile, pic::kDecodeTargetItems, pic::kAttnMaxSplit,
                       /*min_tiles_per_split=*/2, &p->dec);
     const pic::DecodePlan& d = p->dec;
     size_t o = 0;
@@ -801,6 +813,10 @@ pic_status pic_decode_layer(pic_plan* p, int32_t layer, int32_t step, const void
     aa.n_new = h.batch;
     aa.n_split_out = d.n_split_out;
     aa.paired = d.n_split_out < d.n_split;
+    aa.n_split_wg = 1;
+    aa.split_count = nullptr;
+    aa.spart = nullptr;
+    aa.sml = nullptr;
     aa.decode = 1;
     aa.scale_log2 = float(1.4426950408889634 / std::sqrt(double(m.head_dim)));
     aa.out = static_cast<uint16_t*>(out);

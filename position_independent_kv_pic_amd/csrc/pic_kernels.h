@@ -30,6 +30,8 @@ struct PlanArgs {
   const ReqRec* reqs;       // for the tile bounds
   int32_t batch, n_tiles;
   int2* tile_pos;           // [n_tiles]: (min, max) row position; max = INT_MAX for a partial tile
+  int32_t* split_count;     // [n_slots]: the attention kernel's merge counters, cleared here
+  int32_t n_slots;
 };
 
 struct GatherArgs {
@@ -72,7 +74,11 @@ struct AttnArgs {
   const AttnWork* work;
   int32_t n_work, q_heads, group, n_new;
   int32_t n_split_out;      // partials written for merge_kernel (1: outputs written directly)
-  int32_t paired;           // work items 2p, 2p + 1 are the row splits of one column block
+  int32_t paired;           // two work items per workgroup
+  int32_t n_split_wg;       // row splits of a column block in different workgroups (1: none)
+  int32_t* split_count;     // per column block: splits stored so far (left at 0 after the merge)
+  float* spart;             // [column blocks][n_split_wg][4 waves][32][64 lanes] float2: split partial O
+  float* sml;               // [column blocks][n_split_wg][4 waves][64 lanes] float2: (m, sum)
   int32_t decode;           // one query per request (new_begin = its index), every row visible:
                             // tile bounds are not read, rows past the end are masked
   float scale_log2;         // log2(e) / sqrt(head_dim)
@@ -104,7 +110,9 @@ struct AttnF32Args {
 
 constexpr int kAttnRowsPerTile = 64;
 constexpr int kAttnColsPerWG = 128;   // work item: 4 waves x 32 query columns
-constexpr int kAttnTargetWGs = 512;   // work items: two per CU (one workgroup of two items)
+constexpr int kAttnTargetWGs = 256;   // prefill workgroups (two work items each): one per CU
+constexpr int kAttnMinTilesAcross = 64;  // tiles per split that pay for a merge across workgroups
+constexpr int kDecodeTargetItems = 512;  // decode work items: two per CU (one workgroup of two)
 constexpr int kAttnMaxSplit = 16;     // merge_kernel handles at most this many row splits
 
 // Decode step tables: per request, the phases of its decode position and the

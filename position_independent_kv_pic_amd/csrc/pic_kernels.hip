@@ -201,8 +201,10 @@ __global__ __launch_bounds__(256) void decode_plan_kernel(DecodePlanArgs a) {
 
 // One thread per 64-row tile: the smallest and largest row position, with the
 // largest replaced by INT_MAX when the tile runs past the request's rows.
+// The first n_slots threads also clear the attention merge counters.
 __global__ __launch_bounds__(256) void plan_tiles_kernel(PlanArgs a) {
   int tix = int(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (tix < a.n_slots) a.split_count[tix] = 0;
   if (tix >= a.n_tiles) return;
   int lo = 0, hi = a.batch;
   while (hi - lo > 1) {
@@ -671,6 +673,86 @@ __device__ __forceinline__ void store_column(const AttnArgs& a, const Col& c, co
   }
 }
 
+// Row-split partials of a column block.  Each wave stores its unnormalised
+// O and its (m, sum) exactly as its lanes hold them: per (column block,
+// split, wave), 32 float2 of O per lane (fragment-major, lane-minor, so every
+// store and load moves 512 contiguous bytes) and one float2 (m, sum) per lane.
+// The stores write through to device-coherent memory and the merging split
+// loads past its own XCD's cache, so no cache-wide write-back or invalidate is
+// needed; the arrival count is taken after the stores have completed.
+constexpr int kSplitWaveFloats = 32 * 64 * 2;
+
+__device__ __forceinline__ void st_dev2(float* p, float x, float y) {
+  const unsigned long long u = (unsigned long long)__float_as_uint(x) | ((unsigned long long)__float_as_uint(y) << 32);
+  __hip_atomic_store(reinterpret_cast<unsigned long long*>(p), u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ float2 ld_dev2(const float* p) {
+  const unsigned long long u =
+      __hip_atomic_load(reinterpret_cast<const unsigned long long*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return make_float2(__uint_as_float(unsigned(u)), __uint_as_float(unsigned(u >> 32)));
+}
+
+__device__ __forceinline__ int64_t split_wave_block(const AttnArgs& a, int slot, int sp, int wave) {
+  return (int64_t(slot) * a.n_split_wg + sp) * 4 + wave;
+}
+
+__device__ __forceinline__ void store_split_partial(const AttnArgs& a, int slot, int sp, int wave,
+                                                    const f32x16 o[4], float m, float lt) {
+  const int lane = threadIdx.x & 63;
+  const int64_t wb = split_wave_block(a, slot, sp, wave);
+  float* base = a.spart + wb * kSplitWaveFloats + lane * 2;
+#pragma unroll
+  for (int j = 0; j < 32; ++j) {
+    const int db = j >> 3, e = 2 * (j & 7);
+    st_dev2(base + j * 128, o[db][e], o[db][e + 1]);
+  }
+  st_dev2(a.sml + (wb * 64 + lane) * 2, m, lt);
+}
+
+// The last split of a column block to arrive merges every split's partial
+// (its own included, read back like the others) by log-sum-exp with a running
+// maximum, in split order, so the result does not depend on which split came
+// last.  Two splits' (m, sum) and O are requested together.  Returns (m,
+// sum); o receives the merged unnormalised output.
+__device__ __forceinline__ float2 merge_split_partials(const AttnArgs& a, int slot, int wave, f32x16 o[4]) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int db = 0; db < 4; ++db) o[db] = f32x16{};
+  float mrun = -INFINITY, den = 0.0f;
+  auto add = [&](float2 x, const float2 v[32]) {
+    if (!(x.y > 0.0f)) return;
+    const float mnew = den > 0.0f ? fmaxf(mrun, x.x) : x.x;
+    const float sold = den > 0.0f ? __builtin_amdgcn_exp2f(mrun - mnew) : 0.0f;
+    const float wgt = __builtin_amdgcn_exp2f(x.x - mnew);
+    den = __builtin_fmaf(wgt, x.y, den * sold);
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {
+      const int db = j >> 3, e = 2 * (j & 7);
+      o[db][e] = __builtin_fmaf(wgt, v[j].x, o[db][e] * sold);
+      o[db][e + 1] = __builtin_fmaf(wgt, v[j].y, o[db][e + 1] * sold);
+    }
+    mrun = mnew;
+  };
+  for (int sp = 0; sp < a.n_split_wg; sp += 2) {
+    const bool two = sp + 1 < a.n_split_wg;
+    const int64_t wb0 = split_wave_block(a, slot, sp, wave);
+    const int64_t wb1 = two ? wb0 + 4 : wb0;
+    const float* b0 = a.spart + wb0 * kSplitWaveFloats + lane * 2;
+    const float* b1 = a.spart + wb1 * kSplitWaveFloats + lane * 2;
+    const float2 x0 = ld_dev2(a.sml + (wb0 * 64 + lane) * 2);
+    const float2 x1 = ld_dev2(a.sml + (wb1 * 64 + lane) * 2);
+    float2 v0[32], v1[32];
+#pragma unroll
+    for (int j = 0; j < 32; ++j) v0[j] = ld_dev2(b0 + j * 128);
+#pragma unroll
+    for (int j = 0; j < 32; ++j) v1[j] = ld_dev2(b1 + j * 128);
+    add(x0, v0);
+    if (two) add(x1, v1);
+  }
+  return make_float2(mrun, den);
+}
+
 // ---------------------------------------------------------------------------
 // attention kernel
 // ---------------------------------------------------------------------------
@@ -955,6 +1037,22 @@ __global__ __launch_bounds__(PAIRED ? 512 : 256, PAIRED ? 1 : 2) void attention_
       }
     lt = w0f * lt + w1f * ml1.y;
     m = (l0 || l1) ? mm : -INFINITY;
+  } else if (a.n_split_wg > 1) {
+    // rows split over workgroups: each split stores its partial and then
+    // counts itself in the column block's counter; the last to arrive merges
+    // and writes the output, and leaves the counter at 0 for the next launch
+    __shared__ int arrived[G];
+    const bool counted = has && w.slot >= 0;
+    if (counted) store_split_partial(a, w.slot, w.split, wave, o, m, lt);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the stores have reached device scope
+    __syncthreads();
+    if (counted && (threadIdx.x & 255) == 0) arrived[grp] = atomicAdd(a.split_count + w.slot, 1);
+    __syncthreads();
+    if (!counted || arrived[grp] != a.n_split_wg - 1) return;
+    if ((threadIdx.x & 255) == 0) a.split_count[w.slot] = 0;
+    const float2 ml = merge_split_partials(a, w.slot, wave, o);
+    m = ml.x;
+    lt = ml.y;
   } else if (!has) {
     return;
   }
@@ -1074,8 +1172,9 @@ hipError_t launch_plan(const PlanArgs& a, hipStream_t s) {
   if (n2 > 0) {
     hipLaunchKernelGGL(plan_phase_kernel, dim3(unsigned((n2 + 255) / 256)), dim3(256), 0, s, a);
   }
-  if (a.n_tiles > 0) {
-    hipLaunchKernelGGL(plan_tiles_kernel, dim3(unsigned((a.n_tiles + 255) / 256)), dim3(256), 0, s, a);
+  const int n3 = max(a.n_tiles, a.n_slots);
+  if (n3 > 0) {
+    hipLaunchKernelGGL(plan_tiles_kernel, dim3(unsigned((n3 + 255) / 256)), dim3(256), 0, s, a);
   }
   return hipGetLastError();
 }

@@ -256,77 +256,90 @@ pic_status build_plan(const PoolInfo& pool, int32_t batch, const int32_t* span_p
   return PIC_OK;
 }
 
-int32_t choose_attention_split(const HostPlan& plan, int32_t kv_heads, int32_t group, int32_t cols_per_wg,
-                               int32_t rows_per_tile, int32_t target_wgs, int32_t max_split,
-                               int32_t min_tiles_per_split) {
-  int64_t base = 0;
+AttnSplit choose_attention_split(const HostPlan& plan, int32_t kv_heads, int32_t group, int32_t cols_per_wg,
+                                 int32_t rows_per_tile, int32_t target_wgs, int32_t max_split,
+                                 int32_t min_tiles_per_split, int32_t min_tiles_across) {
+  int64_t items = 0, units = 0;   // column blocks; pairs of them (workgroups without a split)
   int32_t max_tiles = 0;
   for (const ReqRec& r : plan.reqs) {
-    int64_t cols = int64_t(r.n_new) * group;
-    base += kv_heads * ((cols + cols_per_wg - 1) / cols_per_wg);
-    int32_t tiles = (r.prefix_rows + r.n_new + rows_per_tile - 1) / rows_per_tile;
-    max_tiles = std::max(max_tiles, tiles);
+    const int64_t cols = int64_t(r.n_new) * group;
+    if (cols == 0) continue;
+    const int64_t ncb = (cols + cols_per_wg - 1) / cols_per_wg;
+    items += kv_heads * ncb;
+    units += kv_heads * ((ncb + 1) / 2);
+    max_tiles = std::max(max_tiles, (r.prefix_rows + r.n_new + rows_per_tile - 1) / rows_per_tile);
   }
-  int32_t split = 1;
-  if (base > 0 && base < target_wgs) {
-    split = int32_t((target_wgs + base - 1) / base);
-    split = std::min(split, max_split);
-    split = std::min(split, std::max(1, max_tiles / std::max(1, min_tiles_per_split)));
-    split = std::max(split, 1);
-    if (split > 1 && (split & 1)) split = std::min(split + 1, max_split & ~1);
-  }
-  return split;
+  AttnSplit out{1, false};
+  if (units == 0 || units >= target_wgs) return out;
+  const int32_t tile_cap = std::max(1, max_tiles / std::max(1, min_tiles_per_split));
+  // long rows: column-block pairs keep sharing their rows, each split in its
+  // own workgroup, merged by the last split to finish
+  int32_t across = int32_t((target_wgs + units - 1) / units);
+  across = std::max(1, std::min({across, max_split, tile_cap}));
+  if (across > 1 && max_tiles / across >= min_tiles_across) return AttnSplit{across, true};
+  // short rows: the two splits of a column block share a workgroup and merge
+  // in LDS (an even split; merge_kernel combines what is left)
+  int32_t split = int32_t((2 * int64_t(target_wgs) + items - 1) / items);
+  split = std::max(1, std::min({split, max_split, tile_cap}));
+  if (split > 1 && (split & 1)) split = std::min(split + 1, max_split & ~1);
+  return AttnSplit{split, false};
 }
 
-int32_t build_attention_work(const HostPlan& plan, int32_t kv_heads, int32_t group, int32_t cols_per_wg,
-                             int32_t rows_per_tile, int32_t split, std::vector<AttnWork>* out) {
-  out->clear();
-  const bool pairs = split > 1 && (split % 2) == 0;
-  for (int32_t b = 0; b < int32_t(plan.reqs.size()); ++b) {
-    const ReqRec& r = plan.reqs[b];
-    int64_t cols = int64_t(r.n_new) * group;
+void build_attention_work(HostPlan* plan, int32_t kv_heads, int32_t group, int32_t cols_per_wg,
+                          int32_t rows_per_tile, AttnSplit sp_cfg) {
+  std::vector<AttnWork>& out = plan->work;
+  out.clear();
+  const int32_t split = sp_cfg.split;
+  const bool across = sp_cfg.across && split > 1;
+  const bool pairs = !across && split > 1 && (split % 2) == 0;
+  int32_t slots = 0;
+  for (int32_t b = 0; b < int32_t(plan->reqs.size()); ++b) {
+    const ReqRec& r = plan->reqs[b];
+    const int64_t cols = int64_t(r.n_new) * group;
     if (cols == 0) continue;
-    int32_t tiles = (r.prefix_rows + r.n_new + rows_per_tile - 1) / rows_per_tile;
-    int32_t ncb = int32_t((cols + cols_per_wg - 1) / cols_per_wg);
+    const int32_t tiles = (r.prefix_rows + r.n_new + rows_per_tile - 1) / rows_per_tile;
+    const int32_t ncb = int32_t((cols + cols_per_wg - 1) / cols_per_wg);
+    auto item = [&](int32_t h, int32_t c, int32_t sp, int32_t slot) {
+      AttnWork w;
+      w.req = b;
+      w.head = h;
+      w.col_begin = c * cols_per_wg;
+      w.tile_begin = int32_t(int64_t(tiles) * sp / split);
+      w.tile_end = int32_t(int64_t(tiles) * (sp + 1) / split);
+      w.split = sp;
+      w.merge_pair = pairs && (sp % 2) == 0;
+      w.share_rows = 0;
+      w.slot = slot;
+      out.push_back(w);
+    };
     for (int32_t h = 0; h < kv_heads; ++h) {
-      for (int32_t c = 0; c < ncb; ++c) {
-        for (int32_t sp = 0; sp < split; ++sp) {
-          AttnWork w;
-          w.req = b;
-          w.head = h;
-          w.col_begin = c * cols_per_wg;
-          w.tile_begin = int32_t(int64_t(tiles) * sp / split);
-          w.tile_end = int32_t(int64_t(tiles) * (sp + 1) / split);
-          w.split = sp;
-          w.merge_pair = pairs && (sp % 2) == 0;
-          w.share_rows = 0;
-          out->push_back(w);
+      if (across || split == 1) {
+        // column-block pairs over the same rows (c == ncb: the empty partner
+        // of an odd count); with `across`, the splits of a pair are
+        // neighbouring workgroups and every real column block has a counter
+        for (int32_t c0 = 0; c0 < ncb; c0 += 2) {
+          for (int32_t sp = 0; sp < split; ++sp)
+            for (int32_t c = c0; c < c0 + 2; ++c) item(h, c, sp, across && c < ncb ? slots + (c - c0) : -1);
+          if (across) slots += std::min(2, ncb - c0);
         }
-      }
-      // unsplit: neighbouring column blocks pair up and share their rows; an
-      // odd count gets an empty partner (no rows, no valid columns) so that
-      // pairs never straddle two (request, kv head)s
-      if (split == 1 && (ncb & 1) && (out->size() & 1)) {
-        AttnWork w;
-        w.req = b;
-        w.head = h;
-        w.col_begin = ncb * cols_per_wg;
-        w.tile_begin = w.tile_end = 0;
-        w.split = 0;
-        w.merge_pair = 0;
-        w.share_rows = 0;
-        out->push_back(w);
+      } else {
+        // splits of one column block next to each other (pairs: 2j, 2j + 1)
+        for (int32_t c = 0; c < ncb; ++c)
+          for (int32_t sp = 0; sp < split; ++sp) item(h, c, sp, -1);
       }
     }
   }
-  for (size_t i = 0; i + 1 < out->size(); i += 2) {
-    AttnWork& x = (*out)[i];
-    AttnWork& y = (*out)[i + 1];
+  for (size_t i = 0; i + 1 < out.size(); i += 2) {
+    AttnWork& x = out[i];
+    AttnWork& y = out[i + 1];
     if (!x.merge_pair && x.req == y.req && x.head == y.head && x.tile_begin == y.tile_begin &&
         x.tile_end == y.tile_end && x.tile_end > x.tile_begin)
       x.share_rows = y.share_rows = 1;
   }
-  return pairs ? split / 2 : split;
+  plan->n_split = split;
+  plan->n_split_out = pairs ? split / 2 : (across ? 1 : split);
+  plan->n_split_wg = across ? split : 1;
+  plan->n_slots = slots;
 }
 
 void build_decode(const HostPlan& plan, int32_t kv_heads, int32_t step, int32_t rows_per_tile,
@@ -376,6 +389,7 @@ void build_decode(const HostPlan& plan, int32_t kv_heads, int32_t step, int32_t 
         w.split = sp;
         w.merge_pair = pairs && (sp % 2) == 0;
         w.share_rows = 0;
+        w.slot = -1;
         out->work.push_back(w);
       }
     }

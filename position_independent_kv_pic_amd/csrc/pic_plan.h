@@ -63,8 +63,11 @@ struct ReqRec {
 // Attention work item: query columns [col_begin, col_begin + cols) of
 // request `req` and kv head `head`, over the request's row tiles
 // [tile_begin, tile_end); split `split` of `n_split`.  Items 2p and 2p + 1
-// share a workgroup; `merge_pair` (set on item 2p) marks them as splits 2j and
-// 2j + 1 of one column block, merged inside the workgroup.
+// share a workgroup.  `merge_pair` (set on item 2p) marks them as splits 2j
+// and 2j + 1 of one column block, merged inside the workgroup.  Otherwise they
+// are neighbouring column blocks, and when their rows are split over
+// workgroups each split writes a partial and counts itself in counter `slot`;
+// the last to arrive merges.
 struct AttnWork {
   int32_t req;
   int32_t head;
@@ -74,6 +77,7 @@ struct AttnWork {
   int32_t split;
   int32_t merge_pair;
   int32_t share_rows;   // items 2p and 2p + 1 cover the same rows of one (request, kv head)
+  int32_t slot;         // merge counter of the column block (-1: rows not split over workgroups)
 };
 
 struct HostPlan {
@@ -91,8 +95,10 @@ struct HostPlan {
   int32_t decode_rows = 0;          // rows reserved after each request's new tokens
   // attention work list
   std::vector<AttnWork> work;
-  int32_t n_split = 1;
-  int32_t n_split_out = 1;          // partials left after the in-workgroup pair merge
+  int32_t n_split = 1;              // row splits per column block
+  int32_t n_split_out = 1;          // partials left for merge_kernel
+  int32_t n_split_wg = 1;           // splits in different workgroups, merged by the last (1: none)
+  int32_t n_slots = 0;              // merge counters (column blocks) when n_split_wg > 1
 };
 
 // Validation helpers return PIC_OK or an error code and fill `err`.
@@ -129,21 +135,32 @@ struct DecodePlan {
 void build_decode(const HostPlan& plan, int32_t kv_heads, int32_t step, int32_t rows_per_tile,
                   int32_t target_items, int32_t max_split, int32_t min_tiles_per_split, DecodePlan* out);
 
-// Row split for the attention kernel: about `target_wgs` work items of
-// `cols_per_wg` query columns when the batch alone gives fewer (at most
-// `max_split` parts, never fewer than `min_tiles_per_split` tiles per part,
-// and an even count so that splits pair up inside workgroups).
-int32_t choose_attention_split(const HostPlan& plan, int32_t kv_heads, int32_t group, int32_t cols_per_wg,
-                               int32_t rows_per_tile, int32_t target_wgs, int32_t max_split,
-                               int32_t min_tiles_per_split);
+// Row split for the attention kernel, used when the batch alone gives fewer
+// than `target_wgs` workgroups (at most `max_split` parts, never fewer than
+// `min_tiles_per_split` tiles per part).  With at least `min_tiles_across`
+// tiles per part (`across`), the neighbouring column blocks of a workgroup
+// keep sharing their rows and the splits run in different workgroups, merged
+// by the last to finish; otherwise the two splits of one column block share a
+// workgroup and merge in LDS (an even count).
+struct AttnSplit {
+  int32_t split;
+  bool across;
+};
+AttnSplit choose_attention_split(const HostPlan& plan, int32_t kv_heads, int32_t group, int32_t cols_per_wg,
+                                 int32_t rows_per_tile, int32_t target_wgs, int32_t max_split,
+                                 int32_t min_tiles_per_split, int32_t min_tiles_across);
 
 // Attention work list: `cols_per_wg` query columns (token-major: column
 // j*G + g is token j, head g of the group) per item, `rows_per_tile` rows per
-// tile, each request's tiles cut into `split` contiguous ranges.  Items are
-// ordered (request, kv head, column block, split), so with an even split the
-// two splits of a pair are adjacent at an even index (merge_pair set).
-// Returns the partials left for merge_kernel (split / 2, or 1).
-int32_t build_attention_work(const HostPlan& plan, int32_t kv_heads, int32_t group, int32_t cols_per_wg,
-                             int32_t rows_per_tile, int32_t split, std::vector<AttnWork>* out);
+// tile, each request's tiles cut into `split` contiguous ranges.  Without a
+// split or with `across`, items are ordered (request, kv head, column-block
+// pair, split, column block): the two column blocks of a pair share a
+// workgroup over one row range (an odd count gets an empty partner), and
+// with `across` every real column block gets a merge counter.  Otherwise they
+// are ordered (request, kv head, column block, split), the two splits of a
+// pair adjacent at an even index (merge_pair).  Fills work, n_split,
+// n_split_out, n_split_wg and n_slots.
+void build_attention_work(HostPlan* plan, int32_t kv_heads, int32_t group, int32_t cols_per_wg,
+                          int32_t rows_per_tile, AttnSplit split);
 
 }  // namespace pic
