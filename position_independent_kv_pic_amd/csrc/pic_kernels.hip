@@ -496,29 +496,34 @@ struct Col {
   unsigned vaddr[4][2];  // LDS addresses of the lane's V^T transpose reads in stage 0
 };
 
-// `lds` is the LDS address of stage 0; later stages are reached through the
-// instructions' immediate offsets.
-__device__ __forceinline__ void col_setup(const AttnArgs& a, const AttnWork& w, const ReqRec& rq,
-                                          int wave, unsigned lds, Col& c, bf16x8 qb[8]) {
+// The lane's query column: its indices, its position and its query
+// fragments, all requested before anything waits on them.  New positions
+// increase strictly within a request, so the range of the wave's query
+// positions is that of its first and last valid column (wave-uniform loads,
+// no cross-lane reduction: a lane exchange would be an LDS instruction, which
+// waits for every outstanding copy into LDS).  `lds` is the LDS address of
+// stage 0; later stages are reached through the instructions' immediate
+// offsets.
+__device__ __forceinline__ void col_setup(const AttnArgs& a, const AttnWork& w, const ReqRec& rq, int wave,
+                                          unsigned lds, Col& c, bf16x8 qb[8]) {
   const int lane = threadIdx.x & 63;
   const int g2 = lane >> 5, lq = lane & 31;
   const int ncols = (a.decode ? 1 : rq.n_new) * a.group;
-  const int col = w.col_begin + wave * 32 + lq;
+  const int c0 = w.col_begin + wave * 32;
+  const int col = c0 + lq;
   c.ok = col < ncols;
   const int colc = c.ok ? col : ncols - 1;
   const int tokj = colc / a.group;
   c.hq = w.head * a.group + (colc - tokj * a.group);
   c.u = rq.new_begin + tokj;
   c.qpos = a.new_pos[c.u];
-  int lo = c.ok ? c.qpos : INT_MAX;
-  int hi = c.ok ? c.qpos : INT_MIN;
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-    lo = min(lo, __shfl_xor(lo, o));
-    hi = max(hi, __shfl_xor(hi, o));
+  c.wq_min = INT_MAX;
+  c.wq_max = INT_MIN;
+  if (c0 < ncols) {
+    const int c1 = min(c0 + 31, ncols - 1);
+    c.wq_min = a.new_pos[rq.new_begin + c0 / a.group];
+    c.wq_max = a.new_pos[rq.new_begin + c1 / a.group];
   }
-  c.wq_min = lo;
-  c.wq_max = hi;
   const u32x4* qp = reinterpret_cast<const u32x4*>(a.q_rot + (int64_t(c.u) * a.q_heads + c.hq) * 128);
 #pragma unroll
   for (int s = 0; s < 8; ++s) qb[s] = __builtin_bit_cast(bf16x8, qp[2 * s + g2]);
@@ -969,8 +974,8 @@ __global__ __launch_bounds__(PAIRED ? 512 : 256, PAIRED ? 1 : 2) void attention_
   if (T > 0) {
     tp_next = bounds(tb);
     issue(std::integral_constant<int, 0>{}, tb);
-    if (FUSED) fused_k_store(a, fk, smem);
   }
+  if (FUSED && T > 0) fused_k_store(a, fk, smem);
   // step i: the group's tile tb + i sits in stage S (i even: 0); wait for its
   // copies, start the next tile's copies into the other stage, consume it
   auto step = [&](auto stage_c, int i) {
