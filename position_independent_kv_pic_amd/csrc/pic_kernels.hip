@@ -911,15 +911,17 @@ __global__ __launch_bounds__(PAIRED ? 512 : 256, PAIRED ? 1 : 2) void attention_
   const int item = G * blk + grp;
   const bool has = item < a.n_work;
   const AttnWork w = a.work[has ? item : G * blk];
-  const int T = has ? w.tile_end - w.tile_begin : 0;
+  // tiles in [gap_begin, gap_end) are skipped
+  const int gap = w.gap_end - w.gap_begin;
+  const int T = has ? w.tile_end - w.tile_begin - gap : 0;
   // both groups of a pair pass the same number of barriers
   const AttnWork w0 = a.work[G * blk];
   // the pair covers the same rows: one stream of copies shared by all 8 waves
   const bool shared = PAIRED && !FUSED && w0.share_rows != 0;
   int steps = T;
   if (PAIRED) {
-    const int T_other = grp == 0 ? (item + 1 < a.n_work ? a.work[item + 1].tile_end - a.work[item + 1].tile_begin : 0)
-                                 : w0.tile_end - w0.tile_begin;
+    auto len = [](const AttnWork& x) { return x.tile_end - x.tile_begin - (x.gap_end - x.gap_begin); };
+    const int T_other = grp == 0 ? (item + 1 < a.n_work ? len(a.work[item + 1]) : 0) : len(w0);
     steps = max(T, T_other);
   }
   char* smem = lds_all + (shared ? 0 : grp * kGroupLdsBytes);
@@ -942,6 +944,9 @@ __global__ __launch_bounds__(PAIRED ? 512 : 256, PAIRED ? 1 : 2) void attention_
   const char* vbase = reinterpret_cast<const char*>(a.v_plane + (int64_t(w.head) * a.cap + rq.row_base) * 128);
   const int32_t* pbase = a.pos + rq.row_base;
   const int tb = w.tile_begin;
+  // the group's i-th tile: tiles from step `gap_at` on come `gap` later
+  const int gap_at = __builtin_amdgcn_readfirstlane(gap > 0 ? w.gap_begin - tb : INT_MAX);
+  auto tile_of = [&](int i) { return i >= gap_at ? tb + i + gap : tb + i; };
   FusedK fk;
 
   // copies of tile t into stage S (0 or 1)
@@ -972,8 +977,8 @@ __global__ __launch_bounds__(PAIRED ? 512 : 256, PAIRED ? 1 : 2) void attention_
   };
   int2 tp_next = make_int2(INT_MAX, INT_MAX);
   if (T > 0) {
-    tp_next = bounds(tb);
-    issue(std::integral_constant<int, 0>{}, tb);
+    tp_next = bounds(tile_of(0));
+    issue(std::integral_constant<int, 0>{}, tile_of(0));
   }
   if (FUSED && T > 0) fused_k_store(a, fk, smem);
   // step i: the group's tile tb + i sits in stage S (i even: 0); wait for its
@@ -983,14 +988,15 @@ __global__ __launch_bounds__(PAIRED ? 512 : 256, PAIRED ? 1 : 2) void attention_
     wait_vm();
     __syncthreads();
     if (i >= T) return;
-    const int t = tb + i;
+    const int t = tile_of(i);
     const bool more = i + 1 < T;
     // this tile's bounds were fetched before the next tile's copies were
     // issued, so reading them never waits on those copies
     const int2 tp = tp_next;
     if (more) {
-      tp_next = bounds(t + 1);
-      issue(std::integral_constant<int, 1 - S>{}, t + 1);
+      const int tn = tile_of(i + 1);
+      tp_next = bounds(tn);
+      issue(std::integral_constant<int, 1 - S>{}, tn);
     }
     if (tp.x <= c.wq_max) {
       f32x16 sacc[2];

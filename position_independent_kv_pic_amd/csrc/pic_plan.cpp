@@ -285,6 +285,26 @@ AttnSplit choose_attention_split(const HostPlan& plan, int32_t kv_heads, int32_t
   return AttnSplit{split, false};
 }
 
+// Smallest row position of each prefix tile of request r (tiles before the
+// one holding its first new row); INT32_MAX for rows past the prefix.
+static void prefix_tile_min(const HostPlan& plan, const ReqRec& r, int32_t rows_per_tile,
+                            std::vector<int32_t>* out) {
+  const int32_t ft = r.prefix_rows / rows_per_tile;
+  out->assign(size_t(ft), INT32_MAX);
+  for (int32_t i = r.span_begin; i < r.span_end; ++i) {
+    const SpanRec& s = plan.spans[size_t(i)];
+    const int32_t r0 = s.dst_row - r.row_base;
+    // within a span positions increase with the row: the first row of the
+    // span inside a tile has the span's smallest position there
+    for (int32_t rr = r0; rr < r0 + s.n;) {
+      const int32_t t = rr / rows_per_tile;
+      if (t >= ft) break;
+      (*out)[size_t(t)] = std::min((*out)[size_t(t)], s.target + (rr - r0));
+      rr = (t + 1) * rows_per_tile;
+    }
+  }
+}
+
 void build_attention_work(HostPlan* plan, int32_t kv_heads, int32_t group, int32_t cols_per_wg,
                           int32_t rows_per_tile, AttnSplit sp_cfg) {
   std::vector<AttnWork>& out = plan->work;
@@ -293,6 +313,7 @@ void build_attention_work(HostPlan* plan, int32_t kv_heads, int32_t group, int32
   const bool across = sp_cfg.across && split > 1;
   const bool pairs = !across && split > 1 && (split % 2) == 0;
   int32_t slots = 0;
+  std::vector<int32_t> tmin;
   for (int32_t b = 0; b < int32_t(plan->reqs.size()); ++b) {
     const ReqRec& r = plan->reqs[b];
     const int64_t cols = int64_t(r.n_new) * group;
@@ -310,17 +331,36 @@ void build_attention_work(HostPlan* plan, int32_t kv_heads, int32_t group, int32
       w.merge_pair = pairs && (sp % 2) == 0;
       w.share_rows = 0;
       w.slot = slot;
+      w.gap_begin = w.gap_end = 0;
       out.push_back(w);
     };
+    if (split == 1) prefix_tile_min(*plan, r, rows_per_tile, &tmin);
+    const int32_t ft = r.prefix_rows / rows_per_tile;   // first tile holding a new row
     for (int32_t h = 0; h < kv_heads; ++h) {
       if (across || split == 1) {
         // column-block pairs over the same rows (c == ncb: the empty partner
         // of an odd count); with `across`, the splits of a pair are
         // neighbouring workgroups and every real column block has a counter
         for (int32_t c0 = 0; c0 < ncb; c0 += 2) {
+          const size_t first = out.size();
           for (int32_t sp = 0; sp < split; ++sp)
             for (int32_t c = c0; c < c0 + 2; ++c) item(h, c, sp, across && c < ncb ? slots + (c - c0) : -1);
           if (across) slots += std::min(2, ncb - c0);
+          if (split == 1) {
+            // prefix tiles after the last one that the pair's latest query
+            // (new positions increase) can see are skipped up to the tile of
+            // the first new row
+            const int64_t last_col = std::min<int64_t>(int64_t(c0 + 2) * cols_per_wg, cols) - 1;
+            const int32_t qmax = plan->new_pos[size_t(r.new_begin + last_col / group)];
+            int32_t a_end = ft;
+            while (a_end > 0 && tmin[size_t(a_end - 1)] > qmax) --a_end;
+            if (a_end < ft) {
+              for (size_t k = first; k < out.size(); ++k) {
+                out[k].gap_begin = a_end;
+                out[k].gap_end = ft;
+              }
+            }
+          }
         }
       } else {
         // splits of one column block next to each other (pairs: 2j, 2j + 1)
@@ -390,6 +430,7 @@ void build_decode(const HostPlan& plan, int32_t kv_heads, int32_t step, int32_t 
         w.merge_pair = pairs && (sp % 2) == 0;
         w.share_rows = 0;
         w.slot = -1;
+        w.gap_begin = w.gap_end = 0;
         out->work.push_back(w);
       }
     }

@@ -78,6 +78,8 @@ struct AttnWork {
   int32_t merge_pair;
   int32_t share_rows;   // items 2p and 2p + 1 cover the same rows of one (request, kv head)
   int32_t slot;         // merge counter of the column block (-1: rows not split over workgroups)
+  int32_t gap_begin;    // tiles [gap_begin, gap_end) of the range are skipped: no query of the
+  int32_t gap_end;      // item can see any of their rows (empty: gap_begin == gap_end)
 };
 
 struct HostPlan {
