@@ -270,7 +270,7 @@ pic_status gather_layers(pic_plan* p, int32_t l0, int32_t l1, hipStream_t s, boo
     ga.page_tokens = pi.page_tokens;
     ga.layers = pi.m.layers;
     ga.kv_heads = pi.m.kv_heads;
-    ga.planes_per_block = 8;
+    ga.planes_per_block = 4;   // 2, 4, 8, 16 measured: 4 is 3% faster than 8 on turborag_b16
     ga.plane_begin = l0 * pi.m.kv_heads;
     ga.plane_end = l1 * pi.m.kv_heads;
     hipError_t e = pic::launch_gather(pi.m.dtype, pi.m.head_dim, ga, s);
