@@ -474,6 +474,26 @@ __device__ __forceinline__ void lds_wait(TrBlock& b) {
                  "+v"(b.x[6]), "+v"(b.x[7]));
 }
 
+// Row positions of a tile, read as inline asm like the fragments (so that
+// the compiler does not wait for copies into other stages first): a lane's 8
+// groups of 4 rows.
+template <int OFF>
+__device__ __forceinline__ i32x4 lds_read_i4(unsigned addr) {
+  i32x4 r;
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
+  return r;
+}
+
+struct PosFrags {
+  i32x4 x[8];
+};
+
+__device__ __forceinline__ void pos_wait(PosFrags& p) {
+  asm volatile("s_waitcnt lgkmcnt(0)"
+               : "+v"(p.x[0]), "+v"(p.x[1]), "+v"(p.x[2]), "+v"(p.x[3]), "+v"(p.x[4]), "+v"(p.x[5]),
+                 "+v"(p.x[6]), "+v"(p.x[7]));
+}
+
 // Max of the 32 scores a lane holds, as a depth-4 tree of 3-input maxima.
 __device__ __forceinline__ float max32(const f32x16& a, const f32x16& b) {
   const float t0 = max3(a[0], a[1], a[2]), t1 = max3(a[3], a[4], a[5]), t2 = max3(a[6], a[7], a[8]);
@@ -562,21 +582,38 @@ __device__ __forceinline__ void s_product(const Col& c, const bf16x8 qb[8], f32x
 
 // Softmax of one tile's scores: mask (when the tile's rows are not all at or
 // before every query of the wave), raise the reference maximum if needed,
-// and form the bf16 probabilities.  `ps` are the tile's row positions in LDS,
-// `r0` its first row, `rows` the request's rows.
-__device__ __forceinline__ void softmax_tile(f32x16 sacc[2], int2 bnd, const int* ps, int r0, int rows,
+// and form the bf16 probabilities.  The tile's row positions sit in LDS at
+// byte offset POFF from `paddr` (the lane's address in stage 0), `r0` is its
+// first row, `rows` the request's rows.
+template <int POFF>
+__device__ __forceinline__ void softmax_tile(f32x16 sacc[2], int2 bnd, unsigned paddr, int r0, int rows,
                                              const Col& c, float scale_log2, float& m, f32x16 o[4],
                                              f32x16& lacc, bf16x8 pb[2][2]) {
   const int g2 = (threadIdx.x & 63) >> 5;
   if (bnd.y > c.wq_min) {
     // rows of this tile may be later than some query (or past the end of
     // the request): mask pos_row > pos_q
+    // group 4 kb + qq holds rows 32 kb + 8 qq + 4 g2 .. + 3
+    // (offsets past the 16-bit immediate go into the address)
+    constexpr unsigned EXTRA = POFF + 224 > 65535 ? unsigned(POFF) : 0u;
+    constexpr int PO = int(POFF - EXTRA);
+    PosFrags pf;
+    const unsigned pa = paddr + EXTRA;
+    pf.x[0] = lds_read_i4<PO>(pa);
+    pf.x[1] = lds_read_i4<PO + 32>(pa);
+    pf.x[2] = lds_read_i4<PO + 64>(pa);
+    pf.x[3] = lds_read_i4<PO + 96>(pa);
+    pf.x[4] = lds_read_i4<PO + 128>(pa);
+    pf.x[5] = lds_read_i4<PO + 160>(pa);
+    pf.x[6] = lds_read_i4<PO + 192>(pa);
+    pf.x[7] = lds_read_i4<PO + 224>(pa);
+    pos_wait(pf);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
       for (int qq = 0; qq < 4; ++qq) {
         const int r4 = 32 * kb + 8 * qq + 4 * g2;
-        const i32x4 p4 = *reinterpret_cast<const i32x4*>(ps + r4);
+        const i32x4 p4 = pf.x[4 * kb + qq];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const bool hide = p4[e] > c.qpos || r0 + r4 + e >= rows;
@@ -931,6 +968,8 @@ __global__ __launch_bounds__(PAIRED ? 512 : 256, PAIRED ? 1 : 2) void attention_
   Col c;
   bf16x8 qb[8];
   col_setup(a, w, rq, wave, lds_addr(smem), c, qb);
+  // this lane's row-position reads in stage 0 (minus kPosOffset)
+  const unsigned paddr = lds_addr(smem) + 16 * ((threadIdx.x & 63) >> 5);
   TileLanes tl;
   tile_lanes(shared ? 2 * wave8 : 4 * wave, tl);
 
@@ -971,9 +1010,15 @@ __global__ __launch_bounds__(PAIRED ? 512 : 256, PAIRED ? 1 : 2) void attention_
 
   // position bounds of tile t; in decode mode every row is visible and only
   // the last tile (rows past the end) needs the mask
+  // (scalar loads through the constant address space, so they never wait on
+  // copies in flight)
+  const int tile_base = __builtin_amdgcn_readfirstlane(rq.tile_base);
+  const __attribute__((address_space(4))) int* tile_pos_c =
+      (const __attribute__((address_space(4))) int*)(a.tile_pos);
   auto bounds = [&](int t) {
     if (a.decode) return make_int2(INT_MIN, (t + 1) * kAttnRowsPerTile > rows ? INT_MAX : INT_MIN);
-    return a.tile_pos[rq.tile_base + t];
+    const int k = 2 * (tile_base + t);
+    return make_int2(tile_pos_c[k], tile_pos_c[k + 1]);
   };
   int2 tp_next = make_int2(INT_MAX, INT_MAX);
   if (T > 0) {
@@ -990,8 +1035,6 @@ __global__ __launch_bounds__(PAIRED ? 512 : 256, PAIRED ? 1 : 2) void attention_
     if (i >= T) return;
     const int t = tile_of(i);
     const bool more = i + 1 < T;
-    // this tile's bounds were fetched before the next tile's copies were
-    // issued, so reading them never waits on those copies
     const int2 tp = tp_next;
     if (more) {
       const int tn = tile_of(i + 1);
@@ -1002,8 +1045,8 @@ __global__ __launch_bounds__(PAIRED ? 512 : 256, PAIRED ? 1 : 2) void attention_
       f32x16 sacc[2];
       bf16x8 pb[2][2];
       s_product<S * kStageBytes>(c, qb, sacc);
-      softmax_tile(sacc, tp, reinterpret_cast<const int*>(smem + S * kStageBytes + kPosOffset),
-                   t * kAttnRowsPerTile, rows, c, a.scale_log2, m, o, lacc, pb);
+      softmax_tile<S * kStageBytes + kPosOffset>(sacc, tp, paddr, t * kAttnRowsPerTile, rows, c, a.scale_log2,
+                                                m, o, lacc, pb);
       pv_product<S * kStageBytes>(c, pb, o, lacc);
     }
     if (FUSED && more) fused_k_store(a, fk, smem + (1 - S) * kStageBytes);
