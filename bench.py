@@ -13,7 +13,12 @@ Prints one JSON line.  `value` is the whole step's attention throughput
 time count against it); per-kernel rates, latency percentiles, the roofline of
 the dominant kernel and the CPU-oracle baseline ride along.
 
-    python bench.py [--steps K] [--warmup W] [--workload NAME] [--variant M|F]
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--variant M|F|FQ]
+
+Variants: M gathers the prefix (assembly kernel) and attends over it; F
+reads the pool inside attention, rotating keys on load; FQ reads the pool
+inside attention, scoring against queries rotated back per 32-row block (opt
+in: it skips the bf16 rounding of the re-rotated keys, see the header).
 """
 from __future__ import annotations
 
@@ -44,7 +49,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=40)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="turborag_b16")
-    ap.add_argument("--variant", default="M", choices=["M", "F"])
+    ap.add_argument("--variant", default="M", choices=["M", "F", "FQ"])
     ap.add_argument("--layouts", type=int, default=8, help="pre-generated batch layouts to cycle through")
     ap.add_argument("--cpu-seconds", type=float, default=20.0, help="time budget of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -222,10 +227,11 @@ def main():
     import torch
     import workloads as W
     from workloads.device import open_workload
-    from position_independent_kv_pic_amd import DEFER_GATHER, VARIANT_FUSED, VARIANT_MATERIALIZED
+    from position_independent_kv_pic_amd import (DEFER_GATHER, PLAN_ONLY, QUERY_ROTATION, VARIANT_FUSED,
+                                                  VARIANT_MATERIALIZED)
 
     assert torch.cuda.is_available(), "bench.py needs a ROCm GPU"
-    variant = VARIANT_FUSED if args.variant == "F" else VARIANT_MATERIALIZED
+    variant = VARIANT_MATERIALIZED if args.variant == "M" else VARIANT_FUSED
     wls = [W.get(args.workload, layout=i) for i in range(args.layouts)]
     wl = wls[0]
     m = wl.model
@@ -242,7 +248,7 @@ def main():
     tables = [(w.span_ptr(), w.spans_flat(), w.new_ptr(), w.new_pos_flat(), w.n_new_total) for w in wls]
     stream = torch.cuda.current_stream()
     plan = sess.plan
-    plan_flag = 1 if variant == VARIANT_FUSED else 0
+    plan_flag = 0 if args.variant == "M" else PLAN_ONLY | (QUERY_ROTATION if args.variant == "FQ" else 0)
 
     side = torch.cuda.Stream() if args.pipelined else None
 

@@ -104,10 +104,11 @@ typedef struct {
 #define PIC_ASSEMBLE_PLAN_ONLY 1     /* plan on host and device, gather nothing (variant F) */
 #define PIC_ASSEMBLE_DRY_RUN   2     /* validate and plan on the host only; touch no device */
 #define PIC_ASSEMBLE_DEFER_GATHER 4  /* plan now; gather layers later with pic_gather_layers */
+#define PIC_ASSEMBLE_QUERY_ROTATION 8  /* with PLAN_ONLY: variant F may rotate queries (pic_query_prefill) */
 
 /* pic_query_prefill variants */
 #define PIC_VARIANT_MATERIALIZED 0  /* read keys/values from the assembled buffers */
-#define PIC_VARIANT_FUSED        1  /* read cached rows from the pool, rotating keys on load */
+#define PIC_VARIANT_FUSED        1  /* read cached rows from the pool, rotating on load (below) */
 
 typedef struct pic_pool pic_pool;
 typedef struct pic_plan pic_plan;
@@ -192,7 +193,8 @@ pic_status pic_plan_release(pic_plan* plan);
  *   asm_k, asm_v   device buffers [layers][kv_heads][asm_rows_capacity][head_dim]
  *                  of the model dtype, 16-byte aligned (may be NULL with DRY_RUN)
  *   asm_rows_capacity  rows per (layer, kv head) plane
- *   flags          0, PIC_ASSEMBLE_PLAN_ONLY or PIC_ASSEMBLE_DRY_RUN
+ *   flags          0, PIC_ASSEMBLE_PLAN_ONLY (optionally | PIC_ASSEMBLE_QUERY_ROTATION),
+ *                  PIC_ASSEMBLE_DRY_RUN or PIC_ASSEMBLE_DEFER_GATHER
  *   stream         hipStream_t
  *
  * Row layout: request b owns rows [row_base_b, row_base_b + prefix_b + n_new_b)
@@ -242,8 +244,25 @@ pic_status pic_gather_layers(pic_plan* plan, int32_t layer_begin, int32_t layer_
  *   out[j][h] = sum_r softmax_r(<q'_j,h, k_r> / sqrt(d)) v_r
  * over the request's rows r with pos_r <= pos_j.  Variant FUSED reads the
  * prefix rows straight from the pool (its plan may come from PLAN_ONLY) and
- * is implemented for bf16 with head_dim 128; MATERIALIZED needs the layer
- * gathered (a full assemble, or pic_gather_layers after a deferred one).  bf16 attention uses bf16 MFMA products with fp32 accumulation
+ * is implemented for bf16 with head_dim 128.  It applies each span's
+ * re-rotation R(delta) on load, in one of two ways:
+ *   - rotated keys: each key is rotated in registers (fp64 arithmetic, one
+ *     rounding, so the scores equal variant M's bit for bit);
+ *   - rotated queries (opt-in): since <q', R(delta) k> = <R(-delta) q', k>,
+ *     a 32-row block whose rows share one delta is scored against the
+ *     queries rotated back by delta (fp32 arithmetic, kept as two bf16
+ *     terms, about 16 significant bits), with the stored keys copied
+ *     unchanged.  Used when the assemble passed PIC_ASSEMBLE_PLAN_ONLY |
+ *     PIC_ASSEMBLE_QUERY_ROTATION, keys are stored rotated and every 32-row
+ *     block of the batch has a single delta
+ *     (pic_plan_summary.fused_query_rotation).  It skips the bf16 rounding
+ *     of each re-rotated key that the assembled cache applies, so it does
+ *     not reproduce variant M's bits, and on caches with large key channels
+ *     (x20 outliers) its outputs differ from variant M's by more than the
+ *     attention tolerance; it is for callers that accept scores against
+ *     exactly re-rotated keys.
+ * MATERIALIZED needs the layer gathered (a full assemble, or
+ * pic_gather_layers after a deferred one).  bf16 attention uses bf16 MFMA products with fp32 accumulation
  * and an fp32 online softmax; f32 attention computes in fp32.
  */
 pic_status pic_query_prefill(pic_plan* plan, int32_t layer, const void* q, const void* k_new,
@@ -297,6 +316,7 @@ typedef struct {
   int64_t rows;            /* prefix_rows + new_rows: rows used in each plane */
   int32_t max_position;    /* largest position of any row */
   int32_t materialized;    /* 1 if the prefix rows were gathered */
+  int32_t fused_query_rotation;  /* 1 if PIC_VARIANT_FUSED rotates queries instead of keys (below) */
 } pic_plan_summary;
 
 pic_status pic_plan_get_summary(const pic_plan* plan, pic_plan_summary* out);

@@ -68,7 +68,7 @@ struct pic_plan {
   char* ws = nullptr;
   size_t ws_cap = 0;
   size_t off_spans = 0, off_crow = 0, off_reqs = 0, off_new_pos = 0, off_new_row = 0,
-         off_new_req = 0, off_work = 0, off_omega = 0, blob_bytes = 0;
+         off_new_req = 0, off_work = 0, off_omega = 0, off_blk_ph = 0, off_phase32 = 0, blob_bytes = 0;
   size_t off_pos = 0, off_rowsrc = 0, off_tile_pos = 0, off_phase_tab = 0, off_phase_new = 0,
          off_qrot = 0, off_opart = 0, off_ml = 0, off_spart = 0, off_sml = 0, off_count = 0,
          ws_bytes = 0;
@@ -158,12 +158,14 @@ void layout_workspace(pic_plan* p) {
   p->off_new_req = take(hp.new_req.size() * sizeof(int32_t));
   p->off_work = take(hp.work.size() * sizeof(pic::AttnWork));
   p->off_omega = take(half * sizeof(double));
+  p->off_blk_ph = take(hp.blk_ph.size() * sizeof(int32_t));
   p->blob_bytes = o;
   p->off_pos = take(size_t(hp.rows) * sizeof(int32_t));
   p->off_rowsrc = take(size_t(hp.rows) * sizeof(int2));
   p->off_tile_pos = take(size_t(hp.n_tiles) * sizeof(int2));
   p->off_phase_tab = take(size_t(hp.phase_rows) * half * sizeof(pic::Phase));
   p->off_phase_new = take(size_t(hp.new_rows) * half * sizeof(pic::Phase));
+  p->off_phase32 = take(size_t(hp.phase_rows) * half * sizeof(float2));
   p->off_qrot = take(size_t(hp.new_rows) * m.q_heads * m.head_dim * m.elem_bytes);
   const size_t nsplit = hp.n_split_out > 1 ? size_t(hp.n_split_out) : 0;
   p->off_opart = take(nsplit * size_t(hp.new_rows) * m.q_heads * m.head_dim * sizeof(float));
@@ -403,10 +405,13 @@ pic_status pic_assemble(pic_plan* p, int32_t batch, const int32_t* span_ptr, con
                         int64_t asm_rows_capacity, int32_t flags, void* stream) {
   if (!p) return set_err(PIC_EINVAL, "plan is NULL");
   if (p->failed) return set_err(PIC_ESTATE, "plan is unusable after a device error");
-  if (flags & ~(PIC_ASSEMBLE_PLAN_ONLY | PIC_ASSEMBLE_DRY_RUN | PIC_ASSEMBLE_DEFER_GATHER))
+  if (flags & ~(PIC_ASSEMBLE_PLAN_ONLY | PIC_ASSEMBLE_DRY_RUN | PIC_ASSEMBLE_DEFER_GATHER |
+                PIC_ASSEMBLE_QUERY_ROTATION))
     return set_err(PIC_EINVAL, "unknown flags 0x%x", flags);
   if ((flags & PIC_ASSEMBLE_PLAN_ONLY) && (flags & PIC_ASSEMBLE_DEFER_GATHER))
     return set_err(PIC_EINVAL, "PIC_ASSEMBLE_PLAN_ONLY and PIC_ASSEMBLE_DEFER_GATHER exclude each other");
+  if ((flags & PIC_ASSEMBLE_QUERY_ROTATION) && !(flags & PIC_ASSEMBLE_PLAN_ONLY))
+    return set_err(PIC_EINVAL, "PIC_ASSEMBLE_QUERY_ROTATION needs PIC_ASSEMBLE_PLAN_ONLY");
   const bool defer = (flags & PIC_ASSEMBLE_DEFER_GATHER) != 0;
   const bool dry = (flags & PIC_ASSEMBLE_DRY_RUN) != 0;
   const bool plan_only = (flags & PIC_ASSEMBLE_PLAN_ONLY) != 0;
@@ -423,10 +428,20 @@ pic_status pic_assemble(pic_plan* p, int32_t batch, const int32_t* span_ptr, con
                                   p->decode_rows_next, &hp, &err);
   if (st != PIC_OK) return set_err(st, "%s", err.c_str());
   if (pi.m.dtype == PIC_BF16 && pi.m.head_dim == 128) {
+    pic::build_qrot_blocks(&hp, pi.m.key_storage == PIC_KEYS_ROTATED, pic::kAttnRowsPerTile);
+    // query rotation asked for and possible: keep every workgroup's column
+    // blocks on shared rows (its queries then fit in LDS next to one stream
+    // of tiles)
+    const bool want_qrot = plan_only && (flags & PIC_ASSEMBLE_QUERY_ROTATION) != 0;
+    const bool qrot_layout = want_qrot && hp.qrot_ok;
     const pic::AttnSplit sp = pic::choose_attention_split(
         hp, pi.m.kv_heads, pi.m.group, pic::kAttnColsPerWG, pic::kAttnRowsPerTile, pic::kAttnTargetWGs,
-        pic::kAttnMaxSplit, /*min_tiles_per_split=*/4, pic::kAttnMinTilesAcross);
+        pic::kAttnMaxSplit, /*min_tiles_per_split=*/4, qrot_layout ? 1 : pic::kAttnMinTilesAcross);
     pic::build_attention_work(&hp, pi.m.kv_heads, pi.m.group, pic::kAttnColsPerWG, pic::kAttnRowsPerTile, sp);
+    pic::finish_qrot(&hp);
+    // otherwise the fused variant rotates keys (the same bits as the
+    // materialised variant)
+    if (!want_qrot) hp.qrot = false;
   }
   p->dec.step = -1;  // decode tables describe the previous batch
   if (dry) {
@@ -480,6 +495,7 @@ pic_status pic_assemble(pic_plan* p, int32_t batch, const int32_t* span_ptr, con
   put(p->staging, p->off_new_req, h.new_req);
   put(p->staging, p->off_work, h.work);
   put(p->staging, p->off_omega, omega);
+  put(p->staging, p->off_blk_ph, h.blk_ph);
   {
     Timed tm(p, 3, s);
     hipError_t e = hipMemcpyAsync(p->ws, p->staging, p->blob_bytes, hipMemcpyHostToDevice, s);
@@ -506,6 +522,7 @@ pic_status pic_assemble(pic_plan* p, int32_t batch, const int32_t* span_ptr, con
     pa.per_position = pi.m.key_storage == PIC_KEYS_UNROTATED;
     pa.phase_rows = h.phase_rows;
     pa.phase_new = reinterpret_cast<pic::Phase*>(p->ws + p->off_phase_new);
+    pa.phase32 = reinterpret_cast<float2*>(p->ws + p->off_phase32);
     pa.reqs = reinterpret_cast<const pic::ReqRec*>(p->ws + p->off_reqs);
     pa.batch = h.batch;
     pa.n_tiles = h.n_tiles;
@@ -645,6 +662,9 @@ pic_status pic_query_prefill(pic_plan* p, int32_t layer, const void* q, const vo
       aa.page_shift = pi.page_shift;
       aa.page_tokens = pi.page_tokens;
       aa.kv_heads = m.kv_heads;
+      aa.qrot = fused && h.qrot ? 1 : 0;
+      aa.blk_ph = reinterpret_cast<const int32_t*>(p->ws + p->off_blk_ph);
+      aa.phase32 = reinterpret_cast<const float2*>(p->ws + p->off_phase32);
       e = pic::launch_attention_bf16(aa, fused, s);
     } else {
       pic::AttnF32Args aa;
@@ -818,6 +838,9 @@ pic_status pic_decode_layer(pic_plan* p, int32_t layer, int32_t step, const void
     aa.spart = nullptr;
     aa.sml = nullptr;
     aa.decode = 1;
+    aa.qrot = 0;
+    aa.blk_ph = nullptr;
+    aa.phase32 = nullptr;
     aa.scale_log2 = float(1.4426950408889634 / std::sqrt(double(m.head_dim)));
     aa.out = static_cast<uint16_t*>(out);
     aa.opart = reinterpret_cast<float*>(p->dws + p->d_opart);
@@ -847,6 +870,7 @@ pic_status pic_plan_get_summary(const pic_plan* p, pic_plan_summary* out) {
   out->rows = p->hp.rows;
   out->max_position = p->hp.max_position;
   out->materialized = p->materialized ? 1 : 0;
+  out->fused_query_rotation = p->hp.qrot ? 1 : 0;
   return ok();
 }
 

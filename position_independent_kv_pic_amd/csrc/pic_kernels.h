@@ -27,6 +27,7 @@ struct PlanArgs {
   int2* rowsrc;             // [rows]: (pool token slot, phase_tab row or -1 for no rotation)
   Phase* phase_tab;         // [phase_rows][half_dim]: per span delta, or per position
   Phase* phase_new;         // [n_new][half_dim]
+  float2* phase32;          // [phase_rows][half_dim]: phase_tab rounded to fp32
   const ReqRec* reqs;       // for the tile bounds
   int32_t batch, n_tiles;
   int2* tile_pos;           // [n_tiles]: (min, max) row position; max = INT_MAX for a partial tile
@@ -93,6 +94,12 @@ struct AttnArgs {
   int64_t kv_plane_off;     // byte offset of (layer, K, head 0) inside a page
   int64_t v_off;            // byte offset from a K row to its V row inside a page
   int32_t page_shift, page_tokens, kv_heads;
+  // fused variant with query rotation (qrot): keys stay as stored and each
+  // 32-row block's rows are scored against the queries rotated back by the
+  // block's delta
+  int32_t qrot;
+  const int32_t* blk_ph;    // [2 n_tiles]: phase-table row of each 32-row block (-1: none)
+  const float2* phase32;    // [phase_rows][64]: (cos, sin) in fp32
 };
 
 struct AttnF32Args {

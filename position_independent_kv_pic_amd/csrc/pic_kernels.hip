@@ -187,7 +187,9 @@ __global__ __launch_bounds__(256) void plan_phase_kernel(PlanArgs a) {
     dst = a.phase_new + int64_t(u) * a.half_dim + k;
   }
   double ang = p * a.omega[k];
-  *dst = make_double2(cos(ang), sin(ang));
+  const double c = cos(ang), sn = sin(ang);
+  *dst = make_double2(c, sn);
+  if (which < a.phase_rows) a.phase32[which * a.half_dim + k] = make_float2(float(c), float(sn));
 }
 
 __global__ __launch_bounds__(256) void decode_plan_kernel(DecodePlanArgs a) {
@@ -937,8 +939,168 @@ __device__ __forceinline__ void fused_k_store(const AttnArgs& a, FusedK& f, char
   }
 }
 
-template <bool FUSED, bool PAIRED>
+// Fused variant with query rotation.  A key stored rotated at its original
+// position and re-rotated by delta scores q . R(delta) k = (R(-delta) q) . k,
+// so where every row of a 32-row block shares one delta the block is scored
+// against the wave's queries rotated back by that delta, and the tiles are
+// copied from the pool pages straight into LDS like the assembled planes.
+// LDS: the two stages, then each wave's rotated queries as the prologue wrote
+// them ([wave][fragment][lane], 16 bytes each), then the fp32 (cos, sin) rows
+// of the 32-row blocks of both stages (stage x 1 KB + block x 512 bytes).
+constexpr int kQOff = 2 * kStageBytes;
+constexpr int kPhOff = kQOff + 8 * 8192;
+constexpr int kQrotLdsBytes = kPhOff + 2048;
+
+// Source of row rr of a request's rows in plane K or V of the layer: the pool
+// page slot of a prefix row, or the assembled planes for a new-token row
+// (slot < 0).
+__device__ __forceinline__ const char* qrot_row(const AttnArgs& a, const ReqRec& rq, int head, int rr, int slot,
+                                                bool value) {
+  if (slot >= 0)
+    return a.pool + int64_t(slot >> a.page_shift) * a.page_bytes + a.kv_plane_off + (value ? a.v_off : 0) +
+           (int64_t(head) * a.page_tokens + (slot & (a.page_tokens - 1))) * 256;
+  const uint16_t* plane = value ? a.v_plane : a.k_plane;
+  return reinterpret_cast<const char*>(plane + (int64_t(head) * a.cap + rq.row_base + rr) * 128);
+}
+
+// rowsrc of the two rows this lane copies from tile t (row blocks 2 w8 and
+// 2 w8 + 1 of 4 rows each): (slot of the first, its phase row, slot of the
+// second).
+__device__ __forceinline__ int3 qrot_src(const AttnArgs& a, const ReqRec& rq, int t, int rows, int wave8) {
+  const int r0 = 8 * wave8 + int((threadIdx.x & 63) >> 4);
+  const int rr0 = min(t * kAttnRowsPerTile + r0, rows - 1);
+  const int rr1 = min(t * kAttnRowsPerTile + r0 + 4, rows - 1);
+  const int2 s0 = a.rowsrc[rq.row_base + rr0];
+  const int2 s1 = a.rowsrc[rq.row_base + rr1];
+  return make_int3(s0.x, s0.y, s1.x);
+}
+
+// Copies of tile t (first row t0) into the stage at `st`: both row blocks of
+// keys and values (granules swizzled as the readers expect), and for waves 1
+// and 5 the phase row of 32-row block 0 or 1 (their first rows lie in it)
+// into `ph_dst` + 512 x block.
+__device__ __forceinline__ void qrot_tile_to_lds(const AttnArgs& a, const ReqRec& rq, int head, int t0, int rows,
+                                                 int3 src, char* st, char* ph_dst, int wave8) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int r = (2 * wave8 + i) * 4 + (lane >> 4);
+    const int rr = min(t0 + r, rows - 1);
+    const int slot = i ? src.z : src.x;
+    const char* kr = qrot_row(a, rq, head, rr, slot, false);
+    const char* vr = qrot_row(a, rq, head, rr, slot, true);
+    __builtin_amdgcn_global_load_lds(kr + ((lane & 15) ^ k_swz(r)) * 16, (lds_void_ptr)(st + (2 * wave8 + i) * 1024),
+                                     16, 0, 0);
+    __builtin_amdgcn_global_load_lds(vr + ((lane & 15) ^ v_swz(r)) * 16,
+                                     (lds_void_ptr)(st + kTileBytes + (2 * wave8 + i) * 1024), 16, 0, 0);
+  }
+  if (wave8 == 1 || wave8 == 5) {
+    const int ph = __builtin_amdgcn_readfirstlane(src.y);
+    // (the lane offset is made opaque so that the 64-bit lane address is
+    // formed here rather than kept live across the loop)
+    unsigned loff = unsigned(lane) * 16u;
+    asm volatile("" : "+v"(loff));
+    if (ph >= 0 && lane < 32)
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const char*>(a.phase32) + int64_t(ph) * 512 + loff,
+                                       (lds_void_ptr)(ph_dst + (wave8 == 5 ? 512 : 0)), 16, 0, 0);
+  }
+}
+
+// Fragment pair (S4, S4 + 4) of the wave's queries rotated by -delta: the
+// lane's pairs (d, d + 64), d = 16 S4 + 8 g2 + e, with the block's
+// (cos, sin)(delta w_d) at byte 8 d of the phase row.  The rotated query is
+// kept as two bf16 terms, hi = bf16(x) and lo = bf16(x - hi) (about 16
+// significant bits): one rounding of a query is shared by every row of the
+// span, so a bf16-only copy would shift all of the block's scores
+// coherently, which long, peaked attention (large outlier key channels)
+// does not average out.
+template <int S4, int PHOFF>
+__device__ __forceinline__ void rotate_query_pair(unsigned qaddr, unsigned phaddr, bf16x8 qb[8], bf16x8 ql[8]) {
+  u32x4 x = lds_read16<S4 * 1024>(qaddr);
+  u32x4 y = lds_read16<(S4 + 4) * 1024>(qaddr);
+  u32x4 c0 = lds_read16<PHOFF + S4 * 128>(phaddr);
+  u32x4 c1 = lds_read16<PHOFF + S4 * 128 + 16>(phaddr);
+  u32x4 c2 = lds_read16<PHOFF + S4 * 128 + 32>(phaddr);
+  u32x4 c3 = lds_read16<PHOFF + S4 * 128 + 48>(phaddr);
+  asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(x), "+v"(y), "+v"(c0), "+v"(c1), "+v"(c2), "+v"(c3));
+  const u32x4 cs[4] = {c0, c1, c2, c3};
+  bf16x8 rx, ry, lx, ly;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const unsigned wx = x[e >> 1], wy = y[e >> 1];
+    const float xf = (e & 1) ? bf16_hi(wx) : bf16_lo(wx);
+    const float yf = (e & 1) ? bf16_hi(wy) : bf16_lo(wy);
+    const float co = __uint_as_float(cs[e >> 1][2 * (e & 1)]);
+    const float sn = __uint_as_float(cs[e >> 1][2 * (e & 1) + 1]);
+    const float xr = __builtin_fmaf(yf, sn, xf * co);
+    const float yr = __builtin_fmaf(-xf, sn, yf * co);
+    rx[e] = (__bf16)xr;
+    ry[e] = (__bf16)yr;
+    lx[e] = (__bf16)(xr - (float)rx[e]);
+    ly[e] = (__bf16)(yr - (float)ry[e]);
+  }
+  qb[S4] = rx;
+  qb[S4 + 4] = ry;
+  ql[S4] = lx;
+  ql[S4 + 4] = ly;
+}
+
+// qb (+ ql) <- the wave's queries rotated by -delta of the block whose phase
+// row is staged at PHOFF (rotate), or the queries themselves (ql unused).
+template <int PHOFF>
+__device__ __forceinline__ void requery(bool rotate, unsigned qaddr, unsigned phaddr, bf16x8 qb[8],
+                                        bf16x8 ql[8]) {
+  if (!rotate) {
+    KFrags f;
+    f.x[0] = lds_read16<0>(qaddr);
+    f.x[1] = lds_read16<1024>(qaddr);
+    f.x[2] = lds_read16<2048>(qaddr);
+    f.x[3] = lds_read16<3072>(qaddr);
+    f.x[4] = lds_read16<4096>(qaddr);
+    f.x[5] = lds_read16<5120>(qaddr);
+    f.x[6] = lds_read16<6144>(qaddr);
+    f.x[7] = lds_read16<7168>(qaddr);
+    kfrag_wait(f);
+#pragma unroll
+    for (int s = 0; s < 8; ++s) qb[s] = __builtin_bit_cast(bf16x8, f.x[s]);
+    return;
+  }
+  rotate_query_pair<0, PHOFF>(qaddr, phaddr, qb, ql);
+  rotate_query_pair<1, PHOFF>(qaddr, phaddr, qb, ql);
+  rotate_query_pair<2, PHOFF>(qaddr, phaddr, qb, ql);
+  rotate_query_pair<3, PHOFF>(qaddr, phaddr, qb, ql);
+}
+
+// S^T = K (hi + lo)^T for one 32-row block (SPLIT; else K hi^T): each key
+// fragment feeds both terms' products.  Four fragment registers: the second
+// half's reads are issued into them right behind the products that consume
+// the first half (an MFMA takes its A operand when it issues).
+template <int OFF, bool SPLIT>
+__device__ __forceinline__ void s_block4(const Col& c, const bf16x8 qb[8], const bf16x8 ql[8], f32x16& acc) {
+  u32x4 k4[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) k4[s] = lds_read16<OFF>(c.kaddr[s]);
+  asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(k4[0]), "+v"(k4[1]), "+v"(k4[2]), "+v"(k4[3]));
+  acc = f32x16{};
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, k4[s]), qb[s], acc, 0, 0, 0);
+    if (SPLIT)
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, k4[s]), ql[s], acc, 0, 0, 0);
+    k4[s] = lds_read16<OFF>(c.kaddr[s + 4]);
+  }
+  asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(k4[0]), "+v"(k4[1]), "+v"(k4[2]), "+v"(k4[3]));
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, k4[s]), qb[s + 4], acc, 0, 0, 0);
+    if (SPLIT)
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, k4[s]), ql[s + 4], acc, 0, 0, 0);
+  }
+}
+
+template <bool FUSED, bool PAIRED, bool QROT = false>
 __global__ __launch_bounds__(PAIRED ? 512 : 256, PAIRED ? 1 : 2) void attention_bf16_kernel(AttnArgs a) {
+  static_assert(!QROT || (FUSED && PAIRED), "query rotation is a paired fused mode");
   extern __shared__ __attribute__((aligned(1024))) char lds_all[];
   constexpr int G = PAIRED ? 2 : 1;           // work items per workgroup
   const int blk = xcd_remap(blockIdx.x, gridDim.x);
@@ -954,7 +1116,7 @@ __global__ __launch_bounds__(PAIRED ? 512 : 256, PAIRED ? 1 : 2) void attention_
   // both groups of a pair pass the same number of barriers
   const AttnWork w0 = a.work[G * blk];
   // the pair covers the same rows: one stream of copies shared by all 8 waves
-  const bool shared = PAIRED && !FUSED && w0.share_rows != 0;
+  const bool shared = QROT || (PAIRED && !FUSED && w0.share_rows != 0);
   int steps = T;
   if (PAIRED) {
     auto len = [](const AttnWork& x) { return x.tile_end - x.tile_begin - (x.gap_end - x.gap_begin); };
@@ -972,6 +1134,17 @@ __global__ __launch_bounds__(PAIRED ? 512 : 256, PAIRED ? 1 : 2) void attention_
   const unsigned paddr = lds_addr(smem) + 16 * ((threadIdx.x & 63) >> 5);
   TileLanes tl;
   tile_lanes(shared ? 2 * wave8 : 4 * wave, tl);
+  // query rotation: the un-rotated-by-delta queries and the phase rows
+  const unsigned qaddr = lds_addr(lds_all) + kQOff + wave8 * 8192 + (threadIdx.x & 63) * 16;
+  const unsigned phaddr = lds_addr(lds_all) + kPhOff + 64 * ((threadIdx.x & 63) >> 5);
+  int cur_ph = -1;   // qb (+ ql) hold the queries rotated back by this block's delta (-1: by none)
+  bf16x8 ql[8];      // low terms of the rotated queries (query rotation)
+  if constexpr (QROT) {
+#pragma unroll
+    for (int s = 0; s < 8; ++s)
+      *reinterpret_cast<u32x4*>(lds_all + kQOff + wave8 * 8192 + s * 1024 + (threadIdx.x & 63) * 16) =
+          __builtin_bit_cast(u32x4, qb[s]);
+  }
 
   f32x16 o[4];
 #pragma unroll
@@ -987,13 +1160,16 @@ __global__ __launch_bounds__(PAIRED ? 512 : 256, PAIRED ? 1 : 2) void attention_
   const int gap_at = __builtin_amdgcn_readfirstlane(gap > 0 ? w.gap_begin - tb : INT_MAX);
   auto tile_of = [&](int i) { return i >= gap_at ? tb + i + gap : tb + i; };
   FusedK fk;
+  int3 qsrc = make_int3(-1, -1, -1);   // rowsrc of the next tile to copy (query rotation)
 
   // copies of tile t into stage S (0 or 1)
   auto issue = [&](auto stage_c, int t) {
     constexpr int S = decltype(stage_c)::value;
     char* st = smem + S * kStageBytes;
     const int t0 = t * kAttnRowsPerTile;
-    if (FUSED) {
+    if (QROT) {
+      qrot_tile_to_lds(a, rq, w.head, t0, rows, qsrc, st, lds_all + kPhOff + S * 1024, wave8);
+    } else if (FUSED) {
       fused_k_load(a, rq, w.head, t0, rows, fk);
       fused_v_to_lds(a, rq, w.head, t0, rows, st + kTileBytes, wave);
     } else {
@@ -1020,12 +1196,23 @@ __global__ __launch_bounds__(PAIRED ? 512 : 256, PAIRED ? 1 : 2) void attention_
     const int k = 2 * (tile_base + t);
     return make_int2(tile_pos_c[k], tile_pos_c[k + 1]);
   };
+  // phase rows of tile t's two 32-row blocks (query rotation)
+  const __attribute__((address_space(4))) int* blk_ph_c = (const __attribute__((address_space(4))) int*)(a.blk_ph);
+  auto blocks_ph = [&](int t) {
+    if (!QROT) return make_int2(-1, -1);
+    const int k = 2 * (tile_base + t);
+    return make_int2(blk_ph_c[k], blk_ph_c[k + 1]);
+  };
   int2 tp_next = make_int2(INT_MAX, INT_MAX);
+  int2 bph_next = make_int2(-1, -1);
   if (T > 0) {
     tp_next = bounds(tile_of(0));
+    bph_next = blocks_ph(tile_of(0));
+    if (QROT) qsrc = qrot_src(a, rq, tile_of(0), rows, wave8);
     issue(std::integral_constant<int, 0>{}, tile_of(0));
+    if (QROT && T > 1) qsrc = qrot_src(a, rq, tile_of(1), rows, wave8);
   }
-  if (FUSED && T > 0) fused_k_store(a, fk, smem);
+  if (FUSED && !QROT && T > 0) fused_k_store(a, fk, smem);
   // step i: the group's tile tb + i sits in stage S (i even: 0); wait for its
   // copies, start the next tile's copies into the other stage, consume it
   auto step = [&](auto stage_c, int i) {
@@ -1036,20 +1223,42 @@ __global__ __launch_bounds__(PAIRED ? 512 : 256, PAIRED ? 1 : 2) void attention_
     const int t = tile_of(i);
     const bool more = i + 1 < T;
     const int2 tp = tp_next;
+    const int2 bph = bph_next;
     if (more) {
       const int tn = tile_of(i + 1);
       tp_next = bounds(tn);
+      bph_next = blocks_ph(tn);
       issue(std::integral_constant<int, 1 - S>{}, tn);
+      if (QROT && i + 2 < T) qsrc = qrot_src(a, rq, tile_of(i + 2), rows, wave8);
     }
     if (tp.x <= c.wq_max) {
       f32x16 sacc[2];
       bf16x8 pb[2][2];
-      s_product<S * kStageBytes>(c, qb, sacc);
+      if constexpr (QROT) {
+        if (bph.x != cur_ph) {
+          requery<S * 1024>(bph.x >= 0, qaddr, phaddr, qb, ql);
+          cur_ph = bph.x;
+        }
+        if (cur_ph >= 0)
+          s_block4<S * kStageBytes, true>(c, qb, ql, sacc[0]);
+        else
+          s_block4<S * kStageBytes, false>(c, qb, ql, sacc[0]);
+        if (bph.y != cur_ph) {
+          requery<S * 1024 + 512>(bph.y >= 0, qaddr, phaddr, qb, ql);
+          cur_ph = bph.y;
+        }
+        if (cur_ph >= 0)
+          s_block4<S * kStageBytes + 8192, true>(c, qb, ql, sacc[1]);
+        else
+          s_block4<S * kStageBytes + 8192, false>(c, qb, ql, sacc[1]);
+      } else {
+        s_product<S * kStageBytes>(c, qb, sacc);
+      }
       softmax_tile<S * kStageBytes + kPosOffset>(sacc, tp, paddr, t * kAttnRowsPerTile, rows, c, a.scale_log2,
                                                 m, o, lacc, pb);
       pv_product<S * kStageBytes>(c, pb, o, lacc);
     }
-    if (FUSED && more) fused_k_store(a, fk, smem + (1 - S) * kStageBytes);
+    if (FUSED && !QROT && more) fused_k_store(a, fk, smem + (1 - S) * kStageBytes);
   };
   for (int i = 0; i < steps; i += 2) {
     step(std::integral_constant<int, 0>{}, i);
@@ -1293,11 +1502,12 @@ hipError_t launch_attention_bf16(const AttnArgs& a, bool fused, hipStream_t s) {
   if (a.n_work <= 0) return hipSuccess;
   // dynamic LDS above 64 KB has to be allowed per kernel, once
   static const hipError_t attr = [] {
-    const void* fns[3] = {reinterpret_cast<const void*>(attention_bf16_kernel<true, true>),
+    const void* fns[4] = {reinterpret_cast<const void*>(attention_bf16_kernel<true, true>),
                           reinterpret_cast<const void*>(attention_bf16_kernel<false, true>),
-                          reinterpret_cast<const void*>(attention_bf16_kernel<true, false>)};
-    const int bytes[3] = {kAttnLdsBytes, kAttnLdsBytes, kGroupLdsBytes};
-    for (int i = 0; i < 3; ++i) {
+                          reinterpret_cast<const void*>(attention_bf16_kernel<true, false>),
+                          reinterpret_cast<const void*>(attention_bf16_kernel<true, true, true>)};
+    const int bytes[4] = {kAttnLdsBytes, kAttnLdsBytes, kGroupLdsBytes, kQrotLdsBytes};
+    for (int i = 0; i < 4; ++i) {
       hipError_t e = hipFuncSetAttribute(fns[i], hipFuncAttributeMaxDynamicSharedMemorySize, bytes[i]);
       if (e != hipSuccess) return e;
     }
@@ -1310,6 +1520,8 @@ hipError_t launch_attention_bf16(const AttnArgs& a, bool fused, hipStream_t s) {
   const unsigned pairs = unsigned((a.n_work + 1) / 2);
   if (!fused)
     hipLaunchKernelGGL((attention_bf16_kernel<false, true>), dim3(pairs), dim3(512), kAttnLdsBytes, s, a);
+  else if (a.qrot)
+    hipLaunchKernelGGL((attention_bf16_kernel<true, true, true>), dim3(pairs), dim3(512), kQrotLdsBytes, s, a);
   else if (a.paired)
     hipLaunchKernelGGL((attention_bf16_kernel<true, true>), dim3(pairs), dim3(512), kAttnLdsBytes, s, a);
   else

@@ -382,6 +382,49 @@ void build_attention_work(HostPlan* plan, int32_t kv_heads, int32_t group, int32
   plan->n_slots = slots;
 }
 
+void build_qrot_blocks(HostPlan* plan, bool keys_rotated, int32_t rows_per_tile) {
+  const int32_t half = rows_per_tile / 2;
+  const size_t nblk = size_t(plan->n_tiles) * 2;
+  plan->blk_ph.assign(nblk, -1);
+  plan->qrot_ok = false;
+  plan->qrot = false;
+  if (!keys_rotated) return;
+  std::vector<int32_t> delta(nblk, 0);
+  std::vector<char> set(nblk, 0);
+  bool ok = true;
+  auto mark = [&](size_t b, int32_t d, int32_t ph) {
+    if (!set[b]) {
+      set[b] = 1;
+      delta[b] = d;
+      plan->blk_ph[b] = ph;
+    } else if (delta[b] != d) {
+      ok = false;
+    }
+  };
+  for (const ReqRec& r : plan->reqs) {
+    const size_t b0 = size_t(r.tile_base) * 2;
+    for (int32_t i = r.span_begin; ok && i < r.span_end; ++i) {
+      const SpanRec& s = plan->spans[size_t(i)];
+      const int32_t r0 = s.dst_row - r.row_base;
+      for (int32_t b = r0 / half; b <= (r0 + s.n - 1) / half; ++b) mark(b0 + size_t(b), s.delta, s.delta != 0 ? i : -1);
+    }
+    if (ok && r.n_new > 0)
+      for (int32_t b = r.prefix_rows / half; b <= (r.prefix_rows + r.n_new - 1) / half; ++b) mark(b0 + size_t(b), 0, -1);
+    if (!ok) break;
+  }
+  plan->qrot_ok = ok;
+}
+
+void finish_qrot(HostPlan* plan) {
+  const std::vector<AttnWork>& w = plan->work;
+  bool shared = plan->qrot_ok && !w.empty() && (w.size() % 2) == 0;
+  for (size_t i = 0; shared && i < w.size(); i += 2) {
+    const bool empty = w[i].tile_end == w[i].tile_begin && w[i + 1].tile_end == w[i + 1].tile_begin;
+    shared = (w[i].share_rows && w[i + 1].share_rows) || empty;
+  }
+  plan->qrot = shared;
+}
+
 void build_decode(const HostPlan& plan, int32_t kv_heads, int32_t step, int32_t rows_per_tile,
                   int32_t target_items, int32_t max_split, int32_t min_tiles_per_split, DecodePlan* out) {
   const int32_t batch = plan.batch;

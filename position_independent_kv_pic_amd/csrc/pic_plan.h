@@ -101,6 +101,13 @@ struct HostPlan {
   int32_t n_split_out = 1;          // partials left for merge_kernel
   int32_t n_split_wg = 1;           // splits in different workgroups, merged by the last (1: none)
   int32_t n_slots = 0;              // merge counters (column blocks) when n_split_wg > 1
+  // Query rotation (fused variant): per 32-row half of every attention tile,
+  // the phase-table row of the one rotation all its rows share (-1: none).
+  // qrot_ok: every half has a single rotation (keys stored rotated);
+  // qrot: also every workgroup's two work items share their rows.
+  std::vector<int32_t> blk_ph;
+  bool qrot_ok = false;
+  bool qrot = false;
 };
 
 // Validation helpers return PIC_OK or an error code and fill `err`.
@@ -164,5 +171,16 @@ AttnSplit choose_attention_split(const HostPlan& plan, int32_t kv_heads, int32_t
 // n_split_out, n_split_wg and n_slots.
 void build_attention_work(HostPlan* plan, int32_t kv_heads, int32_t group, int32_t cols_per_wg,
                           int32_t rows_per_tile, AttnSplit split);
+
+// Fill blk_ph and qrot_ok (see HostPlan): a score against a key rotated by
+// delta equals the score of the query rotated by -delta against the stored
+// key, so a 32-row block whose rows share one delta needs one rotated copy of
+// each query instead of rotated keys.  New-token rows (stored rotated at
+// their positions) count as delta 0.
+void build_qrot_blocks(HostPlan* plan, bool keys_rotated, int32_t rows_per_tile);
+
+// After build_attention_work: qrot = qrot_ok and every item pair shares its
+// rows (or is empty).
+void finish_qrot(HostPlan* plan);
 
 }  // namespace pic

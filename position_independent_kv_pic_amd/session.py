@@ -9,7 +9,8 @@ from typing import Optional
 
 import numpy as np
 
-from .binding import (DEFER_GATHER, DRY_RUN, PLAN_ONLY, VARIANT_MATERIALIZED, Plan, Pool, model_struct)
+from .binding import (DEFER_GATHER, DRY_RUN, PLAN_ONLY, QUERY_ROTATION, VARIANT_MATERIALIZED, Plan, Pool,
+                      model_struct)
 
 
 class Session:
@@ -43,13 +44,15 @@ class Session:
         self.asm_v = t.empty(shape, dtype=self.tdtype, device=self.device)
         self.capacity = max(rows, 1)
 
-    def assemble(self, span_ptr, spans, new_ptr, new_pos=None, plan_only: bool = False, defer: bool = False):
+    def assemble(self, span_ptr, spans, new_ptr, new_pos=None, plan_only: bool = False, defer: bool = False,
+                 query_rotation: bool = False):
         d = self.plan_host(span_ptr, spans, new_ptr, new_pos)
         self.ensure_capacity(d["rows"])
-        flags = (PLAN_ONLY if plan_only else 0) | (DEFER_GATHER if defer else 0)
+        flags = ((PLAN_ONLY if plan_only else 0) | (DEFER_GATHER if defer else 0) |
+                 (QUERY_ROTATION if query_rotation else 0))
         self.plan.assemble(span_ptr, spans, new_ptr, new_pos, self.asm_k, self.asm_v, self.capacity,
                            flags, self.torch.cuda.current_stream())
-        return d
+        return self.plan.summary()
 
     def plan_host(self, span_ptr, spans, new_ptr, new_pos=None) -> dict:
         """Validate and plan on the host only (no device work)."""

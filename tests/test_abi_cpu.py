@@ -152,6 +152,45 @@ def test_deferred_gather_flags_and_states():
     pool.release()
 
 
+def _qrot_expected(wl) -> int:
+    """Independent statement of when query rotation applies: keys stored
+    rotated and, in every request, each 32-row half of a 64-row attention
+    tile holds rows of a single re-rotation delta (new-token rows count as
+    delta 0)."""
+    if wl.keys != "rotated":
+        return 0
+    for r in wl.requests:
+        planned = orc.plan_spans([tuple(int(x) for x in sp) for sp in r.spans], wl.pool.chunk_orig)
+        deltas = [p.delta for p in planned for _ in range(p.length)] + [0] * r.n_new
+        for b0 in range(0, len(deltas), 32):
+            if len(set(deltas[b0:b0 + 32])) > 1:
+                return 0
+    return 1
+
+
+@pytest.mark.parametrize("name", W.FULL_SIZE + W.REDUCED + W.REDUCED_NEXT +
+                         ("turborag_b16_unrot", "turborag_b16_composite"))
+def test_query_rotation_flag_and_eligibility(name):
+    wl = W.get(name)
+    pool = _pool(wl)
+    plan = B.Plan(pool)
+    sp, spans, npt, npos = wl.span_ptr(), wl.spans_flat(), wl.new_ptr(), wl.new_pos_flat()
+    # the option belongs to plan-only batches (variant F)
+    assert _err(lambda: plan.assemble(sp, spans, npt, npos, None, None, 2 ** 40,
+                                      B.DRY_RUN | B.QUERY_ROTATION)) == "PIC_EINVAL"
+    plan.assemble(sp, spans, npt, npos, None, None, 2 ** 40, B.DRY_RUN | B.PLAN_ONLY | B.QUERY_ROTATION)
+    got = plan.summary()["fused_query_rotation"]
+    if wl.model.dtype == "bf16":
+        assert got == _qrot_expected(wl), name
+    else:
+        assert got == 0
+    # never without the option
+    plan.assemble(sp, spans, npt, npos, None, None, 2 ** 40, B.DRY_RUN | B.PLAN_ONLY)
+    assert plan.summary()["fused_query_rotation"] == 0
+    plan.release()
+    pool.release()
+
+
 def test_key_storage_is_validated():
     wl = W.get("tiny_f32")
     p = wl.pool
