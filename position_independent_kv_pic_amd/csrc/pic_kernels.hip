@@ -678,6 +678,158 @@ __device__ __forceinline__ void pv_product(const Col& c, const bf16x8 pb[2][2], 
   }
 }
 
+// ---- one tile, pipelined by 32-row block ----
+// S of block 1 runs on the matrix core while block 0's probabilities are
+// formed, and block 0's PV while block 1's are (independent work in one basic
+// block, which the scheduler interleaves).  A raise of the reference maximum
+// by block 0 rescales O and the sum before block 0's PV; one by block 1
+// rescales them after it, since block 0's probabilities are relative to the
+// old maximum.  Each O element accumulates its products in the same order as
+// the unpipelined tile.
+
+__device__ __forceinline__ float max16(const f32x16& a) {
+  const float t0 = max3(a[0], a[1], a[2]), t1 = max3(a[3], a[4], a[5]), t2 = max3(a[6], a[7], a[8]);
+  const float t3 = max3(a[9], a[10], a[11]), t4 = max3(a[12], a[13], a[14]);
+  return fmaxf(max3(t0, t1, t2), max3(t3, t4, a[15]));
+}
+
+// Mask the scores of 32-row block KB of a tile (rows later than the lane's
+// query, or past the request's end); positions as in softmax_tile.
+template <int POFF, int KB>
+__device__ __forceinline__ void mask_block(f32x16& sc, unsigned paddr, int r0, int rows, const Col& c) {
+  const int g2 = (threadIdx.x & 63) >> 5;
+  constexpr int B = POFF + 128 * KB;
+  constexpr unsigned EXTRA = B + 96 > 65535 ? unsigned(B) : 0u;
+  constexpr int PO = int(B - EXTRA);
+  const unsigned pa = paddr + EXTRA;
+  i32x4 p[4];
+  p[0] = lds_read_i4<PO>(pa);
+  p[1] = lds_read_i4<PO + 32>(pa);
+  p[2] = lds_read_i4<PO + 64>(pa);
+  p[3] = lds_read_i4<PO + 96>(pa);
+  asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(p[0]), "+v"(p[1]), "+v"(p[2]), "+v"(p[3]));
+#pragma unroll
+  for (int qq = 0; qq < 4; ++qq) {
+    const int r4 = 32 * KB + 8 * qq + 4 * g2;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (p[qq][e] > c.qpos || r0 + r4 + e >= rows) sc[4 * qq + e] = -INFINITY;
+  }
+}
+
+// The block's probabilities relative to the reference maximum mb.
+__device__ __forceinline__ void block_probs(const f32x16& sc, float scale_log2, float mb, bf16x8 pb[2]) {
+#pragma unroll
+  for (int i = 0; i < 16; ++i)
+    pb[i >> 3][i & 7] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(sc[i], scale_log2, -mb));
+}
+
+// O^T += V^T P^T and the denominator for 32-row block KB of the tile in the
+// stage at byte offset STAGE: per 32-wide d block, 4 transpose reads (double
+// buffered across d blocks) and 2 MFMAs.
+template <int STAGE, int KB>
+__device__ __forceinline__ void pv_block(const Col& c, const bf16x8 pb[2], f32x16 o[4], f32x16& lacc) {
+  const bf16x8 ones = __builtin_bit_cast(bf16x8, u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
+  constexpr int OFF = STAGE + 8192 * KB;
+  s16x4 vb[2][4];
+  auto rd = [&](int db, s16x4* x) {
+    x[0] = tr_read<OFF>(c.vaddr[db][0]);
+    x[1] = tr_read<OFF>(c.vaddr[db][1]);
+    x[2] = tr_read<OFF + 4096>(c.vaddr[db][0]);
+    x[3] = tr_read<OFF + 4096>(c.vaddr[db][1]);
+  };
+  auto wt = [](s16x4* x) {
+    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]));
+  };
+  rd(0, vb[0]);
+  lacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones, pb[0], lacc, 0, 0, 0);
+  lacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones, pb[1], lacc, 0, 0, 0);
+  wt(vb[0]);
+#pragma unroll
+  for (int db = 0; db < 4; ++db) {
+    s16x4* cur = vb[db & 1];
+    if (db + 1 < 4) rd(db + 1, vb[(db + 1) & 1]);
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      const s16x8 xv = __builtin_shufflevector(cur[2 * s2], cur[2 * s2 + 1], 0, 1, 2, 3, 4, 5, 6, 7);
+      o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, xv), pb[s2], o[db], 0, 0, 0);
+    }
+    if (db + 1 < 4) wt(vb[(db + 1) & 1]);
+  }
+}
+
+// The reference-maximum update of a block whose scaled maximum is mt: lanes
+// whose maximum exceeds the reference by more than the slack raise it; the
+// returned factor rescales what was accumulated against the old reference
+// (1 where nothing is raised; a lane whose maximum is still -inf does not
+// raise, so it never forms exp2(-inf - -inf)).
+__device__ __forceinline__ float raise_ref(float mt, float& m, bool& raise) {
+  raise = mt > m + kRescaleSlack;
+  const float alpha = raise ? __builtin_amdgcn_exp2f(m - mt) : 1.0f;
+  m = raise ? mt : m;
+  return alpha;
+}
+
+// The whole tile in the stage at byte offset STAGE (see above).
+template <int STAGE>
+__device__ __forceinline__ void tile_pipelined(const Col& c, const bf16x8 qb[8], int2 bnd, unsigned paddr, int r0,
+                                               int rows, float scale_log2, float& m, f32x16 o[4], f32x16& lacc) {
+  constexpr int POFF = STAGE + kPosOffset;
+  const bool masked = bnd.y > c.wq_min;
+  // block 0's key fragments, then block 1's into the same registers (an
+  // MFMA takes its A operand when it issues).  An asm read and the wait that
+  // publishes its result enclose straight-line code only: the compiler
+  // treats the result as available at the read and may copy it anywhere
+  // before the wait (a branch in between would allow that).
+  KFrags kf;
+#pragma unroll
+  for (int s = 0; s < 8; ++s) kf.x[s] = lds_read16<STAGE>(c.kaddr[s]);
+  kfrag_wait(kf);
+  f32x16 s0 = f32x16{};
+#pragma unroll
+  for (int s = 0; s < 8; ++s)
+    s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kf.x[s]), qb[s], s0, 0, 0, 0);
+  if (masked) mask_block<POFF, 0>(s0, paddr, r0, rows, c);
+#pragma unroll
+  for (int s = 0; s < 8; ++s) kf.x[s] = lds_read16<STAGE + 8192>(c.kaddr[s]);
+  bool raise0;
+  const float alpha0 = raise_ref(max_halves(max16(s0)) * scale_log2, m, raise0);
+  kfrag_wait(kf);
+  // block 1's S on the matrix core while block 0's probabilities form
+  f32x16 s1 = f32x16{};
+#pragma unroll
+  for (int s = 0; s < 8; ++s)
+    s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kf.x[s]), qb[s], s1, 0, 0, 0);
+  bf16x8 p0[2];
+  block_probs(s0, scale_log2, m == -INFINITY ? 0.0f : m, p0);
+  // (kept in this block rather than sunk to their use in block 0's PV)
+  asm volatile("" ::"v"(p0[0]), "v"(p0[1]));
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+    __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);   // then five VALU
+  }
+  if (__builtin_amdgcn_ballot_w64(raise0)) {
+#pragma unroll
+    for (int db = 0; db < 4; ++db) o[db] *= alpha0;
+    lacc *= alpha0;
+  }
+  if (masked) mask_block<POFF, 1>(s1, paddr, r0, rows, c);
+  bool raise1;
+  const float alpha1 = raise_ref(max_halves(max16(s1)) * scale_log2, m, raise1);
+  // block 0's PV while block 1's probabilities form
+  pv_block<STAGE, 0>(c, p0, o, lacc);
+  bf16x8 p1[2];
+  block_probs(s1, scale_log2, m == -INFINITY ? 0.0f : m, p1);
+  asm volatile("" ::"v"(p1[0]), "v"(p1[1]));
+  if (__builtin_amdgcn_ballot_w64(raise1)) {
+#pragma unroll
+    for (int db = 0; db < 4; ++db) o[db] *= alpha1;
+    lacc *= alpha1;
+  }
+  pv_block<STAGE, 1>(c, p1, o, lacc);
+}
+
 // Write a column's result: a partial (unnormalised O, reference maximum m,
 // sum lt) at partial index `part` for merge_kernel, or the normalised bf16
 // output.
@@ -1232,9 +1384,9 @@ __global__ __launch_bounds__(PAIRED ? 512 : 256, PAIRED ? 1 : 2) void attention_
       if (QROT && i + 2 < T) qsrc = qrot_src(a, rq, tile_of(i + 2), rows, wave8);
     }
     if (tp.x <= c.wq_max) {
-      f32x16 sacc[2];
-      bf16x8 pb[2][2];
       if constexpr (QROT) {
+        f32x16 sacc[2];
+        bf16x8 pb[2][2];
         if (bph.x != cur_ph) {
           requery<S * 1024>(bph.x >= 0, qaddr, phaddr, qb, ql);
           cur_ph = bph.x;
@@ -1251,12 +1403,12 @@ __global__ __launch_bounds__(PAIRED ? 512 : 256, PAIRED ? 1 : 2) void attention_
           s_block4<S * kStageBytes + 8192, true>(c, qb, ql, sacc[1]);
         else
           s_block4<S * kStageBytes + 8192, false>(c, qb, ql, sacc[1]);
+        softmax_tile<S * kStageBytes + kPosOffset>(sacc, tp, paddr, t * kAttnRowsPerTile, rows, c, a.scale_log2,
+                                                  m, o, lacc, pb);
+        pv_product<S * kStageBytes>(c, pb, o, lacc);
       } else {
-        s_product<S * kStageBytes>(c, qb, sacc);
+        tile_pipelined<S * kStageBytes>(c, qb, tp, paddr, t * kAttnRowsPerTile, rows, a.scale_log2, m, o, lacc);
       }
-      softmax_tile<S * kStageBytes + kPosOffset>(sacc, tp, paddr, t * kAttnRowsPerTile, rows, c, a.scale_log2,
-                                                m, o, lacc, pb);
-      pv_product<S * kStageBytes>(c, pb, o, lacc);
     }
     if (FUSED && !QROT && more) fused_k_store(a, fk, smem + (1 - S) * kStageBytes);
   };
