@@ -53,6 +53,9 @@ def parse():
     ap.add_argument("--layouts", type=int, default=8, help="pre-generated batch layouts to cycle through")
     ap.add_argument("--cpu-seconds", type=float, default=20.0, help="time budget of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--values-in-pool", action="store_true",
+                    help="variant M: gather keys only and let attention read the prefix values in the pool "
+                         "(the same bits)")
     ap.add_argument("--pipelined", action="store_true",
                     help="gather layer l+1 on a second stream while layer l's attention runs")
     ap.add_argument("--host-pool", action="store_true",
@@ -227,8 +230,8 @@ def main():
     import torch
     import workloads as W
     from workloads.device import open_workload
-    from position_independent_kv_pic_amd import (DEFER_GATHER, PLAN_ONLY, QUERY_ROTATION, VARIANT_FUSED,
-                                                  VARIANT_MATERIALIZED)
+    from position_independent_kv_pic_amd import (DEFER_GATHER, PLAN_ONLY, QUERY_ROTATION, VALUES_IN_POOL,
+                                                  VARIANT_FUSED, VARIANT_MATERIALIZED)
 
     assert torch.cuda.is_available(), "bench.py needs a ROCm GPU"
     variant = VARIANT_MATERIALIZED if args.variant == "M" else VARIANT_FUSED
@@ -249,6 +252,9 @@ def main():
     stream = torch.cuda.current_stream()
     plan = sess.plan
     plan_flag = 0 if args.variant == "M" else PLAN_ONLY | (QUERY_ROTATION if args.variant == "FQ" else 0)
+    vpool = args.values_in_pool and args.variant == "M"
+    if vpool:
+        plan_flag |= VALUES_IN_POOL
 
     side = torch.cuda.Stream() if args.pipelined else None
 
@@ -256,7 +262,8 @@ def main():
         sp, spans, npt, npos, n = tables[i % len(tables)]
         if args.pipelined and variant != VARIANT_FUSED:
             # per-layer gathers on a second stream, one layer ahead of attention
-            plan.assemble(sp, spans, npt, npos, sess.asm_k, sess.asm_v, sess.capacity, DEFER_GATHER, stream)
+            plan.assemble(sp, spans, npt, npos, sess.asm_k, sess.asm_v, sess.capacity,
+                          DEFER_GATHER | (VALUES_IN_POOL if vpool else 0), stream)
             plan.gather_layers(0, 1, side)
             for l in range(m.layers):
                 if l + 1 < m.layers:
@@ -315,6 +322,8 @@ def main():
     del src, dst
 
     asm_bytes = sum(W.assembly_bytes(w) for w in (wls * args.steps)[:args.steps]) / args.steps
+    if vpool:
+        asm_bytes /= 2   # keys only
     attn_flops = sum(W.attention_flops(w) for w in (wls * args.steps)[:args.steps]) / args.steps
     ms_step = total_ms / args.steps
     n_g, t_g = kt[KERNEL_GATHER]
@@ -345,6 +354,7 @@ def main():
         "config": {"workload": wl.name, "model_shape": f"L{m.layers} Hq{m.q_heads} Hkv{m.kv_heads} d{m.head_dim}",
                    "batch": wl.batch, "prefix_rows_per_step": wl.prefix_rows_total,
                    "new_tokens_per_step": wl.n_new_total, "variant": args.variant,
+                   "values": "read in the pool by attention" if vpool else "gathered with the keys",
                    "layouts": args.layouts, "parallelism": "none (1 GPU)",
                    "pipelined": bool(args.pipelined), "pool": "pinned host" if args.host_pool else "HBM"},
         "assembly_GBps": None if asm_gbps is None else round(asm_gbps, 1),

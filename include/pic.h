@@ -105,6 +105,7 @@ typedef struct {
 #define PIC_ASSEMBLE_DRY_RUN   2     /* validate and plan on the host only; touch no device */
 #define PIC_ASSEMBLE_DEFER_GATHER 4  /* plan now; gather layers later with pic_gather_layers */
 #define PIC_ASSEMBLE_QUERY_ROTATION 8  /* with PLAN_ONLY: variant F may rotate queries (pic_query_prefill) */
+#define PIC_ASSEMBLE_VALUES_IN_POOL 16 /* gather keys only; prefix values are read in the pool (below) */
 
 /* pic_query_prefill variants */
 #define PIC_VARIANT_MATERIALIZED 0  /* read keys/values from the assembled buffers */
@@ -194,7 +195,14 @@ pic_status pic_plan_release(pic_plan* plan);
  *                  of the model dtype, 16-byte aligned (may be NULL with DRY_RUN)
  *   asm_rows_capacity  rows per (layer, kv head) plane
  *   flags          0, PIC_ASSEMBLE_PLAN_ONLY (optionally | PIC_ASSEMBLE_QUERY_ROTATION),
- *                  PIC_ASSEMBLE_DRY_RUN or PIC_ASSEMBLE_DEFER_GATHER
+ *                  PIC_ASSEMBLE_DRY_RUN or PIC_ASSEMBLE_DEFER_GATHER; 0 and
+ *                  DEFER_GATHER may add PIC_ASSEMBLE_VALUES_IN_POOL (bf16,
+ *                  head_dim 128): the gather then writes keys only, leaves
+ *                  the prefix rows of asm_v untouched, and the materialised
+ *                  variant (prefill and decode) copies the prefix values
+ *                  from the pool pages as it streams them (a value is moved
+ *                  unchanged, so the results are the same bits); new-token
+ *                  values are still appended to asm_v
  *   stream         hipStream_t
  *
  * Row layout: request b owns rows [row_base_b, row_base_b + prefix_b + n_new_b)
@@ -317,6 +325,7 @@ typedef struct {
   int32_t max_position;    /* largest position of any row */
   int32_t materialized;    /* 1 if the prefix rows were gathered */
   int32_t fused_query_rotation;  /* 1 if PIC_VARIANT_FUSED rotates queries instead of keys (below) */
+  int32_t values_in_pool;  /* 1 if the batch was assembled with PIC_ASSEMBLE_VALUES_IN_POOL */
 } pic_plan_summary;
 
 pic_status pic_plan_get_summary(const pic_plan* plan, pic_plan_summary* out);

@@ -25,6 +25,7 @@ PLAN_ONLY = 1
 DRY_RUN = 2
 DEFER_GATHER = 4
 QUERY_ROTATION = 8
+VALUES_IN_POOL = 16
 VARIANT_MATERIALIZED = 0
 VARIANT_FUSED = 1
 
@@ -63,7 +64,8 @@ class PicPlanSummary(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("n_spans", ctypes.c_int32),
                 ("prefix_rows", ctypes.c_int64), ("new_rows", ctypes.c_int64),
                 ("rows", ctypes.c_int64), ("max_position", ctypes.c_int32),
-                ("materialized", ctypes.c_int32), ("fused_query_rotation", ctypes.c_int32)]
+                ("materialized", ctypes.c_int32), ("fused_query_rotation", ctypes.c_int32),
+                ("values_in_pool", ctypes.c_int32)]
 
 
 def library_path() -> str:

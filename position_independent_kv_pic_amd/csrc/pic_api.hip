@@ -54,6 +54,7 @@ struct pic_plan {
   pic::HostPlan hp;
   bool has_batch = false;
   bool materialized = false;         // every layer's prefix rows are gathered
+  bool values_in_pool = false;       // only keys are gathered; attention reads prefix values in the pool
   std::vector<char> gathered;        // per layer: prefix rows gathered into the planes
   std::vector<hipEvent_t> layer_ev;  // per layer: completion of a deferred gather
   std::vector<char> layer_ev_live;   // per layer: layer_ev was recorded for this batch
@@ -275,6 +276,7 @@ pic_status gather_layers(pic_plan* p, int32_t l0, int32_t l1, hipStream_t s, boo
     ga.planes_per_block = 4;   // 2, 4, 8, 16 measured: 4 is 3% faster than 8 on turborag_b16
     ga.plane_begin = l0 * pi.m.kv_heads;
     ga.plane_end = l1 * pi.m.kv_heads;
+    ga.values = p->values_in_pool ? 0 : 1;
     hipError_t e = pic::launch_gather(pi.m.dtype, pi.m.head_dim, ga, s);
     if (e != hipSuccess) return device_error(p, e, "gather kernel");
   }
@@ -406,12 +408,17 @@ pic_status pic_assemble(pic_plan* p, int32_t batch, const int32_t* span_ptr, con
   if (!p) return set_err(PIC_EINVAL, "plan is NULL");
   if (p->failed) return set_err(PIC_ESTATE, "plan is unusable after a device error");
   if (flags & ~(PIC_ASSEMBLE_PLAN_ONLY | PIC_ASSEMBLE_DRY_RUN | PIC_ASSEMBLE_DEFER_GATHER |
-                PIC_ASSEMBLE_QUERY_ROTATION))
+                PIC_ASSEMBLE_QUERY_ROTATION | PIC_ASSEMBLE_VALUES_IN_POOL))
     return set_err(PIC_EINVAL, "unknown flags 0x%x", flags);
   if ((flags & PIC_ASSEMBLE_PLAN_ONLY) && (flags & PIC_ASSEMBLE_DEFER_GATHER))
     return set_err(PIC_EINVAL, "PIC_ASSEMBLE_PLAN_ONLY and PIC_ASSEMBLE_DEFER_GATHER exclude each other");
   if ((flags & PIC_ASSEMBLE_QUERY_ROTATION) && !(flags & PIC_ASSEMBLE_PLAN_ONLY))
     return set_err(PIC_EINVAL, "PIC_ASSEMBLE_QUERY_ROTATION needs PIC_ASSEMBLE_PLAN_ONLY");
+  const bool values_in_pool = (flags & PIC_ASSEMBLE_VALUES_IN_POOL) != 0;
+  if (values_in_pool && (flags & PIC_ASSEMBLE_PLAN_ONLY))
+    return set_err(PIC_EINVAL, "PIC_ASSEMBLE_VALUES_IN_POOL applies to a gathered batch, not PLAN_ONLY");
+  if (values_in_pool && !(p->pool->info.m.dtype == PIC_BF16 && p->pool->info.m.head_dim == 128))
+    return set_err(PIC_EUNSUPPORTED, "PIC_ASSEMBLE_VALUES_IN_POOL is implemented for bf16 with head_dim 128");
   const bool defer = (flags & PIC_ASSEMBLE_DEFER_GATHER) != 0;
   const bool dry = (flags & PIC_ASSEMBLE_DRY_RUN) != 0;
   const bool plan_only = (flags & PIC_ASSEMBLE_PLAN_ONLY) != 0;
@@ -448,6 +455,7 @@ pic_status pic_assemble(pic_plan* p, int32_t batch, const int32_t* span_ptr, con
     p->hp = std::move(hp);
     p->has_batch = true;
     p->materialized = false;
+    p->values_in_pool = values_in_pool;
     p->asm_k = p->asm_v = nullptr;
     p->cap = asm_rows_capacity;
     return ok();
@@ -462,6 +470,7 @@ pic_status pic_assemble(pic_plan* p, int32_t batch, const int32_t* span_ptr, con
 
   p->hp = std::move(hp);
   p->has_batch = false;
+  p->values_in_pool = values_in_pool;
   p->gathered.assign(size_t(pi.m.layers), 0);
   p->layer_ev_live.assign(size_t(pi.m.layers), 0);
   p->asm_k = static_cast<char*>(asm_k);
@@ -663,6 +672,7 @@ pic_status pic_query_prefill(pic_plan* p, int32_t layer, const void* q, const vo
       aa.page_tokens = pi.page_tokens;
       aa.kv_heads = m.kv_heads;
       aa.qrot = fused && h.qrot ? 1 : 0;
+      aa.v_pool = !fused && p->values_in_pool ? 1 : 0;
       aa.blk_ph = reinterpret_cast<const int32_t*>(p->ws + p->off_blk_ph);
       aa.phase32 = reinterpret_cast<const float2*>(p->ws + p->off_phase32);
       e = pic::launch_attention_bf16(aa, fused, s);
@@ -839,6 +849,7 @@ pic_status pic_decode_layer(pic_plan* p, int32_t layer, int32_t step, const void
     aa.sml = nullptr;
     aa.decode = 1;
     aa.qrot = 0;
+    aa.v_pool = !fused && p->values_in_pool ? 1 : 0;
     aa.blk_ph = nullptr;
     aa.phase32 = nullptr;
     aa.scale_log2 = float(1.4426950408889634 / std::sqrt(double(m.head_dim)));
@@ -871,6 +882,7 @@ pic_status pic_plan_get_summary(const pic_plan* p, pic_plan_summary* out) {
   out->max_position = p->hp.max_position;
   out->materialized = p->materialized ? 1 : 0;
   out->fused_query_rotation = p->hp.qrot ? 1 : 0;
+  out->values_in_pool = p->values_in_pool ? 1 : 0;
   return ok();
 }
 

@@ -47,6 +47,7 @@ struct GatherArgs {
   int32_t n_spans, page_shift, page_tokens, layers, kv_heads, planes_per_block;
   int32_t per_position;     // keys stored un-rotated: rotate each row by its new position
   int32_t plane_begin, plane_end;  // (layer, kv head) planes l * Hkv + h to gather
+  int32_t values;           // 0: keys only (values stay in the pool, attention reads them there)
 };
 
 struct PrologueArgs {
@@ -99,6 +100,9 @@ struct AttnArgs {
   // block's delta
   int32_t qrot;
   const int32_t* blk_ph;    // [2 n_tiles]: phase-table row of each 32-row block (-1: none)
+  // assembled-plane variant with values left in the pool: prefix rows' values
+  // are copied from the pool pages (through rowsrc), the rest from v_plane
+  int32_t v_pool;
   const float2* phase32;    // [phase_rows][64]: (cos, sin) in fp32
 };
 

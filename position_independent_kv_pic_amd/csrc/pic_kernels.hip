@@ -241,7 +241,7 @@ __global__ __launch_bounds__(256) void plan_tiles_kernel(PlanArgs a) {
 // of the second half, so the half-split rotation pairs stay in one lane.  A
 // block covers 256 / LPR rows of the span table and `planes_per_block`
 // (layer, kv head) planes, reusing each row's source lookup and phases.
-template <bool BF16, int D>
+template <bool BF16, int D, bool VALUES>
 __global__ __launch_bounds__(256) void gather_kernel(GatherArgs a) {
   constexpr int ES = BF16 ? 2 : 4;
   constexpr int EPV = 16 / ES;
@@ -275,7 +275,7 @@ __global__ __launch_bounds__(256) void gather_kernel(GatherArgs a) {
   const int64_t plane_stride = int64_t(a.page_tokens) * RB;  // one (layer, K/V, head) run
   char* __restrict__ ak = a.asm_k;
   char* __restrict__ av = a.asm_v;
-  // two planes per iteration: all eight loads are in flight before any store
+  // two planes per iteration: all loads are in flight before any store
   for (int pl = p0; pl < p1; pl += 2) {
     const bool two = pl + 1 < p1;
     u32x4 k0[2], k1[2], v0[2], v1[2];
@@ -288,8 +288,10 @@ __global__ __launch_bounds__(256) void gather_kernel(GatherArgs a) {
       const char* vs = ks + int64_t(a.kv_heads) * plane_stride;
       k0[q] = ld16(ks + j * 16);
       k1[q] = ld16(ks + RB / 2 + j * 16);
-      v0[q] = ld16(vs + j * 16);
-      v1[q] = ld16(vs + RB / 2 + j * 16);
+      if (VALUES) {
+        v0[q] = ld16(vs + j * 16);
+        v1[q] = ld16(vs + RB / 2 + j * 16);
+      }
     }
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
@@ -298,8 +300,10 @@ __global__ __launch_bounds__(256) void gather_kernel(GatherArgs a) {
       if (rot) rotate_vec<BF16>(k0[q], k1[q], ph);
       st16(ak + off + j * 16, k0[q]);
       st16(ak + off + RB / 2 + j * 16, k1[q]);
-      st16(av + off + j * 16, v0[q]);
-      st16(av + off + RB / 2 + j * 16, v1[q]);
+      if (VALUES) {
+        st16(av + off + j * 16, v0[q]);
+        st16(av + off + RB / 2 + j * 16, v1[q]);
+      }
     }
   }
 }
@@ -1250,9 +1254,28 @@ __device__ __forceinline__ void s_block4(const Col& c, const bf16x8 qb[8], const
   }
 }
 
-template <bool FUSED, bool PAIRED, bool QROT = false>
+// Values left in the pool (assembled keys, pooled values): copy NB row
+// blocks (b0 .. b0 + NB - 1, 4 rows each) of tile t0's values into LDS, the
+// lane's row i from pool slot slots[i] (prefix rows) or the planes (the rest),
+// granules swizzled as the transpose reads expect.
+template <int NB>
+__device__ __forceinline__ void vpool_to_lds(const AttnArgs& a, const ReqRec& rq, int head, int t0, int rows,
+                                             const int* slots, char* lds, int b0) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int i = 0; i < NB; ++i) {
+    const int r = (b0 + i) * 4 + (lane >> 4);
+    const int rr = min(t0 + r, rows - 1);
+    const char* row = qrot_row(a, rq, head, rr, slots[i], true);
+    __builtin_amdgcn_global_load_lds(row + ((lane & 15) ^ v_swz(r)) * 16, (lds_void_ptr)(lds + (b0 + i) * 1024),
+                                     16, 0, 0);
+  }
+}
+
+template <bool FUSED, bool PAIRED, bool QROT = false, bool VPOOL = false>
 __global__ __launch_bounds__(PAIRED ? 512 : 256, PAIRED ? 1 : 2) void attention_bf16_kernel(AttnArgs a) {
   static_assert(!QROT || (FUSED && PAIRED), "query rotation is a paired fused mode");
+  static_assert(!VPOOL || (!FUSED && PAIRED), "pooled values are read by the assembled-plane variant");
   extern __shared__ __attribute__((aligned(1024))) char lds_all[];
   constexpr int G = PAIRED ? 2 : 1;           // work items per workgroup
   const int blk = xcd_remap(blockIdx.x, gridDim.x);
@@ -1313,6 +1336,18 @@ __global__ __launch_bounds__(PAIRED ? 512 : 256, PAIRED ? 1 : 2) void attention_
   auto tile_of = [&](int i) { return i >= gap_at ? tb + i + gap : tb + i; };
   FusedK fk;
   int3 qsrc = make_int3(-1, -1, -1);   // rowsrc of the next tile to copy (query rotation)
+  // pooled values: pool slots of the lane's value rows in the next tile to
+  // copy (-1: not a prefix row), fetched a step ahead
+  int vslot[4] = {-1, -1, -1, -1};
+  auto vpool_src = [&](int t) {
+    const int b0 = shared ? 2 * wave8 : 4 * wave;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (i >= 2 && shared) break;
+      const int rr = min(t * kAttnRowsPerTile + (b0 + i) * 4 + int((threadIdx.x & 63) >> 4), rows - 1);
+      vslot[i] = rr < rq.prefix_rows ? a.rowsrc[rq.row_base + rr].x : -1;
+    }
+  };
 
   // copies of tile t into stage S (0 or 1)
   auto issue = [&](auto stage_c, int t) {
@@ -1327,10 +1362,16 @@ __global__ __launch_bounds__(PAIRED ? 512 : 256, PAIRED ? 1 : 2) void attention_
     } else {
       if (shared) {
         tile_to_lds<false, 2>(kbase, t0, rows, tl, st, 2 * wave8);
-        tile_to_lds<true, 2>(vbase, t0, rows, tl, st + kTileBytes, 2 * wave8);
+        if (VPOOL)
+          vpool_to_lds<2>(a, rq, w.head, t0, rows, vslot, st + kTileBytes, 2 * wave8);
+        else
+          tile_to_lds<true, 2>(vbase, t0, rows, tl, st + kTileBytes, 2 * wave8);
       } else {
         tile_to_lds<false, 4>(kbase, t0, rows, tl, st, 4 * wave);
-        tile_to_lds<true, 4>(vbase, t0, rows, tl, st + kTileBytes, 4 * wave);
+        if (VPOOL)
+          vpool_to_lds<4>(a, rq, w.head, t0, rows, vslot, st + kTileBytes, 4 * wave);
+        else
+          tile_to_lds<true, 4>(vbase, t0, rows, tl, st + kTileBytes, 4 * wave);
       }
     }
     pos_to_lds(pbase, t0, rows, st + kPosOffset, shared ? wave8 : wave);
@@ -1361,8 +1402,10 @@ __global__ __launch_bounds__(PAIRED ? 512 : 256, PAIRED ? 1 : 2) void attention_
     tp_next = bounds(tile_of(0));
     bph_next = blocks_ph(tile_of(0));
     if (QROT) qsrc = qrot_src(a, rq, tile_of(0), rows, wave8);
+    if (VPOOL) vpool_src(tile_of(0));
     issue(std::integral_constant<int, 0>{}, tile_of(0));
     if (QROT && T > 1) qsrc = qrot_src(a, rq, tile_of(1), rows, wave8);
+    if (VPOOL && T > 1) vpool_src(tile_of(1));
   }
   if (FUSED && !QROT && T > 0) fused_k_store(a, fk, smem);
   // step i: the group's tile tb + i sits in stage S (i even: 0); wait for its
@@ -1382,6 +1425,7 @@ __global__ __launch_bounds__(PAIRED ? 512 : 256, PAIRED ? 1 : 2) void attention_
       bph_next = blocks_ph(tn);
       issue(std::integral_constant<int, 1 - S>{}, tn);
       if (QROT && i + 2 < T) qsrc = qrot_src(a, rq, tile_of(i + 2), rows, wave8);
+      if (VPOOL && i + 2 < T) vpool_src(tile_of(i + 2));
     }
     if (tp.x <= c.wq_max) {
       if constexpr (QROT) {
@@ -1607,11 +1651,19 @@ static void gather_launch(const GatherArgs& a, hipStream_t s) {
   const int n_planes = a.plane_end - a.plane_begin;
   dim3 grid(unsigned((a.prefix_rows + RPB - 1) / RPB),
             unsigned((n_planes + a.planes_per_block - 1) / a.planes_per_block));
-  hipLaunchKernelGGL((gather_kernel<BF16, D>), grid, dim3(256), 0, s, a);
+  if constexpr (BF16 && D == 128) {
+    if (!a.values) {
+      hipLaunchKernelGGL((gather_kernel<BF16, D, false>), grid, dim3(256), 0, s, a);
+      return;
+    }
+  }
+  hipLaunchKernelGGL((gather_kernel<BF16, D, true>), grid, dim3(256), 0, s, a);
 }
 
 hipError_t launch_gather(int dtype, int head_dim, const GatherArgs& a, hipStream_t s) {
   if (a.prefix_rows <= 0 || a.plane_end <= a.plane_begin) return hipSuccess;
+  // keys only is implemented where attention can read values from the pool
+  if (!a.values && !(dtype == PIC_BF16 && head_dim == 128)) return hipErrorInvalidValue;
   if (dtype == PIC_BF16) {
     if (head_dim == 128) gather_launch<true, 128>(a, s);
     else gather_launch<true, 64>(a, s);
@@ -1654,12 +1706,13 @@ hipError_t launch_attention_bf16(const AttnArgs& a, bool fused, hipStream_t s) {
   if (a.n_work <= 0) return hipSuccess;
   // dynamic LDS above 64 KB has to be allowed per kernel, once
   static const hipError_t attr = [] {
-    const void* fns[4] = {reinterpret_cast<const void*>(attention_bf16_kernel<true, true>),
+    const void* fns[5] = {reinterpret_cast<const void*>(attention_bf16_kernel<true, true>),
                           reinterpret_cast<const void*>(attention_bf16_kernel<false, true>),
                           reinterpret_cast<const void*>(attention_bf16_kernel<true, false>),
-                          reinterpret_cast<const void*>(attention_bf16_kernel<true, true, true>)};
-    const int bytes[4] = {kAttnLdsBytes, kAttnLdsBytes, kGroupLdsBytes, kQrotLdsBytes};
-    for (int i = 0; i < 4; ++i) {
+                          reinterpret_cast<const void*>(attention_bf16_kernel<true, true, true>),
+                          reinterpret_cast<const void*>(attention_bf16_kernel<false, true, false, true>)};
+    const int bytes[5] = {kAttnLdsBytes, kAttnLdsBytes, kGroupLdsBytes, kQrotLdsBytes, kAttnLdsBytes};
+    for (int i = 0; i < 5; ++i) {
       hipError_t e = hipFuncSetAttribute(fns[i], hipFuncAttributeMaxDynamicSharedMemorySize, bytes[i]);
       if (e != hipSuccess) return e;
     }
@@ -1670,7 +1723,10 @@ hipError_t launch_attention_bf16(const AttnArgs& a, bool fused, hipStream_t s) {
   // splits merged in LDS, or neighbouring column blocks sharing their rows'
   // copies; the fused variant pairs only the row splits it merges
   const unsigned pairs = unsigned((a.n_work + 1) / 2);
-  if (!fused)
+  if (!fused && a.v_pool)
+    hipLaunchKernelGGL((attention_bf16_kernel<false, true, false, true>), dim3(pairs), dim3(512), kAttnLdsBytes, s,
+                       a);
+  else if (!fused)
     hipLaunchKernelGGL((attention_bf16_kernel<false, true>), dim3(pairs), dim3(512), kAttnLdsBytes, s, a);
   else if (a.qrot)
     hipLaunchKernelGGL((attention_bf16_kernel<true, true, true>), dim3(pairs), dim3(512), kQrotLdsBytes, s, a);

@@ -191,6 +191,30 @@ def test_query_rotation_flag_and_eligibility(name):
     pool.release()
 
 
+def test_values_in_pool_flag():
+    wl = W.get("turborag_small")
+    pool = _pool(wl)
+    plan = B.Plan(pool)
+    sp, spans, npt, npos = wl.span_ptr(), wl.spans_flat(), wl.new_ptr(), wl.new_pos_flat()
+    # a gathered batch only: nothing to leave in the pool when nothing is gathered
+    assert _err(lambda: plan.assemble(sp, spans, npt, npos, None, None, 2 ** 40,
+                                      B.DRY_RUN | B.PLAN_ONLY | B.VALUES_IN_POOL)) == "PIC_EINVAL"
+    plan.assemble(sp, spans, npt, npos, None, None, 2 ** 40, B.DRY_RUN | B.VALUES_IN_POOL)
+    assert plan.summary()["values_in_pool"] == 1
+    plan.assemble(sp, spans, npt, npos, None, None, 2 ** 40, B.DRY_RUN)
+    assert plan.summary()["values_in_pool"] == 0
+    plan.release()
+    pool.release()
+    # implemented where the bf16 attention reads the pool (head_dim 128)
+    wl = W.get("tiny_f32")
+    pool = _pool(wl)
+    plan = B.Plan(pool)
+    assert _err(lambda: plan.assemble(wl.span_ptr(), wl.spans_flat(), wl.new_ptr(), wl.new_pos_flat(), None,
+                                      None, 2 ** 40, B.DRY_RUN | B.VALUES_IN_POOL)) == "PIC_EUNSUPPORTED"
+    plan.release()
+    pool.release()
+
+
 def test_key_storage_is_validated():
     wl = W.get("tiny_f32")
     p = wl.pool

@@ -115,6 +115,16 @@ def check_fused_plan_only(dw, layers, res_m, query_rotation=False, requests=None
     return summ["fused_query_rotation"]
 
 
+def check_values_in_pool(dw, layers, res_m):
+    """Variant M after an assembly that gathers keys only (values read in
+    the pool pages by attention): bit for bit what the full gather gives."""
+    summ = dw.assemble(values_in_pool=True)
+    assert summ["values_in_pool"] == 1
+    res = run_prefill(dw, layers, VARIANT_MATERIALIZED)
+    for l in layers:
+        assert torch.equal(res_m[l][3], res[l][3]), f"values in the pool differ on layer {l}"
+
+
 def test_tiny_fp32_config_end_to_end():
     wl = W.get("tiny_f32")
     _say("case tiny_f32")
@@ -146,6 +156,9 @@ def test_reduced_workloads_every_element(name):
     res_f = run_prefill(dw, layers, VARIANT_FUSED)
     for l in layers:
         assert torch.equal(res_m[l][3], res_f[l][3]), f"fused != materialised on layer {l}"
+    # keys gathered, values read in the pool: the same bits
+    check_values_in_pool(dw, layers, res_m)
+    dw.assemble()
     # and it also works from a plan-only assembly, and with query rotation
     # where the blocks allow it
     assert not check_fused_plan_only(dw, layers, res_m)
@@ -241,6 +254,14 @@ def test_decode_after_prefill_reduced(name):
     for l in layers:
         for st in range(DECODE_STEPS):
             assert torch.equal(dec[l][st][3], dec_f[l][st][3]), f"fused decode differs (layer {l}, step {st})"
+    # keys gathered, values read in the pool: prefill and decode, the same bits
+    assert dw.assemble(values_in_pool=True)["values_in_pool"] == 1
+    pre_p = run_prefill(dw, layers, VARIANT_MATERIALIZED)
+    dec_p = run_decode(dw, layers, DECODE_STEPS, VARIANT_MATERIALIZED)
+    for l in layers:
+        assert torch.equal(pre[l][3], pre_p[l][3]), f"values in the pool: prefill differs on layer {l}"
+        for st in range(DECODE_STEPS):
+            assert torch.equal(dec[l][st][3], dec_p[l][st][3]), f"values in the pool: decode differs ({l}, {st})"
     dw.close()
     del dw
     torch.cuda.empty_cache()
@@ -290,6 +311,7 @@ def test_full_size_workloads_sampled(name):
         assert torch.equal(res[l][3], res_f[l][3]), f"fused != materialised on layer {l}"
     assert summ["rows"] == wl.rows_total
     del res_f
+    check_values_in_pool(dw, checked, res)
     # plan-only, as the fused variant is benchmarked
     check_fused_plan_only(dw, checked, res, query_rotation=name in QROT_FULL, requests=sorted({0, wl.batch - 1}),
                           token_subset=_token_subset)
@@ -337,6 +359,7 @@ def test_pool_in_pinned_host_memory(name):
     for b in range(wl.batch):
         _say(name, b, check_request(dw, b, layers, res_m))
     check_fused_plan_only(dw, layers, res_m, query_rotation=True)
+    check_values_in_pool(dw, layers, res_m)
     dw.close()
 
 
@@ -390,6 +413,18 @@ def test_edge_cases_ragged_degenerate_and_canary(keys):
     res_f = run_prefill(dw, layers, VARIANT_FUSED)
     for l in layers:
         assert torch.equal(res[l][3], res_f[l][3])
+    # keys only: the planes' prefix values keep the canary, the rest is written
+    sess.asm_k.view(torch.int16).fill_(nan_bits)
+    sess.asm_v.view(torch.int16).fill_(nan_bits)
+    check_values_in_pool(dw, layers, res)
+    rb, pr, _ = sess.plan.requests()
+    for b in range(wl.batch):
+        base, npre, nn = int(rb[b]), int(pr[b]), wl.requests[b].n_new
+        for l in layers:
+            assert not torch.isnan(sess.asm_k[l, :, base:base + npre + nn].float()).any()
+            assert bool((sess.asm_v[l, :, base:base + npre].view(torch.int16) == -1).all()), \
+                "prefix values were gathered"
+            assert not torch.isnan(sess.asm_v[l, :, base + npre:base + npre + nn].float()).any()
     # odd span lengths: keys rotated on load even when query rotation is asked for
     assert not check_fused_plan_only(dw, layers, res, query_rotation=True)
     dw.close()
