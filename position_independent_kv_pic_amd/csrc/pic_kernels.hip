@@ -1281,7 +1281,10 @@ __global__ __launch_bounds__(PAIRED ? 512 : 256, PAIRED ? 1 : 2) void attention_
   const int blk = xcd_remap(blockIdx.x, gridDim.x);
   const int wave8 = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int grp = PAIRED ? wave8 >> 2 : 0;
-  const int wave = wave8 & 3;                 // wave within the group
+  // wave within the group.  A decode item has one query token, so only its
+  // first wave has columns; the second group's waves are rotated by one so
+  // that the two groups' live waves sit on different SIMDs (wave8 mod 4).
+  const int wave = (PAIRED && grp == 1 && a.decode) ? ((wave8 + 3) & 3) : (wave8 & 3);
   const int item = G * blk + grp;
   const bool has = item < a.n_work;
   const AttnWork w = a.work[has ? item : G * blk];
@@ -1427,7 +1430,8 @@ __global__ __launch_bounds__(PAIRED ? 512 : 256, PAIRED ? 1 : 2) void attention_
       if (QROT && i + 2 < T) qsrc = qrot_src(a, rq, tile_of(i + 2), rows, wave8);
       if (VPOOL && i + 2 < T) vpool_src(tile_of(i + 2));
     }
-    if (tp.x <= c.wq_max) {
+    // (a wave without columns has wq_max INT_MIN and computes nothing)
+    if (tp.x <= c.wq_max && c.wq_max != INT_MIN) {
       if constexpr (QROT) {
         f32x16 sacc[2];
         bf16x8 pb[2][2];
