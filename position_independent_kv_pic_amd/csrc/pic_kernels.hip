@@ -404,10 +404,13 @@ __global__ __launch_bounds__(256) void prologue_kernel(PrologueArgs a) {
 // are masked by index.
 //
 // Softmax: scores are kept relative to a reference maximum that is raised
-// only when a tile's maximum exceeds it by more than 8 (log2 units), so the
+// only when a block's maximum exceeds it by more than 8 (log2 units), so the
 // accumulator rescale is rare; probabilities stay below 2^8.  The denominator
 // is summed on the matrix core from the same bf16 probabilities the PV
 // product uses, so the output is an exact weighted mean of the values.
+//
+// A tile runs as two 32-row blocks pipelined against each other
+// (tile_pipelined); the query-rotation variant runs the whole tile at once.
 
 constexpr int kTileBytes = 16384;
 constexpr int kPosOffset = 2 * kTileBytes;          // 64 row positions after K and V
@@ -566,27 +569,8 @@ __device__ __forceinline__ void col_setup(const AttnArgs& a, const AttnWork& w, 
   }
 }
 
-// S^T = K Q^T for the tile in the stage at byte offset STAGE from stage 0,
-// one 32-row block at a time (its 8 fragment reads in flight before one wait).
-template <int OFF>
-__device__ __forceinline__ void s_block(const Col& c, const bf16x8 qb[8], f32x16& acc) {
-  KFrags kf;
-#pragma unroll
-  for (int s = 0; s < 8; ++s) kf.x[s] = lds_read16<OFF>(c.kaddr[s]);
-  kfrag_wait(kf);
-  acc = f32x16{};
-#pragma unroll
-  for (int s = 0; s < 8; ++s)
-    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kf.x[s]), qb[s], acc, 0, 0, 0);
-}
-
-template <int STAGE>
-__device__ __forceinline__ void s_product(const Col& c, const bf16x8 qb[8], f32x16 sacc[2]) {
-  s_block<STAGE>(c, qb, sacc[0]);
-  s_block<STAGE + 8192>(c, qb, sacc[1]);
-}
-
-// Softmax of one tile's scores: mask (when the tile's rows are not all at or
+// Softmax of one whole tile's scores (query-rotation variant; the other
+// variants run tile_pipelined): mask (when the tile's rows are not all at or
 // before every query of the wave), raise the reference maximum if needed,
 // and form the bf16 probabilities.  The tile's row positions sit in LDS at
 // byte offset POFF from `paddr` (the lane's address in stage 0), `r0` is its
@@ -650,9 +634,10 @@ __device__ __forceinline__ void softmax_tile(f32x16 sacc[2], int2 bnd, unsigned 
   }
 }
 
-// O^T += V^T P^T and the denominator (ones^T P^T) for the tile in the stage
-// at byte offset STAGE from stage 0.  Block db+1's transpose reads are issued before
-// block db's products, and waited for while those run.
+// O^T += V^T P^T and the denominator (ones^T P^T) for the whole tile in the
+// stage at byte offset STAGE from stage 0 (query-rotation variant).  Block
+// db+1's transpose reads are issued before block db's products, and waited
+// for while those run.
 template <int STAGE>
 __device__ __forceinline__ void pv_product(const Col& c, const bf16x8 pb[2][2], f32x16 o[4],
                                            f32x16& lacc) {
