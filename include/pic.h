@@ -326,6 +326,8 @@ typedef struct {
   int32_t materialized;    /* 1 if the prefix rows were gathered */
   int32_t fused_query_rotation;  /* 1 if PIC_VARIANT_FUSED rotates queries instead of keys (below) */
   int32_t values_in_pool;  /* 1 if the batch was assembled with PIC_ASSEMBLE_VALUES_IN_POOL */
+  int32_t attention_items;       /* bf16 attention work items (0 for other models) */
+  int32_t attention_workgroups;  /* entries of the paired kernel's launch order */
 } pic_plan_summary;
 
 pic_status pic_plan_get_summary(const pic_plan* plan, pic_plan_summary* out);
@@ -343,6 +345,22 @@ pic_status pic_plan_get_spans(const pic_plan* plan, int32_t* target, int32_t* de
 
 /* Per-new-token host arrays: position int32[new_rows], assembled row int64[new_rows]. */
 pic_status pic_plan_get_new_tokens(const pic_plan* plan, int32_t* position, int64_t* row);
+
+/* The bf16 attention work list of the current batch, as the host planned it
+ * (any pointer may be NULL; empty for other models):
+ *   items     int32[attention_items][7]: request, kv head, first query column
+ *             (column j*G + g is the request's new token j with query head g
+ *             of the group), first tile, end tile, and the tiles
+ *             [gap_begin, gap_end) skipped inside that range.  A tile is 64
+ *             rows, counted from the request's first assembled row; the
+ *             skipped and trimmed tiles hold no row that a query of the item
+ *             can see.  Items 2p and 2p + 1 run in one workgroup.
+ *   wg_order  int32[attention_workgroups]: the item pair p that workgroup b
+ *             of the paired kernel runs (-1: none).  Workgroup b runs on XCD
+ *             b mod 8; each XCD gets a contiguous range of pairs, longest
+ *             first.
+ * Introspection only: the kernels read the device copy of these tables. */
+pic_status pic_plan_get_attention_work(const pic_plan* plan, int32_t* items, int32_t* wg_order);
 
 /* Kernel timing: when enabled, the library brackets its main kernels with HIP
  * events on the caller's stream.  pic_timing_read synchronises on the last

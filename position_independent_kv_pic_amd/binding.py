@@ -37,7 +37,7 @@ EXPORTED = (
     "pic_assemble", "pic_query_prefill", "pic_plan_get_summary", "pic_plan_get_requests",
     "pic_plan_get_spans", "pic_plan_get_new_tokens", "pic_timing_enable", "pic_timing_read",
     "pic_timing_reset", "pic_last_error", "pic_version", "pic_plan_set_decode_rows", "pic_decode_layer",
-    "pic_pool_register_host", "pic_gather_layers",
+    "pic_pool_register_host", "pic_gather_layers", "pic_plan_get_attention_work",
 )
 
 
@@ -65,7 +65,8 @@ class PicPlanSummary(ctypes.Structure):
                 ("prefix_rows", ctypes.c_int64), ("new_rows", ctypes.c_int64),
                 ("rows", ctypes.c_int64), ("max_position", ctypes.c_int32),
                 ("materialized", ctypes.c_int32), ("fused_query_rotation", ctypes.c_int32),
-                ("values_in_pool", ctypes.c_int32)]
+                ("values_in_pool", ctypes.c_int32), ("attention_items", ctypes.c_int32),
+                ("attention_workgroups", ctypes.c_int32)]
 
 
 def library_path() -> str:
@@ -106,6 +107,7 @@ def lib() -> ctypes.CDLL:
         "pic_plan_get_requests": [P, pi64, pi32, pi32],
         "pic_plan_get_spans": [P, pi32, pi32, pi64],
         "pic_plan_get_new_tokens": [P, pi32, pi64],
+        "pic_plan_get_attention_work": [P, pi32, pi32],
         "pic_timing_enable": [P, I32],
         "pic_timing_read": [P, I32, pi64, ctypes.POINTER(ctypes.c_double)],
         "pic_timing_reset": [P],
@@ -278,6 +280,14 @@ class Plan:
         _check(lib().pic_plan_get_new_tokens(self.handle, _p32(p),
                                              r.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))))
         return p, r
+
+    def attention_work(self):
+        """(items int32[n][7], wg_order int32[m]): see pic_plan_get_attention_work."""
+        s = self.summary()
+        items = np.zeros((s["attention_items"], 7), np.int32)
+        order = np.zeros(s["attention_workgroups"], np.int32)
+        _check(lib().pic_plan_get_attention_work(self.handle, _p32(items), _p32(order)))
+        return items, order
 
     def timing(self, enable: bool):
         _check(lib().pic_timing_enable(self.handle, 1 if enable else 0))

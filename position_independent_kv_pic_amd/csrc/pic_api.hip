@@ -69,7 +69,7 @@ struct pic_plan {
   char* ws = nullptr;
   size_t ws_cap = 0;
   size_t off_spans = 0, off_crow = 0, off_reqs = 0, off_new_pos = 0, off_new_row = 0,
-         off_new_req = 0, off_work = 0, off_omega = 0, off_blk_ph = 0, off_phase32 = 0, blob_bytes = 0;
+         off_new_req = 0, off_work = 0, off_omega = 0, off_blk_ph = 0, off_wg_map = 0, off_phase32 = 0, blob_bytes = 0;
   size_t off_pos = 0, off_rowsrc = 0, off_tile_pos = 0, off_phase_tab = 0, off_phase_new = 0,
          off_qrot = 0, off_opart = 0, off_ml = 0, off_spart = 0, off_sml = 0, off_count = 0,
          ws_bytes = 0;
@@ -160,6 +160,7 @@ void layout_workspace(pic_plan* p) {
   p->off_work = take(hp.work.size() * sizeof(pic::AttnWork));
   p->off_omega = take(half * sizeof(double));
   p->off_blk_ph = take(hp.blk_ph.size() * sizeof(int32_t));
+  p->off_wg_map = take(hp.wg_map.size() * sizeof(int32_t));
   p->blob_bytes = o;
   p->off_pos = take(size_t(hp.rows) * sizeof(int32_t));
   p->off_rowsrc = take(size_t(hp.rows) * sizeof(int2));
@@ -446,6 +447,7 @@ pic_status pic_assemble(pic_plan* p, int32_t batch, const int32_t* span_ptr, con
         pic::kAttnMaxSplit, /*min_tiles_per_split=*/4, qrot_layout ? 1 : pic::kAttnMinTilesAcross);
     pic::build_attention_work(&hp, pi.m.kv_heads, pi.m.group, pic::kAttnColsPerWG, pic::kAttnRowsPerTile, sp);
     pic::finish_qrot(&hp);
+    pic::build_wg_map(&hp, pic::kXcds, pic::kAttnTargetWGs / pic::kXcds);
     // otherwise the fused variant rotates keys (the same bits as the
     // materialised variant)
     if (!want_qrot) hp.qrot = false;
@@ -505,6 +507,7 @@ pic_status pic_assemble(pic_plan* p, int32_t batch, const int32_t* span_ptr, con
   put(p->staging, p->off_work, h.work);
   put(p->staging, p->off_omega, omega);
   put(p->staging, p->off_blk_ph, h.blk_ph);
+  put(p->staging, p->off_wg_map, h.wg_map);
   {
     Timed tm(p, 3, s);
     hipError_t e = hipMemcpyAsync(p->ws, p->staging, p->blob_bytes, hipMemcpyHostToDevice, s);
@@ -648,6 +651,8 @@ pic_status pic_query_prefill(pic_plan* p, int32_t layer, const void* q, const vo
       aa.new_pos = reinterpret_cast<const int32_t*>(p->ws + p->off_new_pos);
       aa.work = reinterpret_cast<const pic::AttnWork*>(p->ws + p->off_work);
       aa.n_work = int32_t(h.work.size());
+      aa.wg_map = h.wg_map.empty() ? nullptr : reinterpret_cast<const int32_t*>(p->ws + p->off_wg_map);
+      aa.n_wg = int32_t(h.wg_map.size());
       aa.q_heads = m.q_heads;
       aa.group = m.group;
       aa.n_new = int32_t(h.new_rows);
@@ -838,6 +843,8 @@ pic_status pic_decode_layer(pic_plan* p, int32_t layer, int32_t step, const void
     aa.new_pos = reinterpret_cast<const int32_t*>(p->dws + p->d_pos);
     aa.work = reinterpret_cast<const pic::AttnWork*>(p->dws + p->d_work);
     aa.n_work = int32_t(d.work.size());
+    aa.wg_map = nullptr;
+    aa.n_wg = 0;
     aa.q_heads = m.q_heads;
     aa.group = m.group;
     aa.n_new = h.batch;
@@ -883,6 +890,26 @@ pic_status pic_plan_get_summary(const pic_plan* p, pic_plan_summary* out) {
   out->materialized = p->materialized ? 1 : 0;
   out->fused_query_rotation = p->hp.qrot ? 1 : 0;
   out->values_in_pool = p->values_in_pool ? 1 : 0;
+  out->attention_items = int32_t(p->hp.work.size());
+  out->attention_workgroups = int32_t(p->hp.wg_map.size());
+  return ok();
+}
+
+pic_status pic_plan_get_attention_work(const pic_plan* p, int32_t* items, int32_t* wg_order) {
+  if (!p) return set_err(PIC_EINVAL, "plan is NULL");
+  if (!p->has_batch) return set_err(PIC_ESTATE, "no batch planned");
+  for (size_t i = 0; items && i < p->hp.work.size(); ++i) {
+    const pic::AttnWork& w = p->hp.work[i];
+    int32_t* o = items + 7 * i;
+    o[0] = w.req;
+    o[1] = w.head;
+    o[2] = w.col_begin;
+    o[3] = w.tile_begin;
+    o[4] = w.tile_end;
+    o[5] = w.gap_begin;
+    o[6] = w.gap_end;
+  }
+  for (size_t b = 0; wg_order && b < p->hp.wg_map.size(); ++b) wg_order[b] = p->hp.wg_map[b];
   return ok();
 }
 

@@ -75,6 +75,8 @@ struct AttnArgs {
   const int32_t* new_pos;
   const AttnWork* work;
   int32_t n_work, q_heads, group, n_new;
+  const int32_t* wg_map;    // paired kernel: item pair of each workgroup (-1: none); null: the
+  int32_t n_wg;             // pairs in order, spread over XCDs by xcd_remap.  n_wg: map entries
   int32_t n_split_out;      // partials written for merge_kernel (1: outputs written directly)
   int32_t paired;           // two work items per workgroup
   int32_t n_split_wg;       // row splits of a column block in different workgroups (1: none)
@@ -122,6 +124,7 @@ struct AttnF32Args {
 constexpr int kAttnRowsPerTile = 64;
 constexpr int kAttnColsPerWG = 128;   // work item: 4 waves x 32 query columns
 constexpr int kAttnTargetWGs = 256;   // prefill workgroups (two work items each): one per CU
+constexpr int kXcds = 8;              // XCDs; workgroup b is dispatched to XCD b mod kXcds
 constexpr int kAttnMinTilesAcross = 64;  // tiles per split that pay for a merge across workgroups
 constexpr int kDecodeTargetItems = 512;  // decode work items: two per CU (one workgroup of two)
 constexpr int kAttnMaxSplit = 16;     // merge_kernel handles at most this many row splits

@@ -1263,7 +1263,10 @@ __global__ __launch_bounds__(PAIRED ? 512 : 256, PAIRED ? 1 : 2) void attention_
   static_assert(!VPOOL || (!FUSED && PAIRED), "pooled values are read by the assembled-plane variant");
   extern __shared__ __attribute__((aligned(1024))) char lds_all[];
   constexpr int G = PAIRED ? 2 : 1;           // work items per workgroup
-  const int blk = xcd_remap(blockIdx.x, gridDim.x);
+  const int blk = PAIRED && a.wg_map
+                      ? ((const __attribute__((address_space(4))) int*)(a.wg_map))[blockIdx.x]
+                      : xcd_remap(blockIdx.x, gridDim.x);
+  if (blk < 0) return;   // a slot of the launch order left empty
   const int wave8 = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int grp = PAIRED ? wave8 >> 2 : 0;
   // wave within the group.  A decode item has one query token, so only its
@@ -1711,7 +1714,7 @@ hipError_t launch_attention_bf16(const AttnArgs& a, bool fused, hipStream_t s) {
   // the assembled-plane variant always runs two items per workgroup: row
   // splits merged in LDS, or neighbouring column blocks sharing their rows'
   // copies; the fused variant pairs only the row splits it merges
-  const unsigned pairs = unsigned((a.n_work + 1) / 2);
+  const unsigned pairs = a.wg_map ? unsigned(a.n_wg) : unsigned((a.n_work + 1) / 2);
   if (!fused && a.v_pool)
     hipLaunchKernelGGL((attention_bf16_kernel<false, true, false, true>), dim3(pairs), dim3(512), kAttnLdsBytes, s,
                        a);

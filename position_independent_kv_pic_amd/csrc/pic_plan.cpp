@@ -6,6 +6,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <functional>
 
 namespace pic {
 namespace {
@@ -349,13 +350,16 @@ void build_attention_work(HostPlan* plan, int32_t kv_heads, int32_t group, int32
           if (split == 1) {
             // prefix tiles after the last one that the pair's latest query
             // (new positions increase) can see are skipped up to the tile of
-            // the first new row
+            // the first new row; new rows after that query's own row are
+            // later positions, so the range ends at the tile holding it
             const int64_t last_col = std::min<int64_t>(int64_t(c0 + 2) * cols_per_wg, cols) - 1;
             const int32_t qmax = plan->new_pos[size_t(r.new_begin + last_col / group)];
             int32_t a_end = ft;
             while (a_end > 0 && tmin[size_t(a_end - 1)] > qmax) --a_end;
-            if (a_end < ft) {
-              for (size_t k = first; k < out.size(); ++k) {
+            const int32_t t_end = int32_t((int64_t(r.prefix_rows) + last_col / group) / rows_per_tile) + 1;
+            for (size_t k = first; k < out.size(); ++k) {
+              out[k].tile_end = std::min(out[k].tile_end, t_end);
+              if (a_end < ft) {
                 out[k].gap_begin = a_end;
                 out[k].gap_end = ft;
               }
@@ -423,6 +427,84 @@ void finish_qrot(HostPlan* plan) {
     shared = (w[i].share_rows && w[i + 1].share_rows) || empty;
   }
   plan->qrot = shared;
+}
+
+namespace {
+
+// Longest-first list schedule of `costs` (sorted, largest first) on `slots`
+// workers: the time the last one finishes.
+int64_t lpt_makespan(const std::vector<int64_t>& costs, int32_t slots) {
+  std::vector<int64_t> busy(size_t(std::max(slots, 1)), 0);   // min-heap of finish times
+  int64_t end = 0;
+  for (int64_t c : costs) {
+    std::pop_heap(busy.begin(), busy.end(), std::greater<int64_t>());
+    busy.back() += c;
+    end = std::max(end, busy.back());
+    std::push_heap(busy.begin(), busy.end(), std::greater<int64_t>());
+  }
+  return end;
+}
+
+}  // namespace
+
+void build_wg_map(HostPlan* plan, int32_t n_xcd, int32_t slots_per_xcd) {
+  const std::vector<AttnWork>& w = plan->work;
+  const int32_t n_pairs = int32_t((w.size() + 1) / 2);
+  plan->wg_map.clear();
+  if (n_pairs == 0) return;
+  // a pair's two items run side by side: its time is the longer one's steps
+  // (skipped gap tiles excluded), plus set-up and the epilogue
+  constexpr int64_t kSetupSteps = 2;
+  auto steps = [](const AttnWork& x) { return int64_t(x.tile_end - x.tile_begin - (x.gap_end - x.gap_begin)); };
+  std::vector<int64_t> cost(static_cast<size_t>(n_pairs));
+  int64_t total = 0;
+  for (int32_t p = 0; p < n_pairs; ++p) {
+    int64_t c = steps(w[size_t(2 * p)]);
+    if (size_t(2 * p + 1) < w.size()) c = std::max(c, steps(w[size_t(2 * p + 1)]));
+    cost[size_t(p)] = c + kSetupSteps;
+    total += cost[size_t(p)];
+  }
+  // candidate cuts: bounds[x] .. bounds[x + 1] is XCD x's range
+  std::vector<int32_t> by_count(size_t(n_xcd) + 1), by_cost(size_t(n_xcd) + 1);
+  const int32_t q = n_pairs / n_xcd, r = n_pairs % n_xcd;
+  for (int32_t x = 0; x <= n_xcd; ++x) by_count[size_t(x)] = x * q + std::min(x, r);
+  {
+    int64_t acc = 0;
+    int32_t p = 0;
+    by_cost[0] = 0;
+    for (int32_t x = 1; x < n_xcd; ++x) {
+      const int64_t goal = total * x / n_xcd;
+      // end the range where its running cost comes closest to the goal
+      while (p < n_pairs && acc + cost[size_t(p)] <= goal) acc += cost[size_t(p++)];
+      if (p < n_pairs && goal - acc > acc + cost[size_t(p)] - goal) acc += cost[size_t(p++)];
+      by_cost[size_t(x)] = p;
+    }
+    by_cost[size_t(n_xcd)] = n_pairs;
+  }
+  // each range longest first (stable: equal costs keep the plan's order)
+  auto order = [&](const std::vector<int32_t>& bounds, std::vector<std::vector<int32_t>>* ranges) {
+    ranges->assign(size_t(n_xcd), {});
+    int64_t span = 0;
+    for (int32_t x = 0; x < n_xcd; ++x) {
+      std::vector<int32_t>& g = (*ranges)[size_t(x)];
+      for (int32_t p = bounds[size_t(x)]; p < bounds[size_t(x) + 1]; ++p) g.push_back(p);
+      std::stable_sort(g.begin(), g.end(), [&](int32_t a, int32_t b) { return cost[size_t(a)] > cost[size_t(b)]; });
+      std::vector<int64_t> c;
+      for (int32_t p : g) c.push_back(cost[size_t(p)]);
+      span = std::max(span, lpt_makespan(c, slots_per_xcd));
+    }
+    return span;
+  };
+  std::vector<std::vector<int32_t>> ra, rb;
+  const int64_t span_count = order(by_count, &ra);
+  const int64_t span_cost = order(by_cost, &rb);
+  const std::vector<std::vector<int32_t>>& ranges = span_cost < span_count ? rb : ra;
+  size_t longest = 0;
+  for (const auto& g : ranges) longest = std::max(longest, g.size());
+  plan->wg_map.assign(longest * size_t(n_xcd), -1);
+  for (int32_t x = 0; x < n_xcd; ++x)
+    for (size_t k = 0; k < ranges[size_t(x)].size(); ++k)
+      plan->wg_map[k * size_t(n_xcd) + size_t(x)] = ranges[size_t(x)][k];
 }
 
 void build_decode(const HostPlan& plan, int32_t kv_heads, int32_t step, int32_t rows_per_tile,

@@ -108,6 +108,13 @@ struct HostPlan {
   std::vector<int32_t> blk_ph;
   bool qrot_ok = false;
   bool qrot = false;
+  // Launch order of the paired attention kernel: workgroup b runs item pair
+  // wg_map[b] (-1: none, it exits at once).  Workgroup b lands on XCD b mod
+  // n_xcd as the (b / n_xcd)-th of that XCD, so the map gives each XCD a
+  // contiguous range of pairs (the pairs of one request and kv head read the
+  // same rows and share that XCD's L2), balanced by cost, and runs each
+  // range's longest pairs first.
+  std::vector<int32_t> wg_map;
 };
 
 // Validation helpers return PIC_OK or an error code and fill `err`.
@@ -182,5 +189,12 @@ void build_qrot_blocks(HostPlan* plan, bool keys_rotated, int32_t rows_per_tile)
 // After build_attention_work: qrot = qrot_ok and every item pair shares its
 // rows (or is empty).
 void finish_qrot(HostPlan* plan);
+
+// After build_attention_work: fill wg_map for `n_xcd` XCDs of
+// `slots_per_xcd` concurrent workgroups each.  A pair costs its tile steps
+// plus a fixed setup; of two cuts of the pairs into contiguous ranges (equal
+// counts, equal costs), the one with the shorter simulated longest-first
+// schedule is kept.
+void build_wg_map(HostPlan* plan, int32_t n_xcd, int32_t slots_per_xcd);
 
 }  // namespace pic

@@ -333,3 +333,81 @@ def test_empty_and_degenerate_batches_plan():
     assert rb.tolist() == [0, 5] and pr.tolist() == [0, 64]
     plan.release()
     pool.release()
+
+
+@pytest.mark.parametrize("name", tuple(n for n in W.FULL_SIZE + W.REDUCED + W.REDUCED_NEXT
+                                       if n != "tiny_f32") + ("turborag_b16_composite",))
+def test_attention_work_covers_every_visible_row_once(name):
+    """The attention work list, checked against the visibility rule (a query
+    at position P sees every row at a position <= P): for each column block,
+    the tiles its items run (range minus skipped gap) hold every row that
+    any of its queries can see, no tile twice; a range without a row split
+    ends at the last such tile.  The launch order covers every item pair once
+    and gives each XCD a contiguous range of pairs, longest first."""
+    wl = W.get(name)
+    pool = _pool(wl)
+    plan = B.Plan(pool)
+    _dry(plan, wl)
+    items, order = plan.attention_work()
+    G = wl.model.q_heads // wl.model.kv_heads
+    target, _, first_row = plan.spans()
+    new_pos, new_row = plan.new_tokens()
+    row_base, prefix_rows, _ = plan.requests()
+    span_ptr, spans_flat = wl.span_ptr(), wl.spans_flat().reshape(-1, 4)
+    new_ptr = wl.new_ptr()
+    # positions of every request's rows, prefix then new tokens
+    tile_min = []
+    for b in range(wl.batch):
+        n_new = int(new_ptr[b + 1] - new_ptr[b])
+        pos = np.empty(int(prefix_rows[b]) + n_new, np.int64)
+        for i in range(span_ptr[b], span_ptr[b + 1]):
+            s, e = int(spans_flat[i, 1]), int(spans_flat[i, 2])
+            r0 = int(first_row[i] - row_base[b])
+            pos[r0:r0 + e - s + 1] = target[i] + np.arange(e - s + 1)
+        pos[prefix_rows[b]:] = new_pos[new_ptr[b]:new_ptr[b + 1]]
+        t = (len(pos) + 63) // 64
+        padded = np.full(t * 64, np.iinfo(np.int64).max)
+        padded[:len(pos)] = pos
+        tile_min.append(padded.reshape(t, 64).min(axis=1))
+    blocks = {}
+    for i, it in enumerate(items):
+        blocks.setdefault((int(it[0]), int(it[1]), int(it[2])), []).append(i)
+    last_needed = {}   # item of an unsplit column block -> last tile it must run
+    for (b, h, c0), idx in blocks.items():
+        n_new = int(new_ptr[b + 1] - new_ptr[b])
+        if c0 >= n_new * G:
+            continue  # the empty partner of an odd count of column blocks
+        last_tok = (min(c0 + 128, n_new * G) - 1) // G
+        qmax = new_pos[new_ptr[b] + last_tok]
+        needed = set(np.nonzero(tile_min[b] <= qmax)[0].tolist())
+        run = []
+        for i in idx:
+            it = items[i]
+            run += [t for t in range(it[3], it[4]) if not (it[5] <= t < it[6])]
+        assert len(run) == len(set(run)), (name, b, h, c0)
+        assert needed <= set(run), (name, b, h, c0, sorted(needed - set(run))[:5])
+        if len(idx) == 1 and needed:
+            last_needed[idx[0]] = max(needed)
+    # two unsplit column blocks in one workgroup run one range: it ends at the
+    # last tile that either of them needs
+    for p in range(0, len(items) - 1, 2):
+        if p in last_needed or p + 1 in last_needed:
+            want = max(last_needed.get(p, -1), last_needed.get(p + 1, -1))
+            if items[p][4] == items[p + 1][4] and items[p][3] == items[p + 1][3]:
+                assert items[p][4] - 1 == want, (name, p)
+    # launch order
+    n_pairs = (len(items) + 1) // 2
+    assert len(order) % 8 == 0 and len(order) >= n_pairs
+    got = order[order >= 0]
+    assert sorted(got.tolist()) == list(range(n_pairs))
+    steps = [max(int(it[4] - it[3] - (it[6] - it[5])) for it in items[2 * p:2 * p + 2]) for p in range(n_pairs)]
+    for x in range(8):
+        col = order[x::8]
+        live = col[col >= 0]
+        assert (col[len(live):] == -1).all()
+        if len(live):
+            assert sorted(live.tolist()) == list(range(min(live), max(live) + 1))
+            c = [steps[p] for p in live]
+            assert c == sorted(c, reverse=True)
+    plan.release()
+    pool.release()
