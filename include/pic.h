@@ -358,7 +358,8 @@ pic_status pic_plan_get_new_tokens(const pic_plan* plan, int32_t* position, int6
  *   wg_order  int32[attention_workgroups]: the item pair p that workgroup b
  *             of the paired kernel runs (-1: none).  Workgroup b runs on XCD
  *             b mod 8; each XCD gets a contiguous range of pairs, longest
- *             first.
+ *             first (pairs within a tenth of the range's longest keep the
+ *             work list's order).
  * Introspection only: the kernels read the device copy of these tables. */
 pic_status pic_plan_get_attention_work(const pic_plan* plan, int32_t* items, int32_t* wg_order);
 

@@ -481,14 +481,21 @@ void build_wg_map(HostPlan* plan, int32_t n_xcd, int32_t slots_per_xcd) {
     }
     by_cost[size_t(n_xcd)] = n_pairs;
   }
-  // each range longest first (stable: equal costs keep the plan's order)
+  // each range longest first.  Costs within a tenth of the range's longest
+  // count as equal and keep the plan's order: the column blocks of one
+  // request and head stay side by side, run together and share the L2
   auto order = [&](const std::vector<int32_t>& bounds, std::vector<std::vector<int32_t>>* ranges) {
     ranges->assign(size_t(n_xcd), {});
     int64_t span = 0;
     for (int32_t x = 0; x < n_xcd; ++x) {
       std::vector<int32_t>& g = (*ranges)[size_t(x)];
-      for (int32_t p = bounds[size_t(x)]; p < bounds[size_t(x) + 1]; ++p) g.push_back(p);
-      std::stable_sort(g.begin(), g.end(), [&](int32_t a, int32_t b) { return cost[size_t(a)] > cost[size_t(b)]; });
+      int64_t top = 1;
+      for (int32_t p = bounds[size_t(x)]; p < bounds[size_t(x) + 1]; ++p) {
+        g.push_back(p);
+        top = std::max(top, cost[size_t(p)]);
+      }
+      auto band = [&](int32_t p) { return (top - cost[size_t(p)]) * 10 / top; };
+      std::stable_sort(g.begin(), g.end(), [&](int32_t a, int32_t b) { return band(a) < band(b); });
       std::vector<int64_t> c;
       for (int32_t p : g) c.push_back(cost[size_t(p)]);
       span = std::max(span, lpt_makespan(c, slots_per_xcd));

@@ -194,7 +194,8 @@ void finish_qrot(HostPlan* plan);
 // `slots_per_xcd` concurrent workgroups each.  A pair costs its tile steps
 // plus a fixed setup; of two cuts of the pairs into contiguous ranges (equal
 // counts, equal costs), the one with the shorter simulated longest-first
-// schedule is kept.
+// schedule is kept.  Costs within a tenth of a range's longest keep the
+// plan's order.
 void build_wg_map(HostPlan* plan, int32_t n_xcd, int32_t slots_per_xcd);
 
 }  // namespace pic
