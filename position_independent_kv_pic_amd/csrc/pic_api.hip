@@ -69,7 +69,7 @@ struct pic_plan {
   char* ws = nullptr;
   size_t ws_cap = 0;
   size_t off_spans = 0, off_crow = 0, off_reqs = 0, off_new_pos = 0, off_new_row = 0,
-         off_new_req = 0, off_work = 0, off_omega = 0, off_blk_ph = 0, off_wg_map = 0, off_phase32 = 0, blob_bytes = 0;
+         off_new_req = 0, off_work = 0, off_omega = 0, off_blk_ph = 0, off_wg_map = 0, off_item_map = 0, off_phase32 = 0, blob_bytes = 0;
   size_t off_pos = 0, off_rowsrc = 0, off_tile_pos = 0, off_phase_tab = 0, off_phase_new = 0,
          off_qrot = 0, off_opart = 0, off_ml = 0, off_spart = 0, off_sml = 0, off_count = 0,
          ws_bytes = 0;
@@ -161,6 +161,7 @@ void layout_workspace(pic_plan* p) {
   p->off_omega = take(half * sizeof(double));
   p->off_blk_ph = take(hp.blk_ph.size() * sizeof(int32_t));
   p->off_wg_map = take(hp.wg_map.size() * sizeof(int32_t));
+  p->off_item_map = take(hp.item_map.size() * sizeof(int32_t));
   p->blob_bytes = o;
   p->off_pos = take(size_t(hp.rows) * sizeof(int32_t));
   p->off_rowsrc = take(size_t(hp.rows) * sizeof(int2));
@@ -508,6 +509,7 @@ pic_status pic_assemble(pic_plan* p, int32_t batch, const int32_t* span_ptr, con
   put(p->staging, p->off_omega, omega);
   put(p->staging, p->off_blk_ph, h.blk_ph);
   put(p->staging, p->off_wg_map, h.wg_map);
+  put(p->staging, p->off_item_map, h.item_map);
   {
     Timed tm(p, 3, s);
     hipError_t e = hipMemcpyAsync(p->ws, p->staging, p->blob_bytes, hipMemcpyHostToDevice, s);
@@ -651,8 +653,6 @@ pic_status pic_query_prefill(pic_plan* p, int32_t layer, const void* q, const vo
       aa.new_pos = reinterpret_cast<const int32_t*>(p->ws + p->off_new_pos);
       aa.work = reinterpret_cast<const pic::AttnWork*>(p->ws + p->off_work);
       aa.n_work = int32_t(h.work.size());
-      aa.wg_map = h.wg_map.empty() ? nullptr : reinterpret_cast<const int32_t*>(p->ws + p->off_wg_map);
-      aa.n_wg = int32_t(h.wg_map.size());
       aa.q_heads = m.q_heads;
       aa.group = m.group;
       aa.n_new = int32_t(h.new_rows);
@@ -680,6 +680,13 @@ pic_status pic_query_prefill(pic_plan* p, int32_t layer, const void* q, const vo
       aa.v_pool = !fused && p->values_in_pool ? 1 : 0;
       aa.blk_ph = reinterpret_cast<const int32_t*>(p->ws + p->off_blk_ph);
       aa.phase32 = reinterpret_cast<const float2*>(p->ws + p->off_phase32);
+      // launch order: the fused variant without row splits or query rotation
+      // runs one item per workgroup, every other kernel a pair
+      const bool unpaired = fused && !aa.qrot && !aa.paired;
+      const std::vector<int32_t>& order = unpaired ? h.item_map : h.wg_map;
+      aa.wg_map = order.empty() ? nullptr
+                                : reinterpret_cast<const int32_t*>(p->ws + (unpaired ? p->off_item_map : p->off_wg_map));
+      aa.n_wg = int32_t(order.size());
       e = pic::launch_attention_bf16(aa, fused, s);
     } else {
       pic::AttnF32Args aa;

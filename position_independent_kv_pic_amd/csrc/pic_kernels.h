@@ -75,8 +75,8 @@ struct AttnArgs {
   const int32_t* new_pos;
   const AttnWork* work;
   int32_t n_work, q_heads, group, n_new;
-  const int32_t* wg_map;    // paired kernel: item pair of each workgroup (-1: none); null: the
-  int32_t n_wg;             // pairs in order, spread over XCDs by xcd_remap.  n_wg: map entries
+  const int32_t* wg_map;    // item pair (paired kernel) or item of each workgroup (-1: none);
+  int32_t n_wg;             // null: in order, spread over XCDs by xcd_remap.  n_wg: map entries
   int32_t n_split_out;      // partials written for merge_kernel (1: outputs written directly)
   int32_t paired;           // two work items per workgroup
   int32_t n_split_wg;       // row splits of a column block in different workgroups (1: none)

@@ -1263,9 +1263,8 @@ __global__ __launch_bounds__(PAIRED ? 512 : 256, PAIRED ? 1 : 2) void attention_
   static_assert(!VPOOL || (!FUSED && PAIRED), "pooled values are read by the assembled-plane variant");
   extern __shared__ __attribute__((aligned(1024))) char lds_all[];
   constexpr int G = PAIRED ? 2 : 1;           // work items per workgroup
-  const int blk = PAIRED && a.wg_map
-                      ? ((const __attribute__((address_space(4))) int*)(a.wg_map))[blockIdx.x]
-                      : xcd_remap(blockIdx.x, gridDim.x);
+  const int blk = a.wg_map ? ((const __attribute__((address_space(4))) int*)(a.wg_map))[blockIdx.x]
+                          : xcd_remap(blockIdx.x, gridDim.x);
   if (blk < 0) return;   // a slot of the launch order left empty
   const int wave8 = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int grp = PAIRED ? wave8 >> 2 : 0;
@@ -1725,7 +1724,8 @@ hipError_t launch_attention_bf16(const AttnArgs& a, bool fused, hipStream_t s) {
   else if (a.paired)
     hipLaunchKernelGGL((attention_bf16_kernel<true, true>), dim3(pairs), dim3(512), kAttnLdsBytes, s, a);
   else
-    hipLaunchKernelGGL((attention_bf16_kernel<true, false>), dim3(unsigned(a.n_work)), dim3(256), kGroupLdsBytes,
+    hipLaunchKernelGGL((attention_bf16_kernel<true, false>), dim3(a.wg_map ? unsigned(a.n_wg) : unsigned(a.n_work)),
+                       dim3(256), kGroupLdsBytes,
                        s, a);
   if (a.n_split_out > 1) {
     const int64_t items = int64_t(a.n_new) * a.q_heads;

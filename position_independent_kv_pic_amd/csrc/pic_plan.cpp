@@ -445,22 +445,22 @@ int64_t lpt_makespan(const std::vector<int64_t>& costs, int32_t slots) {
   return end;
 }
 
-}  // namespace
-
-void build_wg_map(HostPlan* plan, int32_t n_xcd, int32_t slots_per_xcd) {
-  const std::vector<AttnWork>& w = plan->work;
-  const int32_t n_pairs = int32_t((w.size() + 1) / 2);
-  plan->wg_map.clear();
-  if (n_pairs == 0) return;
-  // a pair's two items run side by side: its time is the longer one's steps
-  // (skipped gap tiles excluded), plus set-up and the epilogue
+// Launch order over units of `per_wg` consecutive items (one workgroup each).
+std::vector<int32_t> launch_order(const std::vector<AttnWork>& w, int32_t per_wg, int32_t n_xcd,
+                                  int32_t slots_per_xcd) {
+  const int32_t n_pairs = int32_t((w.size() + size_t(per_wg) - 1) / size_t(per_wg));
+  std::vector<int32_t> map;
+  if (n_pairs == 0) return map;
+  // a workgroup's items run side by side: its time is the longest one's
+  // steps (skipped gap tiles excluded), plus set-up and the epilogue
   constexpr int64_t kSetupSteps = 2;
   auto steps = [](const AttnWork& x) { return int64_t(x.tile_end - x.tile_begin - (x.gap_end - x.gap_begin)); };
   std::vector<int64_t> cost(static_cast<size_t>(n_pairs));
   int64_t total = 0;
   for (int32_t p = 0; p < n_pairs; ++p) {
-    int64_t c = steps(w[size_t(2 * p)]);
-    if (size_t(2 * p + 1) < w.size()) c = std::max(c, steps(w[size_t(2 * p + 1)]));
+    int64_t c = 0;
+    for (int32_t k = 0; k < per_wg && size_t(per_wg * p + k) < w.size(); ++k)
+      c = std::max(c, steps(w[size_t(per_wg * p + k)]));
     cost[size_t(p)] = c + kSetupSteps;
     total += cost[size_t(p)];
   }
@@ -508,10 +508,18 @@ void build_wg_map(HostPlan* plan, int32_t n_xcd, int32_t slots_per_xcd) {
   const std::vector<std::vector<int32_t>>& ranges = span_cost < span_count ? rb : ra;
   size_t longest = 0;
   for (const auto& g : ranges) longest = std::max(longest, g.size());
-  plan->wg_map.assign(longest * size_t(n_xcd), -1);
+  map.assign(longest * size_t(n_xcd), -1);
   for (int32_t x = 0; x < n_xcd; ++x)
-    for (size_t k = 0; k < ranges[size_t(x)].size(); ++k)
-      plan->wg_map[k * size_t(n_xcd) + size_t(x)] = ranges[size_t(x)][k];
+    for (size_t k = 0; k < ranges[size_t(x)].size(); ++k) map[k * size_t(n_xcd) + size_t(x)] = ranges[size_t(x)][k];
+  return map;
+}
+
+}  // namespace
+
+void build_wg_map(HostPlan* plan, int32_t n_xcd, int32_t slots_per_xcd) {
+  plan->wg_map = launch_order(plan->work, 2, n_xcd, slots_per_xcd);
+  // the unpaired kernel fits two workgroups on a CU
+  plan->item_map = launch_order(plan->work, 1, n_xcd, 2 * slots_per_xcd);
 }
 
 void build_decode(const HostPlan& plan, int32_t kv_heads, int32_t step, int32_t rows_per_tile,

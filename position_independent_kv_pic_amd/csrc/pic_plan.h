@@ -115,6 +115,9 @@ struct HostPlan {
   // same rows and share that XCD's L2), balanced by cost, and runs each
   // range's longest pairs first.
   std::vector<int32_t> wg_map;
+  // The same for the unpaired kernel (one item per workgroup, two
+  // workgroups per CU): item_map[b] is an item index.
+  std::vector<int32_t> item_map;
 };
 
 // Validation helpers return PIC_OK or an error code and fill `err`.
@@ -191,7 +194,7 @@ void build_qrot_blocks(HostPlan* plan, bool keys_rotated, int32_t rows_per_tile)
 void finish_qrot(HostPlan* plan);
 
 // After build_attention_work: fill wg_map for `n_xcd` XCDs of
-// `slots_per_xcd` concurrent workgroups each.  A pair costs its tile steps
+// `slots_per_xcd` concurrent paired workgroups each, and item_map.  A pair costs its tile steps
 // plus a fixed setup; of two cuts of the pairs into contiguous ranges (equal
 // counts, equal costs), the one with the shorter simulated longest-first
 // schedule is kept.  Costs within a tenth of a range's longest keep the
