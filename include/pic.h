@@ -328,6 +328,7 @@ typedef struct {
   int32_t values_in_pool;  /* 1 if the batch was assembled with PIC_ASSEMBLE_VALUES_IN_POOL */
   int32_t attention_items;       /* bf16 attention work items (0 for other models) */
   int32_t attention_workgroups;  /* entries of the paired kernel's launch order */
+  int32_t attention_item_workgroups;  /* entries of the one-item kernel's launch order */
 } pic_plan_summary;
 
 pic_status pic_plan_get_summary(const pic_plan* plan, pic_plan_summary* out);
@@ -360,8 +361,12 @@ pic_status pic_plan_get_new_tokens(const pic_plan* plan, int32_t* position, int6
  *             b mod 8; each XCD gets a contiguous range of pairs, longest
  *             first (pairs within a tenth of the range's longest keep the
  *             work list's order).
+ *   item_order int32[attention_item_workgroups]: the same over single items
+ *             (-1: none), for variant F without row splits, which runs one
+ *             item per workgroup and two workgroups per CU.
  * Introspection only: the kernels read the device copy of these tables. */
-pic_status pic_plan_get_attention_work(const pic_plan* plan, int32_t* items, int32_t* wg_order);
+pic_status pic_plan_get_attention_work(const pic_plan* plan, int32_t* items, int32_t* wg_order,
+                                       int32_t* item_order);
 
 /* Kernel timing: when enabled, the library brackets its main kernels with HIP
  * events on the caller's stream.  pic_timing_read synchronises on the last

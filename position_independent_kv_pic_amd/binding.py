@@ -66,7 +66,7 @@ class PicPlanSummary(ctypes.Structure):
                 ("rows", ctypes.c_int64), ("max_position", ctypes.c_int32),
                 ("materialized", ctypes.c_int32), ("fused_query_rotation", ctypes.c_int32),
                 ("values_in_pool", ctypes.c_int32), ("attention_items", ctypes.c_int32),
-                ("attention_workgroups", ctypes.c_int32)]
+                ("attention_workgroups", ctypes.c_int32), ("attention_item_workgroups", ctypes.c_int32)]
 
 
 def library_path() -> str:
@@ -107,7 +107,7 @@ def lib() -> ctypes.CDLL:
         "pic_plan_get_requests": [P, pi64, pi32, pi32],
         "pic_plan_get_spans": [P, pi32, pi32, pi64],
         "pic_plan_get_new_tokens": [P, pi32, pi64],
-        "pic_plan_get_attention_work": [P, pi32, pi32],
+        "pic_plan_get_attention_work": [P, pi32, pi32, pi32],
         "pic_timing_enable": [P, I32],
         "pic_timing_read": [P, I32, pi64, ctypes.POINTER(ctypes.c_double)],
         "pic_timing_reset": [P],
@@ -281,13 +281,15 @@ class Plan:
                                              r.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))))
         return p, r
 
-    def attention_work(self):
-        """(items int32[n][7], wg_order int32[m]): see pic_plan_get_attention_work."""
+    def attention_work(self, single_items: bool = False):
+        """(items int32[n][7], launch order): see pic_plan_get_attention_work.
+        The order is over item pairs, or over single items if `single_items`."""
         s = self.summary()
         items = np.zeros((s["attention_items"], 7), np.int32)
         order = np.zeros(s["attention_workgroups"], np.int32)
-        _check(lib().pic_plan_get_attention_work(self.handle, _p32(items), _p32(order)))
-        return items, order
+        item_order = np.zeros(s["attention_item_workgroups"], np.int32)
+        _check(lib().pic_plan_get_attention_work(self.handle, _p32(items), _p32(order), _p32(item_order)))
+        return items, (item_order if single_items else order)
 
     def timing(self, enable: bool):
         _check(lib().pic_timing_enable(self.handle, 1 if enable else 0))

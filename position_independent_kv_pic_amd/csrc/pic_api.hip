@@ -899,10 +899,11 @@ pic_status pic_plan_get_summary(const pic_plan* p, pic_plan_summary* out) {
   out->values_in_pool = p->values_in_pool ? 1 : 0;
   out->attention_items = int32_t(p->hp.work.size());
   out->attention_workgroups = int32_t(p->hp.wg_map.size());
+  out->attention_item_workgroups = int32_t(p->hp.item_map.size());
   return ok();
 }
 
-pic_status pic_plan_get_attention_work(const pic_plan* p, int32_t* items, int32_t* wg_order) {
+pic_status pic_plan_get_attention_work(const pic_plan* p, int32_t* items, int32_t* wg_order, int32_t* item_order) {
   if (!p) return set_err(PIC_EINVAL, "plan is NULL");
   if (!p->has_batch) return set_err(PIC_ESTATE, "no batch planned");
   for (size_t i = 0; items && i < p->hp.work.size(); ++i) {
@@ -917,6 +918,7 @@ pic_status pic_plan_get_attention_work(const pic_plan* p, int32_t* items, int32_
     o[6] = w.gap_end;
   }
   for (size_t b = 0; wg_order && b < p->hp.wg_map.size(); ++b) wg_order[b] = p->hp.wg_map[b];
+  for (size_t b = 0; item_order && b < p->hp.item_map.size(); ++b) item_order[b] = p->hp.item_map[b];
   return ok();
 }
 

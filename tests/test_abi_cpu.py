@@ -342,8 +342,9 @@ def test_attention_work_covers_every_visible_row_once(name):
     at position P sees every row at a position <= P): for each column block,
     the tiles its items run (range minus skipped gap) hold every row that
     any of its queries can see, no tile twice; a range without a row split
-    ends at the last such tile.  The launch order covers every item pair once
-    and gives each XCD a contiguous range of pairs, longest first."""
+    ends at the last such tile.  Both launch orders (over item pairs and
+    over single items) cover every unit once and give each XCD a contiguous
+    range of units, longest first."""
     wl = W.get(name)
     pool = _pool(wl)
     plan = B.Plan(pool)
@@ -395,23 +396,26 @@ def test_attention_work_covers_every_visible_row_once(name):
             want = max(last_needed.get(p, -1), last_needed.get(p + 1, -1))
             if items[p][4] == items[p + 1][4] and items[p][3] == items[p + 1][3]:
                 assert items[p][4] - 1 == want, (name, p)
-    # launch order
-    n_pairs = (len(items) + 1) // 2
-    assert len(order) % 8 == 0 and len(order) >= n_pairs
-    got = order[order >= 0]
-    assert sorted(got.tolist()) == list(range(n_pairs))
-    steps = [max(int(it[4] - it[3] - (it[6] - it[5])) for it in items[2 * p:2 * p + 2]) for p in range(n_pairs)]
-    for x in range(8):
-        col = order[x::8]
-        live = col[col >= 0]
-        assert (col[len(live):] == -1).all()
-        if len(live):
-            assert sorted(live.tolist()) == list(range(min(live), max(live) + 1))
-            # longest first, in bands of a tenth of the longest (a pair costs
-            # its steps plus 2 of set-up); the work list's order inside a band
-            c = np.array([steps[p] + 2 for p in live])
-            band = (c.max() - c) * 10 // c.max()
-            assert (np.diff(band) >= 0).all()
-            assert all(live[i] < live[i + 1] for i in range(len(live) - 1) if band[i] == band[i + 1])
+    # launch orders: over item pairs (paired kernel), over single items
+    _, item_order = plan.attention_work(single_items=True)
+    for per_wg, seq in ((2, order), (1, item_order)):
+        n_units = (len(items) + per_wg - 1) // per_wg
+        assert len(seq) % 8 == 0 and len(seq) >= n_units
+        assert sorted(seq[seq >= 0].tolist()) == list(range(n_units))
+        steps = [max(int(it[4] - it[3] - (it[6] - it[5])) for it in items[per_wg * p:per_wg * (p + 1)])
+                 for p in range(n_units)]
+        for x in range(8):
+            col = seq[x::8]
+            live = col[col >= 0]
+            assert (col[len(live):] == -1).all()
+            if len(live):
+                assert sorted(live.tolist()) == list(range(min(live), max(live) + 1))
+                # longest first, in bands of a tenth of the longest (a unit
+                # costs its steps plus 2 of set-up); the work list's order
+                # inside a band
+                c = np.array([steps[p] + 2 for p in live])
+                band = (c.max() - c) * 10 // c.max()
+                assert (np.diff(band) >= 0).all()
+                assert all(live[i] < live[i + 1] for i in range(len(live) - 1) if band[i] == band[i + 1])
     plan.release()
     pool.release()
