@@ -448,16 +448,16 @@ int64_t lpt_makespan(const std::vector<int64_t>& costs, int32_t slots) {
 // Launch order over units of `per_wg` consecutive items (one workgroup each).
 std::vector<int32_t> launch_order(const std::vector<AttnWork>& w, int32_t per_wg, int32_t n_xcd,
                                   int32_t slots_per_xcd) {
-  const int32_t n_pairs = int32_t((w.size() + size_t(per_wg) - 1) / size_t(per_wg));
+  const int32_t n_units = int32_t((w.size() + size_t(per_wg) - 1) / size_t(per_wg));
   std::vector<int32_t> map;
-  if (n_pairs == 0) return map;
+  if (n_units == 0) return map;
   // a workgroup's items run side by side: its time is the longest one's
   // steps (skipped gap tiles excluded), plus set-up and the epilogue
   constexpr int64_t kSetupSteps = 2;
   auto steps = [](const AttnWork& x) { return int64_t(x.tile_end - x.tile_begin - (x.gap_end - x.gap_begin)); };
-  std::vector<int64_t> cost(static_cast<size_t>(n_pairs));
+  std::vector<int64_t> cost(static_cast<size_t>(n_units));
   int64_t total = 0;
-  for (int32_t p = 0; p < n_pairs; ++p) {
+  for (int32_t p = 0; p < n_units; ++p) {
     int64_t c = 0;
     for (int32_t k = 0; k < per_wg && size_t(per_wg * p + k) < w.size(); ++k)
       c = std::max(c, steps(w[size_t(per_wg * p + k)]));
@@ -466,7 +466,7 @@ std::vector<int32_t> launch_order(const std::vector<AttnWork>& w, int32_t per_wg
   }
   // candidate cuts: bounds[x] .. bounds[x + 1] is XCD x's range
   std::vector<int32_t> by_count(size_t(n_xcd) + 1), by_cost(size_t(n_xcd) + 1);
-  const int32_t q = n_pairs / n_xcd, r = n_pairs % n_xcd;
+  const int32_t q = n_units / n_xcd, r = n_units % n_xcd;
   for (int32_t x = 0; x <= n_xcd; ++x) by_count[size_t(x)] = x * q + std::min(x, r);
   {
     int64_t acc = 0;
@@ -475,11 +475,11 @@ std::vector<int32_t> launch_order(const std::vector<AttnWork>& w, int32_t per_wg
     for (int32_t x = 1; x < n_xcd; ++x) {
       const int64_t goal = total * x / n_xcd;
       // end the range where its running cost comes closest to the goal
-      while (p < n_pairs && acc + cost[size_t(p)] <= goal) acc += cost[size_t(p++)];
-      if (p < n_pairs && goal - acc > acc + cost[size_t(p)] - goal) acc += cost[size_t(p++)];
+      while (p < n_units && acc + cost[size_t(p)] <= goal) acc += cost[size_t(p++)];
+      if (p < n_units && goal - acc > acc + cost[size_t(p)] - goal) acc += cost[size_t(p++)];
       by_cost[size_t(x)] = p;
     }
-    by_cost[size_t(n_xcd)] = n_pairs;
+    by_cost[size_t(n_xcd)] = n_units;
   }
   // each range longest first.  Costs within a tenth of the range's longest
   // count as equal and keep the plan's order: the column blocks of one
