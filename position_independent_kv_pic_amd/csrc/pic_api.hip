@@ -445,7 +445,7 @@ pic_status pic_assemble(pic_plan* p, int32_t batch, const int32_t* span_ptr, con
     const bool qrot_layout = want_qrot && hp.qrot_ok;
     const pic::AttnSplit sp = pic::choose_attention_split(
         hp, pi.m.kv_heads, pi.m.group, pic::kAttnColsPerWG, pic::kAttnRowsPerTile, pic::kAttnTargetWGs,
-        pic::kAttnMaxSplit, /*min_tiles_per_split=*/4, qrot_layout ? 1 : pic::kAttnMinTilesAcross);
+        pic::kAttnMaxSplit, /*min_tiles_per_split=*/3, qrot_layout ? 1 : pic::kAttnMinTilesAcross);
     pic::build_attention_work(&hp, pi.m.kv_heads, pi.m.group, pic::kAttnColsPerWG, pic::kAttnRowsPerTile, sp);
     pic::finish_qrot(&hp);
     pic::build_wg_map(&hp, pic::kXcds, pic::kAttnTargetWGs / pic::kXcds);
