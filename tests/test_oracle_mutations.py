@@ -107,7 +107,30 @@ def _bf16_truncate(x):
     return b.view(np.float32).astype(np.float64)
 
 
-_ORIG = {n: getattr(orc, n) for n in ("rotate", "rope_frequencies", "plan_spans", "attention", "round_bf16")}
+_ORIG = {n: getattr(orc, n) for n in ("rotate", "rope_frequencies", "plan_spans", "attention", "round_bf16",
+                                     "prologue")}
+
+
+def _prologue_unrounded(q, k_new, v_new, pos_new, theta, dtype):
+    # q' and k' left in fp64: the new keys never take the cache's storage type
+    _, _, v = _ORIG["prologue"](q, k_new, v_new, pos_new, theta, dtype)
+    p = np.asarray(pos_new, dtype=np.float64)[:, None]
+    return orc.rotate(q, p, theta), orc.rotate(k_new, p, theta), v
+
+
+def _prologue_keys_unrounded(q, k_new, v_new, pos_new, theta, dtype):
+    qr, _, v = _ORIG["prologue"](q, k_new, v_new, pos_new, theta, dtype)
+    return qr, orc.rotate(k_new, np.asarray(pos_new, dtype=np.float64)[:, None], theta), v
+
+
+def _prologue_rotates_values(q, k_new, v_new, pos_new, theta, dtype):
+    qr, kr, _ = _ORIG["prologue"](q, k_new, v_new, pos_new, theta, dtype)
+    p = np.asarray(pos_new, dtype=np.float64)[:, None]
+    return qr, kr, orc.to_storage(orc.rotate(v_new, p, theta), dtype)
+
+
+def _prologue_position_off_by_one(q, k_new, v_new, pos_new, theta, dtype):
+    return _ORIG["prologue"](q, k_new, v_new, np.asarray(pos_new) + 1, theta, dtype)
 
 _orig_assemble = orc.assemble
 _orig_new_positions = orc.new_token_positions
@@ -147,6 +170,10 @@ MUTANTS = [
     ("attention", _attention_no_scale),
     ("round_bf16", _bf16_via_fp32),
     ("round_bf16", _bf16_truncate),
+    ("prologue", _prologue_unrounded),
+    ("prologue", _prologue_keys_unrounded),
+    ("prologue", _prologue_rotates_values),
+    ("prologue", _prologue_position_off_by_one),
 ]
 
 

@@ -452,3 +452,73 @@ def test_attention_weight_properties():
         vis = pos_rows <= pos_q[j]
         for h in range(hq):
             assert np.allclose(o[j, h], vals[h // 2][vis].mean(axis=0), atol=1e-13)
+
+
+# ---------------------------------------------------------------------------
+# new-token prologue: rotation to the token's position, one rounding
+# ---------------------------------------------------------------------------
+
+def bf16_nearest_ref(x):
+    """Nearest bfloat16 of each fp64 value (ties to even), built from bit patterns.
+
+    bf16 values are the fp32 values whose low 16 bits are zero.  The
+    candidates are the three such patterns around fp32(x); the difference of
+    x and a nearby candidate is exact in fp64 (Sterbenz), so the nearest one,
+    and a tie, are decided exactly; a tie goes to the candidate whose last
+    kept bit (bit 16) is 0.  Independent of the oracle's frexp/ldexp rounding.
+    """
+    x = np.asarray(x, np.float64)
+    out = np.empty_like(x)
+    for i, xv in np.ndenumerate(x):
+        u = int(np.array([xv], np.float32).view(np.uint32)[0])
+        sign, mag = u & 0x80000000, u & 0x7FFF0000
+        best, best_d = None, None
+        for m in (mag - 0x10000, mag, mag + 0x10000):
+            if m < 0:
+                continue
+            c = float(np.array([sign | m], np.uint32).view(np.float32)[0])
+            dist = abs(xv - c)
+            if best is None or dist < best_d or (dist == best_d and not (m & 0x10000)):
+                best, best_d, best_m = c, dist, m
+        out[i] = best
+    return out
+
+
+def _near_bf16_tie(x, tol):
+    """True where x lies within tol of a midpoint between two bf16 values."""
+    x = np.asarray(x, np.float64)
+    u = x.astype(np.float32).view(np.uint32) & np.uint32(0xFFFF0000)
+    lo = u.view(np.float32).astype(np.float64)
+    step = np.ldexp(1.0, np.frexp(np.where(lo == 0, 1e-30, lo))[1] - 8)
+    mids = np.stack([lo - step / 2, lo + step / 2, lo + 1.5 * step])
+    return np.any(np.abs(np.abs(x)[None] - np.abs(mids)) <= tol, axis=0)
+
+
+@pytest.mark.parametrize("theta", [1e4, 1e6])
+def test_prologue_rounds_rotated_queries_and_keys_once(theta):
+    # KV_M(q; C_ctx) (CoinRAG page, section 2.3): new tokens are rotated to
+    # their positions and their K' is appended to the cache in its storage
+    # type; q' and k' are R(P) q and R(P) k rounded once, v is untouched
+    gen = torch.Generator().manual_seed(31)
+    n, hq, hkv, d = 5, 4, 2, 128
+    bf = lambda *s: torch.randn(*s, generator=gen, dtype=torch.float64).to(torch.bfloat16).double().numpy()
+    q, k, v = bf(n, hq, d), bf(n, hkv, d), bf(n, hkv, d)
+    pos = np.array([0, 3, 77, 1000, 2999])
+    qr, kr, vr = orc.prologue(q, k, v, pos, theta, "bf16")
+    for got, x in ((qr, q), (kr, k)):
+        exact = rope_ref(x, theta, pos[:, None])
+        want = bf16_nearest_ref(exact)
+        # the matrix exponential is accurate to about 1e-13 per radian; an
+        # element that close to a rounding tie may go either way
+        tol = 1e-13 * (1.0 + pos.max()) * np.abs(x).max()
+        ok = (got == want) | (_near_bf16_tie(exact, tol) & (np.abs(got - exact) <= np.abs(want - exact) + tol))
+        assert ok.all(), f"{int((~ok).sum())} elements are not the once-rounded rotation"
+        assert np.array_equal(got[0], x[0])            # P = 0: R(0) = I, a copy
+    assert np.array_equal(vr, v) and np.array_equal(np.signbit(vr), np.signbit(v))
+    # the same with fp32 storage: fp32-representable and within half an fp32 ulp
+    qf, kf, _ = orc.prologue(q, k, v, pos, theta, "f32")
+    for got, x in ((qf, q), (kf, k)):
+        exact = rope_ref(x, theta, pos[:, None])
+        assert np.array_equal(got, got.astype(np.float32).astype(np.float64))
+        half_ulp = np.spacing(np.abs(exact).astype(np.float32)).astype(np.float64) / 2
+        assert np.all(np.abs(got - exact) <= half_ulp + 1e-13 * (1.0 + pos.max()) * np.abs(x).max())
