@@ -13,12 +13,10 @@ Prints one JSON line.  `value` is the whole step's attention throughput
 time count against it); per-kernel rates, latency percentiles, the roofline of
 the dominant kernel and the CPU-oracle baseline ride along.
 
-    python bench.py [--steps K] [--warmup W] [--workload NAME] [--variant M|F|FQ]
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--variant M|F]
 
 Variants: M gathers the prefix (assembly kernel) and attends over it; F
-reads the pool inside attention, rotating keys on load; FQ reads the pool
-inside attention, scoring against queries rotated back per 32-row block (opt
-in: it skips the bf16 rounding of the re-rotated keys, see the header).
+reads the pool inside attention, rotating keys on load.
 """
 from __future__ import annotations
 
@@ -46,12 +44,13 @@ def log(*a):
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=40)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="turborag_b16")
-    ap.add_argument("--variant", default="M", choices=["M", "F", "FQ"])
+    ap.add_argument("--variant", default="M", choices=["M", "F"])
     ap.add_argument("--layouts", type=int, default=8, help="pre-generated batch layouts to cycle through")
-    ap.add_argument("--cpu-seconds", type=float, default=20.0, help="time budget of the oracle sample")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="time budget of each oracle sample (all cores, then one thread)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--values-in-pool", action="store_true",
                     help="variant M: gather keys only and let attention read the prefix values in the pool "
@@ -89,13 +88,12 @@ def percentile(xs, q):
     return s[k]
 
 
-def cpu_baseline(wl, pool, dw, budget_s: float):
-    """Time the fp64 oracle on a bounded sample of the same workload: requests
-    in order, every layer of each, until the time budget is spent (or the
-    whole batch is done).  Only the oracle's own work is timed, not the
-    read-back of its inputs."""
+def _oracle_sample(wl, pool, dw, budget_s: float):
+    """Time the fp64 oracle on requests in order, every layer of each, until
+    the time budget is spent (or the whole batch is done).  Only the oracle's
+    own work is timed, not the read-back of its inputs.  Returns (attention
+    FLOPs of the sample, seconds, (request, layer) pairs, requests touched)."""
     import numpy as np
-    import threadpoolctl
     from oracle import pic_oracle as orc
     import workloads as W
     m = wl.model
@@ -134,12 +132,39 @@ def cpu_baseline(wl, pool, dw, budget_s: float):
         done_reqs = b + 1
         if spent >= budget_s:
             break
+    return flops, spent, pairs, done_reqs
+
+
+def cpu_baseline(wl, pool, dw, budget_s: float):
+    """The fp64 oracle as it stands, on the host cores: once with every BLAS
+    thread numpy has, once limited to one thread, each on a sample of about
+    `budget_s` seconds of oracle time.  `value` is the all-threads rate."""
+    import threadpoolctl
+    affinity = sorted(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else []
     threads = max((d.get("num_threads", 1) for d in threadpoolctl.threadpool_info()), default=1)
-    return {"value": flops / spent / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{pairs} (request, layer) pairs of {wl.name} ({done_reqs} of {wl.batch} requests, "
-                      f"{m.layers} layers each): gather, re-rotation and attention in fp64 numpy, "
-                      f"{spent:.1f} s of oracle time; value = the sample's attention FLOPs / that time; "
-                      f"host has {os.cpu_count()} logical CPUs"}
+    fl, sec, pairs, reqs = _oracle_sample(wl, pool, dw, budget_s)
+    with threadpoolctl.threadpool_limits(1):
+        fl1, sec1, pairs1, _ = _oracle_sample(wl, pool, dw, budget_s)
+    return {"value": fl / sec / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{pairs} (request, layer) pairs of {wl.name} ({reqs} of {wl.batch} requests, "
+                      f"{wl.model.layers} layers each): gather, re-rotation and attention in fp64 numpy, "
+                      f"{sec:.1f} s of oracle time; value = the sample's attention FLOPs / that time",
+            "single_thread": {"value": fl1 / sec1 / 1e12, "unit": "TFLOP/s", "cores": 1,
+                              "sample": f"{pairs1} (request, layer) pairs, {sec1:.1f} s"},
+            "host": {"logical_cpus": os.cpu_count(), "affinity_cpus": len(affinity),
+                     "affinity": _ranges(affinity), "blas_threads": int(threads)}}
+
+
+def _ranges(cpus) -> str:
+    """CPU list as ranges, e.g. '0-15,32-47'."""
+    out, i = [], 0
+    while i < len(cpus):
+        j = i
+        while j + 1 < len(cpus) and cpus[j + 1] == cpus[j] + 1:
+            j += 1
+        out.append(f"{cpus[i]}-{cpus[j]}" if j > i else f"{cpus[i]}")
+        i = j + 1
+    return ",".join(out)
 
 
 def kernel_source_hash() -> str:
@@ -230,7 +255,7 @@ def main():
     import torch
     import workloads as W
     from workloads.device import open_workload
-    from position_independent_kv_pic_amd import (DEFER_GATHER, PLAN_ONLY, QUERY_ROTATION, VALUES_IN_POOL,
+    from position_independent_kv_pic_amd import (DEFER_GATHER, PLAN_ONLY, VALUES_IN_POOL,
                                                   VARIANT_FUSED, VARIANT_MATERIALIZED)
 
     assert torch.cuda.is_available(), "bench.py needs a ROCm GPU"
@@ -251,7 +276,7 @@ def main():
     tables = [(w.span_ptr(), w.spans_flat(), w.new_ptr(), w.new_pos_flat(), w.n_new_total) for w in wls]
     stream = torch.cuda.current_stream()
     plan = sess.plan
-    plan_flag = 0 if args.variant == "M" else PLAN_ONLY | (QUERY_ROTATION if args.variant == "FQ" else 0)
+    plan_flag = 0 if args.variant == "M" else PLAN_ONLY
     vpool = args.values_in_pool and args.variant == "M"
     if vpool:
         plan_flag |= VALUES_IN_POOL

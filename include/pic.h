@@ -104,7 +104,7 @@ typedef struct {
 #define PIC_ASSEMBLE_PLAN_ONLY 1     /* plan on host and device, gather nothing (variant F) */
 #define PIC_ASSEMBLE_DRY_RUN   2     /* validate and plan on the host only; touch no device */
 #define PIC_ASSEMBLE_DEFER_GATHER 4  /* plan now; gather layers later with pic_gather_layers */
-#define PIC_ASSEMBLE_QUERY_ROTATION 8  /* with PLAN_ONLY: variant F may rotate queries (pic_query_prefill) */
+#define PIC_ASSEMBLE_QUERY_ROTATION 8  /* retired: refused with PIC_EUNSUPPORTED (see pic_query_prefill) */
 #define PIC_ASSEMBLE_VALUES_IN_POOL 16 /* gather keys only; prefix values are read in the pool (below) */
 
 /* pic_query_prefill variants */
@@ -194,7 +194,7 @@ pic_status pic_plan_release(pic_plan* plan);
  *   asm_k, asm_v   device buffers [layers][kv_heads][asm_rows_capacity][head_dim]
  *                  of the model dtype, 16-byte aligned (may be NULL with DRY_RUN)
  *   asm_rows_capacity  rows per (layer, kv head) plane
- *   flags          0, PIC_ASSEMBLE_PLAN_ONLY (optionally | PIC_ASSEMBLE_QUERY_ROTATION),
+ *   flags          0, PIC_ASSEMBLE_PLAN_ONLY,
  *                  PIC_ASSEMBLE_DRY_RUN or PIC_ASSEMBLE_DEFER_GATHER; 0 and
  *                  DEFER_GATHER may add PIC_ASSEMBLE_VALUES_IN_POOL (bf16,
  *                  head_dim 128): the gather then writes keys only, leaves
@@ -253,22 +253,12 @@ pic_status pic_gather_layers(pic_plan* plan, int32_t layer_begin, int32_t layer_
  * over the request's rows r with pos_r <= pos_j.  Variant FUSED reads the
  * prefix rows straight from the pool (its plan may come from PLAN_ONLY) and
  * is implemented for bf16 with head_dim 128.  It applies each span's
- * re-rotation R(delta) on load, in one of two ways:
- *   - rotated keys: each key is rotated in registers (fp64 arithmetic, one
- *     rounding, so the scores equal variant M's bit for bit);
- *   - rotated queries (opt-in): since <q', R(delta) k> = <R(-delta) q', k>,
- *     a 32-row block whose rows share one delta is scored against the
- *     queries rotated back by delta (fp32 arithmetic, kept as two bf16
- *     terms, about 16 significant bits), with the stored keys copied
- *     unchanged.  Used when the assemble passed PIC_ASSEMBLE_PLAN_ONLY |
- *     PIC_ASSEMBLE_QUERY_ROTATION, keys are stored rotated and every 32-row
- *     block of the batch has a single delta
- *     (pic_plan_summary.fused_query_rotation).  It skips the bf16 rounding
- *     of each re-rotated key that the assembled cache applies, so it does
- *     not reproduce variant M's bits, and on caches with large key channels
- *     (x20 outliers) its outputs differ from variant M's by more than the
- *     attention tolerance; it is for callers that accept scores against
- *     exactly re-rotated keys.
+ * re-rotation R(delta) on load: each key is rotated in registers (fp64
+ * arithmetic, one rounding), so the scores equal variant M's bit for bit.
+ * (Scoring instead against queries rotated back by delta, since
+ * <q', R(delta) k> = <R(-delta) q', k>, would skip the rounding of each
+ * re-rotated key to the storage type and so not reproduce the assembled
+ * cache; PIC_ASSEMBLE_QUERY_ROTATION, which asked for it, is refused.)
  * MATERIALIZED needs the layer gathered (a full assemble, or
  * pic_gather_layers after a deferred one).  bf16 attention uses bf16 MFMA products with fp32 accumulation
  * and an fp32 online softmax; f32 attention computes in fp32.
@@ -324,7 +314,7 @@ typedef struct {
   int64_t rows;            /* prefix_rows + new_rows: rows used in each plane */
   int32_t max_position;    /* largest position of any row */
   int32_t materialized;    /* 1 if the prefix rows were gathered */
-  int32_t fused_query_rotation;  /* 1 if PIC_VARIANT_FUSED rotates queries instead of keys (below) */
+  int32_t fused_query_rotation;  /* always 0: query rotation is retired (kept for the layout) */
   int32_t values_in_pool;  /* 1 if the batch was assembled with PIC_ASSEMBLE_VALUES_IN_POOL */
   int32_t attention_items;       /* bf16 attention work items (0 for other models) */
   int32_t attention_workgroups;  /* entries of the paired kernel's launch order */

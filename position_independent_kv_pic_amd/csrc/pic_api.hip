@@ -59,6 +59,12 @@ struct pic_plan {
   std::vector<hipEvent_t> layer_ev;  // per layer: completion of a deferred gather
   std::vector<char> layer_ev_live;   // per layer: layer_ev was recorded for this batch
   hipEvent_t plan_ev = nullptr;      // the batch's plan kernels have been enqueued before it
+  // Calls on a plan share its device tables and scratch (rotated queries,
+  // split partials, merge counters, decode tables): the stream of the last
+  // such call, and an event recorded on it when a call comes on another one
+  hipStream_t last_stream = nullptr;
+  bool has_last_stream = false;
+  hipEvent_t switch_ev = nullptr;
   bool failed = false;
   char* asm_k = nullptr;
   char* asm_v = nullptr;
@@ -69,8 +75,8 @@ struct pic_plan {
   char* ws = nullptr;
   size_t ws_cap = 0;
   size_t off_spans = 0, off_crow = 0, off_reqs = 0, off_new_pos = 0, off_new_row = 0,
-         off_new_req = 0, off_work = 0, off_omega = 0, off_blk_ph = 0, off_wg_map = 0, off_item_map = 0, off_phase32 = 0, blob_bytes = 0;
-  size_t off_pos = 0, off_rowsrc = 0, off_tile_pos = 0, off_phase_tab = 0, off_phase_new = 0,
+         off_new_req = 0, off_work = 0, off_omega = 0, off_wg_map = 0, off_item_map = 0, blob_bytes = 0;
+  size_t off_pos = 0, off_rowsrc = 0, off_gsrc = 0, off_tile_pos = 0, off_phase_tab = 0, off_phase_new = 0,
          off_qrot = 0, off_opart = 0, off_ml = 0, off_spart = 0, off_sml = 0, off_count = 0,
          ws_bytes = 0;
 
@@ -108,8 +114,8 @@ struct Timed {
   int k;
   hipStream_t s;
   hipEvent_t stop = nullptr;
-  Timed(pic_plan* plan, int kernel, hipStream_t stream) : p(plan), k(kernel), s(stream) {
-    if (!p->timing) return;
+  Timed(pic_plan* plan, int kernel, hipStream_t stream, bool on = true) : p(plan), k(kernel), s(stream) {
+    if (!p->timing || !on) return;
     auto& v = p->events[k];
     if (p->used[k] == v.size()) {
       hipEvent_t a = nullptr, b = nullptr;
@@ -141,6 +147,45 @@ pic_status ensure_pool_device(pic_pool* pool) {
   return PIC_OK;
 }
 
+// Device scratch of one prefill call: rotated queries, split partials and
+// merge counters.
+struct PrefillScratch {
+  char* q_rot;
+  float* opart;
+  float2* ml;
+  float* spart;
+  float* sml;
+  int32_t* count;
+};
+
+// Byte offsets of a prefill's scratch inside one buffer, each 256-aligned,
+// and its total size (the same quantities layout_workspace reserves).
+struct ScratchLayout {
+  size_t q_rot = 0, opart = 0, ml = 0, spart = 0, sml = 0, count = 0, bytes = 0;
+};
+
+ScratchLayout prefill_scratch_layout(const pic::ModelInfo& m, const pic::HostPlan& hp) {
+  ScratchLayout l;
+  size_t o = 0;
+  auto take = [&o](size_t bytes) {
+    size_t at = o;
+    o = align256(o + bytes);
+    return at;
+  };
+  l.q_rot = take(size_t(hp.new_rows) * m.q_heads * m.head_dim * m.elem_bytes);
+  const size_t nsplit = hp.n_split_out > 1 ? size_t(hp.n_split_out) : 0;
+  l.opart = take(nsplit * size_t(hp.new_rows) * m.q_heads * m.head_dim * sizeof(float));
+  l.ml = take(nsplit * size_t(hp.new_rows) * m.q_heads * sizeof(float2));
+  // row splits merged inside the attention kernel: per column block and
+  // split, 4 waves of 64 lanes x (64 floats of O + (m, sum)), and a counter
+  const size_t split_waves = size_t(hp.n_slots) * size_t(hp.n_split_wg > 1 ? hp.n_split_wg : 0) * 4;
+  l.spart = take(split_waves * 64 * 64 * sizeof(float));
+  l.sml = take(split_waves * 64 * 2 * sizeof(float));
+  l.count = take(size_t(hp.n_slots) * sizeof(int32_t));
+  l.bytes = o;
+  return l;
+}
+
 void layout_workspace(pic_plan* p) {
   const pic::ModelInfo& m = p->pool->info.m;
   const pic::HostPlan& hp = p->hp;
@@ -159,26 +204,24 @@ void layout_workspace(pic_plan* p) {
   p->off_new_req = take(hp.new_req.size() * sizeof(int32_t));
   p->off_work = take(hp.work.size() * sizeof(pic::AttnWork));
   p->off_omega = take(half * sizeof(double));
-  p->off_blk_ph = take(hp.blk_ph.size() * sizeof(int32_t));
   p->off_wg_map = take(hp.wg_map.size() * sizeof(int32_t));
   p->off_item_map = take(hp.item_map.size() * sizeof(int32_t));
   p->blob_bytes = o;
   p->off_pos = take(size_t(hp.rows) * sizeof(int32_t));
   p->off_rowsrc = take(size_t(hp.rows) * sizeof(int2));
+  p->off_gsrc = take(size_t(hp.prefix_rows) * sizeof(int4));
   p->off_tile_pos = take(size_t(hp.n_tiles) * sizeof(int2));
   p->off_phase_tab = take(size_t(hp.phase_rows) * half * sizeof(pic::Phase));
   p->off_phase_new = take(size_t(hp.new_rows) * half * sizeof(pic::Phase));
-  p->off_phase32 = take(size_t(hp.phase_rows) * half * sizeof(float2));
-  p->off_qrot = take(size_t(hp.new_rows) * m.q_heads * m.head_dim * m.elem_bytes);
-  const size_t nsplit = hp.n_split_out > 1 ? size_t(hp.n_split_out) : 0;
-  p->off_opart = take(nsplit * size_t(hp.new_rows) * m.q_heads * m.head_dim * sizeof(float));
-  p->off_ml = take(nsplit * size_t(hp.new_rows) * m.q_heads * sizeof(float2));
-  // row splits merged inside the attention kernel: per column block and
-  // split, 4 waves of 64 lanes x (64 floats of O + (m, sum)), and a counter
-  const size_t split_waves = size_t(hp.n_slots) * size_t(hp.n_split_wg > 1 ? hp.n_split_wg : 0) * 4;
-  p->off_spart = take(split_waves * 64 * 64 * sizeof(float));
-  p->off_sml = take(split_waves * 64 * 2 * sizeof(float));
-  p->off_count = take(size_t(hp.n_slots) * sizeof(int32_t));
+  // the prefill's scratch (rotated queries, split partials, merge counters)
+  const ScratchLayout sl = prefill_scratch_layout(m, hp);
+  const size_t sb = take(sl.bytes);
+  p->off_qrot = sb + sl.q_rot;
+  p->off_opart = sb + sl.opart;
+  p->off_ml = sb + sl.ml;
+  p->off_spart = sb + sl.spart;
+  p->off_sml = sb + sl.sml;
+  p->off_count = sb + sl.count;
   p->ws_bytes = o;
 }
 
@@ -259,21 +302,16 @@ pic_status gather_layers(pic_plan* p, int32_t l0, int32_t l1, hipStream_t s, boo
   if (h.prefix_rows > 0 && l1 > l0) {
     Timed tm(p, 0, s);
     pic::GatherArgs ga;
-    ga.spans = reinterpret_cast<const pic::SpanRec*>(p->ws + p->off_spans);
-    ga.crow = reinterpret_cast<const int32_t*>(p->ws + p->off_crow);
-    ga.page_ids = p->pool->d_page_ids;
+    ga.gsrc = reinterpret_cast<const int4*>(p->ws + p->off_gsrc);
     ga.phase_tab = reinterpret_cast<const pic::Phase*>(p->ws + p->off_phase_tab);
-    ga.per_position = pi.m.key_storage == PIC_KEYS_UNROTATED;
     ga.pool = static_cast<const char*>(pi.device_base);
     ga.asm_k = p->asm_k;
     ga.asm_v = p->asm_v;
     ga.prefix_rows = h.prefix_rows;
     ga.cap = p->cap;
     ga.page_bytes = pi.page_bytes;
-    ga.n_spans = h.n_spans;
     ga.page_shift = pi.page_shift;
     ga.page_tokens = pi.page_tokens;
-    ga.layers = pi.m.layers;
     ga.kv_heads = pi.m.kv_heads;
     ga.planes_per_block = 4;   // 2, 4, 8, 16 measured: 4 is 3% faster than 8 on turborag_b16
     ga.plane_begin = l0 * pi.m.kv_heads;
@@ -294,6 +332,27 @@ pic_status gather_layers(pic_plan* p, int32_t l0, int32_t l1, hipStream_t s, boo
     if (e != hipSuccess) return device_error(p, e, "record a layer event");
     p->layer_ev_live[size_t(l)] = 1;
   }
+  return PIC_OK;
+}
+
+// Order a call that uses the plan's device tables or scratch on stream s
+// after every earlier such call: when the previous one went to another
+// stream, s waits for everything enqueued on that stream so far (an event
+// recorded on it now).  Calls on one stream are ordered by the stream itself
+// and cost nothing here.
+pic_status order_after_last_call(pic_plan* p, hipStream_t s) {
+  if (p->has_last_stream && p->last_stream != s) {
+    if (!p->switch_ev) {
+      hipError_t e = hipEventCreateWithFlags(&p->switch_ev, hipEventDisableTiming);
+      if (e != hipSuccess) return device_error(p, e, "create the stream-switch event");
+    }
+    hipError_t e = hipEventRecord(p->switch_ev, p->last_stream);
+    if (e != hipSuccess) return device_error(p, e, "record the stream-switch event");
+    e = hipStreamWaitEvent(s, p->switch_ev, 0);
+    if (e != hipSuccess) return device_error(p, e, "wait for the previous stream");
+  }
+  p->last_stream = s;
+  p->has_last_stream = true;
   return PIC_OK;
 }
 
@@ -392,6 +451,7 @@ pic_status pic_plan_release(pic_plan* p) {
   if (p->staging) (void)hipHostFree(p->staging);
   if (p->staging_ev) (void)hipEventDestroy(p->staging_ev);
   if (p->plan_ev) (void)hipEventDestroy(p->plan_ev);
+  if (p->switch_ev) (void)hipEventDestroy(p->switch_ev);
   for (hipEvent_t e : p->layer_ev)
     if (e) (void)hipEventDestroy(e);
   for (auto& v : p->events)
@@ -414,8 +474,11 @@ pic_status pic_assemble(pic_plan* p, int32_t batch, const int32_t* span_ptr, con
     return set_err(PIC_EINVAL, "unknown flags 0x%x", flags);
   if ((flags & PIC_ASSEMBLE_PLAN_ONLY) && (flags & PIC_ASSEMBLE_DEFER_GATHER))
     return set_err(PIC_EINVAL, "PIC_ASSEMBLE_PLAN_ONLY and PIC_ASSEMBLE_DEFER_GATHER exclude each other");
-  if ((flags & PIC_ASSEMBLE_QUERY_ROTATION) && !(flags & PIC_ASSEMBLE_PLAN_ONLY))
-    return set_err(PIC_EINVAL, "PIC_ASSEMBLE_QUERY_ROTATION needs PIC_ASSEMBLE_PLAN_ONLY");
+  if (flags & PIC_ASSEMBLE_QUERY_ROTATION)
+    return set_err(PIC_EUNSUPPORTED,
+                   "PIC_ASSEMBLE_QUERY_ROTATION is retired: scoring against queries rotated back by each "
+                   "span's delta skips the storage rounding of the re-rotated keys, so it does not reproduce "
+                   "the assembled cache's results; variant F rotates the keys on load instead");
   const bool values_in_pool = (flags & PIC_ASSEMBLE_VALUES_IN_POOL) != 0;
   if (values_in_pool && (flags & PIC_ASSEMBLE_PLAN_ONLY))
     return set_err(PIC_EINVAL, "PIC_ASSEMBLE_VALUES_IN_POOL applies to a gathered batch, not PLAN_ONLY");
@@ -437,21 +500,11 @@ pic_status pic_assemble(pic_plan* p, int32_t batch, const int32_t* span_ptr, con
                                   p->decode_rows_next, &hp, &err);
   if (st != PIC_OK) return set_err(st, "%s", err.c_str());
   if (pi.m.dtype == PIC_BF16 && pi.m.head_dim == 128) {
-    pic::build_qrot_blocks(&hp, pi.m.key_storage == PIC_KEYS_ROTATED, pic::kAttnRowsPerTile);
-    // query rotation asked for and possible: keep every workgroup's column
-    // blocks on shared rows (its queries then fit in LDS next to one stream
-    // of tiles)
-    const bool want_qrot = plan_only && (flags & PIC_ASSEMBLE_QUERY_ROTATION) != 0;
-    const bool qrot_layout = want_qrot && hp.qrot_ok;
     const pic::AttnSplit sp = pic::choose_attention_split(
         hp, pi.m.kv_heads, pi.m.group, pic::kAttnColsPerWG, pic::kAttnRowsPerTile, pic::kAttnTargetWGs,
-        pic::kAttnMaxSplit, /*min_tiles_per_split=*/3, qrot_layout ? 1 : pic::kAttnMinTilesAcross);
+        pic::kAttnMaxSplit, /*min_tiles_per_split=*/3, pic::kAttnMinTilesAcross);
     pic::build_attention_work(&hp, pi.m.kv_heads, pi.m.group, pic::kAttnColsPerWG, pic::kAttnRowsPerTile, sp);
-    pic::finish_qrot(&hp);
     pic::build_wg_map(&hp, pic::kXcds, pic::kAttnTargetWGs / pic::kXcds);
-    // otherwise the fused variant rotates keys (the same bits as the
-    // materialised variant)
-    if (!want_qrot) hp.qrot = false;
   }
   p->dec.step = -1;  // decode tables describe the previous batch
   if (dry) {
@@ -471,6 +524,15 @@ pic_status pic_assemble(pic_plan* p, int32_t batch, const int32_t* span_ptr, con
   st = ensure_pool_device(p->pool);
   if (st != PIC_OK) return st;
 
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  st = order_after_last_call(p, s);
+  if (st != PIC_OK) return st;
+  // deferred gathers of the previous batch may still read its tables
+  for (size_t l = 0; l < p->layer_ev_live.size(); ++l) {
+    if (!p->layer_ev_live[l]) continue;
+    hipError_t e = hipStreamWaitEvent(s, p->layer_ev[l], 0);
+    if (e != hipSuccess) return device_error(p, e, "wait for the previous batch's gathers");
+  }
   p->hp = std::move(hp);
   p->has_batch = false;
   p->values_in_pool = values_in_pool;
@@ -480,7 +542,6 @@ pic_status pic_assemble(pic_plan* p, int32_t batch, const int32_t* span_ptr, con
   p->asm_v = static_cast<char*>(asm_v);
   p->cap = asm_rows_capacity;
   const pic::HostPlan& h = p->hp;
-  hipStream_t s = static_cast<hipStream_t>(stream);
   if (batch == 0 || h.rows == 0) {
     p->has_batch = true;
     p->materialized = !plan_only && !defer;
@@ -507,7 +568,6 @@ pic_status pic_assemble(pic_plan* p, int32_t batch, const int32_t* span_ptr, con
   put(p->staging, p->off_new_req, h.new_req);
   put(p->staging, p->off_work, h.work);
   put(p->staging, p->off_omega, omega);
-  put(p->staging, p->off_blk_ph, h.blk_ph);
   put(p->staging, p->off_wg_map, h.wg_map);
   put(p->staging, p->off_item_map, h.item_map);
   {
@@ -532,11 +592,11 @@ pic_status pic_assemble(pic_plan* p, int32_t batch, const int32_t* span_ptr, con
     pa.prefix_rows = h.prefix_rows;
     pa.pos = reinterpret_cast<int32_t*>(p->ws + p->off_pos);
     pa.rowsrc = reinterpret_cast<int2*>(p->ws + p->off_rowsrc);
+    pa.gsrc = reinterpret_cast<int4*>(p->ws + p->off_gsrc);
     pa.phase_tab = reinterpret_cast<pic::Phase*>(p->ws + p->off_phase_tab);
     pa.per_position = pi.m.key_storage == PIC_KEYS_UNROTATED;
     pa.phase_rows = h.phase_rows;
     pa.phase_new = reinterpret_cast<pic::Phase*>(p->ws + p->off_phase_new);
-    pa.phase32 = reinterpret_cast<float2*>(p->ws + p->off_phase32);
     pa.reqs = reinterpret_cast<const pic::ReqRec*>(p->ws + p->off_reqs);
     pa.batch = h.batch;
     pa.n_tiles = h.n_tiles;
@@ -549,6 +609,10 @@ pic_status pic_assemble(pic_plan* p, int32_t batch, const int32_t* span_ptr, con
   if (!p->plan_ev) {
     hipError_t e = hipEventCreateWithFlags(&p->plan_ev, hipEventDisableTiming);
     if (e != hipSuccess) return device_error(p, e, "create the plan event");
+  }
+  if (!p->switch_ev) {
+    hipError_t e = hipEventCreateWithFlags(&p->switch_ev, hipEventDisableTiming);
+    if (e != hipSuccess) return device_error(p, e, "create the stream-switch event");
   }
   {
     hipError_t e = hipEventRecord(p->plan_ev, s);
@@ -585,8 +649,12 @@ pic_status pic_gather_layers(pic_plan* p, int32_t layer_begin, int32_t layer_end
   return ok();
 }
 
-pic_status pic_query_prefill(pic_plan* p, int32_t layer, const void* q, const void* k_new,
-                             const void* v_new, void* out, int32_t variant, void* stream) {
+}  // extern "C"
+
+namespace {
+
+pic_status prefill_impl(pic_plan* p, int32_t layer, const void* q, const void* k_new, const void* v_new,
+                        void* out, int32_t variant, void* stream, const PrefillScratch* ext) {
   if (!p) return set_err(PIC_EINVAL, "plan is NULL");
   if (p->failed) return set_err(PIC_ESTATE, "plan is unusable after a device error");
   if (!p->has_batch || !p->asm_k)
@@ -606,12 +674,28 @@ pic_status pic_query_prefill(pic_plan* p, int32_t layer, const void* q, const vo
                    variant, m.dtype, m.head_dim);
   const pic::HostPlan& h = p->hp;
   if (h.new_rows == 0) return ok();
+  // the plan's own scratch, or the caller-provided one
+  PrefillScratch sc;
+  if (ext) {
+    sc = *ext;
+  } else {
+    sc.q_rot = p->ws + p->off_qrot;
+    sc.opart = reinterpret_cast<float*>(p->ws + p->off_opart);
+    sc.ml = reinterpret_cast<float2*>(p->ws + p->off_ml);
+    sc.spart = reinterpret_cast<float*>(p->ws + p->off_spart);
+    sc.sml = reinterpret_cast<float*>(p->ws + p->off_sml);
+    sc.count = reinterpret_cast<int32_t*>(p->ws + p->off_count);
+  }
+  // timing brackets create events on first use: only on the plan's own path
+  const bool timed = p->timing && !ext;
   if (!q || !k_new || !v_new || !out) return set_err(PIC_EINVAL, "q, k_new, v_new and out are required");
   if (!aligned16(q) || !aligned16(k_new) || !aligned16(v_new) || !aligned16(out))
     return set_err(PIC_EALIGN, "q, k_new, v_new and out must be 16-byte aligned");
   pic_status st = check_device(p);
   if (st != PIC_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  st = order_after_last_call(p, s);
+  if (st != PIC_OK) return st;
   if (!fused) {
     st = await_layer(p, layer, s);
     if (st != PIC_OK) return st;
@@ -620,7 +704,7 @@ pic_status pic_query_prefill(pic_plan* p, int32_t layer, const void* q, const vo
   char* kpl = p->asm_k + int64_t(layer) * m.kv_heads * plane_bytes;
   char* vpl = p->asm_v + int64_t(layer) * m.kv_heads * plane_bytes;
   {
-    Timed tm(p, 1, s);
+    Timed tm(p, 1, s, timed);
     pic::PrologueArgs pa;
     pa.q = static_cast<const char*>(q);
     pa.k_new = static_cast<const char*>(k_new);
@@ -628,7 +712,7 @@ pic_status pic_query_prefill(pic_plan* p, int32_t layer, const void* q, const vo
     pa.new_pos = reinterpret_cast<const int32_t*>(p->ws + p->off_new_pos);
     pa.new_row = reinterpret_cast<const int32_t*>(p->ws + p->off_new_row);
     pa.phase_new = reinterpret_cast<const pic::Phase*>(p->ws + p->off_phase_new);
-    pa.q_rot = p->ws + p->off_qrot;
+    pa.q_rot = sc.q_rot;
     pa.asm_k = kpl;
     pa.asm_v = vpl;
     pa.cap = p->cap;
@@ -639,11 +723,11 @@ pic_status pic_query_prefill(pic_plan* p, int32_t layer, const void* q, const vo
     if (e != hipSuccess) return device_error(p, e, "prologue kernel");
   }
   {
-    Timed tm(p, 2, s);
+    Timed tm(p, 2, s, timed);
     hipError_t e;
     if (m.dtype == PIC_BF16) {
       pic::AttnArgs aa;
-      aa.q_rot = reinterpret_cast<const uint16_t*>(p->ws + p->off_qrot);
+      aa.q_rot = reinterpret_cast<const uint16_t*>(sc.q_rot);
       aa.k_plane = reinterpret_cast<const uint16_t*>(kpl);
       aa.v_plane = reinterpret_cast<const uint16_t*>(vpl);
       aa.cap = p->cap;
@@ -659,14 +743,14 @@ pic_status pic_query_prefill(pic_plan* p, int32_t layer, const void* q, const vo
       aa.n_split_out = h.n_split_out;
       aa.paired = h.n_split > 1;
       aa.n_split_wg = h.n_split_wg;
-      aa.split_count = reinterpret_cast<int32_t*>(p->ws + p->off_count);
-      aa.spart = reinterpret_cast<float*>(p->ws + p->off_spart);
-      aa.sml = reinterpret_cast<float*>(p->ws + p->off_sml);
+      aa.split_count = sc.count;
+      aa.spart = sc.spart;
+      aa.sml = sc.sml;
       aa.decode = 0;
       aa.scale_log2 = float(1.4426950408889634 / std::sqrt(double(m.head_dim)));
       aa.out = static_cast<uint16_t*>(out);
-      aa.opart = reinterpret_cast<float*>(p->ws + p->off_opart);
-      aa.ml = reinterpret_cast<float2*>(p->ws + p->off_ml);
+      aa.opart = sc.opart;
+      aa.ml = sc.ml;
       aa.pool = static_cast<const char*>(pi.device_base);
       aa.rowsrc = reinterpret_cast<const int2*>(p->ws + p->off_rowsrc);
       aa.phase_tab = reinterpret_cast<const pic::Phase*>(p->ws + p->off_phase_tab);
@@ -676,13 +760,10 @@ pic_status pic_query_prefill(pic_plan* p, int32_t layer, const void* q, const vo
       aa.page_shift = pi.page_shift;
       aa.page_tokens = pi.page_tokens;
       aa.kv_heads = m.kv_heads;
-      aa.qrot = fused && h.qrot ? 1 : 0;
       aa.v_pool = !fused && p->values_in_pool ? 1 : 0;
-      aa.blk_ph = reinterpret_cast<const int32_t*>(p->ws + p->off_blk_ph);
-      aa.phase32 = reinterpret_cast<const float2*>(p->ws + p->off_phase32);
-      // launch order: the fused variant without row splits or query rotation
-      // runs one item per workgroup, every other kernel a pair
-      const bool unpaired = fused && !aa.qrot && !aa.paired;
+      // launch order: the fused variant without row splits runs one item per
+      // workgroup, every other kernel a pair
+      const bool unpaired = fused && !aa.paired;
       const std::vector<int32_t>& order = unpaired ? h.item_map : h.wg_map;
       aa.wg_map = order.empty() ? nullptr
                                 : reinterpret_cast<const int32_t*>(p->ws + (unpaired ? p->off_item_map : p->off_wg_map));
@@ -690,7 +771,7 @@ pic_status pic_query_prefill(pic_plan* p, int32_t layer, const void* q, const vo
       e = pic::launch_attention_bf16(aa, fused, s);
     } else {
       pic::AttnF32Args aa;
-      aa.q_rot = p->ws + p->off_qrot;
+      aa.q_rot = sc.q_rot;
       aa.k_plane = kpl;
       aa.v_plane = vpl;
       aa.cap = p->cap;
@@ -707,6 +788,15 @@ pic_status pic_query_prefill(pic_plan* p, int32_t layer, const void* q, const vo
     if (e != hipSuccess) return device_error(p, e, "attention kernel");
   }
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+pic_status pic_query_prefill(pic_plan* p, int32_t layer, const void* q, const void* k_new,
+                             const void* v_new, void* out, int32_t variant, void* stream) {
+  return prefill_impl(p, layer, q, k_new, v_new, out, variant, stream, nullptr);
 }
 
 pic_status pic_plan_set_decode_rows(pic_plan* p, int32_t rows) {
@@ -741,6 +831,8 @@ pic_status pic_decode_layer(pic_plan* p, int32_t layer, int32_t step, const void
   pic_status st = check_device(p);
   if (st != PIC_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  st = order_after_last_call(p, s);
+  if (st != PIC_OK) return st;
   if (!fused) {
     st = await_layer(p, layer, s);
     if (st != PIC_OK) return st;
@@ -862,10 +954,7 @@ pic_status pic_decode_layer(pic_plan* p, int32_t layer, int32_t step, const void
     aa.spart = nullptr;
     aa.sml = nullptr;
     aa.decode = 1;
-    aa.qrot = 0;
     aa.v_pool = !fused && p->values_in_pool ? 1 : 0;
-    aa.blk_ph = nullptr;
-    aa.phase32 = nullptr;
     aa.scale_log2 = float(1.4426950408889634 / std::sqrt(double(m.head_dim)));
     aa.out = static_cast<uint16_t*>(out);
     aa.opart = reinterpret_cast<float*>(p->dws + p->d_opart);
@@ -895,7 +984,7 @@ pic_status pic_plan_get_summary(const pic_plan* p, pic_plan_summary* out) {
   out->rows = p->hp.rows;
   out->max_position = p->hp.max_position;
   out->materialized = p->materialized ? 1 : 0;
-  out->fused_query_rotation = p->hp.qrot ? 1 : 0;
+  out->fused_query_rotation = 0;
   out->values_in_pool = p->values_in_pool ? 1 : 0;
   out->attention_items = int32_t(p->hp.work.size());
   out->attention_workgroups = int32_t(p->hp.wg_map.size());

@@ -25,9 +25,9 @@ struct PlanArgs {
   int64_t prefix_rows;
   int32_t* pos;             // [rows]
   int2* rowsrc;             // [rows]: (pool token slot, phase_tab row or -1 for no rotation)
+  int4* gsrc;               // [prefix_rows]: per gathered row (assembled row, pool slot, phase row or -1, 0)
   Phase* phase_tab;         // [phase_rows][half_dim]: per span delta, or per position
   Phase* phase_new;         // [n_new][half_dim]
-  float2* phase32;          // [phase_rows][half_dim]: phase_tab rounded to fp32
   const ReqRec* reqs;       // for the tile bounds
   int32_t batch, n_tiles;
   int2* tile_pos;           // [n_tiles]: (min, max) row position; max = INT_MAX for a partial tile
@@ -36,16 +36,13 @@ struct PlanArgs {
 };
 
 struct GatherArgs {
-  const SpanRec* spans;
-  const int32_t* crow;
-  const int32_t* page_ids;
+  const int4* gsrc;         // [prefix_rows]: (assembled row, pool slot, phase_tab row or -1, 0)
   const Phase* phase_tab;   // per span (rotated keys) or per position (un-rotated keys)
   const char* pool;
   char* asm_k;
   char* asm_v;
   int64_t prefix_rows, cap, page_bytes;
-  int32_t n_spans, page_shift, page_tokens, layers, kv_heads, planes_per_block;
-  int32_t per_position;     // keys stored un-rotated: rotate each row by its new position
+  int32_t page_shift, page_tokens, kv_heads, planes_per_block;
   int32_t plane_begin, plane_end;  // (layer, kv head) planes l * Hkv + h to gather
   int32_t values;           // 0: keys only (values stay in the pool, attention reads them there)
 };
@@ -97,15 +94,9 @@ struct AttnArgs {
   int64_t kv_plane_off;     // byte offset of (layer, K, head 0) inside a page
   int64_t v_off;            // byte offset from a K row to its V row inside a page
   int32_t page_shift, page_tokens, kv_heads;
-  // fused variant with query rotation (qrot): keys stay as stored and each
-  // 32-row block's rows are scored against the queries rotated back by the
-  // block's delta
-  int32_t qrot;
-  const int32_t* blk_ph;    // [2 n_tiles]: phase-table row of each 32-row block (-1: none)
   // assembled-plane variant with values left in the pool: prefix rows' values
   // are copied from the pool pages (through rowsrc), the rest from v_plane
   int32_t v_pool;
-  const float2* phase32;    // [phase_rows][64]: (cos, sin) in fp32
 };
 
 struct AttnF32Args {

@@ -162,6 +162,7 @@ __global__ __launch_bounds__(256) void plan_rows_kernel(PlanArgs a) {
     // -1 where the rotation is by 0 (a bit copy)
     const int ph = a.per_position ? (p != 0 ? p : -1) : (s.delta != 0 ? sp : -1);
     a.rowsrc[row] = make_int2(slot, ph);
+    a.gsrc[i] = make_int4(row, slot, ph, 0);
   } else if (i < a.prefix_rows + a.n_new) {
     int u = int(i - a.prefix_rows);
     int row = a.new_row[u];
@@ -189,7 +190,6 @@ __global__ __launch_bounds__(256) void plan_phase_kernel(PlanArgs a) {
   double ang = p * a.omega[k];
   const double c = cos(ang), sn = sin(ang);
   *dst = make_double2(c, sn);
-  if (which < a.phase_rows) a.phase32[which * a.half_dim + k] = make_float2(float(c), float(sn));
 }
 
 __global__ __launch_bounds__(256) void decode_plan_kernel(DecodePlanArgs a) {
@@ -240,7 +240,9 @@ __global__ __launch_bounds__(256) void plan_tiles_kernel(PlanArgs a) {
 // lane j owns the 16-byte vector j of the first half of the row and vector j
 // of the second half, so the half-split rotation pairs stay in one lane.  A
 // block covers 256 / LPR rows of the span table and `planes_per_block`
-// (layer, kv head) planes, reusing each row's source lookup and phases.
+// (layer, kv head) planes, reusing each row's source record and phases.  The
+// record (assembled row, pool slot, phase row) was resolved once per row by
+// the plan, so a row costs one load before its data loads are issued.
 template <bool BF16, int D, bool VALUES>
 __global__ __launch_bounds__(256) void gather_kernel(GatherArgs a) {
   constexpr int ES = BF16 ? 2 : 4;
@@ -252,21 +254,16 @@ __global__ __launch_bounds__(256) void gather_kernel(GatherArgs a) {
   const int j = threadIdx.x % LPR;
   const int64_t u = int64_t(blockIdx.x) * RPB + rl;
   if (u >= a.prefix_rows) return;
-  const int sp = find_le(a.crow, a.n_spans, u);
-  const SpanRec s = a.spans[sp];
-  const int t = int(u - s.crow);
-  const int tok = s.s + t;
-  const int page = a.page_ids[s.page_off + (tok >> a.page_shift)];
-  const int slot = tok & (a.page_tokens - 1);
-  const char* __restrict__ src_row = a.pool + int64_t(page) * a.page_bytes + int64_t(slot) * RB;
-  const int64_t dst_row = int64_t(s.dst_row) + t;
+  const int4 g = a.gsrc[u];
+  const char* __restrict__ src_row =
+      a.pool + int64_t(g.y >> a.page_shift) * a.page_bytes + int64_t(g.y & (a.page_tokens - 1)) * RB;
+  const int64_t dst_row = g.x;
   // rotation: the span's delta, or for un-rotated keys the row's new position
-  const int newpos = s.target + t;
-  const bool rot = a.per_position ? newpos != 0 : s.delta != 0;
-  const int64_t prow = a.per_position ? newpos : sp;
+  // (phase row g.z; none where the rotation is by 0)
+  const bool rot = g.z >= 0;
   Phase ph[EPV];
   if (rot) {
-    const Phase* pp = a.phase_tab + prow * (D / 2) + j * EPV;
+    const Phase* pp = a.phase_tab + int64_t(g.z) * (D / 2) + j * EPV;
 #pragma unroll
     for (int e = 0; e < EPV; ++e) ph[e] = pp[e];
   }
@@ -410,7 +407,7 @@ __global__ __launch_bounds__(256) void prologue_kernel(PrologueArgs a) {
 // product uses, so the output is an exact weighted mean of the values.
 //
 // A tile runs as two 32-row blocks pipelined against each other
-// (tile_pipelined); the query-rotation variant runs the whole tile at once.
+// (tile_pipelined).
 
 constexpr int kTileBytes = 16384;
 constexpr int kPosOffset = 2 * kTileBytes;          // 64 row positions after K and V
@@ -569,104 +566,6 @@ __device__ __forceinline__ void col_setup(const AttnArgs& a, const AttnWork& w, 
   }
 }
 
-// Softmax of one whole tile's scores (query-rotation variant; the other
-// variants run tile_pipelined): mask (when the tile's rows are not all at or
-// before every query of the wave), raise the reference maximum if needed,
-// and form the bf16 probabilities.  The tile's row positions sit in LDS at
-// byte offset POFF from `paddr` (the lane's address in stage 0), `r0` is its
-// first row, `rows` the request's rows.
-template <int POFF>
-__device__ __forceinline__ void softmax_tile(f32x16 sacc[2], int2 bnd, unsigned paddr, int r0, int rows,
-                                             const Col& c, float scale_log2, float& m, f32x16 o[4],
-                                             f32x16& lacc, bf16x8 pb[2][2]) {
-  const int g2 = (threadIdx.x & 63) >> 5;
-  if (bnd.y > c.wq_min) {
-    // rows of this tile may be later than some query (or past the end of
-    // the request): mask pos_row > pos_q
-    // group 4 kb + qq holds rows 32 kb + 8 qq + 4 g2 .. + 3
-    // (offsets past the 16-bit immediate go into the address)
-    constexpr unsigned EXTRA = POFF + 224 > 65535 ? unsigned(POFF) : 0u;
-    constexpr int PO = int(POFF - EXTRA);
-    PosFrags pf;
-    const unsigned pa = paddr + EXTRA;
-    pf.x[0] = lds_read_i4<PO>(pa);
-    pf.x[1] = lds_read_i4<PO + 32>(pa);
-    pf.x[2] = lds_read_i4<PO + 64>(pa);
-    pf.x[3] = lds_read_i4<PO + 96>(pa);
-    pf.x[4] = lds_read_i4<PO + 128>(pa);
-    pf.x[5] = lds_read_i4<PO + 160>(pa);
-    pf.x[6] = lds_read_i4<PO + 192>(pa);
-    pf.x[7] = lds_read_i4<PO + 224>(pa);
-    pos_wait(pf);
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-      for (int qq = 0; qq < 4; ++qq) {
-        const int r4 = 32 * kb + 8 * qq + 4 * g2;
-        const i32x4 p4 = pf.x[4 * kb + qq];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const bool hide = p4[e] > c.qpos || r0 + r4 + e >= rows;
-          if (hide) sacc[kb][4 * qq + e] = -INFINITY;
-        }
-      }
-    }
-  }
-  const float mt = max_halves(max32(sacc[0], sacc[1])) * scale_log2;
-  const bool raise = mt > m + kRescaleSlack;
-  if (__builtin_amdgcn_ballot_w64(raise)) {
-    // only raising lanes rescale: a lane whose maximum is still -inf must not
-    // form exp2(-inf - -inf)
-    const float alpha = raise ? __builtin_amdgcn_exp2f(m - mt) : 1.0f;
-#pragma unroll
-    for (int db = 0; db < 4; ++db) o[db] *= alpha;
-    lacc *= alpha;
-    m = raise ? mt : m;
-  }
-  const float mb = m == -INFINITY ? 0.0f : m;
-#pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][i], scale_log2, -mb));
-      pb[kb][i >> 3][i & 7] = (__bf16)p;
-    }
-  }
-}
-
-// O^T += V^T P^T and the denominator (ones^T P^T) for the whole tile in the
-// stage at byte offset STAGE from stage 0 (query-rotation variant).  Block
-// db+1's transpose reads are issued before block db's products, and waited
-// for while those run.
-template <int STAGE>
-__device__ __forceinline__ void pv_product(const Col& c, const bf16x8 pb[2][2], f32x16 o[4],
-                                           f32x16& lacc) {
-  const bf16x8 ones = __builtin_bit_cast(bf16x8, u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
-#pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2) lacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones, pb[kb][s2], lacc, 0, 0, 0);
-  TrBlock vb[2];
-  tr_block_read<STAGE>(c.vaddr[0][0], c.vaddr[0][1], vb[0]);
-  lds_wait(vb[0]);
-#pragma unroll
-  for (int db = 0; db < 4; ++db) {
-    TrBlock& cur = vb[db & 1];
-    if (db + 1 < 4) tr_block_read<STAGE>(c.vaddr[db + 1][0], c.vaddr[db + 1][1], vb[(db + 1) & 1]);
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
-        const s16x8 xv =
-            __builtin_shufflevector(cur.x[4 * kb + 2 * s2], cur.x[4 * kb + 2 * s2 + 1], 0, 1, 2, 3, 4, 5, 6, 7);
-        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, xv), pb[kb][s2], o[db], 0, 0,
-                                                        0);
-      }
-    }
-    if (db + 1 < 4) lds_wait(vb[(db + 1) & 1]);
-  }
-}
-
 // ---- one tile, pipelined by 32-row block ----
 // S of block 1 runs on the matrix core while block 0's probabilities are
 // formed, and block 0's PV while block 1's are (independent work in one basic
@@ -683,7 +582,11 @@ __device__ __forceinline__ float max16(const f32x16& a) {
 }
 
 // Mask the scores of 32-row block KB of a tile (rows later than the lane's
-// query, or past the request's end); positions as in softmax_tile.
+// query, or past the request's end).  The tile's row positions sit in LDS at
+// byte offset POFF from `paddr` (the lane's address in stage 0): group
+// 4 KB + qq of the lane holds rows 32 KB + 8 qq + 4 g2 .. + 3; `r0` is the
+// tile's first row, `rows` the request's rows.  (Offsets past the 16-bit
+// immediate go into the address.)
 template <int POFF, int KB>
 __device__ __forceinline__ void mask_block(f32x16& sc, unsigned paddr, int r0, int rows, const Col& c) {
   const int g2 = (threadIdx.x & 63) >> 5;
@@ -862,9 +765,10 @@ __device__ __forceinline__ void store_column(const AttnArgs& a, const Col& c, co
 // O and its (m, sum) exactly as its lanes hold them: per (column block,
 // split, wave), 32 float2 of O per lane (fragment-major, lane-minor, so every
 // store and load moves 512 contiguous bytes) and one float2 (m, sum) per lane.
-// The stores write through to device-coherent memory and the merging split
-// loads past its own XCD's cache, so no cache-wide write-back or invalidate is
-// needed; the arrival count is taken after the stores have completed.
+// The stores are agent-scope atomic stores and the merging split reads them
+// with agent-scope atomic loads; the arrival count that orders them is an
+// agent-scope acquire-release read-modify-write (store_split_partial's
+// caller), taken after the stores have completed.
 constexpr int kSplitWaveFloats = 32 * 64 * 2;
 
 __device__ __forceinline__ void st_dev2(float* p, float x, float y) {
@@ -1080,163 +984,16 @@ __device__ __forceinline__ void fused_k_store(const AttnArgs& a, FusedK& f, char
   }
 }
 
-// Fused variant with query rotation.  A key stored rotated at its original
-// position and re-rotated by delta scores q . R(delta) k = (R(-delta) q) . k,
-// so where every row of a 32-row block shares one delta the block is scored
-// against the wave's queries rotated back by that delta, and the tiles are
-// copied from the pool pages straight into LDS like the assembled planes.
-// LDS: the two stages, then each wave's rotated queries as the prologue wrote
-// them ([wave][fragment][lane], 16 bytes each), then the fp32 (cos, sin) rows
-// of the 32-row blocks of both stages (stage x 1 KB + block x 512 bytes).
-constexpr int kQOff = 2 * kStageBytes;
-constexpr int kPhOff = kQOff + 8 * 8192;
-constexpr int kQrotLdsBytes = kPhOff + 2048;
-
 // Source of row rr of a request's rows in plane K or V of the layer: the pool
 // page slot of a prefix row, or the assembled planes for a new-token row
 // (slot < 0).
-__device__ __forceinline__ const char* qrot_row(const AttnArgs& a, const ReqRec& rq, int head, int rr, int slot,
-                                                bool value) {
+__device__ __forceinline__ const char* pool_or_plane_row(const AttnArgs& a, const ReqRec& rq, int head, int rr,
+                                                         int slot, bool value) {
   if (slot >= 0)
     return a.pool + int64_t(slot >> a.page_shift) * a.page_bytes + a.kv_plane_off + (value ? a.v_off : 0) +
            (int64_t(head) * a.page_tokens + (slot & (a.page_tokens - 1))) * 256;
   const uint16_t* plane = value ? a.v_plane : a.k_plane;
   return reinterpret_cast<const char*>(plane + (int64_t(head) * a.cap + rq.row_base + rr) * 128);
-}
-
-// rowsrc of the two rows this lane copies from tile t (row blocks 2 w8 and
-// 2 w8 + 1 of 4 rows each): (slot of the first, its phase row, slot of the
-// second).
-__device__ __forceinline__ int3 qrot_src(const AttnArgs& a, const ReqRec& rq, int t, int rows, int wave8) {
-  const int r0 = 8 * wave8 + int((threadIdx.x & 63) >> 4);
-  const int rr0 = min(t * kAttnRowsPerTile + r0, rows - 1);
-  const int rr1 = min(t * kAttnRowsPerTile + r0 + 4, rows - 1);
-  const int2 s0 = a.rowsrc[rq.row_base + rr0];
-  const int2 s1 = a.rowsrc[rq.row_base + rr1];
-  return make_int3(s0.x, s0.y, s1.x);
-}
-
-// Copies of tile t (first row t0) into the stage at `st`: both row blocks of
-// keys and values (granules swizzled as the readers expect), and for waves 1
-// and 5 the phase row of 32-row block 0 or 1 (their first rows lie in it)
-// into `ph_dst` + 512 x block.
-__device__ __forceinline__ void qrot_tile_to_lds(const AttnArgs& a, const ReqRec& rq, int head, int t0, int rows,
-                                                 int3 src, char* st, char* ph_dst, int wave8) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int r = (2 * wave8 + i) * 4 + (lane >> 4);
-    const int rr = min(t0 + r, rows - 1);
-    const int slot = i ? src.z : src.x;
-    const char* kr = qrot_row(a, rq, head, rr, slot, false);
-    const char* vr = qrot_row(a, rq, head, rr, slot, true);
-    __builtin_amdgcn_global_load_lds(kr + ((lane & 15) ^ k_swz(r)) * 16, (lds_void_ptr)(st + (2 * wave8 + i) * 1024),
-                                     16, 0, 0);
-    __builtin_amdgcn_global_load_lds(vr + ((lane & 15) ^ v_swz(r)) * 16,
-                                     (lds_void_ptr)(st + kTileBytes + (2 * wave8 + i) * 1024), 16, 0, 0);
-  }
-  if (wave8 == 1 || wave8 == 5) {
-    const int ph = __builtin_amdgcn_readfirstlane(src.y);
-    // (the lane offset is made opaque so that the 64-bit lane address is
-    // formed here rather than kept live across the loop)
-    unsigned loff = unsigned(lane) * 16u;
-    asm volatile("" : "+v"(loff));
-    if (ph >= 0 && lane < 32)
-      __builtin_amdgcn_global_load_lds(reinterpret_cast<const char*>(a.phase32) + int64_t(ph) * 512 + loff,
-                                       (lds_void_ptr)(ph_dst + (wave8 == 5 ? 512 : 0)), 16, 0, 0);
-  }
-}
-
-// Fragment pair (S4, S4 + 4) of the wave's queries rotated by -delta: the
-// lane's pairs (d, d + 64), d = 16 S4 + 8 g2 + e, with the block's
-// (cos, sin)(delta w_d) at byte 8 d of the phase row.  The rotated query is
-// kept as two bf16 terms, hi = bf16(x) and lo = bf16(x - hi) (about 16
-// significant bits): one rounding of a query is shared by every row of the
-// span, so a bf16-only copy would shift all of the block's scores
-// coherently, which long, peaked attention (large outlier key channels)
-// does not average out.
-template <int S4, int PHOFF>
-__device__ __forceinline__ void rotate_query_pair(unsigned qaddr, unsigned phaddr, bf16x8 qb[8], bf16x8 ql[8]) {
-  u32x4 x = lds_read16<S4 * 1024>(qaddr);
-  u32x4 y = lds_read16<(S4 + 4) * 1024>(qaddr);
-  u32x4 c0 = lds_read16<PHOFF + S4 * 128>(phaddr);
-  u32x4 c1 = lds_read16<PHOFF + S4 * 128 + 16>(phaddr);
-  u32x4 c2 = lds_read16<PHOFF + S4 * 128 + 32>(phaddr);
-  u32x4 c3 = lds_read16<PHOFF + S4 * 128 + 48>(phaddr);
-  asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(x), "+v"(y), "+v"(c0), "+v"(c1), "+v"(c2), "+v"(c3));
-  const u32x4 cs[4] = {c0, c1, c2, c3};
-  bf16x8 rx, ry, lx, ly;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const unsigned wx = x[e >> 1], wy = y[e >> 1];
-    const float xf = (e & 1) ? bf16_hi(wx) : bf16_lo(wx);
-    const float yf = (e & 1) ? bf16_hi(wy) : bf16_lo(wy);
-    const float co = __uint_as_float(cs[e >> 1][2 * (e & 1)]);
-    const float sn = __uint_as_float(cs[e >> 1][2 * (e & 1) + 1]);
-    const float xr = __builtin_fmaf(yf, sn, xf * co);
-    const float yr = __builtin_fmaf(-xf, sn, yf * co);
-    rx[e] = (__bf16)xr;
-    ry[e] = (__bf16)yr;
-    lx[e] = (__bf16)(xr - (float)rx[e]);
-    ly[e] = (__bf16)(yr - (float)ry[e]);
-  }
-  qb[S4] = rx;
-  qb[S4 + 4] = ry;
-  ql[S4] = lx;
-  ql[S4 + 4] = ly;
-}
-
-// qb (+ ql) <- the wave's queries rotated by -delta of the block whose phase
-// row is staged at PHOFF (rotate), or the queries themselves (ql unused).
-template <int PHOFF>
-__device__ __forceinline__ void requery(bool rotate, unsigned qaddr, unsigned phaddr, bf16x8 qb[8],
-                                        bf16x8 ql[8]) {
-  if (!rotate) {
-    KFrags f;
-    f.x[0] = lds_read16<0>(qaddr);
-    f.x[1] = lds_read16<1024>(qaddr);
-    f.x[2] = lds_read16<2048>(qaddr);
-    f.x[3] = lds_read16<3072>(qaddr);
-    f.x[4] = lds_read16<4096>(qaddr);
-    f.x[5] = lds_read16<5120>(qaddr);
-    f.x[6] = lds_read16<6144>(qaddr);
-    f.x[7] = lds_read16<7168>(qaddr);
-    kfrag_wait(f);
-#pragma unroll
-    for (int s = 0; s < 8; ++s) qb[s] = __builtin_bit_cast(bf16x8, f.x[s]);
-    return;
-  }
-  rotate_query_pair<0, PHOFF>(qaddr, phaddr, qb, ql);
-  rotate_query_pair<1, PHOFF>(qaddr, phaddr, qb, ql);
-  rotate_query_pair<2, PHOFF>(qaddr, phaddr, qb, ql);
-  rotate_query_pair<3, PHOFF>(qaddr, phaddr, qb, ql);
-}
-
-// S^T = K (hi + lo)^T for one 32-row block (SPLIT; else K hi^T): each key
-// fragment feeds both terms' products.  Four fragment registers: the second
-// half's reads are issued into them right behind the products that consume
-// the first half (an MFMA takes its A operand when it issues).
-template <int OFF, bool SPLIT>
-__device__ __forceinline__ void s_block4(const Col& c, const bf16x8 qb[8], const bf16x8 ql[8], f32x16& acc) {
-  u32x4 k4[4];
-#pragma unroll
-  for (int s = 0; s < 4; ++s) k4[s] = lds_read16<OFF>(c.kaddr[s]);
-  asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(k4[0]), "+v"(k4[1]), "+v"(k4[2]), "+v"(k4[3]));
-  acc = f32x16{};
-#pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, k4[s]), qb[s], acc, 0, 0, 0);
-    if (SPLIT)
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, k4[s]), ql[s], acc, 0, 0, 0);
-    k4[s] = lds_read16<OFF>(c.kaddr[s + 4]);
-  }
-  asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(k4[0]), "+v"(k4[1]), "+v"(k4[2]), "+v"(k4[3]));
-#pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, k4[s]), qb[s + 4], acc, 0, 0, 0);
-    if (SPLIT)
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, k4[s]), ql[s + 4], acc, 0, 0, 0);
-  }
 }
 
 // Values left in the pool (assembled keys, pooled values): copy NB row
@@ -1251,15 +1008,14 @@ __device__ __forceinline__ void vpool_to_lds(const AttnArgs& a, const ReqRec& rq
   for (int i = 0; i < NB; ++i) {
     const int r = (b0 + i) * 4 + (lane >> 4);
     const int rr = min(t0 + r, rows - 1);
-    const char* row = qrot_row(a, rq, head, rr, slots[i], true);
+    const char* row = pool_or_plane_row(a, rq, head, rr, slots[i], true);
     __builtin_amdgcn_global_load_lds(row + ((lane & 15) ^ v_swz(r)) * 16, (lds_void_ptr)(lds + (b0 + i) * 1024),
                                      16, 0, 0);
   }
 }
 
-template <bool FUSED, bool PAIRED, bool QROT = false, bool VPOOL = false>
+template <bool FUSED, bool PAIRED, bool VPOOL = false>
 __global__ __launch_bounds__(PAIRED ? 512 : 256, PAIRED ? 1 : 2) void attention_bf16_kernel(AttnArgs a) {
-  static_assert(!QROT || (FUSED && PAIRED), "query rotation is a paired fused mode");
   static_assert(!VPOOL || (!FUSED && PAIRED), "pooled values are read by the assembled-plane variant");
   extern __shared__ __attribute__((aligned(1024))) char lds_all[];
   constexpr int G = PAIRED ? 2 : 1;           // work items per workgroup
@@ -1281,7 +1037,7 @@ __global__ __launch_bounds__(PAIRED ? 512 : 256, PAIRED ? 1 : 2) void attention_
   // both groups of a pair pass the same number of barriers
   const AttnWork w0 = a.work[G * blk];
   // the pair covers the same rows: one stream of copies shared by all 8 waves
-  const bool shared = QROT || (PAIRED && !FUSED && w0.share_rows != 0);
+  const bool shared = PAIRED && !FUSED && w0.share_rows != 0;
   int steps = T;
   if (PAIRED) {
     auto len = [](const AttnWork& x) { return x.tile_end - x.tile_begin - (x.gap_end - x.gap_begin); };
@@ -1299,17 +1055,6 @@ __global__ __launch_bounds__(PAIRED ? 512 : 256, PAIRED ? 1 : 2) void attention_
   const unsigned paddr = lds_addr(smem) + 16 * ((threadIdx.x & 63) >> 5);
   TileLanes tl;
   tile_lanes(shared ? 2 * wave8 : 4 * wave, tl);
-  // query rotation: the un-rotated-by-delta queries and the phase rows
-  const unsigned qaddr = lds_addr(lds_all) + kQOff + wave8 * 8192 + (threadIdx.x & 63) * 16;
-  const unsigned phaddr = lds_addr(lds_all) + kPhOff + 64 * ((threadIdx.x & 63) >> 5);
-  int cur_ph = -1;   // qb (+ ql) hold the queries rotated back by this block's delta (-1: by none)
-  bf16x8 ql[8];      // low terms of the rotated queries (query rotation)
-  if constexpr (QROT) {
-#pragma unroll
-    for (int s = 0; s < 8; ++s)
-      *reinterpret_cast<u32x4*>(lds_all + kQOff + wave8 * 8192 + s * 1024 + (threadIdx.x & 63) * 16) =
-          __builtin_bit_cast(u32x4, qb[s]);
-  }
 
   f32x16 o[4];
 #pragma unroll
@@ -1325,7 +1070,6 @@ __global__ __launch_bounds__(PAIRED ? 512 : 256, PAIRED ? 1 : 2) void attention_
   const int gap_at = __builtin_amdgcn_readfirstlane(gap > 0 ? w.gap_begin - tb : INT_MAX);
   auto tile_of = [&](int i) { return i >= gap_at ? tb + i + gap : tb + i; };
   FusedK fk;
-  int3 qsrc = make_int3(-1, -1, -1);   // rowsrc of the next tile to copy (query rotation)
   // pooled values: pool slots of the lane's value rows in the next tile to
   // copy (-1: not a prefix row), fetched a step ahead
   int vslot[4] = {-1, -1, -1, -1};
@@ -1344,9 +1088,7 @@ __global__ __launch_bounds__(PAIRED ? 512 : 256, PAIRED ? 1 : 2) void attention_
     constexpr int S = decltype(stage_c)::value;
     char* st = smem + S * kStageBytes;
     const int t0 = t * kAttnRowsPerTile;
-    if (QROT) {
-      qrot_tile_to_lds(a, rq, w.head, t0, rows, qsrc, st, lds_all + kPhOff + S * 1024, wave8);
-    } else if (FUSED) {
+    if (FUSED) {
       fused_k_load(a, rq, w.head, t0, rows, fk);
       fused_v_to_lds(a, rq, w.head, t0, rows, st + kTileBytes, wave);
     } else {
@@ -1379,25 +1121,14 @@ __global__ __launch_bounds__(PAIRED ? 512 : 256, PAIRED ? 1 : 2) void attention_
     const int k = 2 * (tile_base + t);
     return make_int2(tile_pos_c[k], tile_pos_c[k + 1]);
   };
-  // phase rows of tile t's two 32-row blocks (query rotation)
-  const __attribute__((address_space(4))) int* blk_ph_c = (const __attribute__((address_space(4))) int*)(a.blk_ph);
-  auto blocks_ph = [&](int t) {
-    if (!QROT) return make_int2(-1, -1);
-    const int k = 2 * (tile_base + t);
-    return make_int2(blk_ph_c[k], blk_ph_c[k + 1]);
-  };
   int2 tp_next = make_int2(INT_MAX, INT_MAX);
-  int2 bph_next = make_int2(-1, -1);
   if (T > 0) {
     tp_next = bounds(tile_of(0));
-    bph_next = blocks_ph(tile_of(0));
-    if (QROT) qsrc = qrot_src(a, rq, tile_of(0), rows, wave8);
     if (VPOOL) vpool_src(tile_of(0));
     issue(std::integral_constant<int, 0>{}, tile_of(0));
-    if (QROT && T > 1) qsrc = qrot_src(a, rq, tile_of(1), rows, wave8);
     if (VPOOL && T > 1) vpool_src(tile_of(1));
   }
-  if (FUSED && !QROT && T > 0) fused_k_store(a, fk, smem);
+  if (FUSED && T > 0) fused_k_store(a, fk, smem);
   // step i: the group's tile tb + i sits in stage S (i even: 0); wait for its
   // copies, start the next tile's copies into the other stage, consume it
   auto step = [&](auto stage_c, int i) {
@@ -1408,44 +1139,16 @@ __global__ __launch_bounds__(PAIRED ? 512 : 256, PAIRED ? 1 : 2) void attention_
     const int t = tile_of(i);
     const bool more = i + 1 < T;
     const int2 tp = tp_next;
-    const int2 bph = bph_next;
     if (more) {
       const int tn = tile_of(i + 1);
       tp_next = bounds(tn);
-      bph_next = blocks_ph(tn);
       issue(std::integral_constant<int, 1 - S>{}, tn);
-      if (QROT && i + 2 < T) qsrc = qrot_src(a, rq, tile_of(i + 2), rows, wave8);
       if (VPOOL && i + 2 < T) vpool_src(tile_of(i + 2));
     }
     // (a wave without columns has wq_max INT_MIN and computes nothing)
-    if (tp.x <= c.wq_max && c.wq_max != INT_MIN) {
-      if constexpr (QROT) {
-        f32x16 sacc[2];
-        bf16x8 pb[2][2];
-        if (bph.x != cur_ph) {
-          requery<S * 1024>(bph.x >= 0, qaddr, phaddr, qb, ql);
-          cur_ph = bph.x;
-        }
-        if (cur_ph >= 0)
-          s_block4<S * kStageBytes, true>(c, qb, ql, sacc[0]);
-        else
-          s_block4<S * kStageBytes, false>(c, qb, ql, sacc[0]);
-        if (bph.y != cur_ph) {
-          requery<S * 1024 + 512>(bph.y >= 0, qaddr, phaddr, qb, ql);
-          cur_ph = bph.y;
-        }
-        if (cur_ph >= 0)
-          s_block4<S * kStageBytes + 8192, true>(c, qb, ql, sacc[1]);
-        else
-          s_block4<S * kStageBytes + 8192, false>(c, qb, ql, sacc[1]);
-        softmax_tile<S * kStageBytes + kPosOffset>(sacc, tp, paddr, t * kAttnRowsPerTile, rows, c, a.scale_log2,
-                                                  m, o, lacc, pb);
-        pv_product<S * kStageBytes>(c, pb, o, lacc);
-      } else {
-        tile_pipelined<S * kStageBytes>(c, qb, tp, paddr, t * kAttnRowsPerTile, rows, a.scale_log2, m, o, lacc);
-      }
-    }
-    if (FUSED && !QROT && more) fused_k_store(a, fk, smem + (1 - S) * kStageBytes);
+    if (tp.x <= c.wq_max && c.wq_max != INT_MIN)
+      tile_pipelined<S * kStageBytes>(c, qb, tp, paddr, t * kAttnRowsPerTile, rows, a.scale_log2, m, o, lacc);
+    if (FUSED && more) fused_k_store(a, fk, smem + (1 - S) * kStageBytes);
   };
   for (int i = 0; i < steps; i += 2) {
     step(std::integral_constant<int, 0>{}, i);
@@ -1496,7 +1199,11 @@ __global__ __launch_bounds__(PAIRED ? 512 : 256, PAIRED ? 1 : 2) void attention_
     if (counted) store_split_partial(a, w.slot, w.split, wave, o, m, lt);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the stores have reached device scope
     __syncthreads();
-    if (counted && (threadIdx.x & 255) == 0) arrived[grp] = atomicAdd(a.split_count + w.slot, 1);
+    // release: this split's partials (stored above by every wave of the
+    // group, ordered before this by the barrier) happen before the count;
+    // acquire: the last split to count sees every other split's partials
+    if (counted && (threadIdx.x & 255) == 0)
+      arrived[grp] = __hip_atomic_fetch_add(a.split_count + w.slot, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
     __syncthreads();
     if (!counted || arrived[grp] != a.n_split_wg - 1) return;
     if ((threadIdx.x & 255) == 0) a.split_count[w.slot] = 0;
@@ -1697,13 +1404,12 @@ hipError_t launch_attention_bf16(const AttnArgs& a, bool fused, hipStream_t s) {
   if (a.n_work <= 0) return hipSuccess;
   // dynamic LDS above 64 KB has to be allowed per kernel, once
   static const hipError_t attr = [] {
-    const void* fns[5] = {reinterpret_cast<const void*>(attention_bf16_kernel<true, true>),
+    const void* fns[4] = {reinterpret_cast<const void*>(attention_bf16_kernel<true, true>),
                           reinterpret_cast<const void*>(attention_bf16_kernel<false, true>),
                           reinterpret_cast<const void*>(attention_bf16_kernel<true, false>),
-                          reinterpret_cast<const void*>(attention_bf16_kernel<true, true, true>),
-                          reinterpret_cast<const void*>(attention_bf16_kernel<false, true, false, true>)};
-    const int bytes[5] = {kAttnLdsBytes, kAttnLdsBytes, kGroupLdsBytes, kQrotLdsBytes, kAttnLdsBytes};
-    for (int i = 0; i < 5; ++i) {
+                          reinterpret_cast<const void*>(attention_bf16_kernel<false, true, true>)};
+    const int bytes[4] = {kAttnLdsBytes, kAttnLdsBytes, kGroupLdsBytes, kAttnLdsBytes};
+    for (int i = 0; i < 4; ++i) {
       hipError_t e = hipFuncSetAttribute(fns[i], hipFuncAttributeMaxDynamicSharedMemorySize, bytes[i]);
       if (e != hipSuccess) return e;
     }
@@ -1715,12 +1421,9 @@ hipError_t launch_attention_bf16(const AttnArgs& a, bool fused, hipStream_t s) {
   // copies; the fused variant pairs only the row splits it merges
   const unsigned pairs = a.wg_map ? unsigned(a.n_wg) : unsigned((a.n_work + 1) / 2);
   if (!fused && a.v_pool)
-    hipLaunchKernelGGL((attention_bf16_kernel<false, true, false, true>), dim3(pairs), dim3(512), kAttnLdsBytes, s,
-                       a);
+    hipLaunchKernelGGL((attention_bf16_kernel<false, true, true>), dim3(pairs), dim3(512), kAttnLdsBytes, s, a);
   else if (!fused)
     hipLaunchKernelGGL((attention_bf16_kernel<false, true>), dim3(pairs), dim3(512), kAttnLdsBytes, s, a);
-  else if (a.qrot)
-    hipLaunchKernelGGL((attention_bf16_kernel<true, true, true>), dim3(pairs), dim3(512), kQrotLdsBytes, s, a);
   else if (a.paired)
     hipLaunchKernelGGL((attention_bf16_kernel<true, true>), dim3(pairs), dim3(512), kAttnLdsBytes, s, a);
   else

@@ -33,6 +33,15 @@ constexpr int64_t kMaxPosition = INT32_MAX - 1;
 // rows per attention tile (the kernels' tile height)
 constexpr int64_t kTileRows = 64;
 
+// `want` clamped to [1, cap], then made even when above 1 (the two splits of
+// a column block pair up in one workgroup): rounded up if that stays within
+// the cap, else down.
+int32_t even_split(int32_t want, int32_t cap) {
+  int32_t split = std::max(1, std::min(want, std::max(cap, 1)));
+  if (split > 1 && (split & 1)) split = split + 1 <= cap ? split + 1 : split - 1;
+  return split;
+}
+
 }  // namespace
 
 pic_status check_model(const pic_model* m, ModelInfo* out, std::string* err) {
@@ -281,8 +290,7 @@ AttnSplit choose_attention_split(const HostPlan& plan, int32_t kv_heads, int32_t
   // short rows: the two splits of a column block share a workgroup and merge
   // in LDS (an even split; merge_kernel combines what is left)
   int32_t split = int32_t((2 * int64_t(target_wgs) + items - 1) / items);
-  split = std::max(1, std::min({split, max_split, tile_cap}));
-  if (split > 1 && (split & 1)) split = std::min(split + 1, max_split & ~1);
+  split = even_split(split, std::min(max_split, tile_cap));
   return AttnSplit{split, false};
 }
 
@@ -384,49 +392,6 @@ void build_attention_work(HostPlan* plan, int32_t kv_heads, int32_t group, int32
   plan->n_split_out = pairs ? split / 2 : (across ? 1 : split);
   plan->n_split_wg = across ? split : 1;
   plan->n_slots = slots;
-}
-
-void build_qrot_blocks(HostPlan* plan, bool keys_rotated, int32_t rows_per_tile) {
-  const int32_t half = rows_per_tile / 2;
-  const size_t nblk = size_t(plan->n_tiles) * 2;
-  plan->blk_ph.assign(nblk, -1);
-  plan->qrot_ok = false;
-  plan->qrot = false;
-  if (!keys_rotated) return;
-  std::vector<int32_t> delta(nblk, 0);
-  std::vector<char> set(nblk, 0);
-  bool ok = true;
-  auto mark = [&](size_t b, int32_t d, int32_t ph) {
-    if (!set[b]) {
-      set[b] = 1;
-      delta[b] = d;
-      plan->blk_ph[b] = ph;
-    } else if (delta[b] != d) {
-      ok = false;
-    }
-  };
-  for (const ReqRec& r : plan->reqs) {
-    const size_t b0 = size_t(r.tile_base) * 2;
-    for (int32_t i = r.span_begin; ok && i < r.span_end; ++i) {
-      const SpanRec& s = plan->spans[size_t(i)];
-      const int32_t r0 = s.dst_row - r.row_base;
-      for (int32_t b = r0 / half; b <= (r0 + s.n - 1) / half; ++b) mark(b0 + size_t(b), s.delta, s.delta != 0 ? i : -1);
-    }
-    if (ok && r.n_new > 0)
-      for (int32_t b = r.prefix_rows / half; b <= (r.prefix_rows + r.n_new - 1) / half; ++b) mark(b0 + size_t(b), 0, -1);
-    if (!ok) break;
-  }
-  plan->qrot_ok = ok;
-}
-
-void finish_qrot(HostPlan* plan) {
-  const std::vector<AttnWork>& w = plan->work;
-  bool shared = plan->qrot_ok && !w.empty() && (w.size() % 2) == 0;
-  for (size_t i = 0; shared && i < w.size(); i += 2) {
-    const bool empty = w[i].tile_end == w[i].tile_begin && w[i + 1].tile_end == w[i + 1].tile_begin;
-    shared = (w[i].share_rows && w[i + 1].share_rows) || empty;
-  }
-  plan->qrot = shared;
 }
 
 namespace {
@@ -546,10 +511,7 @@ void build_decode(const HostPlan& plan, int32_t kv_heads, int32_t step, int32_t 
   int32_t split = 1;
   if (base > 0 && base < target_items) {
     split = int32_t((target_items + base - 1) / base);
-    split = std::min(split, max_split);
-    split = std::min(split, std::max(1, max_tiles / std::max(1, min_tiles_per_split)));
-    split = std::max(split, 1);
-    if (split > 1 && (split & 1)) split = std::min(split + 1, max_split & ~1);
+    split = even_split(split, std::min(max_split, std::max(1, max_tiles / std::max(1, min_tiles_per_split))));
   }
   const bool pairs = split > 1 && (split % 2) == 0;
   out->n_split = split;

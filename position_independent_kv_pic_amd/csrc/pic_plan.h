@@ -101,13 +101,6 @@ struct HostPlan {
   int32_t n_split_out = 1;          // partials left for merge_kernel
   int32_t n_split_wg = 1;           // splits in different workgroups, merged by the last (1: none)
   int32_t n_slots = 0;              // merge counters (column blocks) when n_split_wg > 1
-  // Query rotation (fused variant): per 32-row half of every attention tile,
-  // the phase-table row of the one rotation all its rows share (-1: none).
-  // qrot_ok: every half has a single rotation (keys stored rotated);
-  // qrot: also every workgroup's two work items share their rows.
-  std::vector<int32_t> blk_ph;
-  bool qrot_ok = false;
-  bool qrot = false;
   // Launch order of the paired attention kernel: workgroup b runs item pair
   // wg_map[b] (-1: none, it exits at once).  Workgroup b lands on XCD b mod
   // n_xcd as the (b / n_xcd)-th of that XCD, so the map gives each XCD a
@@ -155,8 +148,10 @@ void build_decode(const HostPlan& plan, int32_t kv_heads, int32_t step, int32_t 
                   int32_t target_items, int32_t max_split, int32_t min_tiles_per_split, DecodePlan* out);
 
 // Row split for the attention kernel, used when the batch alone gives fewer
-// than `target_wgs` workgroups (at most `max_split` parts, never fewer than
-// `min_tiles_per_split` tiles per part).  With at least `min_tiles_across`
+// than `target_wgs` workgroups: at most `max_split` parts, and at most
+// (longest request's tiles) / `min_tiles_per_split` parts, so that the
+// longest request's parts hold at least `min_tiles_per_split` tiles (shorter
+// requests' parts may hold fewer).  With at least `min_tiles_across`
 // tiles per part (`across`), the neighbouring column blocks of a workgroup
 // keep sharing their rows and the splits run in different workgroups, merged
 // by the last to finish; otherwise the two splits of one column block share a
@@ -181,17 +176,6 @@ AttnSplit choose_attention_split(const HostPlan& plan, int32_t kv_heads, int32_t
 // n_split_out, n_split_wg and n_slots.
 void build_attention_work(HostPlan* plan, int32_t kv_heads, int32_t group, int32_t cols_per_wg,
                           int32_t rows_per_tile, AttnSplit split);
-
-// Fill blk_ph and qrot_ok (see HostPlan): a score against a key rotated by
-// delta equals the score of the query rotated by -delta against the stored
-// key, so a 32-row block whose rows share one delta needs one rotated copy of
-// each query instead of rotated keys.  New-token rows (stored rotated at
-// their positions) count as delta 0.
-void build_qrot_blocks(HostPlan* plan, bool keys_rotated, int32_t rows_per_tile);
-
-// After build_attention_work: qrot = qrot_ok and every item pair shares its
-// rows (or is empty).
-void finish_qrot(HostPlan* plan);
 
 // After build_attention_work: fill wg_map for `n_xcd` XCDs of
 // `slots_per_xcd` concurrent paired workgroups each, and item_map.  A pair costs its tile steps

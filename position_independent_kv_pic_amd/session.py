@@ -9,7 +9,7 @@ from typing import Optional
 
 import numpy as np
 
-from .binding import (DEFER_GATHER, DRY_RUN, PLAN_ONLY, QUERY_ROTATION, VALUES_IN_POOL, VARIANT_MATERIALIZED,
+from .binding import (DEFER_GATHER, DRY_RUN, PLAN_ONLY, VALUES_IN_POOL, VARIANT_MATERIALIZED,
                       Plan, Pool, model_struct)
 
 
@@ -45,11 +45,10 @@ class Session:
         self.capacity = max(rows, 1)
 
     def assemble(self, span_ptr, spans, new_ptr, new_pos=None, plan_only: bool = False, defer: bool = False,
-                 query_rotation: bool = False, values_in_pool: bool = False):
+                 values_in_pool: bool = False):
         d = self.plan_host(span_ptr, spans, new_ptr, new_pos)
         self.ensure_capacity(d["rows"])
-        flags = ((PLAN_ONLY if plan_only else 0) | (DEFER_GATHER if defer else 0) |
-                 (QUERY_ROTATION if query_rotation else 0) | (VALUES_IN_POOL if values_in_pool else 0))
+        flags = (PLAN_ONLY if plan_only else 0) | (DEFER_GATHER if defer else 0) | (VALUES_IN_POOL if values_in_pool else 0)
         self.plan.assemble(span_ptr, spans, new_ptr, new_pos, self.asm_k, self.asm_v, self.capacity,
                            flags, self.torch.cuda.current_stream())
         return self.plan.summary()

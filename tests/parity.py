@@ -6,12 +6,22 @@ Tolerances:
   * rotated bf16 keys (and rotated new keys): within 1 bf16 ulp of the fp64
     oracle rounded to bf16 (ordinal distance of the bit patterns, +0 == -0);
   * rotated fp32 keys: within 2^-21 * |(x_k, x_{k+d/2})| of the fp64 value;
-  * attention: bf16 max-abs <= 1e-2 and relative L2 <= 5e-3 per checked
-    layer; fp32 both <= 1e-5.  Attention is linear in V channel by channel,
-    so an output channel whose value channel carries a scale s > 1 (the
-    x20 outlier channels of the long-context workloads) is compared after
-    dividing its error by s: one bf16 rounding of an exact output near 40 is
-    already 0.125, which no bf16 result can beat in absolute terms.
+  * attention: relative L2 <= 5e-3 (bf16) or 1e-5 (fp32) per checked layer,
+    and per element |got - ref| <= atol + e_out + e_p (atol 1e-2 bf16,
+    1e-5 fp32), where the two other terms are the errors the bf16 path's
+    own arithmetic forces, whatever the kernel:
+      e_out = half a bf16 ulp of the output (the result is stored in bf16:
+              an output near 40 already sits on a grid of 0.25);
+      e_p   = 2^-9 * sum_r p_r |v_r - O| over the visible rows: each
+              probability is rounded to bf16 (relative error <= 2^-9)
+              before the P.V product, and the softmax denominator sums the
+              same rounded weights, so the output moves by the weighted
+              deviation of the values (first order; it matters where value
+              channels are large, as the x20 outlier channels of the
+              long-context workloads are).
+    e_p is computed exactly, from the oracle's fp64 probabilities, for the
+    elements whose error exceeds half of atol + e_out (fp32 outputs:
+    e_out = e_p = 0).
 """
 from __future__ import annotations
 
@@ -59,19 +69,64 @@ def request_positions(wl: W.Workload, b: int):
     return orc.new_token_positions(planned, r.n_new, r.new_pos)
 
 
-def channel_scale(vscale_layer: np.ndarray, group: int) -> np.ndarray:
-    """[Hq][d] divisor for the max-abs check: max(1, scale of the value
-    channel each output channel averages), query head h reading kv head h // G."""
-    s = np.maximum(1.0, np.asarray(vscale_layer, np.float64))      # [Hkv][d]
-    return np.repeat(s, group, axis=0)
+def ulp_bf16(x: np.ndarray) -> np.ndarray:
+    """Spacing of bf16 values at |x|: 2^(e - 8) for |x| = m 2^e, 0.5 <= m < 1
+    (8 significant bits); the smallest normal spacing below that range."""
+    _, e = np.frexp(np.maximum(np.abs(np.asarray(x, np.float64)), 2.0 ** -126))
+    return np.ldexp(1.0, e - 8)
 
 
-def attn_metrics(got: np.ndarray, ref: np.ndarray, scale=None):
-    """(max-abs error, with channels divided by `scale` [Hq][d] if given; relative L2)."""
-    err = np.abs(got - ref)
-    if scale is not None:
-        err = err / scale[None]
-    return float(err.max(initial=0.0)), float(np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-300))
+def prob_rounding_term(q_rot, k_rows, v_rows, pos_rows, pos_q, kv_heads, o_ref, elems):
+    """2^-9 * sum_r p_r |v_r,c - O_c| for the output elements `elems`
+    (indices (token, head, channel)), with p the fp64 softmax weights of the
+    visible rows: the first-order effect of rounding every probability to
+    bf16 when the denominator sums the same rounded weights.  The weights
+    are formed once per (token, head)."""
+    q_rot = np.asarray(q_rot, np.float64)
+    d = q_rot.shape[-1]
+    group = q_rot.shape[1] // kv_heads
+    out = np.zeros(len(elems[0]))
+    by_row = {}
+    for i, (j, h) in enumerate(zip(elems[0], elems[1])):
+        by_row.setdefault((int(j), int(h)), []).append(i)
+    for (j, h), idx in by_row.items():
+        g = h // group
+        vis = np.asarray(pos_rows) <= pos_q[j]
+        z = np.asarray(k_rows[g], np.float64)[vis] @ q_rot[j, h] / np.sqrt(d)
+        p = np.exp(z - z.max())
+        p /= p.sum()
+        cs = np.asarray(elems[2])[idx]
+        v = np.asarray(v_rows[g], np.float64)[vis][:, cs]
+        out[idx] = 2.0 ** -9 * (p @ np.abs(v - o_ref[j, h, cs][None, :]))
+    return out
+
+
+def attn_check(got, o_ref, dtype, q_rot=None, k_rows=None, v_rows=None, pos_rows=None, pos_q=None,
+               kv_heads=None):
+    """Attention parity metrics (see the module header); returns a dict with
+    max_abs, rel_l2, ratio = max |got - ref| / (atol + e_out + e_p), which
+    must be <= 1, and ratio_without_p (the same without e_p).  e_p is formed
+    for every element whose error exceeds half of atol + e_out, so `ratio` is
+    the full bound's wherever it could come near 1.  For bf16 the oracle's
+    q', rows and positions are needed."""
+    got = np.asarray(got, np.float64)
+    o_ref = np.asarray(o_ref, np.float64)
+    err = np.abs(got - o_ref)
+    rl2 = float(np.linalg.norm(got - o_ref) / max(np.linalg.norm(o_ref), 1e-300))
+    bound = np.full(err.shape, ATOL[dtype])
+    if dtype == "bf16":
+        bound += 0.5 * ulp_bf16(np.maximum(np.abs(got), np.abs(o_ref)))
+    ratio_without_p = float((err / bound).max(initial=0.0))
+    near = np.nonzero(err > 0.5 * bound)
+    if dtype == "bf16" and len(near[0]):
+        bound[near] += prob_rounding_term(q_rot, k_rows, v_rows, pos_rows, np.asarray(pos_q), kv_heads,
+                                          o_ref, near)
+    return dict(max_abs=float(err.max(initial=0.0)), rel_l2=rl2, ratio=float((err / bound).max(initial=0.0)),
+                ratio_without_p=ratio_without_p)
+
+
+def attn_ok(st: dict, dtype: str) -> bool:
+    return st["ratio"] <= 1.0 and st["rel_l2"] <= RL2[dtype]
 
 
 def compare_keys(got: np.ndarray, ref: np.ndarray, dtype: str, exact_mask=None):

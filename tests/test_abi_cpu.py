@@ -152,39 +152,17 @@ def test_deferred_gather_flags_and_states():
     pool.release()
 
 
-def _qrot_expected(wl) -> int:
-    """Independent statement of when query rotation applies: keys stored
-    rotated and, in every request, each 32-row half of a 64-row attention
-    tile holds rows of a single re-rotation delta (new-token rows count as
-    delta 0)."""
-    if wl.keys != "rotated":
-        return 0
-    for r in wl.requests:
-        planned = orc.plan_spans([tuple(int(x) for x in sp) for sp in r.spans], wl.pool.chunk_orig)
-        deltas = [p.delta for p in planned for _ in range(p.length)] + [0] * r.n_new
-        for b0 in range(0, len(deltas), 32):
-            if len(set(deltas[b0:b0 + 32])) > 1:
-                return 0
-    return 1
-
-
-@pytest.mark.parametrize("name", W.FULL_SIZE + W.REDUCED + W.REDUCED_NEXT +
-                         ("turborag_b16_unrot", "turborag_b16_composite"))
-def test_query_rotation_flag_and_eligibility(name):
+@pytest.mark.parametrize("name", ("turborag_small", "tiny_f32"))
+def test_query_rotation_flag_is_refused(name):
+    """Scoring against queries rotated back by a span's delta skips the
+    storage rounding of the re-rotated keys (it cannot reproduce the
+    assembled cache), so the option is refused, with or without PLAN_ONLY."""
     wl = W.get(name)
     pool = _pool(wl)
     plan = B.Plan(pool)
     sp, spans, npt, npos = wl.span_ptr(), wl.spans_flat(), wl.new_ptr(), wl.new_pos_flat()
-    # the option belongs to plan-only batches (variant F)
-    assert _err(lambda: plan.assemble(sp, spans, npt, npos, None, None, 2 ** 40,
-                                      B.DRY_RUN | B.QUERY_ROTATION)) == "PIC_EINVAL"
-    plan.assemble(sp, spans, npt, npos, None, None, 2 ** 40, B.DRY_RUN | B.PLAN_ONLY | B.QUERY_ROTATION)
-    got = plan.summary()["fused_query_rotation"]
-    if wl.model.dtype == "bf16":
-        assert got == _qrot_expected(wl), name
-    else:
-        assert got == 0
-    # never without the option
+    for flags in (B.DRY_RUN | B.QUERY_ROTATION, B.DRY_RUN | B.PLAN_ONLY | B.QUERY_ROTATION):
+        assert _err(lambda: plan.assemble(sp, spans, npt, npos, None, None, 2 ** 40, flags)) == "PIC_EUNSUPPORTED"
     plan.assemble(sp, spans, npt, npos, None, None, 2 ** 40, B.DRY_RUN | B.PLAN_ONLY)
     assert plan.summary()["fused_query_rotation"] == 0
     plan.release()
@@ -417,5 +395,33 @@ def test_attention_work_covers_every_visible_row_once(name):
                 band = (c.max() - c) * 10 // c.max()
                 assert (np.diff(band) >= 0).all()
                 assert all(live[i] < live[i + 1] for i in range(len(live) - 1) if band[i] == band[i + 1])
+    plan.release()
+    pool.release()
+
+
+@pytest.mark.parametrize("prefix_rows", [2816, 2880 - 64 + 32, 1000, 64 * 16 - 64])
+def test_row_splits_keep_the_minimum_tiles_per_part(prefix_rows):
+    """A batch too small to fill the chip has its rows split, into parts of
+    at least 3 tiles for the longest request, and into an even number of
+    parts (two splits of a column block share a workgroup).  45 tiles must
+    not round an odd 15 up to 16 parts of 2-3 tiles."""
+    d, hq, hkv, L = 128, 28, 4, 2
+    model = B.model_struct(L, hq, hkv, d, 1e6, "bf16")
+    pt = 16
+    pages = (prefix_rows + pt - 1) // pt
+    pool = B.Pool(model, FAKE_POOL, pages * L * 2 * hkv * pt * d * 2, pt, pages, [prefix_rows], [0, pages],
+                  list(range(pages)))
+    plan = B.Plan(pool)
+    plan.assemble([0, 1], [[0, 0, prefix_rows - 1, B.TARGET_AUTO]], [0, 64], None, None, None, 2 ** 40, B.DRY_RUN)
+    items, _ = plan.attention_work()
+    tiles = (prefix_rows + 64 + 63) // 64
+    parts = {}
+    for it in items:
+        parts.setdefault((int(it[1]), int(it[2])), []).append(int(it[4] - it[3]))
+    for key, lens in parts.items():
+        if len(lens) > 1:
+            assert len(lens) % 2 == 0, (key, lens)
+            assert min(lens) >= 3, (prefix_rows, tiles, key, lens)
+        assert sum(lens) == tiles
     plan.release()
     pool.release()

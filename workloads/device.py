@@ -26,12 +26,10 @@ class DeviceWorkload:
     def decode_inputs(self, layer: int, step: int):
         return decode_tokens(self.wl, layer, step, self.kscale, self.vscale, self.kscale.device)
 
-    def assemble(self, plan_only: bool = False, defer: bool = False, query_rotation: bool = False,
-                 values_in_pool: bool = False):
+    def assemble(self, plan_only: bool = False, defer: bool = False, values_in_pool: bool = False):
         wl = self.wl
         return self.session.assemble(wl.span_ptr(), wl.spans_flat(), wl.new_ptr(), wl.new_pos_flat(),
-                                     plan_only=plan_only, defer=defer, query_rotation=query_rotation,
-                                     values_in_pool=values_in_pool)
+                                     plan_only=plan_only, defer=defer, values_in_pool=values_in_pool)
 
     def close(self):
         self.session.close()
