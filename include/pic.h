@@ -267,6 +267,28 @@ pic_status pic_query_prefill(pic_plan* plan, int32_t layer, const void* q, const
                              const void* v_new, void* out, int32_t variant, void* stream);
 
 /*
+ * pic_query_prefill for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  The same steps, kernels and results (bit for bit) as
+ * pic_query_prefill, with the same arguments and the same plan: the plan's
+ * tables come from its pic_assemble, and the call's own scratch (the rotated
+ * queries, the row-split partials and their merge counters) is taken from a
+ * fixed device array of 128 MiB that the library holds on each device it
+ * runs on, from its load until the process ends, instead of from the plan's
+ * workspace.  The call allocates nothing (no hipMalloc, hipFree or event
+ * creation; it records no kernel-timing events) and clears the merge
+ * counters with a kernel, not a memset.
+ *   PIC_ERANGE   the batch needs more than 128 MiB of scratch (about
+ *                new_rows * q_heads * head_dim * 2 bytes in bf16, plus
+ *                row-split partials); nothing is enqueued.
+ * Every call on a device shares that device's array and leaves its
+ * contents behind: calls that overlap on one device (two streams, two
+ * threads, two plans) race and must be ordered by the caller.
+ */
+pic_status pic_query_prefill_noalloc(pic_plan* plan, int32_t layer, const void* q, const void* k_new,
+                                     const void* v_new, void* out, int32_t variant, void* stream);
+
+/*
  * Decode over the assembled cache (the step after the prefill: ordinary
  * autoregressive decoding; CoinRAG page section 2.3 after KV_M(q; C_ctx),
  * SemPIC page's hit path).

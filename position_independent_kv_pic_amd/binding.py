@@ -38,6 +38,7 @@ EXPORTED = (
     "pic_plan_get_spans", "pic_plan_get_new_tokens", "pic_timing_enable", "pic_timing_read",
     "pic_timing_reset", "pic_last_error", "pic_version", "pic_plan_set_decode_rows", "pic_decode_layer",
     "pic_pool_register_host", "pic_gather_layers", "pic_plan_get_attention_work",
+    "pic_query_prefill_noalloc",
 )
 
 
@@ -101,6 +102,7 @@ def lib() -> ctypes.CDLL:
         "pic_plan_release": [P],
         "pic_assemble": [P, I32, pi32, ctypes.POINTER(PicSpan), pi32, pi32, P, P, I64, I32, P],
         "pic_query_prefill": [P, I32, P, P, P, P, I32, P],
+        "pic_query_prefill_noalloc": [P, I32, P, P, P, P, I32, P],
         "pic_plan_set_decode_rows": [P, I32],
         "pic_decode_layer": [P, I32, I32, P, P, P, P, I32, P],
         "pic_plan_get_summary": [P, ctypes.POINTER(PicPlanSummary)],
@@ -235,6 +237,14 @@ class Plan:
                                        ctypes.c_void_p(_ptr(k_new)), ctypes.c_void_p(_ptr(v_new)),
                                        ctypes.c_void_p(_ptr(out)), int(variant),
                                        ctypes.c_void_p(_stream(stream))))
+
+    def query_prefill_noalloc(self, layer: int, q, k_new, v_new, out, variant: int = VARIANT_MATERIALIZED,
+                              stream=None):
+        """pic_query_prefill with its scratch in the library's fixed device array."""
+        _check(lib().pic_query_prefill_noalloc(self.handle, int(layer), ctypes.c_void_p(_ptr(q)),
+                                               ctypes.c_void_p(_ptr(k_new)), ctypes.c_void_p(_ptr(v_new)),
+                                               ctypes.c_void_p(_ptr(out)), int(variant),
+                                               ctypes.c_void_p(_stream(stream))))
 
     def gather_layers(self, layer_begin: int, layer_end: int, stream=None):
         """Gather layers [layer_begin, layer_end) after a DEFER_GATHER assemble."""

@@ -6,6 +6,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <utility>
 #include <vector>
@@ -103,6 +104,20 @@ struct pic_plan {
 
 namespace {
 
+// Scratch of pic_query_prefill_noalloc: the rotated queries, split partials
+// and merge counters of one call live here instead of in memory the library
+// allocates.  Each device holds its own copy (from the load of the library
+// until the process ends), at its own address; every call on a device shares
+// that copy, so calls that overlap on one device race.  Host code never uses
+// the array's name as an address: the device address is looked up once per
+// device (noalloc_scratch) and passed to the kernels.
+constexpr size_t kNoAllocScratchBytes = size_t(128) << 20;
+static __device__ __align__(256) char scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+char* g_scratch_dev[kMaxDevices] = {};
+
 pic_status device_error(pic_plan* p, hipError_t e, const char* what) {
   if (p) p->failed = true;
   return set_err(PIC_EDEVICE, "%s: %s", what, hipGetErrorString(e));
@@ -156,6 +171,7 @@ struct PrefillScratch {
   float* spart;
   float* sml;
   int32_t* count;
+  bool clear_count;   // zero the merge counters before the kernels (shared scratch)
 };
 
 // Byte offsets of a prefill's scratch inside one buffer, each 256-aligned,
@@ -332,6 +348,25 @@ pic_status gather_layers(pic_plan* p, int32_t l0, int32_t l1, hipStream_t s, boo
     if (e != hipSuccess) return device_error(p, e, "record a layer event");
     p->layer_ev_live[size_t(l)] = 1;
   }
+  return PIC_OK;
+}
+
+// Device address of `scratch` on the current device, looked up (with that
+// device current) on the first call there and kept.
+pic_status noalloc_scratch(char** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return device_error(nullptr, e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return set_err(PIC_EUNSUPPORTED, "device %d: at most %d devices", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return device_error(nullptr, e, "hipGetSymbolAddress of the no-alloc scratch");
+    if (!ptr) return set_err(PIC_EDEVICE, "hipGetSymbolAddress of the no-alloc scratch returned NULL");
+    g_scratch_dev[dev] = static_cast<char*>(ptr);
+  }
+  *out = g_scratch_dev[dev];
   return PIC_OK;
 }
 
@@ -685,6 +720,7 @@ pic_status prefill_impl(pic_plan* p, int32_t layer, const void* q, const void* k
     sc.spart = reinterpret_cast<float*>(p->ws + p->off_spart);
     sc.sml = reinterpret_cast<float*>(p->ws + p->off_sml);
     sc.count = reinterpret_cast<int32_t*>(p->ws + p->off_count);
+    sc.clear_count = false;   // cleared by the plan kernels, left at 0 by every launch
   }
   // timing brackets create events on first use: only on the plan's own path
   const bool timed = p->timing && !ext;
@@ -699,6 +735,10 @@ pic_status prefill_impl(pic_plan* p, int32_t layer, const void* q, const void* k
   if (!fused) {
     st = await_layer(p, layer, s);
     if (st != PIC_OK) return st;
+  }
+  if (sc.clear_count && h.n_slots > 0 && h.n_split_wg > 1) {
+    hipError_t e = pic::launch_fill_zero(sc.count, h.n_slots, s);
+    if (e != hipSuccess) return device_error(p, e, "clear the merge counters");
   }
   const int64_t plane_bytes = p->cap * m.row_bytes;
   char* kpl = p->asm_k + int64_t(layer) * m.kv_heads * plane_bytes;
@@ -797,6 +837,32 @@ extern "C" {
 pic_status pic_query_prefill(pic_plan* p, int32_t layer, const void* q, const void* k_new,
                              const void* v_new, void* out, int32_t variant, void* stream) {
   return prefill_impl(p, layer, q, k_new, v_new, out, variant, stream, nullptr);
+}
+
+pic_status pic_query_prefill_noalloc(pic_plan* p, int32_t layer, const void* q, const void* k_new,
+                                     const void* v_new, void* out, int32_t variant, void* stream) {
+  if (!p) return set_err(PIC_EINVAL, "plan is NULL");
+  if (p->failed) return set_err(PIC_ESTATE, "plan is unusable after a device error");
+  if (!p->has_batch || !p->asm_k)
+    return set_err(PIC_ESTATE, "no assembled batch (call pic_assemble without DRY_RUN first)");
+  const ScratchLayout sl = prefill_scratch_layout(p->pool->info.m, p->hp);
+  if (sl.bytes > kNoAllocScratchBytes)
+    return set_err(PIC_ERANGE,
+                   "the batch needs %zu bytes of prefill scratch; pic_query_prefill_noalloc has %zu "
+                   "(use pic_query_prefill)",
+                   sl.bytes, kNoAllocScratchBytes);
+  char* base = nullptr;
+  pic_status st = noalloc_scratch(&base);
+  if (st != PIC_OK) return st;
+  PrefillScratch sc;
+  sc.q_rot = base + sl.q_rot;
+  sc.opart = reinterpret_cast<float*>(base + sl.opart);
+  sc.ml = reinterpret_cast<float2*>(base + sl.ml);
+  sc.spart = reinterpret_cast<float*>(base + sl.spart);
+  sc.sml = reinterpret_cast<float*>(base + sl.sml);
+  sc.count = reinterpret_cast<int32_t*>(base + sl.count);
+  sc.clear_count = true;
+  return prefill_impl(p, layer, q, k_new, v_new, out, variant, stream, &sc);
 }
 
 pic_status pic_plan_set_decode_rows(pic_plan* p, int32_t rows) {

@@ -137,6 +137,9 @@ hipError_t launch_gather(int dtype, int head_dim, const GatherArgs& a, hipStream
 hipError_t launch_prologue(int dtype, int head_dim, const PrologueArgs& a, hipStream_t s);
 hipError_t launch_attention_bf16(const AttnArgs& a, bool fused, hipStream_t s);
 hipError_t launch_attention_f32(int head_dim, const AttnF32Args& a, hipStream_t s);
+// Zero n int32 values with a kernel (no memset node, for callers that
+// capture the stream into a graph).
+hipError_t launch_fill_zero(int32_t* p, int64_t n, hipStream_t s);
 // head_dim, dtype combinations the kernels implement
 bool gather_supported(int dtype, int head_dim);
 bool attention_supported(int dtype, int head_dim, bool fused);

@@ -1314,6 +1314,18 @@ __global__ __launch_bounds__(256) void attention_f32_kernel(AttnF32Args a) {
 // launchers
 // ---------------------------------------------------------------------------
 
+namespace {
+__global__ __launch_bounds__(256) void fill_zero_kernel(int32_t* p, int64_t n) {
+  const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0;
+}
+}  // namespace
+
+hipError_t launch_fill_zero(int32_t* p, int64_t n, hipStream_t s) {
+  if (n > 0) hipLaunchKernelGGL(fill_zero_kernel, dim3(unsigned((n + 255) / 256)), dim3(256), 0, s, p, n);
+  return hipGetLastError();
+}
+
 hipError_t launch_decode_plan(const DecodePlanArgs& a, hipStream_t s) {
   const int64_t n = int64_t(a.batch) * a.half_dim;
   if (n > 0) hipLaunchKernelGGL(decode_plan_kernel, dim3(unsigned((n + 255) / 256)), dim3(256), 0, s, a);
