@@ -46,16 +46,43 @@ def _both(dw, layers, variant):
     return ref, got
 
 
+def _across_workload():
+    """One request of 16 whole 2048-token documents (512 tiles) and 256 new
+    tokens on 4 kv heads of 8 query heads each, so few column blocks that the
+    rows are split across workgroups (merge counters), then a smaller one."""
+    model = W.ModelShape(1, 32, 4, 128, 1e6, "bf16")
+    rng = np.random.default_rng(11)
+    pool = W.make_pool(rng, [2048] * 16, page_tokens=16)
+    A = W.TARGET_AUTO
+    reqs = [W.Request(np.array([[c, 0, 2047, A] for c in range(16)], np.int32), 256, None),
+            W.Request(np.array([[3, 0, 2047, A], [5, 0, 2047, A]], np.int32), 64, None)]
+    return W.Workload("noalloc_across", 5, model, pool, reqs, W.ValueRecipe("outlier", "outlier"), 11)
+
+
+def _splits_across_workgroups(plan) -> bool:
+    """Every column block of request 0 runs 8 or more row ranges of at least
+    64 tiles each, as only the cross-workgroup split does."""
+    items, _ = plan.attention_work()
+    ranges = {}
+    for it in items:
+        if it[0] == 0:
+            ranges.setdefault((int(it[1]), int(it[2])), set()).add((int(it[3]), int(it[4])))
+    return all(len(r) >= 2 and min(e - b for b, e in r) >= 64 for r in ranges.values())
+
+
 @pytest.mark.parametrize("variant", [VARIANT_MATERIALIZED, VARIANT_FUSED])
 def test_noalloc_prefill_equals_prefill_twice_second_smaller(variant):
     # coinrag_small splits its rows (partials merged in LDS and by the merge
-    # kernel); long_small splits them across workgroups (merge counters)
-    for name in ("coinrag_small", "long_small"):
-        wl = W.get(name)
+    # kernel); the third workload splits them across workgroups (partials
+    # merged by the last split to count itself in a merge counter)
+    for name in ("coinrag_small", "long_small", "across"):
+        wl = _across_workload() if name == "across" else W.get(name)
         _say(f"case noalloc {name} variant {variant}")
         dw = open_workload(wl)
         layers = list(range(wl.model.layers))
         ref, got = _both(dw, layers, variant)
+        if name == "across":
+            assert _splits_across_workgroups(dw.session.plan), "the layout does not split across workgroups"
         for l in layers:
             assert torch.equal(ref[l].view(torch.int16), got[l].view(torch.int16)), \
                 f"{name} layer {l}: no-alloc output differs"
