@@ -60,6 +60,9 @@ def parse():
     ap.add_argument("--host-pool", action="store_true",
                     help="keep the pool in pinned host memory (the staging tier): assembly reads the "
                          "covered rows over the host link")
+    ap.add_argument("--hot-pages", type=int, default=0,
+                    help="with --host-pool: an HBM hot set of this many page slots in front of the pool "
+                         "(least recently used pages evicted); reports the cold first pass over the layouts")
     ap.add_argument("--decode-steps", type=int, default=0,
                     help="also time this many decode steps (every layer, one token per request) after a prefill")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -264,7 +267,7 @@ def main():
     wl = wls[0]
     m = wl.model
     log(f"[bench] workload {wl.name}: batch {wl.batch}, layers {m.layers}, rows {wl.rows_total}")
-    dw = open_workload(wl, host_pool=args.host_pool)
+    dw = open_workload(wl, host_pool=args.host_pool, hot_pages=args.hot_pages)
     sess = dw.session
     cap = max(w.rows_total for w in wls)
     sess.ensure_capacity(cap)
@@ -303,10 +306,29 @@ def main():
             q, k, v = inputs[l]
             plan.query_prefill(l, q[:n], k[:n], v[:n], outs[l][:n], variant, stream)
 
+    # with a hot set: a cold first pass over the layouts, each step timed (the
+    # first misses every page; later ones may find pages an earlier layout
+    # brought in)
+    hot = None
+    if sess.cache is not None:
+        cold = []
+        for i in range(len(tables)):
+            ce0, ce1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            ce0.record(stream)
+            step(i)
+            ce1.record(stream)
+            torch.cuda.synchronize()
+            cold.append(ce0.elapsed_time(ce1))
+        hot = {"pages": args.hot_pages, "first_step_ms": round(cold[0], 3),
+               "first_pass_ms_per_step": round(sum(cold) / len(cold), 3), "first_pass_steps": len(cold),
+               "after_first_pass": sess.cache.stats()}
+        log(f"[bench] hot set cold pass: {hot}")
+
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
     log(f"[bench] warmup done ({args.warmup} steps)")
+    hot_before = sess.cache.stats() if sess.cache is not None else None
 
     # timed region: K steps, per-step events on the launch stream
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
@@ -319,6 +341,11 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     step_ms = [ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps)]
+    if hot is not None:
+        after = sess.cache.stats()
+        hot["timed_bytes_copied_per_step"] = (after["bytes_copied"] - hot_before["bytes_copied"]) / args.steps
+        hot["timed_misses"] = after["misses"] - hot_before["misses"]
+        hot["timed_evictions"] = after["evictions"] - hot_before["evictions"]
     total_ms = ev[0].elapsed_time(ev[-1])
     log(f"[bench] timed {args.steps} steps: {total_ms:.2f} ms (host wall {wall * 1e3:.2f} ms)")
 
@@ -381,7 +408,8 @@ def main():
                    "new_tokens_per_step": wl.n_new_total, "variant": args.variant,
                    "values": "read in the pool by attention" if vpool else "gathered with the keys",
                    "layouts": args.layouts, "parallelism": "none (1 GPU)",
-                   "pipelined": bool(args.pipelined), "pool": "pinned host" if args.host_pool else "HBM"},
+                   "pipelined": bool(args.pipelined), "pool": "pinned host" if args.host_pool else "HBM",
+                   "hot_pages": args.hot_pages if args.host_pool else 0},
         "assembly_GBps": None if asm_gbps is None else round(asm_gbps, 1),
         "assembly_frac_hbm": None if asm_gbps is None else round(asm_gbps / HBM_PEAK_GBPS, 4),
         "hbm_copy_GBps": round(copy_gbps, 1),
@@ -411,6 +439,8 @@ def main():
         res["roofline_assembly"]["note"] = "fused variant gathers inside attention; no gather kernel"
     if args.decode_steps > 0:
         res["decode"] = decode_bench(args, wl, dw, inputs, variant, stream)
+    if hot is not None:
+        res["hot_set"] = hot
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle sample")
         res["cpu_baseline"] = cpu_baseline(wl, dw.pool, dw, args.cpu_seconds)

@@ -162,10 +162,63 @@ pic_status pic_pool_register_host(const pic_model* model, void* pool, int64_t po
                                   const int32_t* chunk_page_ptr, const int32_t* page_ids,
                                   pic_pool** out);
 
-/* Release a pool handle (not the pool memory).  Plans made from it must be
- * released first (PIC_ESTATE otherwise).  Synchronises the device if device
- * tables were made. */
+/* Release a pool handle (not the pool memory).  Plans made from it, and its
+ * hot set, must be released first (PIC_ESTATE otherwise).  Synchronises the
+ * device if device tables were made. */
 pic_status pic_pool_release(pic_pool* pool);
+
+/*
+ * HBM-resident hot set in front of a pool in pinned host memory.  Pages the
+ * batches cover are copied from the host into `capacity_pages` page slots of
+ * device memory (capacity_pages x the pool's page size, allocated here) the
+ * first time they are needed, and stay until evicted: least recently used
+ * first, never while a plan's current batch covers them.  A batch whose
+ * chunks are resident then assembles at HBM speed instead of streaming its
+ * rows over the host link; only the pages that cover a batch's spans move
+ * (the TurboRAG review page, its batch-scaling paragraph and its critique
+ * section, caching high-frequency chunks near the GPU; the CoinRAG page
+ * section 3.3, loading only the selected token ranges).
+ *
+ * After pic_cache_create, pic_assemble on any plan over the pool pins the
+ * pages the batch's spans cover (evicting as needed) and points the batch at
+ * the hot set: PIC_ERANGE, with nothing changed, if they do not fit beside
+ * the pages other plans' batches pin.  A page's data moves one layer at a
+ * time, just before the first call that reads that layer of it: the layer's
+ * gather (pic_assemble, pic_gather_layers) or, when attention reads the pool
+ * itself (variant F, PIC_ASSEMBLE_VALUES_IN_POOL), pic_query_prefill and
+ * pic_decode_layer.  With deferred gathers on a second stream, layer l + 1's
+ * pages therefore move while layer l's attention runs.  The copies are
+ * enqueued on the calling stream, and are timed as the assembly gather
+ * (pic_timing_read kernel 0).
+ *
+ * The pool must be registered with pic_pool_register_host (PIC_EINVAL
+ * otherwise), have no plans yet and no hot set (PIC_ESTATE), and
+ * capacity_pages must be >= 1 (PIC_EINVAL); PIC_ENOMEM if the device memory
+ * cannot be allocated.  Plans sharing a pool with a hot set must not run
+ * calls concurrently on different streams: one plan's pic_assemble may evict
+ * and overwrite pages that another plan's earlier, still running, calls read
+ * (calls on one stream, or synchronised between, are safe).
+ */
+typedef struct pic_cache pic_cache;
+
+typedef struct {
+  int64_t capacity_pages;   /* page slots */
+  int64_t resident_pages;   /* slots holding a page */
+  int64_t hits;             /* page look-ups by pic_assemble that found the page resident */
+  int64_t misses;           /* ... that admitted it */
+  int64_t evictions;        /* pages evicted to admit others */
+  int64_t layer_copies;     /* page-layer slices copied from the host */
+  int64_t bytes_copied;     /* bytes those copies moved */
+} pic_cache_stats;
+
+pic_status pic_cache_create(pic_pool* pool, int32_t capacity_pages, pic_cache** out);
+
+/* Counters since the hot set was created. */
+pic_status pic_cache_get_stats(const pic_cache* cache, pic_cache_stats* out);
+
+/* Release the hot set and its device memory.  The plans over its pool must
+ * be released first (PIC_ESTATE otherwise).  Synchronises the device. */
+pic_status pic_cache_release(pic_cache* cache);
 
 /* Create a plan object for batches over `pool`.  Its host and device tables
  * grow on demand and are reused by later pic_assemble calls. */

@@ -38,7 +38,7 @@ EXPORTED = (
     "pic_plan_get_spans", "pic_plan_get_new_tokens", "pic_timing_enable", "pic_timing_read",
     "pic_timing_reset", "pic_last_error", "pic_version", "pic_plan_set_decode_rows", "pic_decode_layer",
     "pic_pool_register_host", "pic_gather_layers", "pic_plan_get_attention_work",
-    "pic_query_prefill_noalloc",
+    "pic_query_prefill_noalloc", "pic_cache_create", "pic_cache_get_stats", "pic_cache_release",
 )
 
 
@@ -59,6 +59,12 @@ class PicModel(ctypes.Structure):
 class PicSpan(ctypes.Structure):
     _fields_ = [("chunk", ctypes.c_int32), ("s", ctypes.c_int32), ("e", ctypes.c_int32),
                 ("target", ctypes.c_int32)]
+
+
+class PicCacheStats(ctypes.Structure):
+    _fields_ = [("capacity_pages", ctypes.c_int64), ("resident_pages", ctypes.c_int64),
+                ("hits", ctypes.c_int64), ("misses", ctypes.c_int64), ("evictions", ctypes.c_int64),
+                ("layer_copies", ctypes.c_int64), ("bytes_copied", ctypes.c_int64)]
 
 
 class PicPlanSummary(ctypes.Structure):
@@ -98,6 +104,9 @@ def lib() -> ctypes.CDLL:
                                    ctypes.POINTER(P)],
         "pic_gather_layers": [P, I32, I32, P],
         "pic_pool_release": [P],
+        "pic_cache_create": [P, I32, ctypes.POINTER(P)],
+        "pic_cache_get_stats": [P, ctypes.POINTER(PicCacheStats)],
+        "pic_cache_release": [P],
         "pic_plan_create": [P, ctypes.POINTER(P)],
         "pic_plan_release": [P],
         "pic_assemble": [P, I32, pi32, ctypes.POINTER(PicSpan), pi32, pi32, P, P, I64, I32, P],
@@ -188,6 +197,25 @@ class Pool:
     def release(self):
         if self.handle:
             _check(lib().pic_pool_release(self.handle))
+            self.handle = None
+
+
+class Cache:
+    """HBM hot set of `capacity_pages` page slots in front of a host pool."""
+
+    def __init__(self, pool: Pool, capacity_pages: int):
+        h = ctypes.c_void_p()
+        _check(lib().pic_cache_create(pool.handle, int(capacity_pages), ctypes.byref(h)))
+        self.handle = h
+
+    def stats(self) -> dict:
+        s = PicCacheStats()
+        _check(lib().pic_cache_get_stats(self.handle, ctypes.byref(s)))
+        return {f: getattr(s, f) for f, _ in PicCacheStats._fields_}
+
+    def release(self):
+        if self.handle:
+            _check(lib().pic_cache_release(self.handle))
             self.handle = None
 
 

@@ -48,6 +48,23 @@ struct pic_pool {
   int n_plans = 0;
   int device = -1;
   int32_t* d_page_ids = nullptr;
+  pic_cache* cache = nullptr;   // hot set in front of a host pool
+};
+
+// Hot set: page slots in device memory, their residency (pic::HotSet), and
+// per layer a device array of (page, slot) pairs to copy with its pinned
+// staging, reused once the event of its last upload has passed.
+struct pic_cache {
+  pic_pool* pool = nullptr;
+  pic::HotSet hs;
+  char* buf = nullptr;            // capacity x page_bytes
+  int32_t* d_pairs = nullptr;     // [layers][capacity][2]
+  int32_t* h_pairs = nullptr;     // pinned staging of d_pairs
+  std::vector<hipEvent_t> ev;     // per layer: its last pair upload
+  std::vector<char> ev_live;
+  int64_t bytes_copied = 0;
+  int device = -1;
+  pic_cache(int32_t n_pages, int32_t capacity, int32_t layers) : hs(n_pages, capacity, layers) {}
 };
 
 struct pic_plan {
@@ -76,7 +93,8 @@ struct pic_plan {
   char* ws = nullptr;
   size_t ws_cap = 0;
   size_t off_spans = 0, off_crow = 0, off_reqs = 0, off_new_pos = 0, off_new_row = 0,
-         off_new_req = 0, off_work = 0, off_omega = 0, off_wg_map = 0, off_item_map = 0, blob_bytes = 0;
+         off_new_req = 0, off_work = 0, off_omega = 0, off_wg_map = 0, off_item_map = 0, off_page_tab = 0,
+         blob_bytes = 0;
   size_t off_pos = 0, off_rowsrc = 0, off_gsrc = 0, off_tile_pos = 0, off_phase_tab = 0, off_phase_new = 0,
          off_qrot = 0, off_opart = 0, off_ml = 0, off_spart = 0, off_sml = 0, off_count = 0,
          ws_bytes = 0;
@@ -162,6 +180,15 @@ pic_status ensure_pool_device(pic_pool* pool) {
   return PIC_OK;
 }
 
+// Where kernels read the pool's pages: the hot set's slots, or the pool.
+const char* pool_addr(const pic_pool* pool) {
+  return pool->cache ? pool->cache->buf : static_cast<const char*>(pool->info.device_base);
+}
+
+// Copy into the hot set the slices of layers [l0, l1) of the pages that the
+// plan's batch pins and that no earlier call has copied.
+pic_status cache_fill(pic_plan* p, int32_t l0, int32_t l1, hipStream_t s);
+
 // Device scratch of one prefill call: rotated queries, split partials and
 // merge counters.
 struct PrefillScratch {
@@ -222,6 +249,8 @@ void layout_workspace(pic_plan* p) {
   p->off_omega = take(half * sizeof(double));
   p->off_wg_map = take(hp.wg_map.size() * sizeof(int32_t));
   p->off_item_map = take(hp.item_map.size() * sizeof(int32_t));
+  // with a hot set: the batch's page table, pool pages to hot-set slots
+  p->off_page_tab = take(p->pool->cache ? p->pool->info.page_ids.size() * sizeof(int32_t) : 0);
   p->blob_bytes = o;
   p->off_pos = take(size_t(hp.rows) * sizeof(int32_t));
   p->off_rowsrc = take(size_t(hp.rows) * sizeof(int2));
@@ -312,15 +341,50 @@ pic_status check_device(pic_plan* p) {
 // Gather the prefix rows of layers [l0, l1) into the planes on stream s.  A
 // deferred gather records each layer's completion so that the layer's
 // prefill, on any stream, waits for it.
+pic_status cache_fill(pic_plan* p, int32_t l0, int32_t l1, hipStream_t s) {
+  pic_cache* c = p->pool->cache;
+  if (!c) return PIC_OK;
+  const pic::PoolInfo& pi = p->pool->info;
+  // a page's layer: K and V planes of every kv head, page_tokens rows each
+  const int64_t slice = int64_t(2) * pi.m.kv_heads * pi.page_tokens * pi.m.row_bytes;
+  const int64_t cap = c->hs.capacity();
+  std::vector<int32_t> pairs;
+  for (int32_t l = l0; l < l1; ++l) {
+    c->hs.take_layer(reinterpret_cast<int64_t>(p), l, &pairs);
+    if (pairs.empty()) continue;
+    const int32_t n = int32_t(pairs.size() / 2);
+    // the layer's staging region is free once its last upload has passed
+    if (c->ev_live[size_t(l)]) {
+      hipError_t e = hipEventSynchronize(c->ev[size_t(l)]);
+      if (e != hipSuccess) return device_error(p, e, "wait for the hot set's last copy list");
+    }
+    int32_t* hst = c->h_pairs + size_t(l) * size_t(cap) * 2;
+    int32_t* dst = c->d_pairs + size_t(l) * size_t(cap) * 2;
+    std::memcpy(hst, pairs.data(), pairs.size() * sizeof(int32_t));
+    hipError_t e = hipMemcpyAsync(dst, hst, pairs.size() * sizeof(int32_t), hipMemcpyHostToDevice, s);
+    if (e != hipSuccess) return device_error(p, e, "hot-set copy list upload");
+    e = hipEventRecord(c->ev[size_t(l)], s);
+    if (e != hipSuccess) return device_error(p, e, "record the copy list event");
+    c->ev_live[size_t(l)] = 1;
+    e = pic::launch_cache_fill(static_cast<const char*>(pi.device_base), c->buf, dst, n, pi.page_bytes,
+                               int64_t(l) * slice, slice, s);
+    if (e != hipSuccess) return device_error(p, e, "hot-set copy");
+    c->bytes_copied += int64_t(n) * slice;
+  }
+  return PIC_OK;
+}
+
 pic_status gather_layers(pic_plan* p, int32_t l0, int32_t l1, hipStream_t s, bool deferred) {
   const pic::HostPlan& h = p->hp;
   const pic::PoolInfo& pi = p->pool->info;
   if (h.prefix_rows > 0 && l1 > l0) {
     Timed tm(p, 0, s);
+    pic_status st = cache_fill(p, l0, l1, s);
+    if (st != PIC_OK) return st;
     pic::GatherArgs ga;
     ga.gsrc = reinterpret_cast<const int4*>(p->ws + p->off_gsrc);
     ga.phase_tab = reinterpret_cast<const pic::Phase*>(p->ws + p->off_phase_tab);
-    ga.pool = static_cast<const char*>(pi.device_base);
+    ga.pool = pool_addr(p->pool);
     ga.asm_k = p->asm_k;
     ga.asm_v = p->asm_v;
     ga.prefix_rows = h.prefix_rows;
@@ -458,11 +522,75 @@ pic_status pic_pool_register_host(const pic_model* model, void* pool, int64_t po
 pic_status pic_pool_release(pic_pool* pool) {
   if (!pool) return set_err(PIC_EINVAL, "pool is NULL");
   if (pool->n_plans > 0) return set_err(PIC_ESTATE, "%d plans still use this pool", pool->n_plans);
+  if (pool->cache) return set_err(PIC_ESTATE, "the pool's hot set must be released first");
   if (pool->d_page_ids) {
     (void)hipDeviceSynchronize();
     (void)hipFree(pool->d_page_ids);
   }
   delete pool;
+  return ok();
+}
+
+pic_status pic_cache_create(pic_pool* pool, int32_t capacity_pages, pic_cache** out) {
+  if (!out) return set_err(PIC_EINVAL, "out is NULL");
+  *out = nullptr;
+  if (!pool) return set_err(PIC_EINVAL, "pool is NULL");
+  if (!pool->info.host) return set_err(PIC_EINVAL, "a hot set fronts a pool in pinned host memory");
+  if (capacity_pages < 1) return set_err(PIC_EINVAL, "capacity_pages %d < 1", capacity_pages);
+  if (pool->cache) return set_err(PIC_ESTATE, "the pool already has a hot set");
+  if (pool->n_plans > 0) return set_err(PIC_ESTATE, "create the hot set before the pool's plans");
+  const pic::PoolInfo& pi = pool->info;
+  pic_cache* c = new (std::nothrow) pic_cache(pi.n_pages, capacity_pages, pi.m.layers);
+  if (!c) return set_err(PIC_ENOMEM, "out of host memory");
+  c->pool = pool;
+  (void)hipGetDevice(&c->device);
+  const size_t pairs = size_t(pi.m.layers) * size_t(capacity_pages) * 2 * sizeof(int32_t);
+  hipError_t e = hipMalloc(reinterpret_cast<void**>(&c->buf), size_t(capacity_pages) * size_t(pi.page_bytes));
+  if (e == hipSuccess) e = hipMalloc(reinterpret_cast<void**>(&c->d_pairs), pairs);
+  if (e == hipSuccess) e = hipHostMalloc(reinterpret_cast<void**>(&c->h_pairs), pairs, hipHostMallocDefault);
+  c->ev.assign(size_t(pi.m.layers), nullptr);
+  c->ev_live.assign(size_t(pi.m.layers), 0);
+  for (size_t l = 0; e == hipSuccess && l < c->ev.size(); ++l) e = hipEventCreateWithFlags(&c->ev[l], hipEventDisableTiming);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    if (c->buf) (void)hipFree(c->buf);
+    if (c->d_pairs) (void)hipFree(c->d_pairs);
+    if (c->h_pairs) (void)hipHostFree(c->h_pairs);
+    for (hipEvent_t ev : c->ev)
+      if (ev) (void)hipEventDestroy(ev);
+    delete c;
+    return set_err(PIC_ENOMEM, "hot set of %d pages: %s", capacity_pages, hipGetErrorString(e));
+  }
+  pool->cache = c;
+  *out = c;
+  return ok();
+}
+
+pic_status pic_cache_get_stats(const pic_cache* c, pic_cache_stats* out) {
+  if (!c || !out) return set_err(PIC_EINVAL, "cache or out is NULL");
+  out->capacity_pages = c->hs.capacity();
+  int64_t resident = 0;
+  for (int32_t k = 0; k < c->hs.capacity(); ++k) resident += c->hs.page_in(k) >= 0 ? 1 : 0;
+  out->resident_pages = resident;
+  out->hits = c->hs.hits;
+  out->misses = c->hs.misses;
+  out->evictions = c->hs.evictions;
+  out->layer_copies = c->hs.layer_copies;
+  out->bytes_copied = c->bytes_copied;
+  return ok();
+}
+
+pic_status pic_cache_release(pic_cache* c) {
+  if (!c) return set_err(PIC_EINVAL, "cache is NULL");
+  if (c->pool->n_plans > 0) return set_err(PIC_ESTATE, "%d plans still use the pool", c->pool->n_plans);
+  (void)hipDeviceSynchronize();
+  (void)hipFree(c->buf);
+  (void)hipFree(c->d_pairs);
+  (void)hipHostFree(c->h_pairs);
+  for (hipEvent_t ev : c->ev)
+    if (ev) (void)hipEventDestroy(ev);
+  c->pool->cache = nullptr;
+  delete c;
   return ok();
 }
 
@@ -494,6 +622,7 @@ pic_status pic_plan_release(pic_plan* p) {
       (void)hipEventDestroy(pr.first);
       (void)hipEventDestroy(pr.second);
     }
+  if (p->pool->cache) p->pool->cache->hs.unpin(reinterpret_cast<int64_t>(p));
   p->pool->n_plans--;
   delete p;
   return ok();
@@ -559,6 +688,19 @@ pic_status pic_assemble(pic_plan* p, int32_t batch, const int32_t* span_ptr, con
   st = ensure_pool_device(p->pool);
   if (st != PIC_OK) return st;
 
+  // with a hot set: pin the pages the batch covers (this changes nothing
+  // when they do not fit) and map the pool's pages to their slots
+  std::vector<int32_t> page_tab;
+  if (pic_cache* c = p->pool->cache) {
+    const std::vector<int32_t> logical = pic::covered_pages(hp, pi.page_tokens);
+    std::vector<int32_t> phys(logical.size());
+    for (size_t i = 0; i < logical.size(); ++i) phys[i] = pi.page_ids[size_t(logical[i])];
+    std::string perr;
+    if (!c->hs.pin(reinterpret_cast<int64_t>(p), phys, &perr)) return set_err(PIC_ERANGE, "%s", perr.c_str());
+    page_tab.assign(pi.page_ids.size(), 0);
+    for (int32_t q : logical) page_tab[size_t(q)] = c->hs.slot_of(pi.page_ids[size_t(q)]);
+  }
+
   hipStream_t s = static_cast<hipStream_t>(stream);
   st = order_after_last_call(p, s);
   if (st != PIC_OK) return st;
@@ -605,6 +747,7 @@ pic_status pic_assemble(pic_plan* p, int32_t batch, const int32_t* span_ptr, con
   put(p->staging, p->off_omega, omega);
   put(p->staging, p->off_wg_map, h.wg_map);
   put(p->staging, p->off_item_map, h.item_map);
+  put(p->staging, p->off_page_tab, page_tab);
   {
     Timed tm(p, 3, s);
     hipError_t e = hipMemcpyAsync(p->ws, p->staging, p->blob_bytes, hipMemcpyHostToDevice, s);
@@ -618,7 +761,7 @@ pic_status pic_assemble(pic_plan* p, int32_t batch, const int32_t* span_ptr, con
     pa.crow = reinterpret_cast<const int32_t*>(p->ws + p->off_crow);
     pa.new_pos = reinterpret_cast<const int32_t*>(p->ws + p->off_new_pos);
     pa.new_row = reinterpret_cast<const int32_t*>(p->ws + p->off_new_row);
-    pa.page_ids = p->pool->d_page_ids;
+    pa.page_ids = p->pool->cache ? reinterpret_cast<const int32_t*>(p->ws + p->off_page_tab) : p->pool->d_page_ids;
     pa.omega = reinterpret_cast<const double*>(p->ws + p->off_omega);
     pa.n_spans = h.n_spans;
     pa.n_new = int32_t(h.new_rows);
@@ -762,6 +905,12 @@ pic_status prefill_impl(pic_plan* p, int32_t layer, const void* q, const void* k
     hipError_t e = pic::launch_prologue(m.dtype, m.head_dim, pa, s);
     if (e != hipSuccess) return device_error(p, e, "prologue kernel");
   }
+  // attention that reads prefix rows in the pool reads them in the hot set
+  if (fused || p->values_in_pool) {
+    Timed tm(p, 0, s, timed);
+    pic_status fst = cache_fill(p, layer, layer + 1, s);
+    if (fst != PIC_OK) return fst;
+  }
   {
     Timed tm(p, 2, s, timed);
     hipError_t e;
@@ -791,7 +940,7 @@ pic_status prefill_impl(pic_plan* p, int32_t layer, const void* q, const void* k
       aa.out = static_cast<uint16_t*>(out);
       aa.opart = sc.opart;
       aa.ml = sc.ml;
-      aa.pool = static_cast<const char*>(pi.device_base);
+      aa.pool = pool_addr(p->pool);
       aa.rowsrc = reinterpret_cast<const int2*>(p->ws + p->off_rowsrc);
       aa.phase_tab = reinterpret_cast<const pic::Phase*>(p->ws + p->off_phase_tab);
       aa.page_bytes = pi.page_bytes;
@@ -995,6 +1144,11 @@ pic_status pic_decode_layer(pic_plan* p, int32_t layer, int32_t step, const void
     hipError_t e = pic::launch_prologue(m.dtype, m.head_dim, pa, s);
     if (e != hipSuccess) return device_error(p, e, "decode prologue kernel");
   }
+  if (fused || p->values_in_pool) {
+    Timed tm(p, 0, s);
+    pic_status fst = cache_fill(p, layer, layer + 1, s);
+    if (fst != PIC_OK) return fst;
+  }
   {
     Timed tm(p, 2, s);
     pic::AttnArgs aa;
@@ -1025,7 +1179,7 @@ pic_status pic_decode_layer(pic_plan* p, int32_t layer, int32_t step, const void
     aa.out = static_cast<uint16_t*>(out);
     aa.opart = reinterpret_cast<float*>(p->dws + p->d_opart);
     aa.ml = reinterpret_cast<float2*>(p->dws + p->d_ml);
-    aa.pool = static_cast<const char*>(pi.device_base);
+    aa.pool = pool_addr(p->pool);
     aa.rowsrc = reinterpret_cast<const int2*>(p->ws + p->off_rowsrc);
     aa.phase_tab = reinterpret_cast<const pic::Phase*>(p->ws + p->off_phase_tab);
     aa.page_bytes = pi.page_bytes;

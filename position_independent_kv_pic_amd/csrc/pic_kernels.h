@@ -140,6 +140,10 @@ hipError_t launch_attention_f32(int head_dim, const AttnF32Args& a, hipStream_t 
 // Zero n int32 values with a kernel (no memset node, for callers that
 // capture the stream into a graph).
 hipError_t launch_fill_zero(int32_t* p, int64_t n, hipStream_t s);
+// Copy `bytes` at byte offset `off` of n_pairs (pool page, cache slot) pairs
+// (device array) from the host pool to the cache (16-byte multiples).
+hipError_t launch_cache_fill(const char* src_pool, char* cache, const int32_t* pairs, int32_t n_pairs,
+                             int64_t page_bytes, int64_t off, int64_t bytes, hipStream_t s);
 // head_dim, dtype combinations the kernels implement
 bool gather_supported(int dtype, int head_dim);
 bool attention_supported(int dtype, int head_dim, bool fused);

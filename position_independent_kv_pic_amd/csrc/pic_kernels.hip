@@ -1315,11 +1315,44 @@ __global__ __launch_bounds__(256) void attention_f32_kernel(AttnF32Args a) {
 // ---------------------------------------------------------------------------
 
 namespace {
+// Hot-set fill: bytes [off, off + 16 n16) of pool page pairs[2i] (the
+// pinned host pool as the device addresses it) to the same bytes of cache
+// slot pairs[2i + 1]; 16 KB per workgroup, `chunks` workgroups per pair.
+__global__ __launch_bounds__(256) void cache_fill_kernel(const char* src_pool, char* cache, const int32_t* pairs,
+                                                         int64_t page_bytes, int64_t off, int64_t n16, int chunks) {
+  const int i = blockIdx.x / chunks, ch = blockIdx.x - i * chunks;
+  const int64_t page = pairs[2 * i], slot = pairs[2 * i + 1];
+  const u32x4* src = reinterpret_cast<const u32x4*>(src_pool + page * page_bytes + off);
+  u32x4* dst = reinterpret_cast<u32x4*>(cache + slot * page_bytes + off);
+  const int64_t k0 = int64_t(ch) * 256 + threadIdx.x;
+  u32x4 v[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int64_t k = k0 + int64_t(j) * chunks * 256;
+    if (k < n16) v[j] = src[k];
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int64_t k = k0 + int64_t(j) * chunks * 256;
+    if (k < n16) dst[k] = v[j];
+  }
+}
+
 __global__ __launch_bounds__(256) void fill_zero_kernel(int32_t* p, int64_t n) {
   const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
   if (i < n) p[i] = 0;
 }
 }  // namespace
+
+hipError_t launch_cache_fill(const char* src_pool, char* cache, const int32_t* pairs, int32_t n_pairs,
+                             int64_t page_bytes, int64_t off, int64_t bytes, hipStream_t s) {
+  if (n_pairs <= 0 || bytes <= 0) return hipSuccess;
+  const int64_t n16 = bytes / 16;
+  const int chunks = int((n16 + 1023) / 1024);
+  hipLaunchKernelGGL(cache_fill_kernel, dim3(unsigned(int64_t(n_pairs) * chunks)), dim3(256), 0, s, src_pool, cache,
+                     pairs, page_bytes, off, n16, chunks);
+  return hipGetLastError();
+}
 
 hipError_t launch_fill_zero(int32_t* p, int64_t n, hipStream_t s) {
   if (n > 0) hipLaunchKernelGGL(fill_zero_kernel, dim3(unsigned((n + 255) / 256)), dim3(256), 0, s, p, n);

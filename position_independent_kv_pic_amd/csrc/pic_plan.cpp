@@ -487,6 +487,137 @@ void build_wg_map(HostPlan* plan, int32_t n_xcd, int32_t slots_per_xcd) {
   plan->item_map = launch_order(plan->work, 1, n_xcd, 2 * slots_per_xcd);
 }
 
+std::vector<int32_t> covered_pages(const HostPlan& plan, int32_t page_tokens) {
+  std::vector<int32_t> out;
+  for (const SpanRec& sp : plan.spans) {
+    if (sp.n <= 0) continue;
+    const int32_t first = sp.page_off + sp.s / page_tokens;
+    const int32_t last = sp.page_off + (sp.s + sp.n - 1) / page_tokens;
+    for (int32_t q = first; q <= last; ++q) out.push_back(q);
+  }
+  std::sort(out.begin(), out.end());
+  out.erase(std::unique(out.begin(), out.end()), out.end());
+  return out;
+}
+
+HotSet::HotSet(int32_t n_pages, int32_t capacity, int32_t layers)
+    : layers_(layers), words_((layers + 63) / 64), slot_of_(size_t(std::max(0, n_pages)), -1),
+      page_of_(size_t(std::max(0, capacity)), -1), pins_(size_t(std::max(0, capacity)), 0),
+      valid_(size_t(std::max(0, capacity)) * size_t(words_), 0), prev_(size_t(std::max(0, capacity)), -1),
+      next_(size_t(std::max(0, capacity)), -1) {
+  // the recency list starts as slots 0 .. capacity - 1, all free
+  for (int32_t k = 0; k < capacity; ++k) {
+    prev_[size_t(k)] = k - 1;
+    next_[size_t(k)] = k + 1 < capacity ? k + 1 : -1;
+  }
+  head_ = capacity > 0 ? 0 : -1;
+  tail_ = capacity > 0 ? capacity - 1 : -1;
+}
+
+void HotSet::touch(int32_t k) {
+  if (tail_ == k) return;
+  // unlink
+  const int32_t p = prev_[size_t(k)], n = next_[size_t(k)];
+  if (p >= 0) next_[size_t(p)] = n; else head_ = n;
+  if (n >= 0) prev_[size_t(n)] = p; else tail_ = p;
+  // append at the most recent end
+  prev_[size_t(k)] = tail_;
+  next_[size_t(k)] = -1;
+  if (tail_ >= 0) next_[size_t(tail_)] = k; else head_ = k;
+  tail_ = k;
+}
+
+void HotSet::unpin(int64_t owner) {
+  for (size_t i = 0; i < owners_.size(); ++i) {
+    if (owners_[i].first != owner) continue;
+    for (int32_t page : owners_[i].second) --pins_[size_t(slot_of_[size_t(page)])];
+    owners_.erase(owners_.begin() + std::ptrdiff_t(i));
+    return;
+  }
+}
+
+bool HotSet::pin(int64_t owner, const std::vector<int32_t>& pages, std::string* err) {
+  std::vector<int32_t> want(pages);
+  std::sort(want.begin(), want.end());
+  want.erase(std::unique(want.begin(), want.end()), want.end());
+  for (int32_t page : want)
+    if (page < 0 || size_t(page) >= slot_of_.size()) {
+      if (err) *err = "page id out of range";
+      return false;
+    }
+  // capacity check before anything changes: slots pinned by other owners
+  // stay, and every wanted page outside them needs a slot
+  std::vector<char> by_me(page_of_.size(), 0);
+  for (const auto& o : owners_)
+    if (o.first == owner)
+      for (int32_t page : o.second) by_me[size_t(slot_of_[size_t(page)])] = 1;
+  int64_t others = 0;
+  for (size_t k = 0; k < page_of_.size(); ++k)
+    if (pins_[k] - by_me[k] > 0) ++others;
+  int64_t fresh = 0;
+  for (int32_t page : want) {
+    const int32_t k = slot_of_[size_t(page)];
+    if (k < 0 || pins_[size_t(k)] - by_me[size_t(k)] == 0) ++fresh;
+  }
+  if (others + fresh > int64_t(page_of_.size())) {
+    if (err)
+      *err = "the hot set holds " + std::to_string(page_of_.size()) + " pages; this batch needs " +
+             std::to_string(want.size()) + " beside " + std::to_string(others) + " pinned by other plans";
+    return false;
+  }
+  unpin(owner);
+  // resident pages first, so that no page of the batch is evicted for another
+  for (int32_t page : want) {
+    const int32_t k = slot_of_[size_t(page)];
+    if (k < 0) continue;
+    ++hits;
+    ++pins_[size_t(k)];
+    touch(k);
+  }
+  for (int32_t page : want) {
+    if (slot_of_[size_t(page)] >= 0) continue;
+    // a free slot or the least recently used unpinned one (the capacity
+    // check above guarantees one)
+    int32_t k = head_;
+    while (k >= 0 && pins_[size_t(k)] > 0) k = next_[size_t(k)];
+    const int32_t old = page_of_[size_t(k)];
+    if (old >= 0) {
+      slot_of_[size_t(old)] = -1;
+      ++evictions;
+    }
+    page_of_[size_t(k)] = page;
+    slot_of_[size_t(page)] = k;
+    std::fill(valid_.begin() + std::ptrdiff_t(size_t(k) * size_t(words_)),
+              valid_.begin() + std::ptrdiff_t(size_t(k + 1) * size_t(words_)), uint64_t(0));
+    ++misses;
+    ++pins_[size_t(k)];
+    touch(k);
+  }
+  owners_.emplace_back(owner, std::move(want));
+  return true;
+}
+
+bool HotSet::layer_valid(int32_t slot, int32_t layer) const {
+  return (valid_[size_t(slot) * size_t(words_) + size_t(layer / 64)] >> (layer % 64)) & 1u;
+}
+
+void HotSet::take_layer(int64_t owner, int32_t layer, std::vector<int32_t>* pairs) {
+  pairs->clear();
+  for (const auto& o : owners_) {
+    if (o.first != owner) continue;
+    for (int32_t page : o.second) {
+      const int32_t k = slot_of_[size_t(page)];
+      uint64_t& word = valid_[size_t(k) * size_t(words_) + size_t(layer / 64)];
+      const uint64_t bit = uint64_t(1) << (layer % 64);
+      if (word & bit) continue;
+      word |= bit;
+      pairs->push_back(page);
+      pairs->push_back(k);
+      ++layer_copies;
+    }
+  }
+}
+
 void build_decode(const HostPlan& plan, int32_t kv_heads, int32_t step, int32_t rows_per_tile,
                   int32_t target_items, int32_t max_split, int32_t min_tiles_per_split, DecodePlan* out) {
   const int32_t batch = plan.batch;

@@ -185,4 +185,45 @@ void build_attention_work(HostPlan* plan, int32_t kv_heads, int32_t group, int32
 // plan's order.
 void build_wg_map(HostPlan* plan, int32_t n_xcd, int32_t slots_per_xcd);
 
+// Logical pages (indices into the pool's page_ids) whose rows the batch's
+// spans cover, ascending, each once.
+std::vector<int32_t> covered_pages(const HostPlan& plan, int32_t page_tokens);
+
+// Residency of pool pages in a device hot set of `capacity` page slots.
+// Each owner (a plan) pins the pages of its current batch; a page that is not
+// resident gets a free slot, or the slot of the least recently used page
+// that no owner pins, whose copied layers are then forgotten.  A page's
+// layers are copied on first use (take_layer), so the set records per slot
+// which layers hold the page's data.  Host bookkeeping only.
+class HotSet {
+ public:
+  HotSet(int32_t n_pages, int32_t capacity, int32_t layers);
+  int32_t capacity() const { return int32_t(page_of_.size()); }
+  // Replace owner's pinned pages with `pages` (pool page ids; repeats
+  // allowed).  Fails, changing nothing, when they do not fit beside the
+  // pages other owners pin.
+  bool pin(int64_t owner, const std::vector<int32_t>& pages, std::string* err);
+  void unpin(int64_t owner);
+  bool pins_any() const { return !owners_.empty(); }
+  int32_t slot_of(int32_t page) const { return slot_of_[size_t(page)]; }
+  int32_t page_in(int32_t slot) const { return page_of_[size_t(slot)]; }
+  // The owner's pinned pages whose `layer` is not copied yet, as (page,
+  // slot) pairs, and mark them copied.
+  void take_layer(int64_t owner, int32_t layer, std::vector<int32_t>* pairs);
+  bool layer_valid(int32_t slot, int32_t layer) const;
+  // counters since creation
+  int64_t hits = 0, misses = 0, evictions = 0, layer_copies = 0;
+
+ private:
+  void touch(int32_t slot);   // move to the most recent end
+  int32_t layers_, words_;
+  std::vector<int32_t> slot_of_;   // per pool page: its slot or -1
+  std::vector<int32_t> page_of_;   // per slot: its page or -1
+  std::vector<int32_t> pins_;      // per slot: owners pinning it
+  std::vector<uint64_t> valid_;    // per slot: words_ words of copied-layer bits
+  std::vector<int32_t> prev_, next_;   // recency list over slots (head: least recent)
+  int32_t head_ = -1, tail_ = -1;
+  std::vector<std::pair<int64_t, std::vector<int32_t>>> owners_;   // pinned pages per owner
+};
+
 }  // namespace pic

@@ -10,12 +10,13 @@ from typing import Optional
 import numpy as np
 
 from .binding import (DEFER_GATHER, DRY_RUN, PLAN_ONLY, VALUES_IN_POOL, VARIANT_MATERIALIZED,
-                      Plan, Pool, model_struct)
+                      Cache, Plan, Pool, model_struct)
 
 
 class Session:
     def __init__(self, layers, q_heads, kv_heads, head_dim, theta, dtype, pool_tensor,
-                 page_tokens, chunk_len, chunk_page_ptr, page_ids, chunk_orig=None, keys="rotated"):
+                 page_tokens, chunk_len, chunk_page_ptr, page_ids, chunk_orig=None, keys="rotated",
+                 hot_pages: int = 0):
         import torch
         self.torch = torch
         self.layers, self.q_heads, self.kv_heads, self.head_dim = layers, q_heads, kv_heads, head_dim
@@ -29,6 +30,8 @@ class Session:
         self.pool = Pool(self.model, pool_tensor, pool_tensor.numel() * pool_tensor.element_size(),
                          page_tokens, pool_tensor.shape[0], chunk_len, chunk_page_ptr, page_ids,
                          chunk_orig, host=self.host_pool)
+        # an HBM hot set of `hot_pages` page slots in front of a host pool
+        self.cache = Cache(self.pool, hot_pages) if self.host_pool and hot_pages > 0 else None
         self.plan = Plan(self.pool)
         self.asm_k = None
         self.asm_v = None
@@ -76,4 +79,6 @@ class Session:
 
     def close(self):
         self.plan.release()
+        if self.cache is not None:
+            self.cache.release()
         self.pool.release()

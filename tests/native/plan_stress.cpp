@@ -130,6 +130,65 @@ int main(int argc, char** argv) {
       }
     }
   }
-  std::printf("ok %d\n", plans);
+  // hot set: random owners pin random page sets, take layers and unpin; the
+  // residency tables stay a bijection, every pinned page stays resident, no
+  // page is evicted while pinned, and a layer is handed out once per
+  // residency
+  int hot_ops = 0;
+  for (int round = 0; round < 20; ++round) {
+    const int n_pages = uni(1, 300), cap = uni(1, 120), layers = uni(1, 70), n_owners = uni(1, 3);
+    pic::HotSet hs(n_pages, cap, layers);
+    std::vector<std::vector<int32_t>> pinned(static_cast<size_t>(n_owners));
+    std::vector<std::vector<char>> taken(static_cast<size_t>(n_pages), std::vector<char>(static_cast<size_t>(layers), 0));
+    for (int op = 0; op < 200; ++op, ++hot_ops) {
+      const int owner = uni(0, n_owners - 1);
+      const int kind = uni(0, 9);
+      if (kind < 5) {
+        std::vector<int32_t> want(static_cast<size_t>(uni(0, cap + 10)));
+        for (auto& x : want) x = uni(0, n_pages - 1);
+        std::vector<int32_t> before(static_cast<size_t>(n_pages));
+        for (int q = 0; q < n_pages; ++q) before[size_t(q)] = hs.slot_of(q);
+        std::string err;
+        if (hs.pin(owner, want, &err)) {
+          std::sort(want.begin(), want.end());
+          want.erase(std::unique(want.begin(), want.end()), want.end());
+          pinned[size_t(owner)] = want;
+          // a page whose slot changed lost its copied layers
+          for (int q = 0; q < n_pages; ++q)
+            if (hs.slot_of(q) != before[size_t(q)]) std::fill(taken[size_t(q)].begin(), taken[size_t(q)].end(), 0);
+        } else {
+          for (int q = 0; q < n_pages; ++q)
+            if (hs.slot_of(q) != before[size_t(q)]) return fail("failed pin changed residency", op);
+        }
+      } else if (kind < 8) {
+        const int layer = uni(0, layers - 1);
+        std::vector<int32_t> pairs;
+        hs.take_layer(owner, layer, &pairs);
+        for (size_t i = 0; i + 1 < pairs.size(); i += 2) {
+          if (hs.slot_of(pairs[i]) != pairs[i + 1]) return fail("take_layer slot", op);
+          if (taken[size_t(pairs[i])][size_t(layer)]++) return fail("layer handed out twice", op);
+          if (!hs.layer_valid(pairs[i + 1], layer)) return fail("layer not marked", op);
+        }
+        for (int32_t q : pinned[size_t(owner)])
+          if (!taken[size_t(q)][size_t(layer)]) return fail("pinned page layer missing", op);
+      } else {
+        hs.unpin(owner);
+        pinned[size_t(owner)].clear();
+      }
+      // invariants
+      int resident = 0;
+      for (int q = 0; q < n_pages; ++q) {
+        const int k = hs.slot_of(q);
+        if (k < 0) continue;
+        ++resident;
+        if (k >= cap || hs.page_in(k) != q) return fail("residency tables", op);
+      }
+      if (resident > cap) return fail("over capacity", op);
+      for (const auto& pv : pinned)
+        for (int32_t q : pv)
+          if (hs.slot_of(q) < 0) return fail("pinned page not resident", op);
+    }
+  }
+  std::printf("ok %d %d\n", plans, hot_ops);
   return 0;
 }

@@ -425,3 +425,18 @@ def test_row_splits_keep_the_minimum_tiles_per_part(prefix_rows):
         assert sum(lens) == tiles
     plan.release()
     pool.release()
+
+
+def test_hot_set_fronts_only_a_host_pool():
+    """A hot set caches a pool in pinned host memory: on a device pool, with
+    no pool, or with no slots the call is refused and nothing is created."""
+    wl = W.get("turborag_small")
+    pool = _pool(wl)
+    assert _err(lambda: B.Cache(pool, 16)) == "PIC_EINVAL"
+    h = ctypes.c_void_p()
+    assert B.lib().pic_cache_create(None, 16, ctypes.byref(h)) == -1 and not h.value
+    assert B.lib().pic_cache_create(pool.handle, 16, None) == -1
+    assert B.lib().pic_cache_get_stats(None, None) == -1
+    assert B.lib().pic_cache_release(None) == -1
+    # the pool has no hot set, so it releases
+    pool.release()

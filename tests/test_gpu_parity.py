@@ -356,6 +356,63 @@ def test_pool_in_pinned_host_memory(name):
     dw.close()
 
 
+def _covered_pages(wl):
+    """Pool pages (ids) the batch's spans cover."""
+    pt = wl.pool.page_tokens
+    pages = set()
+    for r in wl.requests:
+        for c, s0, e0, _t in r.spans:
+            base = int(wl.pool.chunk_page_ptr[c])
+            for q in range(base + int(s0) // pt, base + int(e0) // pt + 1):
+                pages.add(int(wl.pool.page_ids[q]))
+    return pages
+
+
+@pytest.mark.parametrize("name", ["turborag_small", "coinrag_small_unrot"])
+def test_hot_set_in_front_of_host_pool(name):
+    """An HBM hot set with LRU eviction in front of the pinned-host pool.
+    Batch layouts over one pool go through a hot set that holds any one
+    batch but not all of them: every batch assembles and attends bit for bit
+    as from the device pool (variant M, variant F after a plan-only
+    assembly, values left in the pool); pages are admitted, reused and
+    evicted; a batch whose pages are all resident copies nothing."""
+    wls = [W.get(name, layout=k) for k in range(3)]
+    need = [_covered_pages(w) for w in wls]
+    cap = max(len(x) for x in need)
+    assert len(set().union(*need)) > cap, "the layouts must not fit together"
+    layers = list(range(wls[0].model.layers))
+    ref = {}
+    dref = open_workload(wls[0])
+    for k, w in enumerate(wls):
+        dref.wl = w
+        dref.assemble()
+        ref[k] = run_prefill(dref, layers, VARIANT_MATERIALIZED)
+    dref.close()
+    _say(f"case hot set {name}: {cap} page slots, batches need {[len(x) for x in need]}")
+    dw = open_workload(wls[0], host_pool=True, hot_pages=cap)
+    assert not dw.pool.is_cuda
+    cache = dw.session.cache
+    for k in (0, 1, 2, 0):
+        dw.wl = wls[k]
+        dw.assemble()
+        res = run_prefill(dw, layers, VARIANT_MATERIALIZED)
+        for l in layers:
+            assert torch.equal(ref[k][l][3], res[l][3]), f"layout {k}: hot set differs on layer {l}"
+        check_fused_plan_only(dw, layers, res)
+        check_values_in_pool(dw, layers, res)
+        st = cache.stats()
+        _say(f"  layout {k}: {st}")
+        assert st["resident_pages"] <= cap
+    st = cache.stats()
+    assert st["misses"] > 0 and st["evictions"] > 0 and st["hits"] > 0, st
+    # the same batch again: every page resident, nothing copied
+    dw.assemble()
+    run_prefill(dw, layers, VARIANT_MATERIALIZED)
+    st2 = cache.stats()
+    assert st2["bytes_copied"] == st["bytes_copied"] and st2["misses"] == st["misses"], (st, st2)
+    dw.close()
+
+
 def _edge_workload(keys="rotated"):
     """Ragged shapes and degenerate spans on Qwen2-like heads, two layers."""
     rng = np.random.default_rng(77)

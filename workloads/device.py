@@ -35,9 +35,10 @@ class DeviceWorkload:
         self.session.close()
 
 
-def open_workload(wl: Workload, device="cuda", host_pool: bool = False) -> DeviceWorkload:
+def open_workload(wl: Workload, device="cuda", host_pool: bool = False, hot_pages: int = 0) -> DeviceWorkload:
     """Fill the pool on the device; with host_pool it is then moved to pinned
-    host memory (the staging tier) and the device copy freed."""
+    host memory (the staging tier) and the device copy freed, and hot_pages > 0
+    puts an HBM hot set of that many page slots in front of it."""
     import torch
     from position_independent_kv_pic_amd.session import Session
     ks, vs = channel_scales(wl, device)
@@ -51,5 +52,6 @@ def open_workload(wl: Workload, device="cuda", host_pool: bool = False) -> Devic
         pool = host
     m, p = wl.model, wl.pool
     sess = Session(m.layers, m.q_heads, m.kv_heads, m.head_dim, m.theta, m.dtype, pool, p.page_tokens,
-                   p.chunk_len, p.chunk_page_ptr, p.page_ids, p.chunk_orig, keys=wl.keys)
+                   p.chunk_len, p.chunk_page_ptr, p.page_ids, p.chunk_orig, keys=wl.keys,
+                   hot_pages=hot_pages if host_pool else 0)
     return DeviceWorkload(wl, pool, ks, vs, sess)
