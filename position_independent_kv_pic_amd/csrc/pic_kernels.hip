@@ -272,13 +272,16 @@ __global__ __launch_bounds__(256) void gather_kernel(GatherArgs a) {
   const int64_t plane_stride = int64_t(a.page_tokens) * RB;  // one (layer, K/V, head) run
   char* __restrict__ ak = a.asm_k;
   char* __restrict__ av = a.asm_v;
-  // two planes per iteration: all loads are in flight before any store
-  for (int pl = p0; pl < p1; pl += 2) {
-    const bool two = pl + 1 < p1;
-    u32x4 k0[2], k1[2], v0[2], v1[2];
+  // four planes per iteration, all loads in flight before any store (a
+  // store issued between two planes' loads would hold the later loads' wait
+  // behind its own completion); past the group's end the last plane is
+  // loaded again and not stored
+  constexpr int NPI = 4;
+  for (int pl = p0; pl < p1; pl += NPI) {
+    u32x4 k0[NPI], k1[NPI], v0[NPI], v1[NPI];
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const int pq = two ? pl + q : pl;
+    for (int q = 0; q < NPI; ++q) {
+      const int pq = min(pl + q, p1 - 1);
       const int l = pq / a.kv_heads;
       const int h = pq - l * a.kv_heads;
       const char* ks = src_row + (int64_t(l) * 2 * a.kv_heads + h) * plane_stride;
@@ -291,8 +294,8 @@ __global__ __launch_bounds__(256) void gather_kernel(GatherArgs a) {
       }
     }
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      if (q == 1 && !two) break;
+    for (int q = 0; q < NPI; ++q) {
+      if (pl + q >= p1) break;
       const int64_t off = (int64_t(pl + q) * a.cap + dst_row) * RB;
       if (rot) rotate_vec<BF16>(k0[q], k1[q], ph);
       st16(ak + off + j * 16, k0[q]);
