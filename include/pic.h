@@ -372,7 +372,11 @@ pic_status pic_plan_set_decode_rows(pic_plan* plan, int32_t rows);
  *   out[b][h] = sum_r softmax_r(<q'_b,h, k_r> / sqrt(d)) v_r
  * over all of request b's rows up to and including the token (every earlier
  * row has a smaller position).  The rows are split across workgroups
- * (split-KV) and merged by log-sum-exp.  Requires that this layer was
+ * (split-KV) and merged by log-sum-exp.  When one request's query heads of
+ * a kv head fit one wavefront (Hq / Hkv <= 32) the attention kernel does the
+ * rotation, the writes and the token's own score itself; the bits of k', of
+ * the rows written and of every output are the same either way for a given
+ * variant pair (M and F agree bit for bit).  Requires that this layer was
  * prefilled (pic_query_prefill) and decoded for steps 0 .. step-1 of the
  * current batch, in order.  Implemented for bf16 with head_dim 128
  * (PIC_EUNSUPPORTED otherwise).

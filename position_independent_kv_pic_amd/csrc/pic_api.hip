@@ -915,7 +915,7 @@ pic_status prefill_impl(pic_plan* p, int32_t layer, const void* q, const void* k
     Timed tm(p, 2, s, timed);
     hipError_t e;
     if (m.dtype == PIC_BF16) {
-      pic::AttnArgs aa;
+      pic::AttnArgs aa{};
       aa.q_rot = reinterpret_cast<const uint16_t*>(sc.q_rot);
       aa.k_plane = reinterpret_cast<const uint16_t*>(kpl);
       aa.v_plane = reinterpret_cast<const uint16_t*>(vpl);
@@ -1053,9 +1053,13 @@ pic_status pic_decode_layer(pic_plan* p, int32_t layer, int32_t step, const void
     if (st != PIC_OK) return st;
   }
 
-  if (p->dec.step != step) {
+  // the attention kernel rotates the queries and adds the token's own row
+  // itself when one wave holds a column block's query heads (no prologue and
+  // no merge kernel); wider groups take the prologue and merge_kernel
+  const bool own = m.group <= 32;
+  if (p->dec.step != step || p->dec.own_row != own) {
     pic::build_decode(h, m.kv_heads, step, pic::kAttnRowsPerTile, pic::kDecodeTargetItems, pic::kAttnMaxSplit,
-                      /*min_tiles_per_split=*/2, &p->dec);
+                      /*min_tiles_per_split=*/2, own, &p->dec);
     const pic::DecodePlan& d = p->dec;
     size_t o = 0;
     auto take = [&o](size_t bytes) {
@@ -1070,7 +1074,8 @@ pic_status pic_decode_layer(pic_plan* p, int32_t layer, int32_t step, const void
     p->d_work = take(d.work.size() * sizeof(pic::AttnWork));
     p->d_blob = o;
     p->d_phase = take(nb * (m.head_dim / 2) * sizeof(pic::Phase));
-    p->d_qrot = take(nb * m.q_heads * m.row_bytes);
+    // rotated queries (prologue path only) and merge_kernel's partials
+    p->d_qrot = take(own ? 0 : nb * m.q_heads * m.row_bytes);
     const size_t np = d.n_split_out > 1 ? size_t(d.n_split_out) : 0;
     p->d_opart = take(np * nb * m.q_heads * m.head_dim * sizeof(float));
     p->d_ml = take(np * nb * m.q_heads * sizeof(float2));
@@ -1110,7 +1115,7 @@ pic_status pic_decode_layer(pic_plan* p, int32_t layer, int32_t step, const void
     e = hipEventRecord(p->staging_ev, s);
     if (e != hipSuccess) return device_error(p, e, "record the upload event");
     p->staging_pending = true;
-    pic::DecodePlanArgs da;
+    pic::DecodePlanArgs da{};
     da.dec_pos = reinterpret_cast<const int32_t*>(p->dws + p->d_pos);
     da.dec_row = reinterpret_cast<const int32_t*>(p->dws + p->d_row);
     da.omega = reinterpret_cast<const double*>(p->ws + p->off_omega);
@@ -1125,7 +1130,7 @@ pic_status pic_decode_layer(pic_plan* p, int32_t layer, int32_t step, const void
   const int64_t plane_bytes = p->cap * m.row_bytes;
   char* kpl = p->asm_k + int64_t(layer) * m.kv_heads * plane_bytes;
   char* vpl = p->asm_v + int64_t(layer) * m.kv_heads * plane_bytes;
-  {
+  if (!own) {
     Timed tm(p, 1, s);
     pic::PrologueArgs pa;
     pa.q = static_cast<const char*>(q);
@@ -1151,8 +1156,8 @@ pic_status pic_decode_layer(pic_plan* p, int32_t layer, int32_t step, const void
   }
   {
     Timed tm(p, 2, s);
-    pic::AttnArgs aa;
-    aa.q_rot = reinterpret_cast<const uint16_t*>(p->dws + p->d_qrot);
+    pic::AttnArgs aa{};
+    aa.q_rot = own ? static_cast<const uint16_t*>(q) : reinterpret_cast<const uint16_t*>(p->dws + p->d_qrot);
     aa.k_plane = reinterpret_cast<const uint16_t*>(kpl);
     aa.v_plane = reinterpret_cast<const uint16_t*>(vpl);
     aa.cap = p->cap;
@@ -1174,6 +1179,14 @@ pic_status pic_decode_layer(pic_plan* p, int32_t layer, int32_t step, const void
     aa.spart = nullptr;
     aa.sml = nullptr;
     aa.decode = 1;
+    aa.dec_own = own ? 1 : 0;
+    aa.dec_split = d.n_split;
+    aa.k_new = static_cast<const uint16_t*>(k_new);
+    aa.v_new = static_cast<const uint16_t*>(v_new);
+    aa.dec_phase = reinterpret_cast<const pic::Phase*>(p->dws + p->d_phase);
+    aa.dec_row = reinterpret_cast<const int32_t*>(p->dws + p->d_row);
+    aa.k_own = reinterpret_cast<uint16_t*>(kpl);
+    aa.v_own = reinterpret_cast<uint16_t*>(vpl);
     aa.v_pool = !fused && p->values_in_pool ? 1 : 0;
     aa.scale_log2 = float(1.4426950408889634 / std::sqrt(double(m.head_dim)));
     aa.out = static_cast<uint16_t*>(out);

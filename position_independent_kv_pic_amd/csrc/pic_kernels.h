@@ -82,6 +82,18 @@ struct AttnArgs {
   float* sml;               // [column blocks][n_split_wg][4 waves][64 lanes] float2: (m, sum)
   int32_t decode;           // one query per request (new_begin = its index), every row visible:
                             // tile bounds are not read, rows past the end are masked
+  // decode with the token's own row handled in the kernel (no prologue):
+  // q_rot holds the raw queries, rotated on load by dec_phase; the column
+  // block's last split scores the token's own key (k_new rotated) and value
+  // from registers and writes both to its plane row dec_row
+  int32_t dec_own;
+  int32_t dec_split;        // row splits per column block
+  const uint16_t* k_new;    // [batch][Hkv][128] raw
+  const uint16_t* v_new;
+  const Phase* dec_phase;   // [batch][64]: phases of each request's position
+  const int32_t* dec_row;   // [batch]: assembled row of the token
+  uint16_t* k_own;          // this layer's planes, where the token's rows go
+  uint16_t* v_own;
   float scale_log2;         // log2(e) / sqrt(head_dim)
   uint16_t* out;            // n_split == 1
   float* opart;             // [n_split_out][n_new][Hq][128]

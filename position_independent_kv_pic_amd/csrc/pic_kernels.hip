@@ -845,6 +845,81 @@ __device__ __forceinline__ float2 merge_split_partials(const AttnArgs& a, int sl
   return make_float2(mrun, den);
 }
 
+// ---- decode with the token's own row in the kernel ----
+// A lane's query fragments are the 16-byte granules 2 s + g2 (s = 0..7) of
+// its column's row, so granule s < 4 (elements k) pairs with granule s + 4
+// (elements k + 64) in the same lane: the rotation by the token's position
+// needs no lane exchange, and it rounds exactly as the prologue does.  x[s]
+// holds granule 2 s + g2 of a row of request u's token.  (Holding the
+// lane's 32 phases from before the first tile's copies, so that this waits
+// for them only, made the decode instances spill and ran slower.)
+__device__ __forceinline__ void dec_rotate(const AttnArgs& a, int u, u32x4 x[8]) {
+  if (a.new_pos[u] == 0) return;
+  const int g2 = (threadIdx.x & 63) >> 5;
+  const Phase* pp = a.dec_phase + int64_t(u) * 64;
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    Phase ph[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ph[e] = pp[8 * (2 * s + g2) + e];
+    rotate_vec<true>(x[s], x[s + 4], ph);
+  }
+}
+
+// The column block's last split starts from the token's own row, which the
+// tiles leave out: the key rotated like the queries and scored from registers
+// (a lane holds half of its column's dot product, lane ^ 32 the other half)
+// sets the reference maximum, so its probability is exp2(0) = 1 (exact in
+// bf16): the sum starts at 1 and O at the value (d = 32 db + 8 qq + 4 g2 + e,
+// as the accumulators hold them).  The tiles then continue the online
+// softmax.  The rotated key and the value also go to the token's rows of the
+// planes, for the steps that follow (lanes 0 and 32 hold the whole key
+// between them).
+__device__ __forceinline__ void dec_own_row(const AttnArgs& a, const Col& c, const bf16x8 qb[8], int head,
+                                            float& m, f32x16& lacc, f32x16 o[4]) {
+  const int lane = threadIdx.x & 63, g2 = lane >> 5;
+  const int64_t src = (int64_t(c.u) * a.kv_heads + head) * 128;
+  const uint16_t* vr = a.v_new + src;
+  u32x4 kx[8];
+#pragma unroll
+  for (int s = 0; s < 8; ++s) kx[s] = ld16(a.k_new + src + 8 * (2 * s + g2));
+  u32x2 vv[4][4];
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int qq = 0; qq < 4; ++qq) vv[db][qq] = *reinterpret_cast<const u32x2*>(vr + 32 * db + 8 * qq + 4 * g2);
+  dec_rotate(a, c.u, kx);
+  const int64_t dst = (int64_t(head) * a.cap + a.dec_row[c.u]) * 128;
+  if ((lane & 31) == 0) {
+#pragma unroll
+    for (int s = 0; s < 8; ++s) st16(a.k_own + dst + 8 * (2 * s + g2), kx[s]);
+  }
+  if (lane < 16) st16(a.v_own + dst + 8 * lane, ld16(vr + 8 * lane));
+  float sc = 0.0f;
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    const u32x4 q = __builtin_bit_cast(u32x4, qb[s]);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      sc = __builtin_fmaf(bf16_lo(q[w]), bf16_lo(kx[s][w]), sc);
+      sc = __builtin_fmaf(bf16_hi(q[w]), bf16_hi(kx[s][w]), sc);
+    }
+  }
+  sc += __shfl_xor(sc, 32);
+  m = sc * a.scale_log2;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) lacc[i] = 1.0f;
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int qq = 0; qq < 4; ++qq) {
+      o[db][4 * qq + 0] = bf16_lo(vv[db][qq][0]);
+      o[db][4 * qq + 1] = bf16_hi(vv[db][qq][0]);
+      o[db][4 * qq + 2] = bf16_lo(vv[db][qq][1]);
+      o[db][4 * qq + 3] = bf16_hi(vv[db][qq][1]);
+    }
+}
+
 // ---------------------------------------------------------------------------
 // attention kernel
 // ---------------------------------------------------------------------------
@@ -1017,7 +1092,9 @@ __device__ __forceinline__ void vpool_to_lds(const AttnArgs& a, const ReqRec& rq
   }
 }
 
-template <bool FUSED, bool PAIRED, bool VPOOL = false>
+// DEC: decode with the token's own row handled here (a.dec_own), a separate
+// instance so that the prefill's register allocation is untouched.
+template <bool FUSED, bool PAIRED, bool VPOOL = false, bool DEC = false>
 __global__ __launch_bounds__(PAIRED ? 512 : 256, PAIRED ? 1 : 2) void attention_bf16_kernel(AttnArgs a) {
   static_assert(!VPOOL || (!FUSED && PAIRED), "pooled values are read by the assembled-plane variant");
   extern __shared__ __attribute__((aligned(1024))) char lds_all[];
@@ -1132,6 +1209,17 @@ __global__ __launch_bounds__(PAIRED ? 512 : 256, PAIRED ? 1 : 2) void attention_
     if (VPOOL && T > 1) vpool_src(tile_of(1));
   }
   if (FUSED && T > 0) fused_k_store(a, fk, smem);
+  // decode with the token's own row: the raw queries, loaded by col_setup,
+  // are rotated once the first tile's copies are on their way
+  if (DEC && c.wq_max != INT_MIN) {
+    u32x4 qx[8];
+#pragma unroll
+    for (int s = 0; s < 8; ++s) qx[s] = __builtin_bit_cast(u32x4, qb[s]);
+    dec_rotate(a, c.u, qx);
+#pragma unroll
+    for (int s = 0; s < 8; ++s) qb[s] = __builtin_bit_cast(bf16x8, qx[s]);
+    if (has && w.split == a.dec_split - 1) dec_own_row(a, c, qb, w.head, m, lacc, o);
+  }
   // step i: the group's tile tb + i sits in stage S (i even: 0); wait for its
   // copies, start the next tile's copies into the other stage, consume it
   auto step = [&](auto stage_c, int i) {
@@ -1193,7 +1281,7 @@ __global__ __launch_bounds__(PAIRED ? 512 : 256, PAIRED ? 1 : 2) void attention_
       }
     lt = w0f * lt + w1f * ml1.y;
     m = (l0 || l1) ? mm : -INFINITY;
-  } else if (a.n_split_wg > 1) {
+  } else if (!DEC && a.n_split_wg > 1) {
     // rows split over workgroups: each split stores its partial and then
     // counts itself in the column block's counter; the last to arrive merges
     // and writes the output, and leaves the counter at 0 for the next launch
@@ -1214,6 +1302,18 @@ __global__ __launch_bounds__(PAIRED ? 512 : 256, PAIRED ? 1 : 2) void attention_
     m = ml.x;
     lt = ml.y;
   } else if (!has) {
+    return;
+  }
+  if (DEC) {
+    // decode: one wave of the group has columns (the group's query heads of
+    // one token); the others are done.  Row splits go to merge_kernel: a
+    // merge by the last split here needs an agent-scope acquire-release
+    // count per workgroup, whose L2 write-back and invalidate cost more than
+    // the extra launch.
+    if (c.wq_max == INT_MIN) return;
+    const bool merged = PAIRED && w0.merge_pair;
+    const int part = merged ? w.split / 2 : w.split;
+    store_column(a, c, o, lt, m, a.n_split_out > 1, part);
     return;
   }
   // merged pairs write partial split/2 (or the output when that was the only
@@ -1452,12 +1552,17 @@ hipError_t launch_attention_bf16(const AttnArgs& a, bool fused, hipStream_t s) {
   if (a.n_work <= 0) return hipSuccess;
   // dynamic LDS above 64 KB has to be allowed per kernel, once
   static const hipError_t attr = [] {
-    const void* fns[4] = {reinterpret_cast<const void*>(attention_bf16_kernel<true, true>),
+    const void* fns[8] = {reinterpret_cast<const void*>(attention_bf16_kernel<true, true>),
                           reinterpret_cast<const void*>(attention_bf16_kernel<false, true>),
                           reinterpret_cast<const void*>(attention_bf16_kernel<true, false>),
-                          reinterpret_cast<const void*>(attention_bf16_kernel<false, true, true>)};
-    const int bytes[4] = {kAttnLdsBytes, kAttnLdsBytes, kGroupLdsBytes, kAttnLdsBytes};
-    for (int i = 0; i < 4; ++i) {
+                          reinterpret_cast<const void*>(attention_bf16_kernel<false, true, true>),
+                          reinterpret_cast<const void*>(attention_bf16_kernel<true, true, false, true>),
+                          reinterpret_cast<const void*>(attention_bf16_kernel<false, true, false, true>),
+                          reinterpret_cast<const void*>(attention_bf16_kernel<true, false, false, true>),
+                          reinterpret_cast<const void*>(attention_bf16_kernel<false, true, true, true>)};
+    const int bytes[8] = {kAttnLdsBytes, kAttnLdsBytes, kGroupLdsBytes, kAttnLdsBytes,
+                          kAttnLdsBytes, kAttnLdsBytes, kGroupLdsBytes, kAttnLdsBytes};
+    for (int i = 0; i < 8; ++i) {
       hipError_t e = hipFuncSetAttribute(fns[i], hipFuncAttributeMaxDynamicSharedMemorySize, bytes[i]);
       if (e != hipSuccess) return e;
     }
@@ -1468,16 +1573,28 @@ hipError_t launch_attention_bf16(const AttnArgs& a, bool fused, hipStream_t s) {
   // splits merged in LDS, or neighbouring column blocks sharing their rows'
   // copies; the fused variant pairs only the row splits it merges
   const unsigned pairs = a.wg_map ? unsigned(a.n_wg) : unsigned((a.n_work + 1) / 2);
-  if (!fused && a.v_pool)
+  const unsigned singles = a.wg_map ? unsigned(a.n_wg) : unsigned(a.n_work);
+  if (a.dec_own) {
+    if (!fused && a.v_pool)
+      hipLaunchKernelGGL((attention_bf16_kernel<false, true, true, true>), dim3(pairs), dim3(512), kAttnLdsBytes,
+                         s, a);
+    else if (!fused)
+      hipLaunchKernelGGL((attention_bf16_kernel<false, true, false, true>), dim3(pairs), dim3(512), kAttnLdsBytes,
+                         s, a);
+    else if (a.paired)
+      hipLaunchKernelGGL((attention_bf16_kernel<true, true, false, true>), dim3(pairs), dim3(512), kAttnLdsBytes,
+                         s, a);
+    else
+      hipLaunchKernelGGL((attention_bf16_kernel<true, false, false, true>), dim3(singles), dim3(256),
+                         kGroupLdsBytes, s, a);
+  } else if (!fused && a.v_pool)
     hipLaunchKernelGGL((attention_bf16_kernel<false, true, true>), dim3(pairs), dim3(512), kAttnLdsBytes, s, a);
   else if (!fused)
     hipLaunchKernelGGL((attention_bf16_kernel<false, true>), dim3(pairs), dim3(512), kAttnLdsBytes, s, a);
   else if (a.paired)
     hipLaunchKernelGGL((attention_bf16_kernel<true, true>), dim3(pairs), dim3(512), kAttnLdsBytes, s, a);
   else
-    hipLaunchKernelGGL((attention_bf16_kernel<true, false>), dim3(a.wg_map ? unsigned(a.n_wg) : unsigned(a.n_work)),
-                       dim3(256), kGroupLdsBytes,
-                       s, a);
+    hipLaunchKernelGGL((attention_bf16_kernel<true, false>), dim3(singles), dim3(256), kGroupLdsBytes, s, a);
   if (a.n_split_out > 1) {
     const int64_t items = int64_t(a.n_new) * a.q_heads;
     hipLaunchKernelGGL(merge_kernel, dim3(unsigned((items + 7) / 8)), dim3(256), 0, s, a);

@@ -619,9 +619,11 @@ void HotSet::take_layer(int64_t owner, int32_t layer, std::vector<int32_t>* pair
 }
 
 void build_decode(const HostPlan& plan, int32_t kv_heads, int32_t step, int32_t rows_per_tile,
-                  int32_t target_items, int32_t max_split, int32_t min_tiles_per_split, DecodePlan* out) {
+                  int32_t target_items, int32_t max_split, int32_t min_tiles_per_split, bool own_row,
+                  DecodePlan* out) {
   const int32_t batch = plan.batch;
   out->step = step;
+  out->own_row = own_row;
   out->pos.assign(size_t(batch), 0);
   out->row.assign(size_t(batch), 0);
   out->reqs.assign(size_t(batch), ReqRec{});
@@ -630,7 +632,9 @@ void build_decode(const HostPlan& plan, int32_t kv_heads, int32_t step, int32_t 
     const ReqRec& r = plan.reqs[b];
     ReqRec& d = out->reqs[b];
     d = r;
-    d.n_new = r.n_new + step + 1;   // plane rows after the pool rows, this token last
+    // plane rows after the pool rows: the earlier tokens, then this one
+    // (left out of the tiles when the kernel adds it itself)
+    d.n_new = r.n_new + step + (own_row ? 0 : 1);
     d.new_begin = b;                // query b of the decode batch
     d.tile_base = 0;
     out->pos[b] = plan.req_last_pos[b] + 1 + step;

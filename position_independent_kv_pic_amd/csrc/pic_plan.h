@@ -135,6 +135,7 @@ pic_status build_plan(const PoolInfo& pool, int32_t batch, const int32_t* span_p
 // decode tokens and this one) and the single query.
 struct DecodePlan {
   int32_t step = -1;
+  bool own_row = false;         // the kernel adds the token's own row (not among the tiles)
   std::vector<int32_t> pos;     // per request: the token's position
   std::vector<int32_t> row;     // per request: its assembled row
   std::vector<ReqRec> reqs;     // per request, for the attention kernel in decode mode
@@ -143,9 +144,12 @@ struct DecodePlan {
 };
 
 // `target_items`: about this many work items (row splits of at least
-// `min_tiles_per_split` tiles, at most `max_split`, even).
+// `min_tiles_per_split` tiles, at most `max_split`, even).  With `own_row`
+// the tiles cover only the rows before the token's own (the attention kernel
+// scores that one from registers).
 void build_decode(const HostPlan& plan, int32_t kv_heads, int32_t step, int32_t rows_per_tile,
-                  int32_t target_items, int32_t max_split, int32_t min_tiles_per_split, DecodePlan* out);
+                  int32_t target_items, int32_t max_split, int32_t min_tiles_per_split, bool own_row,
+                  DecodePlan* out);
 
 // Row split for the attention kernel, used when the batch alone gives fewer
 // than `target_wgs` workgroups: at most `max_split` parts, and at most

@@ -123,10 +123,26 @@ int main(int argc, char** argv) {
           return fail("gap", it);
       }
       for (int step = 0; step < decode_rows; ++step) {
-        pic::DecodePlan dp;
-        pic::build_decode(hp, m.kv_heads, step, 64, 512, 16, 2, &dp);
-        if (dp.pos.size() != size_t(batch) || dp.work.size() % size_t(std::max(1, dp.n_split)) != 0)
-          return fail("decode", it);
+        for (int own = 0; own < 2; ++own) {
+          pic::DecodePlan dp;
+          pic::build_decode(hp, m.kv_heads, step, 64, 512, 16, 2, own != 0, &dp);
+          if (dp.pos.size() != size_t(batch) || dp.work.size() != size_t(batch) * m.kv_heads * dp.n_split)
+            return fail("decode", it);
+          // each column block's splits cover its tiles in order, without gaps;
+          // the token's own row is among them unless the kernel adds it
+          for (size_t i = 0; i < dp.work.size(); ++i) {
+            const auto& w = dp.work[i];
+            const auto& r = hp.reqs[size_t(w.req)];
+            const int rows = r.prefix_rows + r.n_new + step + (own ? 0 : 1);
+            if (dp.reqs[size_t(w.req)].prefix_rows + dp.reqs[size_t(w.req)].n_new != rows)
+              return fail("decode rows", it);
+            const int tiles = (rows + 63) / 64;
+            const int first = w.split == 0 ? 0 : dp.work[i - 1].tile_end;
+            if (w.tile_begin != first || w.tile_end < w.tile_begin || w.tile_end > tiles ||
+                (w.split == dp.n_split - 1 && w.tile_end != tiles))
+              return fail("decode tiles", it);
+          }
+        }
       }
     }
   }
