@@ -523,6 +523,32 @@ def test_whole_block_edge_cases_and_retired_query_rotation():
     dw.close()
 
 
+def test_decode_on_edge_layouts():
+    """Decode over the whole-block edge layouts plus a request with neither
+    spans nor new tokens, for 66 steps: its first token attends to itself
+    only, and the earlier rows of every request cross a 64-row tile boundary
+    (a column block's splits may hold no tiles).  Every step against the
+    oracle; the fused variant gives the same bits."""
+    base = _whole_block_edge_workload()
+    reqs = list(base.requests) + [W.Request(np.zeros((0, 4), np.int32), 0, np.zeros(0, np.int32))]
+    wl = W.Workload("edge_decode", 0, base.model, base.pool, reqs, base.values, 902)
+    steps = 66
+    _say("case decode, edge layouts")
+    dw = open_workload(wl)
+    dw.session.set_decode_rows(steps + 4)
+    dw.assemble()
+    layers = [0, 1]
+    pre = run_prefill(dw, layers, VARIANT_MATERIALIZED)
+    dec = run_decode(dw, layers, steps, VARIANT_MATERIALIZED)
+    for b in range(wl.batch):
+        _say("edge_decode", b, check_decode(dw, b, layers, pre, dec))
+    dec_f = run_decode(dw, layers, steps, VARIANT_FUSED)
+    for l in layers:
+        for st in range(steps):
+            assert torch.equal(dec[l][st][3], dec_f[l][st][3]), f"fused decode differs (layer {l}, step {st})"
+    dw.close()
+
+
 def test_plan_reuse_with_smaller_batch():
     wl = W.get("coinrag_small")
     _say("case reuse")
