@@ -621,10 +621,14 @@ __device__ __forceinline__ void block_probs(const f32x16& sc, float scale_log2, 
 
 // O^T += V^T P^T and the denominator for 32-row block KB of the tile in the
 // stage at byte offset STAGE: per 32-wide d block, 4 transpose reads (double
-// buffered across d blocks) and 2 MFMAs.
+// buffered across d blocks) and 2 MFMAs.  The denominator adds the same bf16
+// probabilities that feed the products (v_dot2 against ones, while the first
+// reads are in flight); a lane holds 16 of the block's 32 rows of its column,
+// lane ^ 32 the other 16, and the two halves are added at the end.
 template <int STAGE, int KB>
-__device__ __forceinline__ void pv_block(const Col& c, const bf16x8 pb[2], f32x16 o[4], f32x16& lacc) {
-  const bf16x8 ones = __builtin_bit_cast(bf16x8, u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
+__device__ __forceinline__ void pv_block(const Col& c, const bf16x8 pb[2], f32x16 o[4], float& lsum) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 ones2 = __builtin_bit_cast(bf16x2, 0x3F803F80u);
   constexpr int OFF = STAGE + 8192 * KB;
   s16x4 vb[2][4];
   auto rd = [&](int db, s16x4* x) {
@@ -637,8 +641,15 @@ __device__ __forceinline__ void pv_block(const Col& c, const bf16x8 pb[2], f32x1
     asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]));
   };
   rd(0, vb[0]);
-  lacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones, pb[0], lacc, 0, 0, 0);
-  lacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones, pb[1], lacc, 0, 0, 0);
+#pragma unroll
+  for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      // (pairs built element by element: bit-casting the vector's 32-bit
+      // words to bf16x2 made the compiler feed one register to all four)
+      const bf16x2 pr = {pb[s2][2 * e], pb[s2][2 * e + 1]};
+      lsum = __builtin_amdgcn_fdot2_f32_bf16(pr, ones2, lsum, false);
+    }
   wt(vb[0]);
 #pragma unroll
   for (int db = 0; db < 4; ++db) {
@@ -668,7 +679,7 @@ __device__ __forceinline__ float raise_ref(float mt, float& m, bool& raise) {
 // The whole tile in the stage at byte offset STAGE (see above).
 template <int STAGE>
 __device__ __forceinline__ void tile_pipelined(const Col& c, const bf16x8 qb[8], int2 bnd, unsigned paddr, int r0,
-                                               int rows, float scale_log2, float& m, f32x16 o[4], f32x16& lacc) {
+                                               int rows, float scale_log2, float& m, f32x16 o[4], float& lsum) {
   constexpr int POFF = STAGE + kPosOffset;
   const bool masked = bnd.y > c.wq_min;
   // block 0's key fragments, then block 1's into the same registers (an
@@ -707,22 +718,22 @@ __device__ __forceinline__ void tile_pipelined(const Col& c, const bf16x8 qb[8],
   if (__builtin_amdgcn_ballot_w64(raise0)) {
 #pragma unroll
     for (int db = 0; db < 4; ++db) o[db] *= alpha0;
-    lacc *= alpha0;
+    lsum *= alpha0;
   }
   if (masked) mask_block<POFF, 1>(s1, paddr, r0, rows, c);
   bool raise1;
   const float alpha1 = raise_ref(max_halves(max16(s1)) * scale_log2, m, raise1);
   // block 0's PV while block 1's probabilities form
-  pv_block<STAGE, 0>(c, p0, o, lacc);
+  pv_block<STAGE, 0>(c, p0, o, lsum);
   bf16x8 p1[2];
   block_probs(s1, scale_log2, m == -INFINITY ? 0.0f : m, p1);
   asm volatile("" ::"v"(p1[0]), "v"(p1[1]));
   if (__builtin_amdgcn_ballot_w64(raise1)) {
 #pragma unroll
     for (int db = 0; db < 4; ++db) o[db] *= alpha1;
-    lacc *= alpha1;
+    lsum *= alpha1;
   }
-  pv_block<STAGE, 1>(c, p1, o, lacc);
+  pv_block<STAGE, 1>(c, p1, o, lsum);
 }
 
 // Write a column's result: a partial (unnormalised O, reference maximum m,
@@ -876,7 +887,7 @@ __device__ __forceinline__ void dec_rotate(const AttnArgs& a, int u, u32x4 x[8])
 // planes, for the steps that follow (lanes 0 and 32 hold the whole key
 // between them).
 __device__ __forceinline__ void dec_own_row(const AttnArgs& a, const Col& c, const bf16x8 qb[8], int head,
-                                            float& m, f32x16& lacc, f32x16 o[4]) {
+                                            float& m, float& lsum, f32x16 o[4]) {
   const int lane = threadIdx.x & 63, g2 = lane >> 5;
   const int64_t src = (int64_t(c.u) * a.kv_heads + head) * 128;
   const uint16_t* vr = a.v_new + src;
@@ -907,8 +918,7 @@ __device__ __forceinline__ void dec_own_row(const AttnArgs& a, const Col& c, con
   }
   sc += __shfl_xor(sc, 32);
   m = sc * a.scale_log2;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) lacc[i] = 1.0f;
+  lsum = g2 == 0 ? 1.0f : 0.0f;   // the column's two lanes add up to 1
 #pragma unroll
   for (int db = 0; db < 4; ++db)
 #pragma unroll
@@ -1139,7 +1149,7 @@ __global__ __launch_bounds__(PAIRED ? 512 : 256, PAIRED ? 1 : 2) void attention_
   f32x16 o[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) o[i] = f32x16{};
-  f32x16 lacc = f32x16{};
+  float lsum = 0.0f;   // this lane's half of its column's denominator
   float m = -INFINITY;
 
   const char* kbase = reinterpret_cast<const char*>(a.k_plane + (int64_t(w.head) * a.cap + rq.row_base) * 128);
@@ -1218,7 +1228,7 @@ __global__ __launch_bounds__(PAIRED ? 512 : 256, PAIRED ? 1 : 2) void attention_
     dec_rotate(a, c.u, qx);
 #pragma unroll
     for (int s = 0; s < 8; ++s) qb[s] = __builtin_bit_cast(bf16x8, qx[s]);
-    if (has && w.split == a.dec_split - 1) dec_own_row(a, c, qb, w.head, m, lacc, o);
+    if (has && w.split == a.dec_split - 1) dec_own_row(a, c, qb, w.head, m, lsum, o);
   }
   // step i: the group's tile tb + i sits in stage S (i even: 0); wait for its
   // copies, start the next tile's copies into the other stage, consume it
@@ -1238,7 +1248,7 @@ __global__ __launch_bounds__(PAIRED ? 512 : 256, PAIRED ? 1 : 2) void attention_
     }
     // (a wave without columns has wq_max INT_MIN and computes nothing)
     if (tp.x <= c.wq_max && c.wq_max != INT_MIN)
-      tile_pipelined<S * kStageBytes>(c, qb, tp, paddr, t * kAttnRowsPerTile, rows, a.scale_log2, m, o, lacc);
+      tile_pipelined<S * kStageBytes>(c, qb, tp, paddr, t * kAttnRowsPerTile, rows, a.scale_log2, m, o, lsum);
     if (FUSED && more) fused_k_store(a, fk, smem + (1 - S) * kStageBytes);
   };
   for (int i = 0; i < steps; i += 2) {
@@ -1246,8 +1256,8 @@ __global__ __launch_bounds__(PAIRED ? 512 : 256, PAIRED ? 1 : 2) void attention_
     if (i + 1 < steps) step(std::integral_constant<int, 1>{}, i + 1);
   }
 
-  // rows of lacc are identical: each lane already holds its column's full sum
-  float lt = lacc[0];
+  // the column's denominator: this lane's rows and lane ^ 32's
+  float lt = lsum + __shfl_xor(lsum, 32);
   if (PAIRED && w0.merge_pair) {
     // the second split of the pair hands (O, m, sum) to the first through LDS,
     // laid out [wave][16-byte chunk][lane] so that both sides are
