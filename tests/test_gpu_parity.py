@@ -375,7 +375,8 @@ def test_hot_set_in_front_of_host_pool(name):
     batch but not all of them: every batch assembles and attends bit for bit
     as from the device pool (variant M, variant F after a plan-only
     assembly, values left in the pool); pages are admitted, reused and
-    evicted; a batch whose pages are all resident copies nothing."""
+    evicted; a batch whose pages are all resident copies nothing; decode
+    after a prefill through the hot set gives the device pool's bits."""
     wls = [W.get(name, layout=k) for k in range(3)]
     need = [_covered_pages(w) for w in wls]
     cap = max(len(x) for x in need)
@@ -387,6 +388,11 @@ def test_hot_set_in_front_of_host_pool(name):
         dref.wl = w
         dref.assemble()
         ref[k] = run_prefill(dref, layers, VARIANT_MATERIALIZED)
+    dref.wl = wls[1]
+    dref.session.set_decode_rows(2)
+    dref.assemble()
+    run_prefill(dref, layers, VARIANT_MATERIALIZED)
+    dec_ref = run_decode(dref, layers, 2, VARIANT_MATERIALIZED)
     dref.close()
     _say(f"case hot set {name}: {cap} page slots, batches need {[len(x) for x in need]}")
     dw = open_workload(wls[0], host_pool=True, hot_pages=cap)
@@ -410,6 +416,18 @@ def test_hot_set_in_front_of_host_pool(name):
     run_prefill(dw, layers, VARIANT_MATERIALIZED)
     st2 = cache.stats()
     assert st2["bytes_copied"] == st["bytes_copied"] and st2["misses"] == st["misses"], (st, st2)
+    # decode through the hot set: M, F after a plan-only assembly, values in the pool
+    dw.wl = wls[1]
+    dw.session.set_decode_rows(2)
+    for how in ("gathered", "plan_only", "values_in_pool"):
+        dw.assemble(plan_only=how == "plan_only", values_in_pool=how == "values_in_pool")
+        variant = VARIANT_FUSED if how == "plan_only" else VARIANT_MATERIALIZED
+        run_prefill(dw, layers, variant)
+        dec = run_decode(dw, layers, 2, variant)
+        for l in layers:
+            for stp in range(2):
+                assert torch.equal(dec_ref[l][stp][3], dec[l][stp][3]), f"hot set decode ({how}) differs ({l}, {stp})"
+    _say(f"  decode through the hot set: {cache.stats()}")
     dw.close()
 
 
