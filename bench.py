@@ -21,6 +21,7 @@ reads the pool inside attention, rotating keys on load.
 from __future__ import annotations
 
 import argparse
+import gc
 import json
 import os
 import sys
@@ -227,15 +228,20 @@ def decode_bench(args, wl, dw, inputs, variant, stream) -> dict:
     dec_in = [[W.decode_tokens(wl, l, st, dw.kscale, dw.vscale, dw.kscale.device) for l in range(m.layers)]
               for st in range(K)]
     dout = torch.empty_like(dec_in[0][0][0])
+    dptr = [[tuple(t.data_ptr() for t in dec_in[st][l]) for l in range(m.layers)] for st in range(K)]
+    optr, sptr = dout.data_ptr(), stream.cuda_stream
+    dl = plan.decode_layer
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
+    gc.collect()
+    gc.disable()   # (as in the prefill's timed region)
     torch.cuda.synchronize()
     ev[0].record(stream)
     for st in range(K):
         for l in range(m.layers):
-            q, k, v = dec_in[st][l]
-            plan.decode_layer(l, st, q, k, v, dout, variant, stream)
+            dl(l, st, *dptr[st][l], optr, variant, sptr)
         ev[st + 1].record(stream)
     torch.cuda.synchronize()
+    gc.enable()
     ms = [ev[i].elapsed_time(ev[i + 1]) for i in range(K)]
     plan.set_decode_rows(0)
     rows = wl.rows_total
@@ -278,6 +284,11 @@ def main():
     outs = [torch.empty_like(inputs[l][0]) for l in range(m.layers)]
     tables = [(w.span_ptr(), w.spans_flat(), w.new_ptr(), w.new_pos_flat(), w.n_new_total) for w in wls]
     stream = torch.cuda.current_stream()
+    # device pointers of each layer's inputs and output, taken once: a step
+    # reads the leading rows its layout needs, which start at the same address
+    lptr = [(inputs[l][0].data_ptr(), inputs[l][1].data_ptr(), inputs[l][2].data_ptr(), outs[l].data_ptr())
+            for l in range(m.layers)]
+    sptr = stream.cuda_stream
     plan = sess.plan
     plan_flag = 0 if args.variant == "M" else PLAN_ONLY
     vpool = args.values_in_pool and args.variant == "M"
@@ -296,15 +307,14 @@ def main():
             for l in range(m.layers):
                 if l + 1 < m.layers:
                     plan.gather_layers(l + 1, l + 2, side)
-                q, k, v = inputs[l]
-                plan.query_prefill(l, q[:n], k[:n], v[:n], outs[l][:n], variant, stream)
+                plan.query_prefill(l, *lptr[l], variant, sptr)
             # the next step's planes may only be overwritten after this one is done
             stream.wait_stream(side)
             return
         plan.assemble(sp, spans, npt, npos, sess.asm_k, sess.asm_v, sess.capacity, plan_flag, stream)
+        qp = plan.query_prefill
         for l in range(m.layers):
-            q, k, v = inputs[l]
-            plan.query_prefill(l, q[:n], k[:n], v[:n], outs[l][:n], variant, stream)
+            qp(l, *lptr[l], variant, sptr)
 
     # with a hot set: a cold first pass over the layouts, each step timed (the
     # first misses every page; later ones may find pages an earlier layout
@@ -330,16 +340,24 @@ def main():
     log(f"[bench] warmup done ({args.warmup} steps)")
     hot_before = sess.cache.stats() if sess.cache is not None else None
 
-    # timed region: K steps, per-step events on the launch stream
+    # timed region: K steps, per-step events on the launch stream.  Python's
+    # cyclic garbage collector stays off inside it: a full collection stalls
+    # the issuing thread for tens of milliseconds at a step fixed by the
+    # allocation count, longer than the one step the host runs ahead, and
+    # the GPU would wait (measured: one step of 36-39 ms in 200)
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    gc.collect()
+    gc.disable()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     ev[0].record(stream)
     for i in range(args.steps):
         step(i)
         ev[i + 1].record(stream)
+    issued = time.perf_counter() - t0
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    gc.enable()
     step_ms = [ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps)]
     if hot is not None:
         after = sess.cache.stats()
@@ -347,7 +365,12 @@ def main():
         hot["timed_misses"] = after["misses"] - hot_before["misses"]
         hot["timed_evictions"] = after["evictions"] - hot_before["evictions"]
     total_ms = ev[0].elapsed_time(ev[-1])
-    log(f"[bench] timed {args.steps} steps: {total_ms:.2f} ms (host wall {wall * 1e3:.2f} ms)")
+    log(f"[bench] timed {args.steps} steps: {total_ms:.2f} ms (host wall {wall * 1e3:.2f} ms, "
+        f"issued in {issued * 1e3:.2f} ms)")
+    srt = sorted(step_ms)
+    log(f"[bench] step ms: min {srt[0]:.3f} p50 {srt[len(srt) // 2]:.3f} p90 {srt[int(0.9 * (len(srt) - 1))]:.3f} "
+        f"max {srt[-1]:.3f}; slowest {[round(x, 2) for x in srt[-5:]]} at steps "
+        f"{sorted(range(len(step_ms)), key=lambda i: step_ms[i])[-5:]}")
 
     # per-kernel durations: the same K steps again with the library's HIP-event
     # brackets around each kernel class on the launch stream (kept out of the
@@ -398,6 +421,9 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 4),
+        # host time to issue one step (plan, upload, one call per layer); at or
+        # above the GPU's per-step time (p50 below) the step waits for the host
+        "host_issue_ms_per_step": round(issued * 1e3 / args.steps, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

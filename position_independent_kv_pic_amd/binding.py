@@ -190,7 +190,7 @@ class Pool:
             raise ValueError("page_ids is shorter than chunk_page_ptr[-1]")
         h = ctypes.c_void_p()
         reg = lib().pic_pool_register_host if host else lib().pic_pool_register
-        _check(reg(ctypes.byref(model), ctypes.c_void_p(_ptr(pool)), int(pool_bytes), int(page_tokens),
+        _check(reg(ctypes.byref(model), _ptr(pool), int(pool_bytes), int(page_tokens),
                    int(n_pages), int(cl.shape[0]), _p32(cl), _p32(co), _p32(cp), _p32(pg), ctypes.byref(h)))
         self.handle = h
 
@@ -254,30 +254,30 @@ class Plan:
             raise ValueError(f"new_ptr ends at {int(npt[-1])} but {npos.shape[0]} positions were given")
         self._keep = (sp, npt, tbl, arr, npos)
         _check(lib().pic_assemble(self.handle, batch, _p32(sp), arr, _p32(npt), _p32(npos),
-                                  ctypes.c_void_p(_ptr(asm_k)), ctypes.c_void_p(_ptr(asm_v)),
-                                  int(capacity), int(flags), ctypes.c_void_p(_stream(stream))))
+                                  _ptr(asm_k), _ptr(asm_v),
+                                  int(capacity), int(flags), _stream(stream)))
         self.batch = batch
         self.n_spans = int(tbl.shape[0])
 
     def query_prefill(self, layer: int, q, k_new, v_new, out, variant: int = VARIANT_MATERIALIZED,
                       stream=None):
-        _check(lib().pic_query_prefill(self.handle, int(layer), ctypes.c_void_p(_ptr(q)),
-                                       ctypes.c_void_p(_ptr(k_new)), ctypes.c_void_p(_ptr(v_new)),
-                                       ctypes.c_void_p(_ptr(out)), int(variant),
-                                       ctypes.c_void_p(_stream(stream))))
+        _check(lib().pic_query_prefill(self.handle, int(layer), _ptr(q),
+                                       _ptr(k_new), _ptr(v_new),
+                                       _ptr(out), int(variant),
+                                       _stream(stream)))
 
     def query_prefill_noalloc(self, layer: int, q, k_new, v_new, out, variant: int = VARIANT_MATERIALIZED,
                               stream=None):
         """pic_query_prefill with its scratch in the library's fixed device array."""
-        _check(lib().pic_query_prefill_noalloc(self.handle, int(layer), ctypes.c_void_p(_ptr(q)),
-                                               ctypes.c_void_p(_ptr(k_new)), ctypes.c_void_p(_ptr(v_new)),
-                                               ctypes.c_void_p(_ptr(out)), int(variant),
-                                               ctypes.c_void_p(_stream(stream))))
+        _check(lib().pic_query_prefill_noalloc(self.handle, int(layer), _ptr(q),
+                                               _ptr(k_new), _ptr(v_new),
+                                               _ptr(out), int(variant),
+                                               _stream(stream)))
 
     def gather_layers(self, layer_begin: int, layer_end: int, stream=None):
         """Gather layers [layer_begin, layer_end) after a DEFER_GATHER assemble."""
         _check(lib().pic_gather_layers(self.handle, int(layer_begin), int(layer_end),
-                                       ctypes.c_void_p(_stream(stream))))
+                                       _stream(stream)))
 
     def set_decode_rows(self, rows: int):
         """Rows reserved per request for decode tokens at the next assemble."""
@@ -285,10 +285,10 @@ class Plan:
 
     def decode_layer(self, layer: int, step: int, q, k_new, v_new, out, variant: int = VARIANT_MATERIALIZED,
                      stream=None):
-        _check(lib().pic_decode_layer(self.handle, int(layer), int(step), ctypes.c_void_p(_ptr(q)),
-                                      ctypes.c_void_p(_ptr(k_new)), ctypes.c_void_p(_ptr(v_new)),
-                                      ctypes.c_void_p(_ptr(out)), int(variant),
-                                      ctypes.c_void_p(_stream(stream))))
+        _check(lib().pic_decode_layer(self.handle, int(layer), int(step), _ptr(q),
+                                      _ptr(k_new), _ptr(v_new),
+                                      _ptr(out), int(variant),
+                                      _stream(stream)))
 
     def summary(self) -> dict:
         s = PicPlanSummary()
