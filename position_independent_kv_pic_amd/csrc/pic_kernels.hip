@@ -8,7 +8,8 @@
 //             TurboRAG review page, Reordered Positions: apply RoPE again at
 //             the new position)
 //   prologue  rotate the new tokens' queries and keys to their positions and
-//             append the new keys/values after the prefix
+//             append the new keys/values after the prefix (decode does this
+//             inside its attention instance)
 //   attention query-prefill attention over prefix + new rows with the mask
 //             pos_row <= pos_query (TurboRAG Figure 4: the query sees every
 //             chunk and itself; SemPIC: causal interleave), GQA, bf16 MFMA
@@ -406,8 +407,8 @@ __global__ __launch_bounds__(256) void prologue_kernel(PrologueArgs a) {
 // Softmax: scores are kept relative to a reference maximum that is raised
 // only when a block's maximum exceeds it by more than 8 (log2 units), so the
 // accumulator rescale is rare; probabilities stay below 2^8.  The denominator
-// is summed on the matrix core from the same bf16 probabilities the PV
-// product uses, so the output is an exact weighted mean of the values.
+// sums (v_dot2) the same bf16 probabilities the PV product uses, so the
+// output is an exact weighted mean of the values.
 //
 // A tile runs as two 32-row blocks pipelined against each other
 // (tile_pipelined).
