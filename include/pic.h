@@ -337,6 +337,12 @@ pic_status pic_query_prefill(pic_plan* plan, int32_t layer, const void* q, const
  * Every call on a device shares that device's array and leaves its
  * contents behind: calls that overlap on one device (two streams, two
  * threads, two plans) race and must be ordered by the caller.
+ * With a hot set in front of a host pool (pic_cache_create), the FUSED
+ * variant and plans assembled with PIC_ASSEMBLE_VALUES_IN_POOL copy the
+ * layer's missing pages first, as pic_query_prefill does: that uploads a
+ * copy list from the hot set's pinned staging and may wait on the host for
+ * the previous list of the same layer, so such calls are not fit for graph
+ * capture (they still allocate nothing).
  */
 pic_status pic_query_prefill_noalloc(pic_plan* plan, int32_t layer, const void* q, const void* k_new,
                                      const void* v_new, void* out, int32_t variant, void* stream);
