@@ -45,6 +45,7 @@ struct GatherArgs {
   int32_t page_shift, page_tokens, kv_heads, planes_per_block;
   int32_t plane_begin, plane_end;  // (layer, kv head) planes l * Hkv + h to gather
   int32_t values;           // 0: keys only (values stay in the pool, attention reads them there)
+  int64_t row_blocks8;      // (set by the launcher) row blocks rounded up to a multiple of 8
 };
 
 struct PrologueArgs {

@@ -253,7 +253,16 @@ __global__ __launch_bounds__(256) void gather_kernel(GatherArgs a) {
   constexpr int64_t RB = int64_t(D) * ES;
   const int rl = threadIdx.x / LPR;
   const int j = threadIdx.x % LPR;
-  const int64_t u = int64_t(blockIdx.x) * RPB + rl;
+  // Workgroup b runs on XCD b mod 8.  The row blocks (padded to a multiple
+  // of 8) are cut into 8 slices; XCD x takes slice x under every plane
+  // group, rows fastest, so the source records and phase rows it reads stay
+  // in its own L2.  (A bijection: per XCD, k < per * groups.)
+  const int per = int(a.row_blocks8 >> 3);
+  const int bid = int(blockIdx.x);
+  const int xcd = bid & 7, k = bid >> 3;
+  const int pgrp = k / per;
+  const int64_t rb = int64_t(xcd) * per + (k - pgrp * per);
+  const int64_t u = rb * RPB + rl;
   if (u >= a.prefix_rows) return;
   const int4 g = a.gsrc[u];
   const char* __restrict__ src_row =
@@ -268,7 +277,7 @@ __global__ __launch_bounds__(256) void gather_kernel(GatherArgs a) {
 #pragma unroll
     for (int e = 0; e < EPV; ++e) ph[e] = pp[e];
   }
-  const int p0 = a.plane_begin + blockIdx.y * a.planes_per_block;
+  const int p0 = a.plane_begin + pgrp * a.planes_per_block;
   const int p1 = min(p0 + a.planes_per_block, a.plane_end);
   const int64_t plane_stride = int64_t(a.page_tokens) * RB;  // one (layer, K/V, head) run
   char* __restrict__ ak = a.asm_k;
@@ -1506,15 +1515,17 @@ static void gather_launch(const GatherArgs& a, hipStream_t s) {
   constexpr int LPR = D / (2 * (16 / ES));
   constexpr int RPB = 256 / LPR;
   const int n_planes = a.plane_end - a.plane_begin;
-  dim3 grid(unsigned((a.prefix_rows + RPB - 1) / RPB),
-            unsigned((n_planes + a.planes_per_block - 1) / a.planes_per_block));
+  const int64_t groups = (n_planes + a.planes_per_block - 1) / a.planes_per_block;
+  GatherArgs b = a;
+  b.row_blocks8 = ((a.prefix_rows + RPB - 1) / RPB + 7) / 8 * 8;
+  dim3 grid(unsigned(b.row_blocks8 * groups));
   if constexpr (BF16 && D == 128) {
     if (!a.values) {
-      hipLaunchKernelGGL((gather_kernel<BF16, D, false>), grid, dim3(256), 0, s, a);
+      hipLaunchKernelGGL((gather_kernel<BF16, D, false>), grid, dim3(256), 0, s, b);
       return;
     }
   }
-  hipLaunchKernelGGL((gather_kernel<BF16, D, true>), grid, dim3(256), 0, s, a);
+  hipLaunchKernelGGL((gather_kernel<BF16, D, true>), grid, dim3(256), 0, s, b);
 }
 
 hipError_t launch_gather(int dtype, int head_dim, const GatherArgs& a, hipStream_t s) {
