@@ -567,6 +567,60 @@ def test_decode_on_edge_layouts():
     dw.close()
 
 
+def _random_workload(seed):
+    """A seeded random layout on Qwen2-like heads, two layers: 3-8 chunks of
+    1-299 tokens at random original positions; 1-5 requests of 0-6 spans
+    (any sub-span, one token up to a whole chunk, repeats allowed) placed
+    automatically, at their original positions or at explicit targets; 0-40
+    new tokens that follow the prefix or (every request of the batch) sit at
+    random increasing positions (the first request has at least one)."""
+    rng = np.random.default_rng(4000 + seed)
+    model = W.ModelShape(2, 28, 4, 128, 1e6, "bf16")
+    n_chunks = int(rng.integers(3, 9))
+    lens = rng.integers(1, 300, n_chunks)
+    pool = W.make_pool(rng, lens, page_tokens=16)
+    pool.chunk_orig = rng.integers(0, 5000, n_chunks).astype(np.int32)
+    reqs = []
+    explicit = rng.random() < 0.5
+    for b in range(int(rng.integers(1, 6))):
+        spans = []
+        for _ in range(int(rng.integers(0, 7))):
+            c = int(rng.integers(0, n_chunks))
+            s0 = int(rng.integers(0, lens[c]))
+            e0 = int(rng.integers(s0, lens[c]))
+            kind = rng.random()
+            t = W.TARGET_AUTO if kind < 0.6 else (W.TARGET_ORIGINAL if kind < 0.75 else int(rng.integers(0, 3000)))
+            spans.append([c, s0, e0, t])
+        n_new = int(rng.integers(1 if b == 0 else 0, 41))
+        new_pos = np.sort(rng.choice(6000, n_new, replace=False)).astype(np.int32) if explicit else None
+        reqs.append(W.Request(np.array(spans, np.int32).reshape(-1, 4), n_new, new_pos))
+    return W.Workload(f"random_{seed}", 0, model, pool, reqs, W.ValueRecipe("lognormal", "half"), 950 + seed)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_random_layouts_every_element(seed):
+    """Seeded random layouts: every output element and every assembled row
+    against the oracle, the fused variant and values left in the pool bit
+    for bit against M, and three decode steps."""
+    wl = _random_workload(seed)
+    _say(f"case random {seed}: (spans, new tokens) {[(len(r.spans), r.n_new) for r in wl.requests]}")
+    dw = open_workload(wl)
+    dw.session.set_decode_rows(3)
+    dw.assemble()
+    layers = [0, 1]
+    res = run_prefill(dw, layers, VARIANT_MATERIALIZED)
+    for b in range(wl.batch):
+        _say(f"random {seed}", b, check_request(dw, b, layers, res))
+    res_f = run_prefill(dw, layers, VARIANT_FUSED)
+    for l in layers:
+        assert torch.equal(res[l][3], res_f[l][3]), f"fused != materialised on layer {l}"
+    dec = run_decode(dw, layers, 3, VARIANT_MATERIALIZED)
+    for b in range(wl.batch):
+        check_decode(dw, b, layers, res, dec)
+    check_values_in_pool(dw, layers, res)
+    dw.close()
+
+
 def test_plan_reuse_with_smaller_batch():
     wl = W.get("coinrag_small")
     _say("case reuse")
