@@ -64,6 +64,11 @@ def parse():
     ap.add_argument("--hot-pages", type=int, default=0,
                     help="with --host-pool: an HBM hot set of this many page slots in front of the pool "
                          "(least recently used pages evicted); reports the cold first pass over the layouts")
+    ap.add_argument("--store-dir", default=None,
+                    help="with --host-pool: write the pool to one file per chunk in this directory and let "
+                         "assembly read the pages each batch covers from the files; reports cold steps "
+                         "(every page read from the files, the OS cache dropped first)")
+    ap.add_argument("--store-threads", type=int, default=8, help="host threads reading chunk files")
     ap.add_argument("--decode-steps", type=int, default=0,
                     help="also time this many decode steps (every layer, one token per request) after a prefill")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -273,7 +278,15 @@ def main():
     wl = wls[0]
     m = wl.model
     log(f"[bench] workload {wl.name}: batch {wl.batch}, layers {m.layers}, rows {wl.rows_total}")
-    dw = open_workload(wl, host_pool=args.host_pool, hot_pages=args.hot_pages)
+    if args.store_dir and not args.host_pool:
+        sys.exit("--store-dir needs --host-pool")
+    if args.store_dir:
+        os.makedirs(args.store_dir, exist_ok=True)
+    t_open = time.perf_counter()
+    dw = open_workload(wl, host_pool=args.host_pool, hot_pages=args.hot_pages, store_dir=args.store_dir,
+                       store_threads=args.store_threads)
+    if args.store_dir:
+        log(f"[bench] pool written to {len(wl.pool.chunk_len)} chunk files in {time.perf_counter() - t_open:.1f} s")
     sess = dw.session
     cap = max(w.rows_total for w in wls)
     sess.ensure_capacity(cap)
@@ -315,6 +328,32 @@ def main():
         qp = plan.query_prefill
         for l in range(m.layers):
             qp(l, *lptr[l], variant, sptr)
+
+    # with chunk files: each layout once from cold files (pages forgotten and
+    # the OS cache dropped first), host wall time to the end of the step
+    store = None
+    if sess.store is not None:
+        cold, nbytes, waits = [], [], []
+        for i in range(len(tables)):
+            torch.cuda.synchronize()
+            sess.store.forget(drop_os_cache=True)
+            s0 = sess.store.stats()
+            t0 = time.perf_counter()
+            step(i)
+            torch.cuda.synchronize()
+            cold.append((time.perf_counter() - t0) * 1e3)
+            s1 = sess.store.stats()
+            nbytes.append(s1["bytes_read"] - s0["bytes_read"])
+            waits.append(s1["wait_seconds"] - s0["wait_seconds"])
+        store = {"threads": args.store_threads, "cold_step_ms": [round(x, 2) for x in cold],
+                 "cold_bytes_read": nbytes, "cold_read_seconds": [round(x, 4) for x in waits],
+                 "read_GBps": round(sum(nbytes) / max(sum(waits), 1e-9) / 1e9, 2),
+                 "after_cold_pass": sess.store.stats()}
+        log(f"[bench] chunk files, cold steps: {store}")
+        # the timed steps below find every page loaded
+        for t in tables:
+            sess.store.request(t[0], t[1])
+        sess.store.wait()
 
     # with a hot set: a cold first pass over the layouts, each step timed (the
     # first misses every page; later ones may find pages an earlier layout
@@ -467,6 +506,9 @@ def main():
         res["decode"] = decode_bench(args, wl, dw, inputs, variant, stream)
     if hot is not None:
         res["hot_set"] = hot
+    if store is not None:
+        res["chunk_files"] = store
+        res["config"]["pool"] = "pinned host, filled from chunk files"
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle sample")
         res["cpu_baseline"] = cpu_baseline(wl, dw.pool, dw, args.cpu_seconds)

@@ -57,7 +57,8 @@ typedef enum {
   PIC_EDEVICE = -4,      /* the HIP runtime reported an error */
   PIC_ESTATE = -5,       /* handle in the wrong state (released, not assembled, failed) */
   PIC_EALIGN = -6,       /* a device pointer is not 16-byte aligned */
-  PIC_EUNSUPPORTED = -7  /* valid request this build does not implement */
+  PIC_EUNSUPPORTED = -7, /* valid request this build does not implement */
+  PIC_EIO = -8           /* reading or writing a chunk file failed */
 } pic_status;
 
 typedef enum { PIC_F32 = 0, PIC_BF16 = 1 } pic_dtype;
@@ -219,6 +220,92 @@ pic_status pic_cache_get_stats(const pic_cache* cache, pic_cache_stats* out);
 /* Release the hot set and its device memory.  The plans over its pool must
  * be released first (PIC_ESTATE otherwise).  Synchronises the device. */
 pic_status pic_cache_release(pic_cache* cache);
+
+/*
+ * Chunk files: the storage tier behind a pool in host memory.  Each chunk's
+ * cache is one file, and only the pages that a batch's spans cover are read,
+ * per chunk by a pool of host threads (the CoinRAG page, section 3.3: one
+ * cache file per chunk on NVMe, loaded asynchronously per document, only the
+ * selected token ranges).
+ *
+ * File layout (little-endian): a 4096-byte header (magic "PICCHUNK", version
+ * 1, the model shape, page_tokens, len, orig, page_bytes, page count), then
+ * the chunk's ceil(len / page_tokens) pages in the pool's page layout (see
+ * pic_pool_register), page j at byte offset 4096 + j * page_bytes.
+ *
+ * pic_chunk_file_write writes one such file for a chunk of `len` tokens
+ * encoded at original position `orig`: page j is copied from host memory at
+ * pages + page_list[j] * page_bytes (page_list: host int32[ceil(len /
+ * page_tokens)], each >= 0; the caller guarantees the memory is there).  The
+ * file is created or truncated, and flushed to the device before the call
+ * returns; on a failure it is removed.  PIC_EINVAL / PIC_ERANGE for bad
+ * arguments, PIC_EIO if the file cannot be written.
+ */
+pic_status pic_chunk_file_write(const pic_model* model, int32_t page_tokens, int32_t len, int32_t orig,
+                                const void* pages, const int32_t* page_list, const char* path);
+
+/*
+ * Open the files of a pool's chunks (paths: host array of n_chunks paths,
+ * copied) to be loaded into `dst`, host memory of dst_bytes >= n_pages *
+ * page_bytes laid out like the pool (page p at dst + p * page_bytes; the
+ * memory stays the caller's).  Every header is checked against the pool
+ * (model, page size, the chunk's length and origin) and every file's size
+ * against its pages: PIC_EINVAL or PIC_EIO naming the file otherwise.  The
+ * chunk pages the files back must be distinct pool pages (PIC_EINVAL).
+ * `threads` (1..256) host threads do the reads.  No page counts as loaded
+ * after opening.
+ *
+ * When `dst` is the pool's own memory and the pool was registered with
+ * pic_pool_register_host, the store is attached to the pool: from then on
+ * pic_assemble reads the pages its batch covers that are not loaded yet,
+ * and returns only once they are in host memory (PIC_EIO, with nothing
+ * enqueued, if a read fails), so every later reader (gathers over the host
+ * link, the hot set's copies, attention reading the pool) finds them.  At
+ * most one store is attached to a pool, before the pool's plans are created
+ * (PIC_ESTATE otherwise); the pool cannot be released while it is attached.
+ * A store over a pool in device memory fills a separate host buffer and is
+ * not attached (dst equal to the device pool's own pointer is PIC_EINVAL).
+ * None of the store calls touch the device.
+ */
+typedef struct pic_store pic_store;
+
+typedef struct {
+  int64_t resident_pages;   /* pages loaded and not forgotten */
+  int64_t requested;        /* covered pages named by requests (pic_store_request, pic_assemble) */
+  int64_t hits;             /* ... that were loaded or being loaded already */
+  int64_t pages_read;       /* pages read from the files */
+  int64_t bytes_read;       /* bytes those reads moved */
+  int64_t reads;            /* vectored read calls (one per run of consecutive pages of a file) */
+  double wait_seconds;      /* time callers were blocked waiting for loads */
+} pic_store_stats;
+
+pic_status pic_store_open(pic_pool* pool, void* dst, int64_t dst_bytes, const char* const* paths,
+                          int32_t threads, pic_store** out);
+
+/* Start loading the pages that a batch's spans cover (span_ptr: host
+ * int32[batch + 1], spans: host pic_span[span_ptr[batch]], validated as
+ * pic_assemble validates them; targets are not used) and return at once.
+ * Pages loaded or being loaded are not read again.  Lets a caller read the
+ * next batch's pages while the current batch runs. */
+pic_status pic_store_request(pic_store* store, int32_t batch, const int32_t* span_ptr, const pic_span* spans);
+
+/* Block until every requested load has finished.  PIC_EIO with the first
+ * read error since the previous wait; the pages of a failed read stay
+ * unloaded (a later request tries them again). */
+pic_status pic_store_wait(pic_store* store);
+
+/* Wait for the loads in flight, then count every page as not loaded, so the
+ * next requests read them again; with drop_os_cache != 0, also ask the OS to
+ * drop the files' cached pages (posix_fadvise DONTNEED), so those reads come
+ * from the device.  The caller must make sure no device work still reads
+ * the pool's pages (pages are rewritten with the same bytes). */
+pic_status pic_store_forget(pic_store* store, int32_t drop_os_cache);
+
+pic_status pic_store_get_stats(pic_store* store, pic_store_stats* out);
+
+/* Wait for the loads in flight and release the store (not `dst`).  An
+ * attached store needs the pool's plans released first (PIC_ESTATE). */
+pic_status pic_store_release(pic_store* store);
 
 /* Create a plan object for batches over `pool`.  Its host and device tables
  * grow on demand and are reused by later pic_assemble calls. */

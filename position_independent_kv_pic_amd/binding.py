@@ -39,6 +39,8 @@ EXPORTED = (
     "pic_timing_reset", "pic_last_error", "pic_version", "pic_plan_set_decode_rows", "pic_decode_layer",
     "pic_pool_register_host", "pic_gather_layers", "pic_plan_get_attention_work",
     "pic_query_prefill_noalloc", "pic_cache_create", "pic_cache_get_stats", "pic_cache_release",
+    "pic_chunk_file_write", "pic_store_open", "pic_store_request", "pic_store_wait", "pic_store_forget",
+    "pic_store_get_stats", "pic_store_release",
 )
 
 
@@ -65,6 +67,12 @@ class PicCacheStats(ctypes.Structure):
     _fields_ = [("capacity_pages", ctypes.c_int64), ("resident_pages", ctypes.c_int64),
                 ("hits", ctypes.c_int64), ("misses", ctypes.c_int64), ("evictions", ctypes.c_int64),
                 ("layer_copies", ctypes.c_int64), ("bytes_copied", ctypes.c_int64)]
+
+
+class PicStoreStats(ctypes.Structure):
+    _fields_ = [("resident_pages", ctypes.c_int64), ("requested", ctypes.c_int64), ("hits", ctypes.c_int64),
+                ("pages_read", ctypes.c_int64), ("bytes_read", ctypes.c_int64), ("reads", ctypes.c_int64),
+                ("wait_seconds", ctypes.c_double)]
 
 
 class PicPlanSummary(ctypes.Structure):
@@ -107,6 +115,13 @@ def lib() -> ctypes.CDLL:
         "pic_cache_create": [P, I32, ctypes.POINTER(P)],
         "pic_cache_get_stats": [P, ctypes.POINTER(PicCacheStats)],
         "pic_cache_release": [P],
+        "pic_chunk_file_write": [ctypes.POINTER(PicModel), I32, I32, I32, P, pi32, ctypes.c_char_p],
+        "pic_store_open": [P, P, I64, ctypes.POINTER(ctypes.c_char_p), I32, ctypes.POINTER(P)],
+        "pic_store_request": [P, I32, pi32, ctypes.POINTER(PicSpan)],
+        "pic_store_wait": [P],
+        "pic_store_forget": [P, I32],
+        "pic_store_get_stats": [P, ctypes.POINTER(PicStoreStats)],
+        "pic_store_release": [P],
         "pic_plan_create": [P, ctypes.POINTER(P)],
         "pic_plan_release": [P],
         "pic_assemble": [P, I32, pi32, ctypes.POINTER(PicSpan), pi32, pi32, P, P, I64, I32, P],
@@ -216,6 +231,68 @@ class Cache:
     def release(self):
         if self.handle:
             _check(lib().pic_cache_release(self.handle))
+            self.handle = None
+
+
+def _span_array(spans):
+    tbl = _i32(spans).reshape(-1, 4)
+    arr = (PicSpan * max(1, tbl.shape[0]))()
+    if tbl.shape[0]:
+        ctypes.memmove(arr, tbl.ctypes.data, tbl.nbytes)
+    return tbl, arr
+
+
+def write_chunk_file(model: PicModel, page_tokens: int, length: int, orig: int, pages, page_list, path: str):
+    """Write one chunk file: the chunk's pages, page j taken from host memory
+    at pages + page_list[j] * page_bytes (`pages`: an address or a numpy
+    array)."""
+    pl = _i32(page_list)
+    need = (int(length) + int(page_tokens) - 1) // int(page_tokens)
+    if pl.shape[0] < need:
+        raise ValueError(f"page_list needs {need} entries, got {pl.shape[0]}")
+    base = pages if isinstance(pages, int) else pages.ctypes.data
+    _check(lib().pic_chunk_file_write(ctypes.byref(model), int(page_tokens), int(length), int(orig),
+                                      base, _p32(pl), os.fsencode(path)))
+
+
+class Store:
+    """Chunk files loaded on demand into host memory laid out like the pool
+    (attached to the pool when `dst` is the host pool's own memory)."""
+
+    def __init__(self, pool: Pool, dst, dst_bytes: int, paths, threads: int = 8):
+        n_chunks = pool._keep[0].shape[0]
+        if len(paths) != n_chunks:
+            raise ValueError(f"{n_chunks} chunk paths needed, got {len(paths)}")
+        self._paths = (ctypes.c_char_p * max(1, len(paths)))(*[os.fsencode(p) for p in paths])
+        base = dst if isinstance(dst, int) else (dst.ctypes.data if isinstance(dst, np.ndarray) else _ptr(dst))
+        h = ctypes.c_void_p()
+        _check(lib().pic_store_open(pool.handle, base, int(dst_bytes), self._paths, int(threads),
+                                    ctypes.byref(h)))
+        self.handle = h
+
+    def request(self, span_ptr, spans):
+        """Start loading the pages a batch's spans cover; returns at once."""
+        sp = _i32(span_ptr)
+        tbl, arr = _span_array(spans)
+        if sp.shape[0] < 1 or int(sp[-1]) != tbl.shape[0]:
+            raise ValueError("span_ptr must end at the number of spans")
+        self._keep = (sp, tbl, arr)
+        _check(lib().pic_store_request(self.handle, int(sp.shape[0]) - 1, _p32(sp), arr))
+
+    def wait(self):
+        _check(lib().pic_store_wait(self.handle))
+
+    def forget(self, drop_os_cache: bool = False):
+        _check(lib().pic_store_forget(self.handle, 1 if drop_os_cache else 0))
+
+    def stats(self) -> dict:
+        s = PicStoreStats()
+        _check(lib().pic_store_get_stats(self.handle, ctypes.byref(s)))
+        return {f: getattr(s, f) for f, _ in PicStoreStats._fields_}
+
+    def release(self):
+        if self.handle:
+            _check(lib().pic_store_release(self.handle))
             self.handle = None
 
 

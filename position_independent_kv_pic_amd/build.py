@@ -18,7 +18,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libpic.so")
 
-SOURCES = ["pic_api.hip", "pic_kernels.hip", "pic_plan.cpp"]
+SOURCES = ["pic_api.hip", "pic_kernels.hip", "pic_plan.cpp", "pic_store.cpp"]
 
 HIP_FLAGS = [
     "--offload-arch=gfx950",
@@ -54,7 +54,7 @@ def build(verbose: bool = False) -> str:
         _run(cmd, verbose)
         objs.append(obj)
     tmp = LIB + ".tmp"
-    _run([cc, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
+    _run([cc, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-pthread", "-o", tmp], verbose)
     os.replace(tmp, LIB)
     return LIB
 

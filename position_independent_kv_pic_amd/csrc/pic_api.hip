@@ -6,6 +6,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <memory>
 #include <mutex>
 #include <string>
 #include <utility>
@@ -14,6 +15,7 @@
 #include "pic.h"
 #include "pic_kernels.h"
 #include "pic_plan.h"
+#include "pic_store.h"
 
 namespace {
 
@@ -49,6 +51,7 @@ struct pic_pool {
   int device = -1;
   int32_t* d_page_ids = nullptr;
   pic_cache* cache = nullptr;   // hot set in front of a host pool
+  pic_store* store = nullptr;   // chunk files that fill a host pool on demand
 };
 
 // Hot set: page slots in device memory, their residency (pic::HotSet), and
@@ -65,6 +68,14 @@ struct pic_cache {
   int64_t bytes_copied = 0;
   int device = -1;
   pic_cache(int32_t n_pages, int32_t capacity, int32_t layers) : hs(n_pages, capacity, layers) {}
+};
+
+// Chunk files loaded into a host buffer laid out like the pool; attached to
+// the pool when that buffer is the pool's own pinned memory.
+struct pic_store {
+  pic_pool* pool = nullptr;
+  bool attached = false;
+  std::unique_ptr<pic::ChunkStore> cs;
 };
 
 struct pic_plan {
@@ -523,6 +534,7 @@ pic_status pic_pool_release(pic_pool* pool) {
   if (!pool) return set_err(PIC_EINVAL, "pool is NULL");
   if (pool->n_plans > 0) return set_err(PIC_ESTATE, "%d plans still use this pool", pool->n_plans);
   if (pool->cache) return set_err(PIC_ESTATE, "the pool's hot set must be released first");
+  if (pool->store) return set_err(PIC_ESTATE, "the pool's chunk store must be released first");
   if (pool->d_page_ids) {
     (void)hipDeviceSynchronize();
     (void)hipFree(pool->d_page_ids);
@@ -591,6 +603,106 @@ pic_status pic_cache_release(pic_cache* c) {
     if (ev) (void)hipEventDestroy(ev);
   c->pool->cache = nullptr;
   delete c;
+  return ok();
+}
+
+pic_status pic_chunk_file_write(const pic_model* model, int32_t page_tokens, int32_t len, int32_t orig,
+                                const void* pages, const int32_t* page_list, const char* path) {
+  std::string err;
+  const pic_status st = pic::write_chunk_file(model, page_tokens, len, orig, pages, page_list, path, &err);
+  if (st != PIC_OK) return set_err(st, "%s", err.c_str());
+  return ok();
+}
+
+pic_status pic_store_open(pic_pool* pool, void* dst, int64_t dst_bytes, const char* const* paths,
+                          int32_t threads, pic_store** out) {
+  if (!out) return set_err(PIC_EINVAL, "out is NULL");
+  *out = nullptr;
+  if (!pool) return set_err(PIC_EINVAL, "pool is NULL");
+  const bool attach = pool->info.host && dst == pool->info.base;
+  if (attach) {
+    if (pool->store) return set_err(PIC_ESTATE, "the pool already has a chunk store");
+    if (pool->n_plans > 0) return set_err(PIC_ESTATE, "open the pool's chunk store before its plans");
+  } else if (dst == pool->info.base || dst == pool->info.device_base) {
+    return set_err(PIC_EINVAL, "the pool's memory is device memory; the store fills host memory");
+  }
+  std::unique_ptr<pic::ChunkStore> cs;
+  std::string err;
+  const pic_status st = pic::ChunkStore::open(pool->info, static_cast<char*>(dst), dst_bytes, paths, threads, &cs, &err);
+  if (st != PIC_OK) return set_err(st, "%s", err.c_str());
+  pic_store* s = new (std::nothrow) pic_store;
+  if (!s) return set_err(PIC_ENOMEM, "out of host memory");
+  s->pool = pool;
+  s->attached = attach;
+  s->cs = std::move(cs);
+  if (attach) pool->store = s;
+  *out = s;
+  return ok();
+}
+
+pic_status pic_store_request(pic_store* s, int32_t batch, const int32_t* span_ptr, const pic_span* spans) {
+  if (!s) return set_err(PIC_EINVAL, "store is NULL");
+  const pic::PoolInfo& pi = s->cs->pool();
+  if (batch < 0) return set_err(PIC_EINVAL, "batch must be >= 0");
+  if (batch == 0) return ok();
+  if (!span_ptr) return set_err(PIC_EINVAL, "span_ptr is NULL");
+  if (span_ptr[0] != 0) return set_err(PIC_EINVAL, "span_ptr[0] must be 0");
+  for (int32_t b = 0; b < batch; ++b)
+    if (span_ptr[b + 1] < span_ptr[b]) return set_err(PIC_EINVAL, "span_ptr decreases at %d", b);
+  const int32_t n = span_ptr[batch];
+  if (n > 0 && !spans) return set_err(PIC_EINVAL, "spans is NULL");
+  std::vector<int32_t> pages;
+  for (int32_t i = 0; i < n; ++i) {
+    const pic_span& sp = spans[i];
+    if (sp.chunk < 0 || sp.chunk >= pi.n_chunks)
+      return set_err(PIC_ERANGE, "span %d: chunk %d outside [0, %d)", i, sp.chunk, pi.n_chunks);
+    const int32_t len = pi.chunk_len[size_t(sp.chunk)];
+    if (sp.s < 0 || sp.s > sp.e || sp.e >= len)
+      return set_err(PIC_ERANGE, "span %d: need 0 <= s <= e < len, got s=%d e=%d len=%d", i, sp.s, sp.e, len);
+    const int32_t q0 = pi.chunk_page_ptr[size_t(sp.chunk)];
+    for (int32_t j = sp.s / pi.page_tokens; j <= sp.e / pi.page_tokens; ++j) pages.push_back(q0 + j);
+  }
+  std::sort(pages.begin(), pages.end());
+  pages.erase(std::unique(pages.begin(), pages.end()), pages.end());
+  s->cs->request_logical(pages);
+  return ok();
+}
+
+pic_status pic_store_wait(pic_store* s) {
+  if (!s) return set_err(PIC_EINVAL, "store is NULL");
+  std::string err;
+  const pic_status st = s->cs->wait(&err);
+  if (st != PIC_OK) return set_err(st, "%s", err.c_str());
+  return ok();
+}
+
+pic_status pic_store_forget(pic_store* s, int32_t drop_os_cache) {
+  if (!s) return set_err(PIC_EINVAL, "store is NULL");
+  std::string err;
+  const pic_status st = s->cs->forget(drop_os_cache != 0, &err);
+  if (st != PIC_OK) return set_err(st, "%s", err.c_str());
+  return ok();
+}
+
+pic_status pic_store_get_stats(pic_store* s, pic_store_stats* out) {
+  if (!s || !out) return set_err(PIC_EINVAL, "store or out is NULL");
+  const pic::StoreStats st = s->cs->stats();
+  out->resident_pages = st.resident_pages;
+  out->requested = st.requested;
+  out->hits = st.hits;
+  out->pages_read = st.pages_read;
+  out->bytes_read = st.bytes_read;
+  out->reads = st.reads;
+  out->wait_seconds = st.wait_seconds;
+  return ok();
+}
+
+pic_status pic_store_release(pic_store* s) {
+  if (!s) return set_err(PIC_EINVAL, "store is NULL");
+  if (s->attached && s->pool->n_plans > 0)
+    return set_err(PIC_ESTATE, "%d plans still use the pool", s->pool->n_plans);
+  if (s->attached) s->pool->store = nullptr;
+  delete s;   // waits for the loads in flight
   return ok();
 }
 
@@ -688,11 +800,22 @@ pic_status pic_assemble(pic_plan* p, int32_t batch, const int32_t* span_ptr, con
   st = ensure_pool_device(p->pool);
   if (st != PIC_OK) return st;
 
+  // pages the batch's spans cover (indices into the pool's page table)
+  std::vector<int32_t> logical;
+  if (p->pool->cache || p->pool->store) logical = pic::covered_pages(hp, pi.page_tokens);
+  // with chunk files: the covered pages that are not in host memory yet are
+  // read now (an earlier pic_store_request may have started them), before
+  // anything can read them
+  if (pic_store* ps = p->pool->store) {
+    ps->cs->request_logical(logical);
+    std::string lerr;
+    st = ps->cs->wait(&lerr);
+    if (st != PIC_OK) return set_err(st, "%s", lerr.c_str());
+  }
   // with a hot set: pin the pages the batch covers (this changes nothing
   // when they do not fit) and map the pool's pages to their slots
   std::vector<int32_t> page_tab;
   if (pic_cache* c = p->pool->cache) {
-    const std::vector<int32_t> logical = pic::covered_pages(hp, pi.page_tokens);
     std::vector<int32_t> phys(logical.size());
     for (size_t i = 0; i < logical.size(); ++i) phys[i] = pi.page_ids[size_t(logical[i])];
     std::string perr;

@@ -10,13 +10,13 @@ from typing import Optional
 import numpy as np
 
 from .binding import (DEFER_GATHER, DRY_RUN, PLAN_ONLY, VALUES_IN_POOL, VARIANT_MATERIALIZED,
-                      Cache, Plan, Pool, model_struct)
+                      Cache, Plan, Pool, Store, model_struct)
 
 
 class Session:
     def __init__(self, layers, q_heads, kv_heads, head_dim, theta, dtype, pool_tensor,
                  page_tokens, chunk_len, chunk_page_ptr, page_ids, chunk_orig=None, keys="rotated",
-                 hot_pages: int = 0):
+                 hot_pages: int = 0, store_paths=None, store_threads: int = 8):
         import torch
         self.torch = torch
         self.layers, self.q_heads, self.kv_heads, self.head_dim = layers, q_heads, kv_heads, head_dim
@@ -32,6 +32,14 @@ class Session:
                          chunk_orig, host=self.host_pool)
         # an HBM hot set of `hot_pages` page slots in front of a host pool
         self.cache = Cache(self.pool, hot_pages) if self.host_pool and hot_pages > 0 else None
+        # chunk files behind a host pool: pic_assemble reads the pages each
+        # batch covers into the pool's memory
+        self.store = None
+        if store_paths is not None:
+            if not self.host_pool:
+                raise ValueError("chunk files fill a pool in pinned host memory")
+            self.store = Store(self.pool, pool_tensor, pool_tensor.numel() * pool_tensor.element_size(),
+                               store_paths, store_threads)
         self.plan = Plan(self.pool)
         self.asm_k = None
         self.asm_v = None
@@ -79,6 +87,8 @@ class Session:
 
     def close(self):
         self.plan.release()
+        if self.store is not None:
+            self.store.release()
         if self.cache is not None:
             self.cache.release()
         self.pool.release()

@@ -431,6 +431,78 @@ def test_hot_set_in_front_of_host_pool(name):
     dw.close()
 
 
+@pytest.mark.parametrize("name,hot", [("turborag_small", False), ("coinrag_small_unrot", True)])
+def test_chunk_files_behind_the_host_pool(name, hot, tmp_path):
+    """One file per chunk behind the pinned-host pool (and a hot set): the
+    pool memory starts as NaN bytes and pic_assemble reads exactly the pages
+    each batch covers from the files.  Every layout then attends bit for bit
+    as from the device pool; pages outside every batch stay unread; a page
+    already read is not read again; a request made ahead of the assembly
+    (prefetch) leaves nothing for the assembly to read; decode after a
+    prefill matches too."""
+    wls = [W.get(name, layout=k) for k in range(3)]
+    need = [_covered_pages(w) for w in wls]
+    layers = list(range(wls[0].model.layers))
+    ref = {}
+    dref = open_workload(wls[0])
+    for k, w in enumerate(wls):
+        dref.wl = w
+        dref.assemble()
+        ref[k] = run_prefill(dref, layers, VARIANT_MATERIALIZED)
+    dref.wl = wls[2]
+    dref.session.set_decode_rows(2)
+    dref.assemble()
+    run_prefill(dref, layers, VARIANT_MATERIALIZED)
+    dec_ref = run_decode(dref, layers, 2, VARIANT_MATERIALIZED)
+    dref.close()
+    cap = max(len(x) for x in need) if hot else 0
+    _say(f"case chunk files {name}: hot set {cap} slots, batches cover {[len(x) for x in need]} pages")
+    dw = open_workload(wls[0], host_pool=True, hot_pages=cap, store_dir=str(tmp_path), store_threads=4)
+    store = dw.session.store
+    page_bytes = W.page_bytes(wls[0].model, wls[0].pool.page_tokens)
+    host = dw.pool.view(torch.uint8).reshape(dw.pool.shape[0], page_bytes)
+    seen = set()
+    for k in (0, 1):
+        dw.wl = wls[k]
+        dw.assemble()
+        res = run_prefill(dw, layers, VARIANT_MATERIALIZED)
+        for l in layers:
+            assert torch.equal(ref[k][l][3], res[l][3]), f"layout {k}: chunk files differ on layer {l}"
+        seen |= need[k]
+        st = store.stats()
+        _say(f"  layout {k}: {st}")
+        assert st["pages_read"] == len(seen) == st["resident_pages"], (st, len(seen))
+        # pages no batch has covered yet were never written
+        untouched = [pg for pg in range(dw.pool.shape[0]) if pg not in seen]
+        assert untouched or k > 0, "the first layout covers every page: nothing to check"
+        assert bool((host[untouched] == 0xFF).all()), f"layout {k}: a page outside the batches was written"
+    # layout 2 read ahead of its assembly: the assembly then reads nothing
+    wl2 = wls[2]
+    store.request(wl2.span_ptr(), wl2.spans_flat())
+    store.wait()
+    before = store.stats()["pages_read"]
+    dw.wl = wl2
+    dw.session.set_decode_rows(2)
+    dw.assemble()
+    assert store.stats()["pages_read"] == before
+    run_prefill(dw, layers, VARIANT_MATERIALIZED)
+    dec = run_decode(dw, layers, 2, VARIANT_MATERIALIZED)
+    for l in layers:
+        for stp in range(2):
+            assert torch.equal(dec_ref[l][stp][3], dec[l][stp][3]), f"decode over chunk files differs ({l}, {stp})"
+    # forgotten pages are read again, with the same bits
+    torch.cuda.synchronize()
+    store.forget(drop_os_cache=True)
+    dw.wl = wls[0]
+    dw.session.set_decode_rows(0)
+    dw.assemble()
+    res = run_prefill(dw, layers, VARIANT_MATERIALIZED)
+    for l in layers:
+        assert torch.equal(ref[0][l][3], res[l][3]), f"re-read layout 0 differs on layer {l}"
+    _say(f"  after forget: {store.stats()}")
+    dw.close()
+
+
 def _edge_workload(keys="rotated"):
     """Ragged shapes and degenerate spans on Qwen2-like heads, two layers."""
     rng = np.random.default_rng(77)

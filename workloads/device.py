@@ -6,6 +6,7 @@ buffers, produce each layer's new-token inputs.  No arithmetic of the method.
 from __future__ import annotations
 
 from dataclasses import dataclass
+from typing import Optional
 
 import numpy as np
 
@@ -35,10 +36,31 @@ class DeviceWorkload:
         self.session.close()
 
 
-def open_workload(wl: Workload, device="cuda", host_pool: bool = False, hot_pages: int = 0) -> DeviceWorkload:
+def write_chunk_files(wl: Workload, pool, folder: str):
+    """One file per chunk of the filled pool (host memory), written by the
+    library; returns the paths."""
+    import os
+    from position_independent_kv_pic_amd.binding import model_struct, write_chunk_file
+    m, p = wl.model, wl.pool
+    model = model_struct(m.layers, m.q_heads, m.kv_heads, m.head_dim, m.theta, m.dtype, wl.keys)
+    paths = []
+    for c in range(len(p.chunk_len)):
+        path = os.path.join(folder, f"chunk{c:06d}.pic")
+        lo, hi = int(p.chunk_page_ptr[c]), int(p.chunk_page_ptr[c + 1])
+        write_chunk_file(model, p.page_tokens, int(p.chunk_len[c]), int(p.chunk_orig[c]), int(pool.data_ptr()),
+                         np.asarray(p.page_ids[lo:hi], np.int32), path)
+        paths.append(path)
+    return paths
+
+
+def open_workload(wl: Workload, device="cuda", host_pool: bool = False, hot_pages: int = 0,
+                  store_dir: Optional[str] = None, store_threads: int = 8) -> DeviceWorkload:
     """Fill the pool on the device; with host_pool it is then moved to pinned
     host memory (the staging tier) and the device copy freed, and hot_pages > 0
-    puts an HBM hot set of that many page slots in front of it."""
+    puts an HBM hot set of that many page slots in front of it.  With
+    store_dir (host_pool only) the filled pool is written to one file per
+    chunk there and replaced by pinned memory holding 0xFF bytes (NaN in
+    bf16), which the chunk files then fill page by page as batches need."""
     import torch
     from position_independent_kv_pic_amd.session import Session
     ks, vs = channel_scales(wl, device)
@@ -50,8 +72,17 @@ def open_workload(wl: Workload, device="cuda", host_pool: bool = False, hot_page
         del pool
         torch.cuda.empty_cache()
         pool = host
+    paths = None
+    if store_dir is not None:
+        if not host_pool:
+            raise ValueError("chunk files sit behind a pool in pinned host memory")
+        paths = write_chunk_files(wl, pool, store_dir)
+        empty = torch.empty(pool.shape, dtype=pool.dtype, pin_memory=True)
+        empty.view(torch.uint8).fill_(0xFF)
+        del pool
+        pool = empty
     m, p = wl.model, wl.pool
     sess = Session(m.layers, m.q_heads, m.kv_heads, m.head_dim, m.theta, m.dtype, pool, p.page_tokens,
                    p.chunk_len, p.chunk_page_ptr, p.page_ids, p.chunk_orig, keys=wl.keys,
-                   hot_pages=hot_pages if host_pool else 0)
+                   hot_pages=hot_pages if host_pool else 0, store_paths=paths, store_threads=store_threads)
     return DeviceWorkload(wl, pool, ks, vs, sess)
