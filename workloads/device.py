@@ -59,8 +59,8 @@ def open_workload(wl: Workload, device="cuda", host_pool: bool = False, hot_page
     host memory (the staging tier) and the device copy freed, and hot_pages > 0
     puts an HBM hot set of that many page slots in front of it.  With
     store_dir (host_pool only) the filled pool is written to one file per
-    chunk there and replaced by pinned memory holding 0xFF bytes (NaN in
-    bf16), which the chunk files then fill page by page as batches need."""
+    chunk there and overwritten with 0xFF bytes (NaN in bf16), which the
+    chunk files then replace page by page as batches need."""
     import torch
     from position_independent_kv_pic_amd.session import Session
     ks, vs = channel_scales(wl, device)
@@ -77,10 +77,7 @@ def open_workload(wl: Workload, device="cuda", host_pool: bool = False, hot_page
         if not host_pool:
             raise ValueError("chunk files sit behind a pool in pinned host memory")
         paths = write_chunk_files(wl, pool, store_dir)
-        empty = torch.empty(pool.shape, dtype=pool.dtype, pin_memory=True)
-        empty.view(torch.uint8).fill_(0xFF)
-        del pool
-        pool = empty
+        pool.view(torch.uint8).fill_(0xFF)
     m, p = wl.model, wl.pool
     sess = Session(m.layers, m.q_heads, m.kv_heads, m.head_dim, m.theta, m.dtype, pool, p.page_tokens,
                    p.chunk_len, p.chunk_page_ptr, p.page_ids, p.chunk_orig, keys=wl.keys,
