@@ -243,7 +243,9 @@ __global__ __launch_bounds__(256) void plan_tiles_kernel(PlanArgs a) {
 // block covers 256 / LPR rows of the span table and `planes_per_block`
 // (layer, kv head) planes, reusing each row's source record and phases.  The
 // record (assembled row, pool slot, phase row) was resolved once per row by
-// the plan, so a row costs one load before its data loads are issued.
+// the plan, so a row costs one load before its data loads are issued.  A
+// phase row is fetched once per run of rows sharing it within a wave (the
+// rows of one span) and handed to the run's other rows through LDS.
 template <bool BF16, int D, bool VALUES>
 __global__ __launch_bounds__(256) void gather_kernel(GatherArgs a) {
   constexpr int ES = BF16 ? 2 : 4;
@@ -271,12 +273,23 @@ __global__ __launch_bounds__(256) void gather_kernel(GatherArgs a) {
   // rotation: the span's delta, or for un-rotated keys the row's new position
   // (phase row g.z; none where the rotation is by 0)
   const bool rot = g.z >= 0;
+  // Phase rows: consecutive rows of a span share one.  Within a wave only
+  // the first row of each run of equal phase rows (a leader) loads it; the
+  // leader stages it in LDS and the other rows of the run read it there.
+  constexpr int RPW = 64 / LPR;
+  __shared__ Phase ph_lds[4][RPW][D / 2];
+  const int lane = threadIdx.x & 63;
+  const int wv = threadIdx.x >> 6;
+  const int riw = lane / LPR;
+  const int zprev = __shfl_up(g.z, LPR);
+  const bool lead = rot && (riw == 0 || zprev != g.z);
   Phase ph[EPV];
-  if (rot) {
+  if (lead) {
     const Phase* pp = a.phase_tab + int64_t(g.z) * (D / 2) + j * EPV;
 #pragma unroll
     for (int e = 0; e < EPV; ++e) ph[e] = pp[e];
   }
+  const uint64_t leaders = __builtin_amdgcn_ballot_w64(lead && j == 0);
   const int p0 = a.plane_begin + pgrp * a.planes_per_block;
   const int p1 = min(p0 + a.planes_per_block, a.plane_end);
   const int64_t plane_stride = int64_t(a.page_tokens) * RB;  // one (layer, K/V, head) run
@@ -301,6 +314,23 @@ __global__ __launch_bounds__(256) void gather_kernel(GatherArgs a) {
       if (VALUES) {
         v0[q] = ld16(vs + j * 16);
         v1[q] = ld16(vs + RB / 2 + j * 16);
+      }
+    }
+    if (pl == p0 && leaders != 0) {
+      // leaders publish their phase rows; every rotating row takes its run's
+      // (one wave: LDS operations complete in order)
+      if (lead) {
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) ph_lds[wv][riw][j * EPV + e] = ph[e];
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      if (rot && !lead) {
+        const uint64_t below = leaders & ((uint64_t(2) << (riw * LPR)) - 1);
+        const int lr = (63 - __builtin_clzll(below)) / LPR;
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) ph[e] = ph_lds[wv][lr][j * EPV + e];
       }
     }
 #pragma unroll
