@@ -354,9 +354,10 @@ __global__ __launch_bounds__(256) void gather_kernel(GatherArgs a) {
 
 // Each token owns Hq query rows, Hkv key rows and Hkv value rows.  A group of
 // LPR lanes takes one token and kPrologueRows consecutive rows of it, so the
-// token's phases are loaded once per group and reused for every row.  The
-// phases, the rows and the token's position are requested together (nothing
-// waits on another load before its own loads are issued).
+// token's phases are loaded once per group and reused for every row (and
+// once per wave: the wave's other groups on the token read them from LDS).
+// The phases, the rows and the token's position are requested together
+// (nothing waits on another load before its own loads are issued).
 constexpr int kPrologueRows = 2;
 
 template <bool BF16, int D>
@@ -376,12 +377,24 @@ __global__ __launch_bounds__(256) void prologue_kernel(PrologueArgs a) {
   const int w1 = min(w0 + kPrologueRows, per_tok);
   const int pos = a.new_pos[u];
   const int row = a.new_row[u];
+  // A token's phase row is loaded once per wave: the first of the wave's
+  // lane groups on that token (a leader) loads it and hands it to the
+  // token's other groups through LDS.
+  constexpr int GPW = 64 / LPR;   // lane groups per wave
+  __shared__ Phase ph_lds[4][GPW][D / 2];
+  const int lane = threadIdx.x & 63;
+  const int wv = threadIdx.x >> 6;
+  const int giw = lane / LPR;
+  const int uprev = __shfl_up(u, LPR);
+  const bool needs = w0 < a.q_heads + a.kv_heads;
+  const bool lead = needs && (giw == 0 || uprev != u);
   Phase ph[EPV];
-  if (w0 < a.q_heads + a.kv_heads) {
+  if (lead) {
     const Phase* pp = a.phase_new + int64_t(u) * (D / 2) + j * EPV;
 #pragma unroll
     for (int e = 0; e < EPV; ++e) ph[e] = pp[e];
   }
+  const uint64_t leaders = __builtin_amdgcn_ballot_w64(lead && j == 0);
   const bool rot_tok = pos != 0;
   // issue every row's loads before any rotation or store
   u32x4 x0[kPrologueRows], x1[kPrologueRows];
@@ -410,6 +423,21 @@ __global__ __launch_bounds__(256) void prologue_kernel(PrologueArgs a) {
     }
     x0[i] = ld16(src + j * 16);
     x1[i] = ld16(src + RB / 2 + j * 16);
+  }
+  if (leaders != 0) {
+    if (lead) {
+#pragma unroll
+      for (int e = 0; e < EPV; ++e) ph_lds[wv][giw][j * EPV + e] = ph[e];
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    if (needs && !lead) {
+      const uint64_t below = leaders & ((uint64_t(2) << (giw * LPR)) - 1);
+      const int lg = (63 - __builtin_clzll(below)) / LPR;
+#pragma unroll
+      for (int e = 0; e < EPV; ++e) ph[e] = ph_lds[wv][lg][j * EPV + e];
+    }
   }
 #pragma unroll
   for (int i = 0; i < kPrologueRows; ++i) {
